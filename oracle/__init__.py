@@ -1,0 +1,171 @@
+"""CPU oracle for paged-KV decode attention. TEST INFRASTRUCTURE ONLY.
+
+A thin ctypes wrapper over ``oracle.c`` (plain C, fp64). Only the tests, the
+smoke check and the benchmark's CPU-baseline leg may import this package; the
+HIP library never does, and this package never imports the HIP library.
+
+Arrays are NumPy arrays on the host. dtype codes follow the element type:
+``np.float32`` is fp32, ``np.uint16``/``np.int16`` hold bf16 bit patterns and
+``np.int8`` is the INT8 cache. Shapes:
+
+* q            [num_seqs][num_q_heads][head_dim]
+* k/v cache    [num_blocks][num_kv_heads][16][head_dim]
+* k/v scale    [num_blocks][num_kv_heads][16] float32 (INT8 cache only)
+* block_tables [num_seqs][max_blocks_per_seq] int32
+* context_lens [num_seqs] int32
+* slot_mapping [num_tokens] int64 (negative = skip)
+
+What each function computes, and which page it follows, is stated in
+``oracle.c``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BLOCK_SIZE = 16
+F32, BF16, I8 = 0, 1, 2
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_kv_write.argtypes = [P, P, I, P, L, I, I, P, P, P, P, L, I]
+        lib.oracle_kv_write.restype = I
+        lib.oracle_decode.argtypes = [P, I, I, P, P, P, P, I, I, I, P, I, P, D, P, P, L, P]
+        lib.oracle_decode.restype = None
+        lib.oracle_decode_split.argtypes = [P, I, I, I, P, P, P, P, I, I, I, P, I, P, D, I, I,
+                                            P, P, P]
+        lib.oracle_decode_split.restype = None
+        lib.oracle_merge.argtypes = [P, P, P, L, I, I, P]
+        lib.oracle_merge.restype = None
+        lib.oracle_num_splits.argtypes = [I, I]
+        lib.oracle_num_splits.restype = I
+        _lib = lib
+    return _lib
+
+
+def _code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype in (np.uint16, np.int16):
+        return BF16
+    if a.dtype == np.int8:
+        return I8
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if dtype is not None and a.dtype != dtype:
+        a = a.astype(dtype)
+    return np.ascontiguousarray(a)
+
+
+def num_splits(context_len: int, split_tokens: int) -> int:
+    return int(_load().oracle_num_splits(int(context_len), int(split_tokens)))
+
+
+def kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
+    """Write new K/V rows into the pool in place (k_cache etc. are modified)."""
+    k, v = _c(k), _c(v)
+    slot_mapping = _c(slot_mapping, np.int64)
+    for a in (k_cache, v_cache, k_scale, v_scale):
+        if a is not None and not a.flags.c_contiguous:
+            raise ValueError("cache arrays must be C-contiguous")
+    num_blocks, num_kv_heads, bs, head_dim = k_cache.shape
+    assert bs == BLOCK_SIZE and k.shape[1:] == (num_kv_heads, head_dim)
+    rc = _load().oracle_kv_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), k.shape[0],
+                                 num_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), num_blocks, _code(k_cache))
+    if rc != 0:
+        raise ValueError("oracle_kv_write rejected its arguments")
+
+
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    block_tables, context_lens = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, bs, hd = k_cache.shape
+    assert bs == BLOCK_SIZE and hd == head_dim and num_q_heads % num_kv_heads == 0
+    if _code(k_cache) == I8:
+        assert k_scale is not None and v_scale is not None
+    # Every block the definition will read must exist in the pool.
+    for s in range(num_seqs):
+        nb = -(-int(context_lens[s]) // BLOCK_SIZE)
+        assert nb <= block_tables.shape[1]
+        ids = block_tables[s, :nb]
+        assert (ids >= 0).all() and (ids < num_blocks).all()
+    return q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None,
+           rows=None):
+    """Decode attention by definition, in fp64.
+
+    rows: optional (seq_ids, head_ids) pair of equal-length int arrays; the
+    result is then [n_rows][head_dim]. Without rows it is [B][Hq][D].
+    """
+    q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
+    num_seqs, num_q_heads, head_dim = q.shape
+    if rows is None:
+        seq_ids = np.repeat(np.arange(num_seqs, dtype=np.int32), num_q_heads)
+        head_ids = np.tile(np.arange(num_q_heads, dtype=np.int32), num_seqs)
+    else:
+        seq_ids, head_ids = _c(rows[0], np.int32), _c(rows[1], np.int32)
+    out = np.zeros((len(seq_ids), head_dim), dtype=np.float64)
+    _load().oracle_decode(_ptr(q), _code(q), num_q_heads, _ptr(k_cache), _ptr(v_cache),
+                          _ptr(k_scale), _ptr(v_scale), _code(k_cache), k_cache.shape[1],
+                          head_dim, _ptr(block_tables), block_tables.shape[1],
+                          _ptr(context_lens), float(scale), _ptr(seq_ids), _ptr(head_ids),
+                          len(seq_ids), _ptr(out))
+    if rows is None:
+        out = out.reshape(num_seqs, num_q_heads, head_dim)
+    return out
+
+
+def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, split_tokens,
+                 max_splits=None, k_scale=None, v_scale=None):
+    """Split-K partials (m, l, acc) in fp64; acc is not divided by l."""
+    q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
+    num_seqs, num_q_heads, head_dim = q.shape
+    if max_splits is None:
+        max_splits = max(num_splits(int(L), split_tokens) for L in context_lens)
+    m = np.zeros((num_seqs, num_q_heads, max_splits), dtype=np.float64)
+    l = np.zeros_like(m)
+    acc = np.zeros((num_seqs, num_q_heads, max_splits, head_dim), dtype=np.float64)
+    _load().oracle_decode_split(_ptr(q), _code(q), num_seqs, num_q_heads, _ptr(k_cache),
+                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _code(k_cache),
+                                k_cache.shape[1], head_dim, _ptr(block_tables),
+                                block_tables.shape[1], _ptr(context_lens), float(scale),
+                                int(split_tokens), int(max_splits), _ptr(m), _ptr(l), _ptr(acc))
+    return m, l, acc
+
+
+def merge(m, l, acc):
+    """Reduce split partials to the attention output, in fp64."""
+    m, l, acc = _c(m, np.float64), _c(l, np.float64), _c(acc, np.float64)
+    max_splits, head_dim = acc.shape[-2], acc.shape[-1]
+    lead = m.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.zeros(lead + (head_dim,), dtype=np.float64)
+    _load().oracle_merge(_ptr(m), _ptr(l), _ptr(acc), rows, max_splits, head_dim, _ptr(out))
+    return out

@@ -1,0 +1,302 @@
+/*
+ * Reference oracle for paged-KV decode attention. TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, obviously correct CPU definition that the HIP
+ * library is checked against. It shares no code, header, table or helper with
+ * the GPU path and is never linked into it. Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call it.
+ *
+ * Sources (the pages this follows):
+ *   [Primer 8.1]  "LLM Primer VI, chapter 8: next-generation KV memory
+ *                 management", section 8.1 "PagedAttention is virtual memory for
+ *                 KV": KV is cut into fixed blocks of (usually) 16 tokens held in
+ *                 one flat physical pool; a per-sequence block table maps logical
+ *                 positions to physical block ids; the attention kernel takes the
+ *                 table as an extra input and gathers K and V through it.
+ *   [ATOM 5.1]    "AMD ATOM Inference Engine" article, section 5.1 (BlockManager):
+ *                 16-token blocks by default, one block_table per Sequence.
+ *   [Echo 2]      "EchoLLMServing inference framework notes", section 2,
+ *                 "PagedAttention (V1 -> V2)" and "FlashDecoding": online softmax
+ *                 over blocks of the context; split-K over the context where
+ *                 each split leaves temporaries (m, l, acc) and a second reduce
+ *                 kernel merges them.
+ *   [Echo 3]      same notes, section 3, "KV Cache INT8 quantisation": INT8
+ *                 cache with per-token scales, dequantised right after loading.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   - cache layout [num_blocks][num_kv_heads][16][head_dim]; physical slot of
+ *     token t of sequence s is block_tables[s][t/16]*16 + t%16; a negative
+ *     slot in slot_mapping means "skip";
+ *   - grouped-query heads: query head h reads KV head h / (Hq/Hkv);
+ *   - logits are scale * q.k with a natural-exponent softmax over all tokens
+ *     t < context_len (the token written this step included);
+ *   - context_len 0 gives a zero output and empty partials (m=-inf, l=0, acc=0);
+ *   - split j of a sequence holds tokens [j*T, min((j+1)*T, L)), T =
+ *     split_tokens, and there are max(1, ceil(L/T)) splits;
+ *   - partials: m = max logit of the split, l = sum exp(z - m), acc =
+ *     sum exp(z - m) * v, NOT divided by l;
+ *   - INT8 quantiser per (token, KV head): a = max |x| in fp32, sc = a/127 (IEEE
+ *     fp32 divide), q = clamp(round-half-even(x/sc), -127, 127), a = 0 -> q = 0;
+ *     its input is the bf16/fp32 source widened exactly to fp32.
+ *
+ * Floating point: every attention quantity is computed in double. Build with
+ * -ffp-contract=off and without -ffast-math (the INT8 quantiser relies on IEEE
+ * fp32 division and the default round-to-nearest-even mode).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_BLOCK = 16 };
+
+/* bf16 is the top half of an IEEE binary32: widening is a 16-bit shift. */
+static float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Element idx of an array of `dtype` values, widened exactly to double. */
+static double load_elem(const void *base, int dtype, int64_t idx) {
+  if (dtype == OR_F32) return (double)((const float *)base)[idx];
+  if (dtype == OR_BF16) return (double)bf16_bits_to_float(((const uint16_t *)base)[idx]);
+  return (double)((const int8_t *)base)[idx];
+}
+
+/* Element idx of an fp32 or bf16 array, widened exactly to float. */
+static float load_elem_f32(const void *base, int dtype, int64_t idx) {
+  if (dtype == OR_F32) return ((const float *)base)[idx];
+  return bf16_bits_to_float(((const uint16_t *)base)[idx]);
+}
+
+static size_t dtype_size(int dtype) { return dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : 1; }
+
+/* Flat index of element d of (block b, kv head h, offset o) in the pool. */
+static int64_t cache_index(int64_t b, int h, int o, int d, int num_kv_heads, int head_dim) {
+  return ((b * num_kv_heads + h) * OR_BLOCK + o) * (int64_t)head_dim + d;
+}
+
+/* Flat index of the per-token scale of (block b, kv head h, offset o). */
+static int64_t scale_index(int64_t b, int h, int o, int num_kv_heads) {
+  return (b * num_kv_heads + h) * OR_BLOCK + o;
+}
+
+/* INT8 quantiser of one row of head_dim values [Echo 3]. */
+static void quantise_row(const void *src, int src_dtype, int64_t row_off, int head_dim,
+                         int8_t *dst, float *scale_out) {
+  float a = 0.0f;
+  for (int d = 0; d < head_dim; ++d) {
+    float ax = fabsf(load_elem_f32(src, src_dtype, row_off + d));
+    if (ax > a) a = ax;
+  }
+  float sc = a / 127.0f;
+  for (int d = 0; d < head_dim; ++d) {
+    if (a == 0.0f) {
+      dst[d] = 0;
+      continue;
+    }
+    float x = load_elem_f32(src, src_dtype, row_off + d);
+    float r = rintf(x / sc); /* default rounding mode: ties to even */
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    dst[d] = (int8_t)r;
+  }
+  *scale_out = sc;
+}
+
+/*
+ * KV write ("reshape and cache"): each new token's K and V rows go to the
+ * physical slot slot_mapping[t] of the pool [ATOM 5.1, Primer 8.1].
+ *   k, v        [num_tokens][num_kv_heads][head_dim] of in_dtype (0 fp32, 1 bf16)
+ *   k_cache,... [num_blocks][num_kv_heads][16][head_dim] of cache_dtype
+ *   k_scale,... [num_blocks][num_kv_heads][16] fp32, used when cache_dtype is INT8
+ * Non-INT8 caches need in_dtype == cache_dtype and receive an exact copy.
+ * Returns 0, or -1 on an unsupported combination or a slot outside the pool.
+ */
+int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *slot_mapping,
+                    int64_t num_tokens, int num_kv_heads, int head_dim, void *k_cache,
+                    void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
+                    int cache_dtype) {
+  if (in_dtype != OR_F32 && in_dtype != OR_BF16) return -1;
+  if (cache_dtype != OR_I8 && cache_dtype != in_dtype) return -1;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t b = slot / OR_BLOCK;
+    int o = (int)(slot % OR_BLOCK);
+    if (b >= num_blocks) return -1;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      int64_t src_off = (t * num_kv_heads + h) * (int64_t)head_dim;
+      int64_t dst_off = cache_index(b, h, o, 0, num_kv_heads, head_dim);
+      if (cache_dtype == OR_I8) {
+        int64_t si = scale_index(b, h, o, num_kv_heads);
+        quantise_row(k, in_dtype, src_off, head_dim, (int8_t *)k_cache + dst_off, &k_scale[si]);
+        quantise_row(v, in_dtype, src_off, head_dim, (int8_t *)v_cache + dst_off, &v_scale[si]);
+      } else {
+        size_t es = dtype_size(cache_dtype);
+        memcpy((char *)k_cache + dst_off * es, (const char *)k + src_off * es, es * head_dim);
+        memcpy((char *)v_cache + dst_off * es, (const char *)v + src_off * es, es * head_dim);
+      }
+    }
+  }
+  return 0;
+}
+
+/* Everything the decode definition reads. */
+typedef struct {
+  const void *q;          /* [num_seqs][num_q_heads][head_dim] of q_dtype */
+  int q_dtype, num_q_heads;
+  const void *k, *v;      /* pool, [num_blocks][num_kv_heads][16][head_dim] */
+  const float *k_scale, *v_scale; /* [num_blocks][num_kv_heads][16], INT8 only */
+  int cache_dtype, num_kv_heads, head_dim;
+  const int32_t *block_tables; /* [num_seqs][max_blocks_per_seq] */
+  int max_blocks_per_seq;
+  double scale;
+} decode_args;
+
+/* Dequantised element d of the K (which=0) or V (which=1) row of logical
+ * token t of sequence s in KV head kv, reached through the block table. */
+static double kv_elem(const decode_args *a, int which, int s, int kv, int t, int d) {
+  int64_t b = a->block_tables[(int64_t)s * a->max_blocks_per_seq + t / OR_BLOCK];
+  int o = t % OR_BLOCK;
+  const void *base = which ? a->v : a->k;
+  double x = load_elem(base, a->cache_dtype, cache_index(b, kv, o, d, a->num_kv_heads, a->head_dim));
+  if (a->cache_dtype == OR_I8) {
+    const float *sc = which ? a->v_scale : a->k_scale;
+    x *= (double)sc[scale_index(b, kv, o, a->num_kv_heads)];
+  }
+  return x;
+}
+
+/* Logit z_t = scale * q[s][h] . k_t. */
+static double logit(const decode_args *a, int s, int h, int t) {
+  int kv = h / (a->num_q_heads / a->num_kv_heads);
+  double dot = 0.0;
+  for (int d = 0; d < a->head_dim; ++d) {
+    double qd = load_elem(a->q, a->q_dtype, ((int64_t)s * a->num_q_heads + h) * a->head_dim + d);
+    dot += qd * kv_elem(a, 0, s, kv, t, d);
+  }
+  return a->scale * dot;
+}
+
+/* Softmax-weighted sums over tokens [t0, t1) of sequence s, head h, taken
+ * relative to the maximum logit of that range:
+ *   *m = max z_t,  *l = sum exp(z_t - m),  acc[d] = sum exp(z_t - m) v_t[d].
+ * An empty range gives m = -inf, l = 0, acc = 0. */
+static void weighted_sums(const decode_args *a, int s, int h, int t0, int t1, double *m,
+                          double *l, double *acc) {
+  int kv = h / (a->num_q_heads / a->num_kv_heads);
+  for (int d = 0; d < a->head_dim; ++d) acc[d] = 0.0;
+  *l = 0.0;
+  *m = -INFINITY;
+  if (t1 <= t0) return;
+  double *z = (double *)malloc(sizeof(double) * (size_t)(t1 - t0));
+  double mx = -INFINITY;
+  for (int t = t0; t < t1; ++t) {
+    z[t - t0] = logit(a, s, h, t);
+    if (z[t - t0] > mx) mx = z[t - t0];
+  }
+  double sum = 0.0;
+  for (int t = t0; t < t1; ++t) {
+    double w = exp(z[t - t0] - mx);
+    sum += w;
+    for (int d = 0; d < a->head_dim; ++d) acc[d] += w * kv_elem(a, 1, s, kv, t, d);
+  }
+  free(z);
+  *m = mx;
+  *l = sum;
+}
+
+/*
+ * Decode attention by definition [Primer 8.1, Echo 2]: for each requested
+ * (sequence, query head) row,
+ *   out = sum_t softmax_t(scale * q.k_t) v_t   over t < context_lens[s],
+ * with K and V gathered token by token through the block table and the whole
+ * context taken at once (no splitting). Rows are given as index lists so that
+ * a caller can check a sample of a large batch; out is [n_rows][head_dim].
+ */
+void oracle_decode(const void *q, int q_dtype, int num_q_heads, const void *k_cache,
+                   const void *v_cache, const float *k_scale, const float *v_scale,
+                   int cache_dtype, int num_kv_heads, int head_dim,
+                   const int32_t *block_tables, int max_blocks_per_seq,
+                   const int32_t *context_lens, double scale, const int32_t *row_seq,
+                   const int32_t *row_head, int64_t n_rows, double *out) {
+  decode_args a = {q, q_dtype, num_q_heads, k_cache, v_cache, k_scale, v_scale, cache_dtype,
+                   num_kv_heads, head_dim, block_tables, max_blocks_per_seq, scale};
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int s = row_seq[r], h = row_head[r];
+    double m, l;
+    double *o = out + r * head_dim;
+    weighted_sums(&a, s, h, 0, context_lens[s], &m, &l, o);
+    for (int d = 0; d < head_dim; ++d) o[d] = l > 0.0 ? o[d] / l : 0.0;
+  }
+}
+
+/* Number of splits of a context of length L: max(1, ceil(L / split_tokens)). */
+int oracle_num_splits(int context_len, int split_tokens) {
+  int n = (context_len + split_tokens - 1) / split_tokens;
+  return n < 1 ? 1 : n;
+}
+
+/*
+ * Split-K partials [Echo 2, FlashDecoding]: split j of sequence s covers
+ * tokens [j*split_tokens, min((j+1)*split_tokens, L)) and yields (m_j, l_j,
+ * acc_j) as defined for weighted_sums. Splits j >= num_splits(L) are empty.
+ * Layout: m, l [num_seqs][num_q_heads][max_splits];
+ *         acc  [num_seqs][num_q_heads][max_splits][head_dim].
+ */
+void oracle_decode_split(const void *q, int q_dtype, int num_seqs, int num_q_heads,
+                         const void *k_cache, const void *v_cache, const float *k_scale,
+                         const float *v_scale, int cache_dtype, int num_kv_heads, int head_dim,
+                         const int32_t *block_tables, int max_blocks_per_seq,
+                         const int32_t *context_lens, double scale, int split_tokens,
+                         int max_splits, double *m, double *l, double *acc) {
+  decode_args a = {q, q_dtype, num_q_heads, k_cache, v_cache, k_scale, v_scale, cache_dtype,
+                   num_kv_heads, head_dim, block_tables, max_blocks_per_seq, scale};
+  int64_t jobs = (int64_t)num_seqs * num_q_heads * max_splits;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < jobs; ++r) {
+    int j = (int)(r % max_splits);
+    int s = (int)(r / max_splits / num_q_heads);
+    int h = (int)(r / max_splits % num_q_heads);
+    int L = context_lens[s];
+    int t0 = j * split_tokens;
+    int t1 = t0 + split_tokens < L ? t0 + split_tokens : L;
+    if (j >= oracle_num_splits(L, split_tokens)) t1 = t0; /* empty split */
+    weighted_sums(&a, s, h, t0, t1, &m[r], &l[r], acc + r * head_dim);
+  }
+}
+
+/*
+ * Reduce of split partials [Echo 2, FlashDecoding]: with M = max_j m_j over
+ * non-empty splits and w_j = exp(m_j - M),
+ *   out = sum_j w_j acc_j / sum_j w_j l_j.
+ * Empty splits (l_j == 0) are skipped; no non-empty split gives out = 0.
+ * Layouts as for oracle_decode_split; out is [num_rows][head_dim] where a row is
+ * one (sequence, head) pair, num_rows = num_seqs * num_q_heads.
+ */
+void oracle_merge(const double *m, const double *l, const double *acc, int64_t num_rows,
+                  int max_splits, int head_dim, double *out) {
+  for (int64_t r = 0; r < num_rows; ++r) {
+    const double *mr = m + r * max_splits, *lr = l + r * max_splits;
+    double M = -INFINITY;
+    for (int j = 0; j < max_splits; ++j)
+      if (lr[j] > 0.0 && mr[j] > M) M = mr[j];
+    double den = 0.0;
+    double *o = out + r * head_dim;
+    for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+    for (int j = 0; j < max_splits; ++j) {
+      if (!(lr[j] > 0.0)) continue;
+      double w = exp(mr[j] - M);
+      den += w * lr[j];
+      const double *aj = acc + (r * max_splits + j) * head_dim;
+      for (int d = 0; d < head_dim; ++d) o[d] += w * aj[d];
+    }
+    for (int d = 0; d < head_dim; ++d) o[d] = den > 0.0 ? o[d] / den : 0.0;
+  }
+}
