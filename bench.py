@@ -1,0 +1,238 @@
+"""Benchmark of the paged-KV decode hot path on one MI355X.
+
+One step = one decode step of one attention layer over a synthetic batch:
+write the new token of every sequence into the pool (paged_kv_write), the
+split-K decode kernel, and the reduce kernel. Inputs are resident in HBM
+before the timed region starts.
+
+Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
+head_dim 128, block 16, context lengths uniform in [512, 4096], random
+non-contiguous block tables over a pool of 1.1x the tokens).
+
+Prints ONE JSON line. `value` is tokens/s for the whole step (B / t_step);
+the split kernel's roofline uses its own average duration measured with HIP
+events on the launch stream in a second pass with identical launches.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode attention tokens/s and achieved KV-read GB/s (% of HBM peak), 1 MI355X")
+HBM_PEAK_GBPS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_llama8b_bf16_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_bf16")
+    ap.add_argument("--split-tokens", type=int, default=0, help="0: library default")
+    ap.add_argument("--contiguous-tables", action="store_true",
+                    help="blocks in logical order (contiguous-slice layout)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--seed", type=int, default=1)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_52_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "pagedattn.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(b):
+    """Bytes the split kernel must read by definition: every attended token's
+    K and V rows (plus INT8 scales), q, and the block-table entries used."""
+    import workloads
+    L = b.context_lens.to("cpu").long()
+    w = b.workload
+    per_token = workloads.kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.cache_dtype)
+    kv = int(L.sum()) * per_token
+    q = b.q.numel() * b.q.element_size()
+    tables = int(((L + 15) // 16).sum()) * 4 + L.numel() * 4
+    return kv, kv + q + tables
+
+
+def cpu_baseline(b, seconds):
+    """Time the oracle on a bounded sample of the same batch: whole sequences
+    (all heads) in order until about `seconds` of CPU time have passed."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    q, kc, vc = host(b.q), host(b.k_cache), host(b.v_cache)
+    ks = None if b.k_scale is None else host(b.k_scale)
+    vs = None if b.v_scale is None else host(b.v_scale)
+    bt, cl = host(b.block_tables), host(b.context_lens)
+    B, Hq = q.shape[:2]
+    h = np.arange(Hq, dtype=np.int32)
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    elapsed = 0.0
+    # Whole sequences in batch order, wrapping around, until the time budget.
+    while elapsed < seconds:
+        s = done % B
+        oracle.decode(q, kc, vc, bt, cl, b.scale, ks, vs, rows=(np.full(Hq, s, np.int32), h))
+        tokens += int(cl[s])
+        done += 1
+        elapsed = time.perf_counter() - t0
+    return {
+        "value": done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{done} sequence decodes ({done / B:.2f} passes over the {B}-sequence "
+                  f"batch, all {Hq} q heads, {tokens} context tokens), fp64 block-table "
+                  f"walk, {elapsed:.1f} s",
+    }
+
+
+def load_counters():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X and "
+              "this build has no multi-GPU leg (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_52_amd as pa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b = workloads.make_batch(args.workload, args.seed, dev,
+                             contiguous_tables=args.contiguous_tables)
+    w = b.workload
+    if b.k_cache.dtype == torch.int8:
+        pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
+                          b.v_scale)
+        b.fill_k = b.fill_v = None
+    B, Hq, D = b.q.shape
+    T = args.split_tokens or pa.default_split_tokens(B, w.num_kv_heads, b.max_context_len)
+    S = pa.num_splits(b.max_context_len, T)
+    out = torch.empty_like(b.q)
+    parts = pa.Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
+                        l=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
+                        acc=torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev),
+                        context_lens=b.context_lens, split_tokens=T)
+    stream = torch.cuda.current_stream(dev)
+
+    def write():
+        pa.paged_kv_write(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale,
+                          b.v_scale)
+
+    def decode():
+        pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                     b.scale, b.k_scale, b.v_scale,
+                                     max_context_len=b.max_context_len, split_tokens=T,
+                                     partials=parts)
+
+    def reduce():
+        pa.paged_attn_reduce(parts, out)
+
+    for _ in range(args.warmup):
+        write(); decode(); reduce()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` whole steps.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        write(); decode(); reduce()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel durations: identical launches with events between them.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream); write()
+        e[1].record(stream); decode()
+        e[2].record(stream); reduce()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_write = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_red = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    kv_bytes, alg_bytes = algorithmic_bytes(b)
+    dec_gbps = alg_bytes / (t_dec * 1e-3) / 1e9
+    kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
+    counters = load_counters()
+    traffic = None
+    if counters is not None:
+        traffic = counters["fetch_bytes_per_launch"] + counters["write_bytes_per_launch"]
+
+    line = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16"}[w.dtype] + ("+i8kv" if w.cache_dtype == "int8" else ""),
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": B, "q_heads": Hq, "kv_heads": w.num_kv_heads,
+            "head_dim": D, "block_size": 16, "cache_dtype": w.cache_dtype,
+            "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
+            "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
+            "tables": "contiguous" if args.contiguous_tables else "permuted",
+            "seed": args.seed,
+        },
+        "kv_read_gbps": kv_gbps_step,
+        "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
+        "decode_reduce_tokens_per_s": B / ((t_dec + t_red) * 1e-3),
+        "kernel_ms": {"kv_write": t_write, "decode_split": t_dec, "reduce": t_red},
+        "roofline": {
+            "kernel": "decode_split_kernel", "bound": "hbm", "achieved": dec_gbps,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": alg_bytes, "traffic": traffic,
+        },
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * libpagedattn: decode-phase attention over a paged KV cache, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes (the pages it follows):
+ *   - "LLM Primer VI, chapter 8", section 8.1 (PagedAttention is virtual memory
+ *     for KV): the KV cache is one flat pool of fixed 16-token blocks; each
+ *     sequence owns a block table that maps its logical positions to physical
+ *     block ids; attention takes the table as an extra input and gathers K and
+ *     V through it.
+ *   - "AMD ATOM Inference Engine" article, section 5.1 (BlockManager): blocks of
+ *     16 tokens; new tokens are written into the KV cache before attention runs.
+ *   - "EchoLLMServing inference framework notes", section 2 (PagedAttention
+ *     V1 -> V2, FlashDecoding): online softmax over blocks of the context,
+ *     split-K over the context with per-split temporaries (m, l, acc) merged by
+ *     a second reduce kernel, and a split count that follows the context length
+ *     (split_num = context_len / chunk, chunk 256 or 512 from profiling);
+ *     section 3 (KV Cache INT8): INT8 cache with per-token scales, dequantised
+ *     inside the attention kernel right after loading.
+ *
+ * Conventions shared by every entry point:
+ *   - Pool layout: k_cache, v_cache are [num_blocks][num_kv_heads][16][head_dim]
+ *     of the cache dtype, so one (block, KV head) tile is 16*head_dim contiguous
+ *     elements. INT8 pools carry k_scale, v_scale [num_blocks][num_kv_heads][16]
+ *     fp32, one scale per (token, KV head).
+ *   - Token t of sequence s lives in block block_tables[s][t / 16], row t % 16.
+ *     A slot is block * 16 + row.
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - Logits are scale * q.k; softmax uses the natural exponent over every
+ *     token t < context_lens[s]. context_lens[s] == 0 gives a zero output.
+ *   - Split j of sequence s covers tokens [j*T, min((j+1)*T, L)), T =
+ *     split_tokens (a positive multiple of 16, at most 4096), and a sequence of
+ *     length L has max(1, ceil(L / T)) splits.
+ *   - Partials: m[s][h][j] is the split's maximum logit (natural-log units),
+ *     l[s][h][j] = sum exp(z - m), acc[s][h][j][:] = sum exp(z - m) v (not
+ *     divided by l). A split with no tokens stores m = -inf, l = 0, acc = 0.
+ *     Entries for j >= max(1, ceil(L / T)) are not written.
+ *   - Pointers: every array argument is a device pointer owned by the caller;
+ *     the library never allocates, frees or synchronises. q, k/v, k_cache,
+ *     v_cache must be 16-byte aligned and contiguous in the layouts above.
+ *   - Streams: work is enqueued on `stream` and nothing else, so a call can be
+ *     captured in a HIP graph.
+ *   - Errors: host-detectable problems return a negative PA_ERR_* code before
+ *     anything is enqueued; a failed launch returns PA_ERR_LAUNCH. Device data
+ *     is trusted for meaning but never read out of bounds: context lengths are
+ *     clamped to [0, min(max_context_len, 16 * max_blocks_per_seq)], block ids
+ *     to [0, num_blocks), and slots outside the pool are skipped, so bad data
+ *     gives unspecified results, not memory faults.
+ *   - Thread safety: the library keeps no mutable global state.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+#define PA_MAX_SPLIT_TOKENS 4096
+
+/* Element types. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+
+/* Status codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,      /* a required pointer is NULL */
+  PA_ERR_DTYPE = -2,     /* unsupported dtype or dtype combination */
+  PA_ERR_SHAPE = -3,     /* unsupported sizes (head_dim, head counts, ...) */
+  PA_ERR_SPLIT = -4,     /* bad split_tokens, or max_splits below what is needed */
+  PA_ERR_WORKSPACE = -5, /* workspace smaller than pa_workspace_bytes() */
+  PA_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned */
+  PA_ERR_LAUNCH = -7     /* the kernel launch failed */
+};
+
+/* Human-readable text for a status code (static storage). */
+const char *pa_strerror(int status);
+
+/* Number of splits for a context of length context_len:
+ * max(1, ceil(context_len / split_tokens)); 0 if split_tokens <= 0.
+ * [EchoLLMServing notes, section 2, FlashDecoding split heuristic.] */
+int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
+
+/* Split size (tokens, a multiple of 16) the library picks when the caller
+ * passes split_tokens = 0: the chunk is tuned on MI355X for the batch shape.
+ * Host-only arithmetic. */
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
+
+/* Bytes of workspace paged_attn_decode needs for the partials (m, l, acc). */
+size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                          int32_t max_splits);
+
+/*
+ * KV write ("reshape and cache") [ATOM article 5.1; Primer 8.1]: for every
+ * token t < num_tokens with slot = slot_mapping[t] >= 0, copy k[t][h][:] and
+ * v[t][h][:] into row slot % 16 of block slot / 16 for every KV head h.
+ *   k, v          [num_tokens][num_kv_heads][head_dim] of in_dtype (PA_F32/PA_BF16)
+ *   slot_mapping  [num_tokens] int64; negative entries are skipped
+ *   k_cache, ...  pool of cache_dtype. cache_dtype == in_dtype: exact copy.
+ *                 cache_dtype == PA_I8 [EchoLLMServing notes, section 3]: per
+ *                 (token, head) a = max|x| (x widened to fp32), scale = a/127
+ *                 (IEEE fp32 division), code = clamp(rint_half_even(x/scale),
+ *                 -127, 127), a == 0 gives scale 0 and codes 0; the scale goes
+ *                 to k_scale / v_scale (required for PA_I8, ignored otherwise).
+ *   head_dim      64 or 128.
+ * Duplicate slots in one call race (unspecified winner). Writing into a block
+ * shared by several sequences is the caller's decision.
+ */
+int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
+                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void *k_cache,
+                   void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
+                   int32_t cache_dtype, hipStream_t stream);
+
+/*
+ * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
+ * s, query head h and split j < max(1, ceil(L_s / T)), write the partials
+ * (m, l, acc) of that split. One launch covers the batch; the g = Hq/Hkv query
+ * heads of a KV head share every K/V load.
+ *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (PA_F32/PA_BF16)
+ *   k_cache, ...   pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
+ *                  (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and
+ *                  v_scale required). num_blocks < 2^31.
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32
+ *   context_lens   [num_seqs] int32, each <= max_context_len
+ *   max_context_len  host bound on context_lens, sizes the launch grid
+ *   scale          logit scale (commonly 1/sqrt(head_dim))
+ *   split_tokens   T, a positive multiple of 16 <= 4096, or 0 for
+ *                  pa_default_split_tokens()
+ *   max_splits     leading stride of the partials; >= pa_num_splits(max_context_len, T)
+ *   part_m, part_l [num_seqs][num_q_heads][max_splits] fp32
+ *   part_acc       [num_seqs][num_q_heads][max_splits][head_dim] fp32
+ * head_dim must be 64 or 128 and num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16.
+ */
+int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t head_dim, const void *k_cache,
+                              const void *v_cache, const float *k_scale, const float *v_scale,
+                              int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
+                              const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t max_context_len, float scale,
+                              int32_t split_tokens, int32_t max_splits, float *part_m,
+                              float *part_l, float *part_acc, hipStream_t stream);
+
+/*
+ * Reduce kernel [EchoLLMServing notes, section 2]: merge the partials of every
+ * (sequence, query head) over its splits j < max(1, ceil(L_s / T)):
+ *   M = max_j m_j over splits with l_j > 0, w_j = exp(m_j - M),
+ *   out = sum_j w_j acc_j / sum_j w_j l_j   (0 when no split holds a token),
+ * written as out_dtype (PA_F32, or PA_BF16 rounded to nearest even).
+ *   part_*        as written by paged_attn_decode_partial with the same
+ *                 split_tokens (T > 0) and max_splits
+ *   context_lens  [num_seqs] int32 (lengths are clamped to >= 0)
+ *   out           [num_seqs][num_q_heads][head_dim]
+ */
+int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, int32_t split_tokens, int32_t max_splits, void *out,
+                      int32_t out_dtype, hipStream_t stream);
+
+/*
+ * Whole decode step of one attention layer: paged_attn_decode_partial into
+ * the caller's workspace, then paged_attn_reduce into out (dtype = q_dtype).
+ * The split count is pa_num_splits(max_context_len, T) with T = split_tokens
+ * (0: pa_default_split_tokens()). workspace must hold
+ * pa_workspace_bytes(num_seqs, num_q_heads, head_dim, that split count)
+ * bytes, 256-byte aligned.
+ */
+int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, const void *k_cache, const void *v_cache,
+                      const float *k_scale, const float *v_scale, int32_t cache_dtype,
+                      int64_t num_blocks, int32_t num_kv_heads, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, int32_t split_tokens, void *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

@@ -50,6 +50,8 @@ def _load():
         lib.oracle_merge.restype = None
         lib.oracle_num_splits.argtypes = [I, I]
         lib.oracle_num_splits.restype = I
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = I
         _lib = lib
     return _lib
 
@@ -75,6 +77,11 @@ def _c(a, dtype=None):
     if dtype is not None and a.dtype != dtype:
         a = a.astype(dtype)
     return np.ascontiguousarray(a)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def num_splits(context_len: int, split_tokens: int) -> int:

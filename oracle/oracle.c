@@ -45,6 +45,7 @@
  * fp32 division and the default round-to-nearest-even mode).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -300,3 +301,6 @@ void oracle_merge(const double *m, const double *l, const double *acc, int64_t n
     for (int d = 0; d < head_dim; ++d) o[d] = den > 0.0 ? o[d] / den : 0.0;
   }
 }
+
+/* Threads the OpenMP loops above use (reported with the CPU baseline). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,203 @@
+"""Paged-KV decode attention for MI355X: Python binding of libpagedattn.
+
+Every function here only checks and marshals arguments (torch tensors ->
+device pointers, torch's current stream) and calls the C ABI declared in
+include/pagedattn.h; all arithmetic runs in the library's HIP kernels. The
+library must be built (``__graft_entry__.build()``); there is no fallback.
+
+Tensor layouts (block size 16):
+
+* q, out          [num_seqs][num_q_heads][head_dim], fp32 or bf16
+* k_cache, v_cache [num_blocks][num_kv_heads][16][head_dim], fp32/bf16/int8
+* k_scale, v_scale [num_blocks][num_kv_heads][16] fp32 (int8 caches only)
+* block_tables    [num_seqs][max_blocks_per_seq] int32
+* context_lens    [num_seqs] int32
+* slot_mapping    [num_tokens] int64 (negative = skip)
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+BLOCK_SIZE = 16
+PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+_DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+
+
+class PagedAttnError(RuntimeError):
+    pass
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = _lib.load().pa_strerror(status).decode()
+        raise PagedAttnError(f"libpagedattn status {status}: {msg}")
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODES[t.dtype]
+    except KeyError:
+        raise PagedAttnError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PagedAttnError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise PagedAttnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PagedAttnError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def num_splits(context_len: int, split_tokens: int) -> int:
+    """max(1, ceil(context_len / split_tokens))."""
+    return int(_lib.load().pa_num_splits(int(context_len), int(split_tokens)))
+
+
+def default_split_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int) -> int:
+    return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len))
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_splits: int) -> int:
+    return int(_lib.load().pa_workspace_bytes(num_seqs, num_q_heads, head_dim, max_splits))
+
+
+def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None) -> None:
+    """Write one step's new K/V rows into the pool at their slots (in place)."""
+    T, Hkv, D = k.shape
+    NB = k_cache.shape[0]
+    if k_cache.shape != (NB, Hkv, BLOCK_SIZE, D) or v_cache.shape != k_cache.shape:
+        raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
+    if v.shape != k.shape or slot_mapping.shape != (T,):
+        raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
+    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    for sc in (k_scale, v_scale):
+        if sc is not None and sc.shape != (NB, Hkv, BLOCK_SIZE):
+            raise PagedAttnError("scales must be [num_blocks][num_kv_heads][16]")
+    lib = _lib.load()
+    _check(lib.paged_kv_write(
+        _dev(k, "k"), _dev(v, "v", k.dtype), _code(k), _dev(slot_mapping, "slot_mapping",
+                                                            torch.int64),
+        T, Hkv, D, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32), NB,
+        _code(k_cache), _stream(k.device)))
+
+
+@dataclasses.dataclass
+class Partials:
+    """Split-K partials of one decode call (see paged_attn_decode_partial)."""
+    m: torch.Tensor             # [B][Hq][max_splits] fp32, natural-log units
+    l: torch.Tensor             # [B][Hq][max_splits] fp32
+    acc: torch.Tensor           # [B][Hq][max_splits][D] fp32, not divided by l
+    context_lens: torch.Tensor  # [B] int32
+    split_tokens: int
+
+    @property
+    def max_splits(self) -> int:
+        return self.m.shape[-1]
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if bs != BLOCK_SIZE or Dk != D or v_cache.shape != k_cache.shape:
+        raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise PagedAttnError("block_tables must be [B][max_blocks], context_lens [B]")
+    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    return (_dev(q, "q"), _code(q), B, Hq, D, _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
+            _dev(v_scale, "v_scale", torch.float32), _code(k_cache), NB, Hkv,
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32))
+
+
+def _max_len(context_lens, max_context_len):
+    # Passing max_context_len avoids a device->host sync (and keeps the call
+    # capturable in a graph).
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+    return int(max_context_len)
+
+
+def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
+                              k_scale=None, v_scale=None, *, max_context_len=None,
+                              split_tokens=None, partials: Optional[Partials] = None) -> Partials:
+    """Split kernel only: returns the per-split (m, l, acc)."""
+    lib = _lib.load()
+    B, Hq, D = q.shape
+    mcl = _max_len(context_lens, max_context_len)
+    T = int(split_tokens) if split_tokens else default_split_tokens(B, k_cache.shape[1], mcl)
+    S = max(1, num_splits(mcl, T))
+    if partials is None:
+        partials = Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
+                            l=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
+                            acc=torch.empty((B, Hq, S, D), dtype=torch.float32,
+                                            device=q.device),
+                            context_lens=context_lens, split_tokens=T)
+    else:
+        partials.context_lens, partials.split_tokens = context_lens, T
+    args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
+    _check(lib.paged_attn_decode_partial(
+        *args, mcl, float(scale), T, partials.max_splits, _dev(partials.m, "m", torch.float32),
+        _dev(partials.l, "l", torch.float32), _dev(partials.acc, "acc", torch.float32),
+        _stream(q.device)))
+    return partials
+
+
+def paged_attn_reduce(partials: Partials, out: torch.Tensor) -> torch.Tensor:
+    """Reduce kernel: merge the partials into out [B][Hq][D] (fp32 or bf16)."""
+    lib = _lib.load()
+    B, Hq, S = partials.m.shape
+    D = partials.acc.shape[-1]
+    if out.shape != (B, Hq, D):
+        raise PagedAttnError("out must be [B][Hq][D]")
+    _check(lib.paged_attn_reduce(
+        _dev(partials.m, "m", torch.float32), _dev(partials.l, "l", torch.float32),
+        _dev(partials.acc, "acc", torch.float32),
+        _dev(partials.context_lens, "context_lens", torch.int32), B, Hq, D,
+        partials.split_tokens, S, _dev(out, "out"), _code(out), _stream(out.device)))
+    return out
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                      k_scale=None, v_scale=None, *, max_context_len=None, split_tokens=None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Whole decode step: split kernel then reduce kernel, out in q's dtype."""
+    lib = _lib.load()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedAttnError("out must match q's shape and dtype")
+    mcl = _max_len(context_lens, max_context_len)
+    T = int(split_tokens) if split_tokens else default_split_tokens(B, k_cache.shape[1], mcl)
+    need = workspace_bytes(B, Hq, D, max(1, num_splits(mcl, T)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
+    _check(lib.paged_attn_decode(*args, mcl, float(scale), T, _dev(out, "out"),
+                                 _dev(workspace, "workspace"), workspace.numel(),
+                                 _stream(q.device)))
+    return out
+
+
+__all__ = [
+    "BLOCK_SIZE", "PagedAttnError", "Partials", "num_splits", "default_split_tokens",
+    "workspace_bytes", "paged_kv_write", "paged_attn_decode_partial", "paged_attn_reduce",
+    "paged_attn_decode",
+]

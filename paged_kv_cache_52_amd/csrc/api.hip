@@ -1,0 +1,196 @@
+// C ABI of libpagedattn: argument checks, launch planning and dispatch.
+// The operations and their conventions are documented in include/pagedattn.h.
+#include <limits.h>
+#include <math.h>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+bool misaligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+int check_split_tokens(int32_t split_tokens) {
+  if (split_tokens <= 0 || split_tokens % PA_BLOCK_SIZE != 0 || split_tokens > PA_MAX_SPLIT_TOKENS)
+    return PA_ERR_SPLIT;
+  return PA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case PA_ERR_SHAPE: return "unsupported sizes (head_dim 64/128, Hq/Hkv in {1,2,4,8,16}, counts >= 0)";
+    case PA_ERR_SPLIT: return "split_tokens must be a positive multiple of 16 up to 4096, and max_splits must cover max_context_len";
+    case PA_ERR_WORKSPACE: return "workspace smaller than pa_workspace_bytes()";
+    case PA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_num_splits(int32_t context_len, int32_t split_tokens) {
+  if (split_tokens <= 0) return 0;
+  if (context_len <= 0) return 1;
+  const int64_t n = ((int64_t)context_len + split_tokens - 1) / split_tokens;
+  return (int32_t)(n < 1 ? 1 : n);
+}
+
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  return 512;
+}
+
+size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                          int32_t max_splits) {
+  if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_splits < 0) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_splits;
+  return 2 * align256(rows * sizeof(float)) + align256(rows * head_dim * sizeof(float));
+}
+
+int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
+                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void *k_cache,
+                   void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
+                   int32_t cache_dtype, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  if (in_dtype != PA_F32 && in_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (cache_dtype != PA_I8 && cache_dtype != in_dtype) return PA_ERR_DTYPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (misaligned16(k) || misaligned16(v) || misaligned16(k_cache) || misaligned16(v_cache))
+    return PA_ERR_ALIGN;
+  if (num_blocks > INT64_MAX / (PA_BLOCK_SIZE * (int64_t)num_kv_heads * head_dim * 4))
+    return PA_ERR_SHAPE;
+  pa::WriteParams p{k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens,
+                    num_blocks, num_kv_heads, head_dim, in_dtype, cache_dtype};
+  return launch_status(pa::launch_kv_write(p, stream));
+}
+
+int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t head_dim, const void *k_cache,
+                              const void *v_cache, const float *k_scale, const float *v_scale,
+                              int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
+                              const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t max_context_len, float scale,
+                              int32_t split_tokens, int32_t max_splits, float *part_m,
+                              float *part_l, float *part_acc, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
+    return PA_ERR_SHAPE;
+  if (num_blocks <= 0 || num_blocks > INT_MAX) return PA_ERR_SHAPE;
+  const bool dt_ok = (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
+                     (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
+                     ((q_dtype == PA_BF16 || q_dtype == PA_F32) && cache_dtype == PA_I8);
+  if (!dt_ok) return PA_ERR_DTYPE;
+  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
+  const int32_t grid_splits = pa_num_splits(max_context_len, split_tokens);
+  if (max_splits < grid_splits) return PA_ERR_SPLIT;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !part_m || !part_l ||
+      !part_acc)
+    return PA_ERR_NULL;
+  if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
+
+  const int group = num_q_heads / num_kv_heads;
+  pa::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.part_m = part_m;
+  p.part_l = part_l;
+  p.part_acc = part_acc;
+  p.num_blocks = num_blocks;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.split_tokens = split_tokens;
+  p.max_splits = max_splits;
+  p.head_groups = group > 8 ? group / 8 : 1;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipError_t e;
+  if (q_dtype == PA_BF16 && cache_dtype == PA_BF16)
+    e = pa::decode_bf16_bf16(p, group, grid_splits, stream);
+  else if (q_dtype == PA_F32 && cache_dtype == PA_F32)
+    e = pa::decode_f32_f32(p, group, grid_splits, stream);
+  else if (q_dtype == PA_BF16)
+    e = pa::decode_bf16_i8(p, group, grid_splits, stream);
+  else
+    e = pa::decode_f32_i8(p, group, grid_splits, stream);
+  return launch_status(e);
+}
+
+int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, int32_t split_tokens, int32_t max_splits, void *out,
+                      int32_t out_dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (check_split_tokens(split_tokens) != PA_OK || max_splits <= 0) return PA_ERR_SPLIT;
+  if (num_seqs == 0) return PA_OK;
+  if (!part_m || !part_l || !part_acc || !context_lens || !out) return PA_ERR_NULL;
+  pa::ReduceParams p{part_m, part_l, part_acc, context_lens, out, num_seqs, num_q_heads,
+                     head_dim, split_tokens, max_splits, out_dtype};
+  return launch_status(pa::launch_reduce(p, stream));
+}
+
+int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, const void *k_cache, const void *v_cache,
+                      const float *k_scale, const float *v_scale, int32_t cache_dtype,
+                      int64_t num_blocks, int32_t num_kv_heads, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, int32_t split_tokens, void *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
+  if (max_context_len < 0 || num_seqs < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  const int32_t ns = pa_num_splits(max_context_len, split_tokens);
+  const size_t need = pa_workspace_bytes(num_seqs, num_q_heads, head_dim, ns);
+  if (num_seqs == 0) return PA_OK;
+  if (!workspace || !out) return PA_ERR_NULL;
+  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_seqs * num_q_heads * ns;
+  float *m = (float *)workspace;
+  float *l = (float *)((char *)workspace + align256(rows * sizeof(float)));
+  float *acc = (float *)((char *)workspace + 2 * align256(rows * sizeof(float)));
+  int st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_q_heads, head_dim, k_cache,
+                                     v_cache, k_scale, v_scale, cache_dtype, num_blocks,
+                                     num_kv_heads, block_tables, max_blocks_per_seq,
+                                     context_lens, max_context_len, scale, split_tokens, ns, m,
+                                     l, acc, stream);
+  if (st != PA_OK) return st;
+  return paged_attn_reduce(m, l, acc, context_lens, num_seqs, num_q_heads, head_dim,
+                           split_tokens, ns, out, q_dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,10 @@
+// Decode kernel instances for q dtype / cache dtype BF16 / BF16.
+#include "pa_internal.h"
+
+namespace pa {
+
+hipError_t decode_bf16_bf16(const DecodeParams &p, int group, int grid_splits, hipStream_t s) {
+  return dispatch_decode<PA_BF16, PA_BF16>(p, group, grid_splits, s);
+}
+
+}  // namespace pa

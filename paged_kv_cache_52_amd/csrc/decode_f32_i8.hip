@@ -1,0 +1,10 @@
+// Decode kernel instances for q dtype / cache dtype F32 / I8.
+#include "pa_internal.h"
+
+namespace pa {
+
+hipError_t decode_f32_i8(const DecodeParams &p, int group, int grid_splits, hipStream_t s) {
+  return dispatch_decode<PA_F32, PA_I8>(p, group, grid_splits, s);
+}
+
+}  // namespace pa

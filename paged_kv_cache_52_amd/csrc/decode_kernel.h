@@ -1,0 +1,415 @@
+// Split-K paged decode attention kernel for gfx950.
+//
+// One workgroup handles one (split j, KV head, sequence). Its NW wavefronts
+// share the split's blocks; each wave streams whole (block, KV head) tiles of
+// 16 x head_dim elements with 16-byte loads and keeps an online softmax
+// [EchoLLMServing notes, section 2, PagedAttention V2] for every query head of
+// the KV head's group, so each K/V byte is read from HBM once for all g query
+// heads. K/V are gathered through the block table [LLM Primer ch. 8, 8.1].
+//
+// Lane layout inside a wave (for one 16-token tile of one KV head):
+//   E   = elements per 16-byte load (8 bf16, 4 fp32, 16 int8)
+//   LPR = head_dim / E   lanes that together hold one token row
+//   RPI = 64 / LPR       token rows one load instruction covers
+//   NI  = 16 / RPI       load instructions per tile (per K or per V)
+// Lane l holds dims [E*(l % LPR), E*(l % LPR) + E) of tokens l / LPR + RPI*i,
+// i < NI. One load instruction therefore reads 64 x 16 = 1024 contiguous bytes
+// of the tile. q.k partial sums are combined across the LPR lanes of a row
+// with DPP; the LPR lanes of a row then hold identical logits, and each of the
+// RPI row groups keeps its own running (m, l, acc) over the tokens it owns.
+// Row groups and waves are merged once, at the end of the split.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_common.h"
+
+namespace pa {
+
+struct DecodeParams {
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const float *k_scale;
+  const float *v_scale;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *part_m;
+  float *part_l;
+  float *part_acc;
+  int64_t num_blocks;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_blocks_per_seq, max_context_len;
+  int32_t split_tokens, max_splits;
+  int32_t head_groups;  // query-head groups per KV head handled by separate workgroups
+  float scale_log2;     // scale * log2(e)
+};
+
+template <int QT, int CT, int D, int G>
+struct DecodeShape {
+  static constexpr int ELT = DtypeBytes<CT>::value;
+  static constexpr int E = 16 / ELT;
+  static constexpr int LPR = D / E;
+  static constexpr int RPI = kWave / LPR;
+  static constexpr int NI = kBlock / RPI;
+  static constexpr int ROW_BYTES = D * ELT;
+  static constexpr int TILE_BYTES = kBlock * ROW_BYTES;
+  static constexpr bool DOT2 = (QT == PA_BF16 && CT == PA_BF16);
+  static constexpr int QW = DOT2 ? E / 2 : E;  // q registers per head per lane
+  static_assert(LPR >= 1 && LPR <= kWave && RPI * LPR == kWave && NI * RPI == kBlock, "layout");
+};
+
+// Registers of one in-flight tile: K and V rows plus INT8 per-token scales.
+template <class S>
+struct Tile {
+  u32x4 k[S::NI];
+  u32x4 v[S::NI];
+  float ks[S::NI];
+  float vs[S::NI];
+};
+
+template <int QT, int CT, int D, int G, int NW>
+struct DecodeWave {
+  using S = DecodeShape<QT, CT, D, G>;
+
+  float qr[G][S::QW];  // q slice (fp32, pre-scaled) or packed bf16 pairs (DOT2)
+  float m[G];          // running max of this row group, log2 units
+  float l[G];          // running sum of exp2(z - m) over this lane's tokens
+  float acc[G][S::E];  // running sum of exp2(z - m) * v, this lane's dims
+
+  __device__ __forceinline__ void load_tile(Tile<S> &t, const DecodeParams &p, int blk, int kvh,
+                                            int lane) {
+    const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
+    const char *kt = (const char *)p.k_cache + tile * S::TILE_BYTES;
+    const char *vt = (const char *)p.v_cache + tile * S::TILE_BYTES;
+    const int r0 = lane / S::LPR;
+    const int off = r0 * S::ROW_BYTES + (lane % S::LPR) * 16;
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+      t.k[i] = *(const u32x4 *)(kt + off + i * S::RPI * S::ROW_BYTES);
+      t.v[i] = *(const u32x4 *)(vt + off + i * S::RPI * S::ROW_BYTES);
+    }
+    if constexpr (CT == PA_I8) {
+      const float *kst = p.k_scale + tile * kBlock;
+      const float *vst = p.v_scale + tile * kBlock;
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i) {
+        t.ks[i] = kst[r0 + i * S::RPI];
+        t.vs[i] = vst[r0 + i * S::RPI];
+      }
+    }
+  }
+
+  // 16 dims of an INT8 row chunk, widened to fp32.
+  __device__ __forceinline__ static void widen_i8(const u32x4 &w, float (&x)[16]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int32_t v = (int32_t)w[k];
+      x[4 * k + 0] = (float)((v << 24) >> 24);
+      x[4 * k + 1] = (float)((v << 16) >> 24);
+      x[4 * k + 2] = (float)((v << 8) >> 24);
+      x[4 * k + 3] = (float)(v >> 24);
+    }
+  }
+
+  // Fold one tile into the running state. `valid_rows` is the number of
+  // leading token rows of the tile inside the split (16 except at the end).
+  __device__ __forceinline__ void consume(const Tile<S> &t, int valid_rows, int lane,
+                                         float scale_log2) {
+    const int r0 = lane / S::LPR;
+    float z[S::NI][G];
+    // q . k over this lane's E dims, for each owned token row and query head.
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+      if constexpr (S::DOT2) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int k = 0; k < S::E / 2; ++k) {
+            // Copy the vector element to a scalar first: a bit cast applied
+            // directly to an ext-vector element reads element 0 (clang).
+            const uint32_t kw = t.k[i][k];
+            const float qw = qr[h][k];
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
+                                                __builtin_bit_cast(bf16x2, qw), a, false);
+          }
+          z[i][h] = a;
+        }
+      } else if constexpr (CT == PA_F32) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < S::E; ++e) a = fmaf(qr[h][e], __uint_as_float(t.k[i][e]), a);
+          z[i][h] = a;
+        }
+      } else {  // INT8 codes; the per-token scale multiplies the finished sum
+        float x[16];
+        widen_i8(t.k[i], x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) a = fmaf(qr[h][e], x[e], a);
+          z[i][h] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[i][h] = group_sum<S::LPR>(z[i][h]);
+    if constexpr (S::DOT2) {
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) z[i][h] *= scale_log2;
+    }
+    if constexpr (CT == PA_I8) {
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) z[i][h] *= t.ks[i];
+    }
+    const bool tail = valid_rows < kBlock;  // uniform
+    bool valid[S::NI];
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) valid[i] = !tail || (r0 + i * S::RPI) < valid_rows;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) z[i][h] = valid[i] ? z[i][h] : -INFINITY;
+    }
+
+    // Online softmax update of this row group.
+    float mnew[G];
+    bool grow = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float bm = z[0][h];
+#pragma unroll
+      for (int i = 1; i < S::NI; ++i) bm = fmaxf(bm, z[i][h]);
+      mnew[h] = fmaxf(m[h], bm);
+      grow |= mnew[h] > m[h];
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float alpha = fast_exp2(m[h] - mnew[h]);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) acc[h][e] *= alpha;
+        m[h] = mnew[h];
+      }
+    }
+    float pr[S::NI][G];
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pr[i][h] = fast_exp2(z[i][h] - m[h]);
+        l[h] += pr[i][h];
+      }
+
+    // P . V over this lane's tokens and dims.
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+      float vf[S::E];
+      if constexpr (CT == PA_BF16) {
+#pragma unroll
+        for (int k = 0; k < S::E / 2; ++k) {
+          vf[2 * k] = bf16_lo(t.v[i][k]);
+          vf[2 * k + 1] = bf16_hi(t.v[i][k]);
+        }
+      } else if constexpr (CT == PA_F32) {
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) vf[e] = __uint_as_float(t.v[i][e]);
+      } else {
+        widen_i8(t.v[i], vf);
+      }
+      float w[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) w[h] = pr[i][h];
+      if constexpr (CT == PA_I8) {
+        const float vs = valid[i] ? t.vs[i] : 0.f;  // a poisoned scale must not leak
+#pragma unroll
+        for (int h = 0; h < G; ++h) w[h] *= vs;
+      } else if (tail && !valid[i]) {
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) vf[e] = 0.f;  // NaN * 0 would leak: select, not scale
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) acc[h][e] = fmaf(w[h], vf[e], acc[h][e]);
+    }
+  }
+};
+
+template <int QT, int CT, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodeParams p) {
+  using S = DecodeShape<QT, CT, D, G>;
+  using W = DecodeWave<QT, CT, D, G, NW>;
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+
+  const int j = blockIdx.x;
+  const int kvh = blockIdx.y / p.head_groups;
+  const int hg = blockIdx.y % p.head_groups;
+  const int s = blockIdx.z;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+
+  // Context length, clamped so that no read leaves the table or the pool.
+  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  const int L = max(0, min(p.context_lens[s], lmax));
+  const int nsplit = max(1, (L + p.split_tokens - 1) / p.split_tokens);
+  if (j >= nsplit) return;  // whole workgroup
+  const int t0 = j * p.split_tokens;
+  const int t1 = min(t0 + p.split_tokens, L);
+  const int b0 = t0 / kBlock;
+  const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;
+  const int per = (nb + NW - 1) / NW;
+  const int wb0 = min(nb, wave * per);
+  const int wb1 = min(nb, wb0 + per);
+  const int hq0 = kvh * (p.num_q_heads / p.num_kv_heads) + hg * G;
+
+  W st;
+  // q slice for this lane's dims.
+  {
+    const int c = lane % S::LPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int64_t row = ((int64_t)s * p.num_q_heads + hq0 + h) * D;
+      if constexpr (S::DOT2) {
+        const u32x4 w = *(const u32x4 *)((const uint16_t *)p.q + row + c * S::E);
+#pragma unroll
+        for (int k = 0; k < S::E / 2; ++k) st.qr[h][k] = __uint_as_float(w[k]);
+      } else if constexpr (QT == PA_F32) {
+#pragma unroll
+        for (int e = 0; e < S::E; e += 4) {
+          const u32x4 w = *(const u32x4 *)((const float *)p.q + row + c * S::E + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) st.qr[h][e + k] = __uint_as_float(w[k]) * p.scale_log2;
+        }
+      } else {  // bf16 q against a non-bf16 cache: widen
+#pragma unroll
+        for (int e = 0; e < S::E; e += 8) {
+          const u32x4 w = *(const u32x4 *)((const uint16_t *)p.q + row + c * S::E + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            st.qr[h][e + 2 * k] = bf16_lo(w[k]) * p.scale_log2;
+            st.qr[h][e + 2 * k + 1] = bf16_hi(w[k]) * p.scale_log2;
+          }
+        }
+      }
+      st.m[h] = kNegBig;
+      st.l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) st.acc[h][e] = 0.f;
+    }
+  }
+
+  // Physical block ids of this wave's blocks, one per lane (per <= 64).
+  int my_id = 0;
+  {
+    const int cnt = wb1 - wb0;
+    if (lane < cnt) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
+  }
+  const int last_block = (int)(p.num_blocks - 1);  // the host checks 0 < num_blocks < 2^31
+  auto block_id = [&](int n) {
+    int b = __builtin_amdgcn_readlane(my_id, n - wb0);
+    return min(max(b, 0), last_block);
+  };
+  auto rows_in = [&](int n) { return min(kBlock, t1 - (b0 + n) * kBlock); };
+
+  // Two tiles in flight: load n+1 while consuming n.
+  Tile<S> ta, tb;
+  int n = wb0;
+  if (n < wb1) st.load_tile(ta, p, block_id(n), kvh, lane);
+  while (n < wb1) {
+    if (n + 1 < wb1) st.load_tile(tb, p, block_id(n + 1), kvh, lane);
+    st.consume(ta, rows_in(n), lane, p.scale_log2);
+    if (++n >= wb1) break;
+    if (n + 1 < wb1) st.load_tile(ta, p, block_id(n + 1), kvh, lane);
+    st.consume(tb, rows_in(n), lane, p.scale_log2);
+    ++n;
+  }
+
+  // Merge the RPI row groups of the wave.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = stride_max<S::LPR>(st.m[h]);
+    const float f = fast_exp2(st.m[h] - M);
+    st.l[h] = stride_sum<S::LPR>(st.l[h] * f);
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) st.acc[h][e] = stride_sum<S::LPR>(st.acc[h][e] * f);
+    st.m[h] = M;
+  }
+  if (lane < S::LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) sm_acc[wave][h][lane * S::E + e] = st.acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sm_m[wave][h] = st.m[h];
+      sm_l[wave][h] = st.l[h];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves and write the split's partials.
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int h = idx / D, d = idx % D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    float a = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm_m[w][h] - M);
+      a = fmaf(f, sm_acc[w][h][d], a);
+      lsum = fmaf(f, sm_l[w][h], lsum);
+    }
+    const int64_t row = ((int64_t)s * p.num_q_heads + hq0 + h) * p.max_splits + j;
+    p.part_acc[row * D + d] = a;
+    if (d == 0) {
+      p.part_l[row] = lsum;
+      p.part_m[row] = lsum > 0.f ? M * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
+template <int QT, int CT, int D, int G>
+hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t stream) {
+  constexpr int NW = 4;
+  dim3 grid(grid_splits, p.num_kv_heads * p.head_groups, p.num_seqs);
+  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), grid, dim3(NW * kWave), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+// Dispatch on (head_dim, group size) for one (q dtype, cache dtype) pair.
+template <int QT, int CT>
+hipError_t dispatch_decode(const DecodeParams &p, int group, int grid_splits, hipStream_t stream) {
+  auto by_group = [&](auto dtag) -> hipError_t {
+    constexpr int D = decltype(dtag)::value;
+    switch (group) {
+      case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
+      case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
+      case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
+      default: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);  // 8, and 16 as 2 x 8
+    }
+  };
+  if (p.head_dim == 64) return by_group(std::integral_constant<int, 64>{});
+  return by_group(std::integral_constant<int, 128>{});
+}
+
+}  // namespace pa

@@ -1,0 +1,94 @@
+// Device helpers shared by the libpagedattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+constexpr int kBlock = PA_BLOCK_SIZE;  // tokens per KV block
+constexpr int kWave = 64;              // CDNA wavefront width
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max start value: finite, so exp2(m_old - m_new) never sees inf - inf.
+constexpr float kNegBig = -3.0e38f;
+
+template <int DT> struct DtypeBytes;
+template <> struct DtypeBytes<PA_F32> { static constexpr int value = 4; };
+template <> struct DtypeBytes<PA_BF16> { static constexpr int value = 2; };
+template <> struct DtypeBytes<PA_I8> { static constexpr int value = 1; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Lane permutation inside a 16-lane DPP row; every lane's source is active.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over each aligned group of N consecutive lanes; every lane of the group
+// receives the same (bitwise) result because each step adds commutative pairs.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kQuadXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// Sum / max over the lanes that share lane % N (strides N, 2N, ... < 64).
+template <int N>
+__device__ __forceinline__ float stride_sum(float x) {
+#pragma unroll
+  for (int k = N; k < kWave; k <<= 1) x += __shfl_xor(x, k);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float stride_max(float x) {
+#pragma unroll
+  for (int k = N; k < kWave; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
+  return x;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf, 1 for 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,42 @@
+// Host-side launch interfaces between the C ABI layer and the kernel units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_kernel.h"
+
+namespace pa {
+
+struct ReduceParams {
+  const float *part_m;
+  const float *part_l;
+  const float *part_acc;
+  const int32_t *context_lens;
+  void *out;
+  int32_t num_seqs, num_q_heads, head_dim, split_tokens, max_splits, out_dtype;
+};
+
+struct WriteParams {
+  const void *k;
+  const void *v;
+  const int64_t *slot_mapping;
+  void *k_cache;
+  void *v_cache;
+  float *k_scale;
+  float *v_scale;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int32_t num_kv_heads, head_dim, in_dtype, cache_dtype;
+};
+
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream);
+hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream);
+
+// One per (q dtype, cache dtype) pair; group is Hq / Hkv in {1, 2, 4, 8, 16}.
+hipError_t decode_bf16_bf16(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
+hipError_t decode_f32_f32(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
+hipError_t decode_bf16_i8(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
+hipError_t decode_f32_i8(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
+
+}  // namespace pa

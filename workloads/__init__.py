@@ -141,17 +141,18 @@ def _randn(shape, gen: torch.Generator, device, dtype: torch.dtype) -> torch.Ten
     return x.to(dtype)
 
 
-def make_batch(name: str, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
+def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
                ctx_range: Optional[tuple] = None, poison: bool = False,
                contiguous_tables: bool = False, groups: Optional[int] = None,
                suffix_max: Optional[int] = None) -> Batch:
-    """Draw one decode batch of workload ``name``.
+    """Draw one decode batch of workload ``name`` (a key of WORKLOADS or a
+    Workload).
 
     num_seqs / ctx_range / groups / suffix_max shrink a workload for tests;
     contiguous_tables assigns physical blocks in logical order instead of a
     random permutation (the "contiguous slice" layout).
     """
-    w = WORKLOADS[name]
+    w = name if isinstance(name, Workload) else WORKLOADS[name]
     if groups is not None or suffix_max is not None:
         w = dataclasses.replace(w, groups=groups or w.groups, suffix_max=suffix_max or w.suffix_max)
     rng = np.random.default_rng(seed)
