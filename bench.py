@@ -1,8 +1,8 @@
 """Benchmark of the paged-KV decode hot path on one MI355X.
 
 One step = one decode step of one attention layer over a synthetic batch:
-write the new token of every sequence into the pool (paged_kv_write), the
-split-K decode kernel, and the reduce kernel. Inputs are resident in HBM
+write the new token of every sequence into the pool (paged_kv_write), plan
+the splits (paged_attn_plan), the split-K decode kernel, and the reduce kernel. Inputs are resident in HBM
 before the timed region starts.
 
 Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
@@ -42,6 +42,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--ctx-range", type=int, nargs=2, default=None, metavar=("LO", "HI"),
+                    help="override the workload's context-length range (inclusive)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -132,7 +137,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     b = workloads.make_batch(args.workload, args.seed, dev,
-                             contiguous_tables=args.contiguous_tables)
+                             contiguous_tables=args.contiguous_tables,
+                             ctx_range=tuple(args.ctx_range) if args.ctx_range else None)
     w = b.workload
     if b.k_cache.dtype == torch.int8:
         pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
@@ -146,23 +152,33 @@ def main():
                         l=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
                         acc=torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev),
                         context_lens=b.context_lens, split_tokens=T)
+    sched = torch.empty(pa.sched_bytes(B, S) // 4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    plan = [None]
 
     def write():
         pa.paged_kv_write(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale,
                           b.v_scale)
 
+    def make_plan():
+        plan[0] = pa.paged_attn_plan(b.context_lens, Hq, w.num_kv_heads,
+                                     b.block_tables.shape[1], max_context_len=b.max_context_len,
+                                     split_tokens=T, sched=sched)
+
     def decode():
         pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
                                      b.scale, b.k_scale, b.v_scale,
                                      max_context_len=b.max_context_len, split_tokens=T,
-                                     partials=parts)
+                                     plan=plan[0], partials=parts)
 
     def reduce():
         pa.paged_attn_reduce(parts, out)
 
+    def step():
+        write(); make_plan(); decode(); reduce()
+
     for _ in range(args.warmup):
-        write(); decode(); reduce()
+        step()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` whole steps.
@@ -171,23 +187,25 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        write(); decode(); reduce()
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # Per-kernel durations: identical launches with events between them.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for e in evs:
         e[0].record(stream); write()
-        e[1].record(stream); decode()
-        e[2].record(stream); reduce()
-        e[3].record(stream)
+        e[1].record(stream); make_plan()
+        e[2].record(stream); decode()
+        e[3].record(stream); reduce()
+        e[4].record(stream)
     torch.cuda.synchronize()
     t_write = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_red = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    t_plan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    t_red = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
 
     kv_bytes, alg_bytes = algorithmic_bytes(b)
     dec_gbps = alg_bytes / (t_dec * 1e-3) / 1e9
@@ -216,12 +234,15 @@ def main():
             "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
             "tables": "contiguous" if args.contiguous_tables else "permuted",
+            "context_range": list(args.ctx_range) if args.ctx_range else
+            [b.workload.ctx_lo, b.workload.ctx_hi],
             "seed": args.seed,
         },
         "kv_read_gbps": kv_gbps_step,
         "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
-        "decode_reduce_tokens_per_s": B / ((t_dec + t_red) * 1e-3),
-        "kernel_ms": {"kv_write": t_write, "decode_split": t_dec, "reduce": t_red},
+        "decode_reduce_tokens_per_s": B / ((t_plan + t_dec + t_red) * 1e-3),
+        "kernel_ms": {"kv_write": t_write, "plan": t_plan, "decode_split": t_dec,
+                      "reduce": t_red},
         "roofline": {
             "kernel": "decode_split_kernel", "bound": "hbm", "achieved": dec_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
@@ -229,6 +250,15 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -62,6 +62,7 @@ extern "C" {
 
 #define PA_BLOCK_SIZE 16
 #define PA_MAX_SPLIT_TOKENS 4096
+#define PA_MAX_SEQS 65535
 
 /* Element types. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
@@ -91,7 +92,12 @@ int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
  * Host-only arithmetic. */
 int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
-/* Bytes of workspace paged_attn_decode needs for the partials (m, l, acc). */
+/* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
+ * a small header). */
+size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits);
+
+/* Bytes of workspace paged_attn_decode needs: scheduling scratch plus the
+ * partials (m, l, acc). */
 size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                           int32_t max_splits);
 
@@ -117,10 +123,32 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
                    int32_t cache_dtype, hipStream_t stream);
 
 /*
+ * Plan of a decode step [EchoLLMServing notes, section 2: the split count of a
+ * sequence follows its context length]: one small kernel reads context_lens on
+ * the device and writes into `sched` the list of every split of the batch,
+ * max(1, ceil(L_s / T)) per sequence, full splits first and then the last
+ * split of each sequence, longest first. The list depends only on the lengths,
+ * T and the head counts, so one plan serves every attention layer of a step.
+ *   context_lens     [num_seqs] int32 (device)
+ *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
+ *   split_tokens     T as for paged_attn_decode_partial (0: default)
+ *   sched            device scratch of pa_sched_bytes(num_seqs, max_splits) bytes
+ *                    with max_splits >= pa_num_splits(max_context_len, T)
+ */
+int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int32_t split_tokens, int32_t *sched, hipStream_t stream);
+
+/*
  * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
  * s, query head h and split j < max(1, ceil(L_s / T)), write the partials
- * (m, l, acc) of that split. One launch covers the batch; the g = Hq/Hkv query
- * heads of a KV head share every K/V load.
+ * (m, l, acc) of that split. The g = Hq/Hkv query heads of a KV head share
+ * every K/V load. Works through the split list of `sched`, which
+ * paged_attn_plan must have written (on this stream, before this call) for the
+ * same context_lens, num_seqs, head counts, max_blocks_per_seq,
+ * max_context_len and split_tokens; a plan for other split_tokens, head
+ * counts or num_seqs is ignored (nothing is written), other mismatches give
+ * unspecified results.
  *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (PA_F32/PA_BF16)
  *   k_cache, ...   pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
  *                  (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and
@@ -134,7 +162,9 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  *   max_splits     leading stride of the partials; >= pa_num_splits(max_context_len, T)
  *   part_m, part_l [num_seqs][num_q_heads][max_splits] fp32
  *   part_acc       [num_seqs][num_q_heads][max_splits][head_dim] fp32
- * head_dim must be 64 or 128 and num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16.
+ *   sched          the plan (read only)
+ * head_dim must be 64 or 128, num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16,
+ * and num_seqs at most PA_MAX_SEQS.
  */
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               int32_t num_q_heads, int32_t head_dim, const void *k_cache,
@@ -143,7 +173,8 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               const int32_t *block_tables, int32_t max_blocks_per_seq,
                               const int32_t *context_lens, int32_t max_context_len, float scale,
                               int32_t split_tokens, int32_t max_splits, float *part_m,
-                              float *part_l, float *part_acc, hipStream_t stream);
+                              float *part_l, float *part_acc, const int32_t *sched,
+                              hipStream_t stream);
 
 /*
  * Reduce kernel [EchoLLMServing notes, section 2]: merge the partials of every
@@ -162,8 +193,9 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
                       int32_t out_dtype, hipStream_t stream);
 
 /*
- * Whole decode step of one attention layer: paged_attn_decode_partial into
- * the caller's workspace, then paged_attn_reduce into out (dtype = q_dtype).
+ * Whole decode step of one attention layer: paged_attn_plan and
+ * paged_attn_decode_partial into the caller's workspace, then
+ * paged_attn_reduce into out (dtype = q_dtype).
  * The split count is pa_num_splits(max_context_len, T) with T = split_tokens
  * (0: pa_default_split_tokens()). workspace must hold
  * pa_workspace_bytes(num_seqs, num_q_heads, head_dim, that split count)
@@ -176,6 +208,16 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       int32_t max_blocks_per_seq, const int32_t *context_lens,
                       int32_t max_context_len, float scale, int32_t split_tokens, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Measurement aid (not part of the attention path): read `bytes` (a multiple
+ * of 16) from device buffer `src` once with 16-byte loads, using
+ * sink_words / 256 workgroups of 256 threads; each thread writes one word of
+ * its XOR to sink[sink_words]. Used to measure the device's practical HBM
+ * read bandwidth next to the decode kernel's.
+ */
+int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

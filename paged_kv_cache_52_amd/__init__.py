@@ -70,6 +70,10 @@ def default_split_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int)
     return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len))
 
 
+def sched_bytes(num_seqs: int, max_splits: int) -> int:
+    return int(_lib.load().pa_sched_bytes(num_seqs, max_splits))
+
+
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_splits: int) -> int:
     return int(_lib.load().pa_workspace_bytes(num_seqs, num_q_heads, head_dim, max_splits))
 
@@ -94,6 +98,20 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
         T, Hkv, D, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32), NB,
         _code(k_cache), _stream(k.device)))
+
+
+@dataclasses.dataclass
+class Plan:
+    """Work list of one decode step (see paged_attn_plan); reusable by every
+    layer of the step."""
+    sched: torch.Tensor         # int32 scratch, pa_sched_bytes(num_seqs, max_splits)
+    context_lens: torch.Tensor  # [B] int32 the plan was made from
+    num_q_heads: int
+    num_kv_heads: int
+    max_blocks_per_seq: int
+    max_context_len: int
+    split_tokens: int
+    max_splits: int
 
 
 @dataclasses.dataclass
@@ -134,15 +152,43 @@ def _max_len(context_lens, max_context_len):
     return int(max_context_len)
 
 
+def paged_attn_plan(context_lens, num_q_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
+                    *, max_context_len=None, split_tokens=None,
+                    sched: Optional[torch.Tensor] = None) -> Plan:
+    """Plan kernel: list every split of the batch (device side, from
+    context_lens) for the split kernel."""
+    lib = _lib.load()
+    B = context_lens.shape[0]
+    mcl = _max_len(context_lens, max_context_len)
+    T = int(split_tokens) if split_tokens else default_split_tokens(B, num_kv_heads, mcl)
+    S = max(1, num_splits(mcl, T))
+    need = sched_bytes(B, S)
+    if sched is None or sched.numel() * sched.element_size() < need:
+        sched = torch.empty(max(need, 16) // 4, dtype=torch.int32, device=context_lens.device)
+    _check(lib.paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B, num_q_heads,
+                               num_kv_heads, max_blocks_per_seq, mcl, T,
+                               _dev(sched, "sched", torch.int32), _stream(context_lens.device)))
+    return Plan(sched, context_lens, num_q_heads, num_kv_heads, max_blocks_per_seq, mcl, T, S)
+
+
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
                               k_scale=None, v_scale=None, *, max_context_len=None,
-                              split_tokens=None, partials: Optional[Partials] = None) -> Partials:
-    """Split kernel only: returns the per-split (m, l, acc)."""
+                              split_tokens=None, plan: Optional[Plan] = None,
+                              partials: Optional[Partials] = None) -> Partials:
+    """Split kernel: returns the per-split (m, l, acc). Without `plan`, the
+    plan kernel runs first."""
     lib = _lib.load()
     B, Hq, D = q.shape
-    mcl = _max_len(context_lens, max_context_len)
-    T = int(split_tokens) if split_tokens else default_split_tokens(B, k_cache.shape[1], mcl)
-    S = max(1, num_splits(mcl, T))
+    Hkv = k_cache.shape[1]
+    if plan is None:
+        plan = paged_attn_plan(context_lens, Hq, Hkv, block_tables.shape[1],
+                               max_context_len=max_context_len, split_tokens=split_tokens)
+    elif ((plan.num_q_heads, plan.num_kv_heads, plan.max_blocks_per_seq) !=
+          (Hq, Hkv, block_tables.shape[1]) or plan.context_lens is not context_lens or
+          (split_tokens and int(split_tokens) != plan.split_tokens) or
+          (max_context_len is not None and int(max_context_len) != plan.max_context_len)):
+        raise PagedAttnError("plan was made for other arguments")
+    T, S = plan.split_tokens, plan.max_splits
     if partials is None:
         partials = Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
                             l=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
@@ -153,8 +199,9 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
         partials.context_lens, partials.split_tokens = context_lens, T
     args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
     _check(lib.paged_attn_decode_partial(
-        *args, mcl, float(scale), T, partials.max_splits, _dev(partials.m, "m", torch.float32),
-        _dev(partials.l, "l", torch.float32), _dev(partials.acc, "acc", torch.float32),
+        *args, plan.max_context_len, float(scale), T, partials.max_splits,
+        _dev(partials.m, "m", torch.float32), _dev(partials.l, "l", torch.float32),
+        _dev(partials.acc, "acc", torch.float32), _dev(plan.sched, "sched", torch.int32),
         _stream(q.device)))
     return partials
 
@@ -196,8 +243,17 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     return out
 
 
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read all of `buf` once (measurement aid: practical HBM read bandwidth)."""
+    if buf.numel() * buf.element_size() % 16:
+        raise PagedAttnError("probe buffer size must be a multiple of 16 bytes")
+    _check(_lib.load().pa_hbm_read_probe(
+        _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink", torch.int32),
+        sink.numel(), _stream(buf.device)))
+
+
 __all__ = [
-    "BLOCK_SIZE", "PagedAttnError", "Partials", "num_splits", "default_split_tokens",
-    "workspace_bytes", "paged_kv_write", "paged_attn_decode_partial", "paged_attn_reduce",
-    "paged_attn_decode",
+    "BLOCK_SIZE", "PagedAttnError", "Plan", "Partials", "num_splits", "default_split_tokens",
+    "sched_bytes", "workspace_bytes", "paged_kv_write", "paged_attn_plan", "paged_attn_decode_partial", "paged_attn_reduce",
+    "paged_attn_decode", "hbm_read_probe",
 ]

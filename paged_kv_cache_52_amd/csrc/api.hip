@@ -3,6 +3,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 #include "pagedattn.h"
 
@@ -54,11 +56,18 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   return 512;
 }
 
+size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits) {
+  if (num_seqs < 0 || max_splits < 0) return 0;
+  return align256((pa::kSchedHeader + 2 * (size_t)num_seqs * std::max(max_splits, 1)) *
+                  sizeof(int32_t));
+}
+
 size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                           int32_t max_splits) {
   if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_splits < 0) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * max_splits;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * head_dim * sizeof(float));
+  return pa_sched_bytes(num_seqs, max_splits) + 2 * align256(rows * sizeof(float)) +
+         align256(rows * head_dim * sizeof(float));
 }
 
 int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
@@ -88,9 +97,10 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               const int32_t *block_tables, int32_t max_blocks_per_seq,
                               const int32_t *context_lens, int32_t max_context_len, float scale,
                               int32_t split_tokens, int32_t max_splits, float *part_m,
-                              float *part_l, float *part_acc, hipStream_t stream) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0)
+                              float *part_l, float *part_acc, const int32_t *sched,
+                              hipStream_t stream) {
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
@@ -106,7 +116,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   if (max_splits < grid_splits) return PA_ERR_SPLIT;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !part_m || !part_l ||
-      !part_acc)
+      !part_acc || !sched)
     return PA_ERR_NULL;
   if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
@@ -132,6 +142,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   p.max_context_len = max_context_len;
   p.split_tokens = split_tokens;
   p.max_splits = max_splits;
+  p.sched = sched;
   p.head_groups = group > 8 ? group / 8 : 1;
   p.scale_log2 = scale * 1.4426950408889634f;
 
@@ -145,6 +156,26 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   else
     e = pa::decode_f32_i8(p, group, grid_splits, stream);
   return launch_status(e);
+}
+
+int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
+    return PA_ERR_SHAPE;
+  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
+  if (num_seqs == 0) return PA_OK;
+  if (!context_lens || !sched) return PA_ERR_NULL;
+  const int group = num_q_heads / num_kv_heads;
+  const pa::PlanParams plan{
+      context_lens, sched, num_seqs,
+      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE),
+      split_tokens, num_kv_heads * (group > 8 ? group / 8 : 1)};
+  return launch_status(pa::launch_plan(plan, stream));
 }
 
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
@@ -171,7 +202,8 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  if (max_context_len < 0 || num_seqs < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0)
+    return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   const int32_t ns = pa_num_splits(max_context_len, split_tokens);
   const size_t need = pa_workspace_bytes(num_seqs, num_q_heads, head_dim, ns);
@@ -180,17 +212,32 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   const size_t rows = (size_t)num_seqs * num_q_heads * ns;
-  float *m = (float *)workspace;
-  float *l = (float *)((char *)workspace + align256(rows * sizeof(float)));
-  float *acc = (float *)((char *)workspace + 2 * align256(rows * sizeof(float)));
-  int st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_q_heads, head_dim, k_cache,
+  char *base = (char *)workspace;
+  int32_t *sched = (int32_t *)base;
+  base += pa_sched_bytes(num_seqs, ns);
+  float *m = (float *)base;
+  float *l = (float *)(base + align256(rows * sizeof(float)));
+  float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
+  int st = paged_attn_plan(context_lens, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                           max_context_len, split_tokens, sched, stream);
+  if (st != PA_OK) return st;
+  st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_q_heads, head_dim, k_cache,
                                      v_cache, k_scale, v_scale, cache_dtype, num_blocks,
                                      num_kv_heads, block_tables, max_blocks_per_seq,
                                      context_lens, max_context_len, scale, split_tokens, ns, m,
-                                     l, acc, stream);
+                                     l, acc, sched, stream);
   if (st != PA_OK) return st;
   return paged_attn_reduce(m, l, acc, context_lens, num_seqs, num_q_heads, head_dim,
                            split_tokens, ns, out, q_dtype, stream);
+}
+
+int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,
+                      hipStream_t stream) {
+  if (!src || !sink) return PA_ERR_NULL;
+  if (misaligned16(src)) return PA_ERR_ALIGN;
+  if (sink_words < 256 || bytes % 16 != 0) return PA_ERR_SHAPE;
+  const int blocks = sink_words / 256;
+  return launch_status(pa::launch_read_probe(src, bytes, sink, blocks, stream));
 }
 
 }  // extern "C"

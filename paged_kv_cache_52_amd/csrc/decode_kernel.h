@@ -20,6 +20,7 @@
 // Row groups and waves are merged once, at the end of the split.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_common.h"
@@ -37,6 +38,7 @@ struct DecodeParams {
   float *part_m;
   float *part_l;
   float *part_acc;
+  const int32_t *sched;  // work list from the plan kernel (see kSchedHeader)
   int64_t num_blocks;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, max_context_len;
@@ -44,6 +46,19 @@ struct DecodeParams {
   int32_t head_groups;  // query-head groups per KV head handled by separate workgroups
   float scale_log2;     // scale * log2(e)
 };
+
+// Tiles a wave keeps in flight beyond the one it is consuming (0 or 1).
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 0
+#endif
+constexpr int kPrefetch = PA_PREFETCH;
+
+// Layout of the scheduling scratch written by the plan kernel:
+//   [0] number of work items (splits x KV-head groups)
+//   [1] split_tokens, [2] KV-head groups, [3] num_seqs the plan was made for
+//   then two words per split, full splits first: (sequence << 16 | split) and
+//   the sequence's clamped context length.
+constexpr int kSchedHeader = 4;
 
 template <int QT, int CT, int D, int G>
 struct DecodeShape {
@@ -77,26 +92,39 @@ struct DecodeWave {
   float l[G];          // running sum of exp2(z - m) over this lane's tokens
   float acc[G][S::E];  // running sum of exp2(z - m) * v, this lane's dims
 
+  // Tile loads go through buffer descriptors built per tile in SGPRs: the
+  // lane offset stays a 32-bit VGPR (no 64-bit address pairs), and the record
+  // count is the tile size, so an offset outside the tile reads zeros.
   __device__ __forceinline__ void load_tile(Tile<S> &t, const DecodeParams &p, int blk, int kvh,
-                                            int lane) {
+                                            int lane_off, int scale_off) {
     const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
-    const char *kt = (const char *)p.k_cache + tile * S::TILE_BYTES;
-    const char *vt = (const char *)p.v_cache + tile * S::TILE_BYTES;
-    const int r0 = lane / S::LPR;
-    const int off = r0 * S::ROW_BYTES + (lane % S::LPR) * 16;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc((const char *)p.k_cache + tile * S::TILE_BYTES,
+                                                S::TILE_BYTES);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc((const char *)p.v_cache + tile * S::TILE_BYTES,
+                                                S::TILE_BYTES);
+    // K (and its scales) first, then V: the q.k step waits only for K while
+    // V and the next tile stay in flight.
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-      t.k[i] = *(const u32x4 *)(kt + off + i * S::RPI * S::ROW_BYTES);
-      t.v[i] = *(const u32x4 *)(vt + off + i * S::RPI * S::ROW_BYTES);
-    }
+    for (int i = 0; i < S::NI; ++i)
+      t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
+                                                     kStreamPolicy);
     if constexpr (CT == PA_I8) {
-      const float *kst = p.k_scale + tile * kBlock;
-      const float *vst = p.v_scale + tile * kBlock;
+      const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, kBlock * 4);
 #pragma unroll
-      for (int i = 0; i < S::NI; ++i) {
-        t.ks[i] = kst[r0 + i * S::RPI];
-        t.vs[i] = vst[r0 + i * S::RPI];
-      }
+      for (int i = 0; i < S::NI; ++i)
+        t.ks[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                ksr, scale_off + i * S::RPI * 4, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i)
+      t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
+                                                     kStreamPolicy);
+    if constexpr (CT == PA_I8) {
+      const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, kBlock * 4);
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i)
+        t.vs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                vsr, scale_off + i * S::RPI * 4, 0, 0));
     }
   }
 
@@ -248,26 +276,21 @@ struct DecodeWave {
   }
 };
 
+// One work item: split j of sequence s for KV head kvh (query-head group hg).
+// The NW waves of the workgroup share the split's tiles, merge their states in
+// LDS and write the split's partials. Contains one workgroup barrier.
 template <int QT, int CT, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodeParams p) {
+__device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
+                                              int kvh, int hg, int lane, int wave,
+                                              float (&sm_m)[NW][G],
+                                              float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
   using S = DecodeShape<QT, CT, D, G>;
   using W = DecodeWave<QT, CT, D, G, NW>;
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-
-  const int j = blockIdx.x;
-  const int kvh = blockIdx.y / p.head_groups;
-  const int hg = blockIdx.y % p.head_groups;
-  const int s = blockIdx.z;
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
-  const int L = max(0, min(p.context_lens[s], lmax));
+  const int L = max(0, min(len, lmax));
   const int nsplit = max(1, (L + p.split_tokens - 1) / p.split_tokens);
-  if (j >= nsplit) return;  // whole workgroup
+  if (j >= nsplit) return;  // never for planned items; uniform across the workgroup
   const int t0 = j * p.split_tokens;
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
@@ -326,17 +349,34 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodePa
   };
   auto rows_in = [&](int n) { return min(kBlock, t1 - (b0 + n) * kBlock); };
 
-  // Two tiles in flight: load n+1 while consuming n.
+  const int lane_off = (lane / S::LPR) * S::ROW_BYTES + (lane % S::LPR) * 16;
+  const int scale_off = (lane / S::LPR) * 4;
+  // Double-buffered stream: tile n+1 is in flight while tile n is consumed.
+  // The steady-state loop issues its loads unconditionally so that the
+  // compiler's memory-counter waits only cover the tile being consumed; the
+  // last one or two tiles are peeled.
   Tile<S> ta, tb;
-  int n = wb0;
-  if (n < wb1) st.load_tile(ta, p, block_id(n), kvh, lane);
-  while (n < wb1) {
-    if (n + 1 < wb1) st.load_tile(tb, p, block_id(n + 1), kvh, lane);
-    st.consume(ta, rows_in(n), lane, p.scale_log2);
-    if (++n >= wb1) break;
-    if (n + 1 < wb1) st.load_tile(ta, p, block_id(n + 1), kvh, lane);
-    st.consume(tb, rows_in(n), lane, p.scale_log2);
-    ++n;
+  if constexpr (kPrefetch == 0) {
+    for (int n = wb0; n < wb1; ++n) {
+      st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
+      st.consume(ta, rows_in(n), lane, p.scale_log2);
+    }
+  } else if (wb0 < wb1) {
+    int n = wb0;
+    st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
+    for (; n + 2 < wb1; n += 2) {
+      st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
+      st.consume(ta, rows_in(n), lane, p.scale_log2);
+      st.load_tile(ta, p, block_id(n + 2), kvh, lane_off, scale_off);
+      st.consume(tb, rows_in(n + 1), lane, p.scale_log2);
+    }
+    if (n + 1 < wb1) {
+      st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
+      st.consume(ta, rows_in(n), lane, p.scale_log2);
+      st.consume(tb, rows_in(n + 1), lane, p.scale_log2);
+    } else {
+      st.consume(ta, rows_in(n), lane, p.scale_log2);
+    }
   }
 
   // Merge the RPI row groups of the wave.
@@ -386,13 +426,54 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodePa
   }
 }
 
+// Split kernel. Work item k is split sched[kSchedHeader + 2*(k / heff)]
+// (packed sequence << 16 | split, followed by the sequence's context length)
+// for KV-head group k % heff, from the list the plan kernel wrote (full splits
+// first, the shortest last splits at the end). Workgroup k processes item k;
+// the grid is an upper bound on the number of items and the workgroups past
+// the end of the list, all at the end of the grid, exit at once. A plan made
+// for other parameters counts as an empty list.
+template <int QT, int CT, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodeParams p) {
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+
+  const int heff = p.num_kv_heads * p.head_groups;
+  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == heff &&
+                       p.sched[3] == p.num_seqs;
+  const int n_items = plan_ok ? p.sched[0] : 0;
+  const int k = blockIdx.x;
+  if (k >= n_items) return;
+  const int lane = lane_id();
+  // Wave index as a scalar, so that per-wave ranges and loop counters stay in
+  // SGPRs and the tile loop runs without exec masking.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int e = k % heff;
+  const int packed = p.sched[kSchedHeader + 2 * (k / heff)];
+  const int len = p.sched[kSchedHeader + 2 * (k / heff) + 1];
+  // The sequence index is clamped so that no entry can send a read out of
+  // bounds; process_split ignores a split index past the sequence's end.
+  process_split<QT, CT, D, G, NW>(p, min(packed >> 16, p.num_seqs - 1), len, packed & 0xffff,
+                                  e / p.head_groups, e % p.head_groups, lane, wave, sm_m, sm_l,
+                                  sm_acc);
+}
+
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
+// Waves per workgroup (they share one split).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+
 template <int QT, int CT, int D, int G>
 hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t stream) {
-  constexpr int NW = 4;
-  dim3 grid(grid_splits, p.num_kv_heads * p.head_groups, p.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), grid, dim3(NW * kWave), 0, stream,
-                     p);
+  constexpr int NW = PA_DECODE_WAVES;
+  // Each wave keeps its blocks' ids one per lane: at most 64 blocks per wave.
+  static_assert(PA_MAX_SPLIT_TOKENS <= kWave * kBlock * NW, "split_tokens cap vs waves");
+  // One workgroup per possible item; those past the planned list exit at once.
+  const int64_t max_items = (int64_t)p.num_seqs * grid_splits * p.num_kv_heads * p.head_groups;
+  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), dim3((unsigned)max_items),
+                     dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -30,8 +30,17 @@ struct WriteParams {
   int32_t num_kv_heads, head_dim, in_dtype, cache_dtype;
 };
 
+struct PlanParams {
+  const int32_t *context_lens;
+  int32_t *sched;
+  int32_t num_seqs, max_len, split_tokens, heff;
+};
+
+hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int blocks,
+                             hipStream_t stream);
 
 // One per (q dtype, cache dtype) pair; group is Hq / Hkv in {1, 2, 4, 8, 16}.
 hipError_t decode_bf16_bf16(const DecodeParams &p, int group, int grid_splits, hipStream_t s);

@@ -59,9 +59,12 @@ def test_default_split_tokens_is_valid(lib):
 
 def test_workspace_bytes(lib):
     rows = 64 * 32 * 8
-    expect = 2 * (-(-rows * 4 // 256) * 256) + (-(-rows * 128 * 4 // 256) * 256)
+    sched = -(-(2 + 2 * 64 * 8) * 4 // 256) * 256
+    assert lib.pa_sched_bytes(64, 8) == sched
+    expect = sched + 2 * (-(-rows * 4 // 256) * 256) + (-(-rows * 128 * 4 // 256) * 256)
     assert lib.pa_workspace_bytes(64, 32, 128, 8) == expect
     assert lib.pa_workspace_bytes(-1, 32, 128, 8) == 0
+    assert lib.pa_sched_bytes(-1, 8) == 0
 
 
 def _write(lib, **kw):
@@ -87,12 +90,12 @@ def test_kv_write_validation(lib):
 def _partial(lib, **kw):
     a = dict(q=FAKE, qdt=BF16, B=4, Hq=32, D=128, kc=FAKE, vc=FAKE, ks=None, vs=None, cdt=BF16,
              NB=100, Hkv=8, bt=FAKE, mb=8, cl=FAKE, mcl=128, scale=0.1, T=512, S=1, m=FAKE,
-             l=FAKE, acc=FAKE)
+             l=FAKE, acc=FAKE, sched=FAKE)
     a.update(kw)
     return lib.paged_attn_decode_partial(a["q"], a["qdt"], a["B"], a["Hq"], a["D"], a["kc"],
                                          a["vc"], a["ks"], a["vs"], a["cdt"], a["NB"], a["Hkv"],
                                          a["bt"], a["mb"], a["cl"], a["mcl"], a["scale"], a["T"],
-                                         a["S"], a["m"], a["l"], a["acc"], None)
+                                         a["S"], a["m"], a["l"], a["acc"], a["sched"], None)
 
 
 def test_decode_partial_validation(lib):
@@ -108,6 +111,8 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, T=8192) == ERR_SPLIT
     assert _partial(lib, mcl=1025, S=2) == ERR_SPLIT    # needs 3 splits
     assert _partial(lib, q=None) == ERR_NULL
+    assert _partial(lib, sched=None) == ERR_NULL
+    assert _partial(lib, B=65536) == ERR_SHAPE
     assert _partial(lib, cdt=I8) == ERR_NULL            # INT8 needs scales
     assert _partial(lib, q=FAKE_ODD) == ERR_ALIGN
     assert _partial(lib, B=0, q=None) == OK

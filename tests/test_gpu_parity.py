@@ -327,6 +327,69 @@ def test_identity_and_permuted_tables_agree():
         _check_out(out32, _oracle_decode(b), TOL_BF16, f"contiguous={contiguous}")
 
 
+@pytest.mark.parametrize("T", [16, 512])
+def test_plan_lists_every_split_once(T):
+    """The plan kernel's work list holds each (sequence, split) exactly once:
+    full splits first, then last splits ordered by decreasing tile count."""
+    print(f"[case] plan T={T}", flush=True)
+    lens = [0, 1, 15, 16, 17, 511, 512, 513, 1024, 31, 2, 700]
+    b = workloads.make_batch("llama8b_bf16", 151, "cpu", num_seqs=len(lens),
+                             ctx_range=(1024, 1024))
+    b.context_lens = torch.tensor(lens, dtype=torch.int32)
+    g = _to(b, "cuda")
+    plan = pa().paged_attn_plan(g.context_lens, g.q.shape[1], g.k_cache.shape[1],
+                                g.block_tables.shape[1], max_context_len=g.max_context_len,
+                                split_tokens=T)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    heff = b.k_cache.shape[1]
+    nsplit = [max(1, -(-L // T)) for L in lens]
+    n = sum(nsplit)
+    assert list(sched[:4]) == [n * heff, T, heff, len(lens)]
+    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[4:4 + 2 * n:2]]
+    assert list(sched[5:5 + 2 * n:2]) == [lens[s] for s, _ in entries]
+    assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
+    n_full = n - len(lens)
+    assert all(j < nsplit[s] - 1 for s, j in entries[:n_full])
+    tiles = [max(1, -(-(lens[s] - j * T) // 16)) if lens[s] else 1 for s, j in entries[n_full:]]
+    assert tiles == sorted(tiles, reverse=True)
+
+
+def test_plan_is_shared_and_mismatch_is_ignored():
+    """One plan serves several decode calls; a plan made for another split size
+    writes nothing (the partials keep their previous contents)."""
+    print("[case] plan reuse", flush=True)
+    b = workloads.make_batch("llama8b_bf16", 161, "cpu", num_seqs=5, ctx_range=(1, 900))
+    g = _to(b, "cuda")
+    ref = _oracle_decode(b)
+    plan = pa().paged_attn_plan(g.context_lens, g.q.shape[1], g.k_cache.shape[1],
+                                g.block_tables.shape[1], max_context_len=g.max_context_len,
+                                split_tokens=64)
+    for _ in range(2):
+        parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                               g.context_lens, g.scale, plan=plan)
+        out = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+        pa().paged_attn_reduce(parts, out)
+        torch.cuda.synchronize()
+        _check_out(out.cpu().double().numpy(), ref, TOL_BF16, "plan reuse")
+    # Raw C call with split_tokens 32 against the 64-token plan: nothing is written.
+    from paged_kv_cache_52_amd import _lib
+    lib = _lib.load()
+    S = pa().num_splits(g.max_context_len, 32)
+    m = torch.full((5, g.q.shape[1], S), 7.0, device="cuda")
+    l = torch.full_like(m, 7.0)
+    acc = torch.full((5, g.q.shape[1], S, 128), 7.0, device="cuda")
+    rc = lib.paged_attn_decode_partial(
+        g.q.data_ptr(), 1, 5, g.q.shape[1], 128, g.k_cache.data_ptr(), g.v_cache.data_ptr(),
+        None, None, 1, g.k_cache.shape[0], g.k_cache.shape[1], g.block_tables.data_ptr(),
+        g.block_tables.shape[1], g.context_lens.data_ptr(), g.max_context_len, g.scale, 32, S,
+        m.data_ptr(), l.data_ptr(), acc.data_ptr(), plan.sched.data_ptr(),
+        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert bool((m == 7.0).all()) and bool((acc == 7.0).all())
+
+
 def test_decode_is_deterministic():
     b = workloads.make_batch("llama8b_bf16", 131, "cpu", num_seqs=6, ctx_range=(1, 2000))
     g = _to(b, "cuda")
