@@ -1,8 +1,9 @@
 """Benchmark of the paged-KV decode hot path on one MI355X.
 
 One step = one decode step of one attention layer over a synthetic batch:
-write the new token of every sequence into the pool (paged_kv_write), plan
-the splits (paged_attn_plan), the split-K decode kernel, and the reduce kernel. Inputs are resident in HBM
+write the new token of every sequence into the pool and plan the splits
+(paged_decode_prepare: paged_kv_write + paged_attn_plan in one launch), the
+split-K decode kernel, and the reduce kernel. Inputs are resident in HBM
 before the timed region starts.
 
 Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
@@ -156,14 +157,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
     plan = [None]
 
-    def write():
-        pa.paged_kv_write(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.k_scale,
-                          b.v_scale)
-
-    def make_plan():
-        plan[0] = pa.paged_attn_plan(b.context_lens, Hq, w.num_kv_heads,
-                                     b.block_tables.shape[1], max_context_len=b.max_context_len,
-                                     split_tokens=T, sched=sched)
+    def prepare():
+        # KV write of the step's new tokens and the split plan, one launch.
+        plan[0] = pa.paged_decode_prepare(b.new_k, b.new_v, b.slot_mapping, b.k_cache,
+                                          b.v_cache, b.context_lens, Hq,
+                                          b.block_tables.shape[1], b.k_scale, b.v_scale,
+                                          max_context_len=b.max_context_len, split_tokens=T,
+                                          sched=sched)
 
     def decode():
         pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
@@ -175,7 +175,7 @@ def main():
         pa.paged_attn_reduce(parts, out)
 
     def step():
-        write(); make_plan(); decode(); reduce()
+        prepare(); decode(); reduce()
 
     for _ in range(args.warmup):
         step()
@@ -194,18 +194,16 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # Per-kernel durations: identical launches with events between them.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
-        e[0].record(stream); write()
-        e[1].record(stream); make_plan()
-        e[2].record(stream); decode()
-        e[3].record(stream); reduce()
-        e[4].record(stream)
+        e[0].record(stream); prepare()
+        e[1].record(stream); decode()
+        e[2].record(stream); reduce()
+        e[3].record(stream)
     torch.cuda.synchronize()
-    t_write = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_plan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    t_red = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+    t_prep = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_red = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
     kv_bytes, alg_bytes = algorithmic_bytes(b)
     dec_gbps = alg_bytes / (t_dec * 1e-3) / 1e9
@@ -240,9 +238,8 @@ def main():
         },
         "kv_read_gbps": kv_gbps_step,
         "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
-        "decode_reduce_tokens_per_s": B / ((t_plan + t_dec + t_red) * 1e-3),
-        "kernel_ms": {"kv_write": t_write, "plan": t_plan, "decode_split": t_dec,
-                      "reduce": t_red},
+        "decode_reduce_tokens_per_s": B / ((t_dec + t_red) * 1e-3),
+        "kernel_ms": {"write_and_plan": t_prep, "decode_split": t_dec, "reduce": t_red},
         "roofline": {
             "kernel": "decode_split_kernel", "bound": "hbm", "achieved": dec_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,

@@ -140,6 +140,21 @@ int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q
                     int32_t split_tokens, int32_t *sched, hipStream_t stream);
 
 /*
+ * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
+ * depend on each other, so one kernel does both (its last workgroup plans, the
+ * others write). Arguments, layouts and errors are those of the two calls; the
+ * results are identical to calling them in turn. Serves the start of a decode
+ * step, where the new tokens are written and the batch's splits are listed.
+ */
+int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
+                         const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
+                         float *v_scale, int64_t num_blocks, int32_t cache_dtype,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t split_tokens, int32_t *sched, hipStream_t stream);
+
+/*
  * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
  * s, query head h and split j < max(1, ceil(L_s / T)), write the partials
  * (m, l, acc) of that split. The g = Hq/Hkv query heads of a KV head share

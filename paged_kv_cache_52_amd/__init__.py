@@ -171,6 +171,36 @@ def paged_attn_plan(context_lens, num_q_heads: int, num_kv_heads: int, max_block
     return Plan(sched, context_lens, num_q_heads, num_kv_heads, max_blocks_per_seq, mcl, T, S)
 
 
+def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens, num_q_heads: int,
+                         max_blocks_per_seq: int, k_scale=None, v_scale=None, *,
+                         max_context_len=None, split_tokens=None,
+                         sched: Optional[torch.Tensor] = None) -> Plan:
+    """paged_kv_write + paged_attn_plan in one launch; returns the plan."""
+    T_tok, Hkv, D = k.shape
+    NB = k_cache.shape[0]
+    if k_cache.shape != (NB, Hkv, BLOCK_SIZE, D) or v_cache.shape != k_cache.shape:
+        raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
+    if v.shape != k.shape or slot_mapping.shape != (T_tok,):
+        raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
+    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    B = context_lens.shape[0]
+    mcl = _max_len(context_lens, max_context_len)
+    T = int(split_tokens) if split_tokens else default_split_tokens(B, Hkv, mcl)
+    S = max(1, num_splits(mcl, T))
+    need = sched_bytes(B, S)
+    if sched is None or sched.numel() * sched.element_size() < need:
+        sched = torch.empty(max(need, 16) // 4, dtype=torch.int32, device=context_lens.device)
+    _check(_lib.load().paged_decode_prepare(
+        _dev(k, "k"), _dev(v, "v", k.dtype), _code(k),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), NB, _code(k_cache),
+        _dev(context_lens, "context_lens", torch.int32), B, num_q_heads, max_blocks_per_seq,
+        mcl, T, _dev(sched, "sched", torch.int32), _stream(k.device)))
+    return Plan(sched, context_lens, num_q_heads, Hkv, max_blocks_per_seq, mcl, T, S)
+
+
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
                               k_scale=None, v_scale=None, *, max_context_len=None,
                               split_tokens=None, plan: Optional[Plan] = None,
@@ -254,6 +284,6 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
 
 __all__ = [
     "BLOCK_SIZE", "PagedAttnError", "Plan", "Partials", "num_splits", "default_split_tokens",
-    "sched_bytes", "workspace_bytes", "paged_kv_write", "paged_attn_plan", "paged_attn_decode_partial", "paged_attn_reduce",
+    "sched_bytes", "workspace_bytes", "paged_kv_write", "paged_attn_plan", "paged_decode_prepare", "paged_attn_decode_partial", "paged_attn_reduce",
     "paged_attn_decode", "hbm_read_probe",
 ]

@@ -70,24 +70,94 @@ size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
          align256(rows * head_dim * sizeof(float));
 }
 
-int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
-                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void *k_cache,
-                   void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
-                   int32_t cache_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the KV write; fills `out` on success.
+int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
+                int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void *k_cache,
+                void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
+                int32_t cache_dtype, pa::WriteParams *out) {
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (in_dtype != PA_F32 && in_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (cache_dtype != PA_I8 && cache_dtype != in_dtype) return PA_ERR_DTYPE;
-  if (num_tokens == 0) return PA_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-  if (misaligned16(k) || misaligned16(v) || misaligned16(k_cache) || misaligned16(v_cache))
-    return PA_ERR_ALIGN;
   if (num_blocks > INT64_MAX / (PA_BLOCK_SIZE * (int64_t)num_kv_heads * head_dim * 4))
     return PA_ERR_SHAPE;
-  pa::WriteParams p{k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens,
-                    num_blocks, num_kv_heads, head_dim, in_dtype, cache_dtype};
-  return launch_status(pa::launch_kv_write(p, stream));
+  if (num_tokens > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (misaligned16(k) || misaligned16(v) || misaligned16(k_cache) || misaligned16(v_cache))
+      return PA_ERR_ALIGN;
+  }
+  *out = pa::WriteParams{k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens,
+                         num_blocks, num_kv_heads, head_dim, in_dtype, cache_dtype};
+  return PA_OK;
+}
+
+// Argument checks of the plan; fills `out` on success.
+int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+               int32_t split_tokens, int32_t *sched, pa::PlanParams *out) {
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
+    return PA_ERR_SHAPE;
+  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
+  if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
+  const int group = num_q_heads / num_kv_heads;
+  *out = pa::PlanParams{
+      context_lens, sched, num_seqs,
+      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE),
+      split_tokens, num_kv_heads * (group > 8 ? group / 8 : 1)};
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t *slot_mapping,
+                   int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, void *k_cache,
+                   void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
+                   int32_t cache_dtype, hipStream_t stream) {
+  pa::WriteParams w;
+  const int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                             k_cache, v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
+  if (st != PA_OK || num_tokens == 0) return st;
+  return launch_status(pa::launch_kv_write(w, stream));
+}
+
+int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+  pa::PlanParams pl;
+  const int st = check_plan(context_lens, num_seqs, num_q_heads, num_kv_heads,
+                            max_blocks_per_seq, max_context_len, split_tokens, sched, &pl);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return launch_status(pa::launch_plan(pl, stream));
+}
+
+int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
+                         const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
+                         float *v_scale, int64_t num_blocks, int32_t cache_dtype,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+  pa::WriteParams w;
+  pa::PlanParams pl;
+  int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
+                       v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
+  if (st != PA_OK) return st;
+  st = check_plan(context_lens, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                  max_context_len, split_tokens, sched, &pl);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
+  return launch_status(pa::launch_prepare(w, pl, stream));
 }
 
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
@@ -156,26 +226,6 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   else
     e = pa::decode_f32_i8(p, group, grid_splits, stream);
   return launch_status(e);
-}
-
-int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
-                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
-  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0)
-    return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
-    return PA_ERR_SHAPE;
-  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
-  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  if (num_seqs == 0) return PA_OK;
-  if (!context_lens || !sched) return PA_ERR_NULL;
-  const int group = num_q_heads / num_kv_heads;
-  const pa::PlanParams plan{
-      context_lens, sched, num_seqs,
-      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE),
-      split_tokens, num_kv_heads * (group > 8 ? group / 8 : 1)};
-  return launch_status(pa::launch_plan(plan, stream));
 }
 
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,

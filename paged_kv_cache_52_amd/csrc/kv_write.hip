@@ -4,13 +4,13 @@
 // with one fp32 scale [EchoLLMServing notes, section 3].
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "plan_device.h"
 
 namespace pa {
 
 // Exact copy: one thread moves one 16-byte chunk of a K row and of a V row.
-__global__ __launch_bounds__(256) void kv_copy_kernel(const WriteParams p, int row_bytes) {
+__device__ __forceinline__ void kv_copy_thread(const WriteParams &p, int row_bytes, int64_t gid) {
   const int cpr = row_bytes / 16;  // chunks per (token, head) row
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = p.num_tokens * p.num_kv_heads * cpr;
   if (gid >= total) return;
   const int64_t row = gid / cpr;
@@ -25,6 +25,10 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(const WriteParams p, int r
   const int64_t src = row * row_bytes + chunk * 16;
   *(u32x4 *)((char *)p.k_cache + dst) = *(const u32x4 *)((const char *)p.k + src);
   *(u32x4 *)((char *)p.v_cache + dst) = *(const u32x4 *)((const char *)p.v + src);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void kv_copy_kernel(const WriteParams p, int row_bytes) {
+  kv_copy_thread(p, row_bytes, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // INT8 quantiser: a group of D/8 lanes owns one (token, head) row, 8 values
@@ -76,9 +80,8 @@ __device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, i
 }
 
 template <int IT, int D>
-__global__ __launch_bounds__(256) void kv_quant_kernel(const WriteParams p) {
+__device__ __forceinline__ void kv_quant_thread(const WriteParams &p, int64_t gid) {
   constexpr int LPG = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = p.num_tokens * p.num_kv_heads * LPG;
   if (gid >= total) return;  // whole lane groups leave together (total % LPG == 0)
   const int64_t row = gid / LPG;
@@ -94,28 +97,73 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const WriteParams p) {
   quantise_row<IT, D>(p.v, row, part, (int8_t *)p.v_cache + srow * D, p.v_scale + srow, part == 0);
 }
 
-hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream) {
-  const int threads = 256;
+template <int IT, int D>
+__global__ __launch_bounds__(kPlanThreads) void kv_quant_kernel(const WriteParams p) {
+  kv_quant_thread<IT, D>(p, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// KV write and plan of one decode step in one launch (they do not depend on
+// each other): the last workgroup plans, the others write. Variant 0 copies,
+// variants 1..4 quantise ({bf16, fp32} input x head_dim {64, 128}).
+template <int VARIANT>
+__global__ __launch_bounds__(kPlanThreads) void prepare_kernel(const WriteParams w,
+                                                               const PlanParams pl,
+                                                               int row_bytes) {
+  if (blockIdx.x == gridDim.x - 1) {
+    plan_workgroup(pl);
+    return;
+  }
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if constexpr (VARIANT == 0) kv_copy_thread(w, row_bytes, gid);
+  if constexpr (VARIANT == 1) kv_quant_thread<PA_BF16, 64>(w, gid);
+  if constexpr (VARIANT == 2) kv_quant_thread<PA_BF16, 128>(w, gid);
+  if constexpr (VARIANT == 3) kv_quant_thread<PA_F32, 64>(w, gid);
+  if constexpr (VARIANT == 4) kv_quant_thread<PA_F32, 128>(w, gid);
+}
+
+namespace {
+
+// Write variant, row bytes (copy) and number of write workgroups.
+struct WriteShape {
+  int variant, row_bytes;
+  int64_t blocks;
+};
+
+WriteShape write_shape(const WriteParams &p) {
   if (p.cache_dtype != PA_I8) {
     const int row_bytes = p.head_dim * (p.cache_dtype == PA_F32 ? 4 : 2);
     const int64_t total = p.num_tokens * p.num_kv_heads * (row_bytes / 16);
-    const int64_t blocks = (total + threads - 1) / threads;
-    hipLaunchKernelGGL(kv_copy_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, p,
-                       row_bytes);
-    return hipGetLastError();
+    return {0, row_bytes, (total + kPlanThreads - 1) / kPlanThreads};
   }
   const int64_t total = p.num_tokens * p.num_kv_heads * (p.head_dim / 8);
-  const dim3 grid((unsigned)((total + threads - 1) / threads));
-  if (p.in_dtype == PA_BF16) {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 64>), grid, dim3(threads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 128>), grid, dim3(threads), 0, stream, p);
-  } else {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 64>), grid, dim3(threads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 128>), grid, dim3(threads), 0, stream, p);
+  const int variant = (p.in_dtype == PA_BF16 ? 1 : 3) + (p.head_dim == 128 ? 1 : 0);
+  return {variant, 0, (total + kPlanThreads - 1) / kPlanThreads};
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream) {
+  const WriteShape ws = write_shape(p);
+  const dim3 grid((unsigned)ws.blocks), block(kPlanThreads);
+  switch (ws.variant) {
+    case 0: hipLaunchKernelGGL(kv_copy_kernel, grid, block, 0, stream, p, ws.row_bytes); break;
+    case 1: hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 64>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 128>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 64>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 128>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare(const WriteParams &w, const PlanParams &pl, hipStream_t stream) {
+  const WriteShape ws = write_shape(w);
+  const dim3 grid((unsigned)(ws.blocks + 1)), block(kPlanThreads);
+  switch (ws.variant) {
+    case 0: hipLaunchKernelGGL(prepare_kernel<0>, grid, block, 0, stream, w, pl, ws.row_bytes); break;
+    case 1: hipLaunchKernelGGL(prepare_kernel<1>, grid, block, 0, stream, w, pl, 0); break;
+    case 2: hipLaunchKernelGGL(prepare_kernel<2>, grid, block, 0, stream, w, pl, 0); break;
+    case 3: hipLaunchKernelGGL(prepare_kernel<3>, grid, block, 0, stream, w, pl, 0); break;
+    default: hipLaunchKernelGGL(prepare_kernel<4>, grid, block, 0, stream, w, pl, 0); break;
   }
   return hipGetLastError();
 }

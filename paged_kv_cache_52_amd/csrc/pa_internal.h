@@ -30,6 +30,8 @@ struct WriteParams {
   int32_t num_kv_heads, head_dim, in_dtype, cache_dtype;
 };
 
+constexpr int kPlanThreads = 256;  // threads of the plan workgroup (and write workgroups)
+
 struct PlanParams {
   const int32_t *context_lens;
   int32_t *sched;
@@ -37,6 +39,8 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
+// KV write and plan in one launch: the last workgroup plans, the others write.
+hipError_t launch_prepare(const WriteParams &w, const PlanParams &p, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream);
 hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int blocks,

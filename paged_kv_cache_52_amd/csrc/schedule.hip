@@ -1,123 +1,11 @@
-// Plan kernel of the split-K decode: turns context_lens into the list of
-// splits the split kernel works through [EchoLLMServing notes, section 2:
-// split count derived from the context length, max(1, ceil(L/T))].
-//
-// One workgroup of 256 threads writes, into the scheduling scratch:
-//   sched[0]  = (#splits) * heff       work items (heff = KV heads x head groups)
-//   sched[1..3] = split_tokens, heff, num_seqs   (checked by the split kernel)
-//   sched[4+2i], sched[5+2i] = (s << 16) | j, L_s   split i, in this order:
-//     1. all splits but the last of each sequence (full T-token splits),
-//        sequence by sequence;
-//     2. the last split of each sequence, longest first (counting sort on its
-//        16-token tile count), so the shortest work runs at the very end.
-// A sequence of length 0 contributes one empty split. Lengths are clamped
-// exactly as the split kernel clamps them.
-#include "pa_common.h"
-#include "pa_internal.h"
+// Plan kernel: one workgroup running the plan of a decode step (see
+// plan_device.h).
+#include "plan_device.h"
 
 namespace pa {
 
-constexpr int kPlanThreads = 256;
-constexpr int kMaxTileBuckets = PA_MAX_SPLIT_TOKENS / kBlock;  // tile counts 1..256
-
-__device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
-  return max(0, min(p.context_lens[s], p.max_len));
-}
-
-__device__ __forceinline__ int num_splits_of(int L, int T) { return max(1, (L + T - 1) / T); }
-
-// Tiles of the last split (1 for an empty sequence, which sorts last).
-__device__ __forceinline__ int last_tiles(int L, int T) {
-  if (L <= 0) return 1;
-  const int rest = L - (num_splits_of(L, T) - 1) * T;
-  return (rest + kBlock - 1) / kBlock;
-}
-
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const PlanParams p) {
-  __shared__ int wave_sum[kPlanThreads / kWave];
-  __shared__ int bucket[kMaxTileBuckets + 1];  // count, then start offset, of each tile count
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid / kWave;
-  const int T = p.split_tokens;
-
-  for (int i = tid; i <= kMaxTileBuckets; i += kPlanThreads) bucket[i] = 0;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-
-  // Pass 1: the full splits, with a workgroup-wide exclusive scan of their
-  // per-sequence counts; also histogram the last splits by tile count.
-  for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
-    const int s = base + tid;
-    const bool valid = s < p.num_seqs;
-    const int L = valid ? clamp_len(p, s) : 0;
-    const int f = valid ? num_splits_of(L, T) - 1 : 0;
-    int incl = f;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == kWave - 1) wave_sum[wave] = incl;
-    if (valid) atomicAdd(&bucket[last_tiles(L, T)], 1);
-    __syncthreads();
-    int before = carry, total = 0;
-#pragma unroll
-    for (int w = 0; w < kPlanThreads / kWave; ++w) {
-      if (w < wave) before += wave_sum[w];
-      total += wave_sum[w];
-    }
-    const int first = before + incl - f;
-    for (int q = 0; q < f; ++q) {
-      p.sched[kSchedHeader + 2 * (first + q)] = (s << 16) | q;
-      p.sched[kSchedHeader + 2 * (first + q) + 1] = L;
-    }
-    __syncthreads();
-    if (tid == 0) carry += total;
-    __syncthreads();
-  }
-  const int n_full = carry;
-
-  // Start offset of each tile-count bucket, longest first: a reverse
-  // exclusive scan over buckets kMaxTileBuckets .. 1 (one bucket per thread).
-  {
-    const int b = kMaxTileBuckets - tid;  // tid 0 -> 256, ..., tid 255 -> 1
-    const int c = bucket[b];
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) wave_sum[wave] = incl;
-    __syncthreads();
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < kPlanThreads / kWave; ++w)
-      if (w < wave) before += wave_sum[w];
-    bucket[b] = n_full + before + incl - c;
-  }
-  __syncthreads();
-
-  // Pass 2: place each sequence's last split in its bucket (the order inside
-  // a bucket does not affect any result).
-  for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
-    const int s = base + tid;
-    if (s < p.num_seqs) {
-      const int L = clamp_len(p, s);
-      const int pos = atomicAdd(&bucket[last_tiles(L, T)], 1);
-      p.sched[kSchedHeader + 2 * pos] = (s << 16) | (num_splits_of(L, T) - 1);
-      p.sched[kSchedHeader + 2 * pos + 1] = L;
-    }
-  }
-  if (tid == 0) {
-    p.sched[0] = (n_full + p.num_seqs) * p.heff;
-    p.sched[1] = T;
-    p.sched[2] = p.heff;
-    p.sched[3] = p.num_seqs;
-  }
+  plan_workgroup(p);
 }
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream) {

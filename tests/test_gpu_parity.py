@@ -390,6 +390,39 @@ def test_plan_is_shared_and_mismatch_is_ignored():
     assert bool((m == 7.0).all()) and bool((acc == 7.0).all())
 
 
+@pytest.mark.parametrize("name", ["llama8b_bf16", "int8_kv"])
+def test_prepare_equals_write_then_plan(name):
+    """The fused write-and-plan launch gives the same pool bytes and the same
+    plan as the two separate calls."""
+    print(f"[case] prepare {name}", flush=True)
+    b = workloads.make_batch(name, 171, "cpu", num_seqs=9, ctx_range=(1, 700))
+    g1, g2 = _to(b, "cuda"), _to(b, "cuda")
+    if b.k_cache.dtype == torch.int8:
+        for g in (g1, g2):
+            pa().paged_kv_write(g.fill_k, g.fill_v, g.fill_slots, g.k_cache, g.v_cache,
+                                g.k_scale, g.v_scale)
+    Hq, mb = b.q.shape[1], b.block_tables.shape[1]
+    pa().paged_kv_write(g1.new_k, g1.new_v, g1.slot_mapping, g1.k_cache, g1.v_cache, g1.k_scale,
+                        g1.v_scale)
+    p1 = pa().paged_attn_plan(g1.context_lens, Hq, b.k_cache.shape[1], mb,
+                              max_context_len=b.max_context_len, split_tokens=64)
+    p2 = pa().paged_decode_prepare(g2.new_k, g2.new_v, g2.slot_mapping, g2.k_cache, g2.v_cache,
+                                   g2.context_lens, Hq, mb, g2.k_scale, g2.v_scale,
+                                   max_context_len=b.max_context_len, split_tokens=64)
+    torch.cuda.synchronize()
+    for a, c in [(g1.k_cache, g2.k_cache), (g1.v_cache, g2.v_cache)]:
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
+    if b.k_scale is not None:
+        assert torch.equal(g1.k_scale, g2.k_scale) and torch.equal(g1.v_scale, g2.v_scale)
+    n = int(p1.sched[0].item()) // b.k_cache.shape[1]
+    s1, s2 = p1.sched[:4 + 2 * n].cpu(), p2.sched[:4 + 2 * n].cpu()
+    assert torch.equal(s1[:4], s2[:4])
+    # Entries within one tile-count bucket may come in any order.
+    e1 = sorted(zip(s1[4::2].tolist(), s1[5::2].tolist()))
+    e2 = sorted(zip(s2[4::2].tolist(), s2[5::2].tolist()))
+    assert e1 == e2
+
+
 def test_decode_is_deterministic():
     b = workloads.make_batch("llama8b_bf16", 131, "cpu", num_seqs=6, ctx_range=(1, 2000))
     g = _to(b, "cuda")
