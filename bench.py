@@ -160,7 +160,7 @@ def main():
     def prepare():
         # KV write of the step's new tokens and the split plan, one launch.
         plan[0] = pa.paged_decode_prepare(b.new_k, b.new_v, b.slot_mapping, b.k_cache,
-                                          b.v_cache, b.context_lens, Hq,
+                                          b.v_cache, b.context_lens,
                                           b.block_tables.shape[1], b.k_scale, b.v_scale,
                                           max_context_len=b.max_context_len, split_tokens=T,
                                           sched=sched)

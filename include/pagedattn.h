@@ -88,8 +88,9 @@ const char *pa_strerror(int status);
 int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
 
 /* Split size (tokens, a multiple of 16) the library picks when the caller
- * passes split_tokens = 0: the chunk is tuned on MI355X for the batch shape.
- * Host-only arithmetic. */
+ * passes split_tokens = 0, tuned on MI355X; it depends only on the batch size
+ * and the length bound (num_kv_heads is accepted for future tuning and
+ * ignored). Host-only arithmetic. */
 int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
 /* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
@@ -128,16 +129,16 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  * the device and writes into `sched` the list of every split of the batch,
  * max(1, ceil(L_s / T)) per sequence, full splits first and then the last
  * split of each sequence, longest first. The list depends only on the lengths,
- * T and the head counts, so one plan serves every attention layer of a step.
+ * T and the length bounds, so one plan serves every attention layer of a step.
  *   context_lens     [num_seqs] int32 (device)
  *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
  *   split_tokens     T as for paged_attn_decode_partial (0: default)
  *   sched            device scratch of pa_sched_bytes(num_seqs, max_splits) bytes
  *                    with max_splits >= pa_num_splits(max_context_len, T)
  */
-int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
-                    int32_t split_tokens, int32_t *sched, hipStream_t stream);
+int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int32_t split_tokens, int32_t *sched,
+                    hipStream_t stream);
 
 /*
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
@@ -150,7 +151,7 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         const int32_t *context_lens, int32_t num_seqs,
                          int32_t max_blocks_per_seq, int32_t max_context_len,
                          int32_t split_tokens, int32_t *sched, hipStream_t stream);
 
@@ -160,10 +161,9 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
  * (m, l, acc) of that split. The g = Hq/Hkv query heads of a KV head share
  * every K/V load. Works through the split list of `sched`, which
  * paged_attn_plan must have written (on this stream, before this call) for the
- * same context_lens, num_seqs, head counts, max_blocks_per_seq,
- * max_context_len and split_tokens; a plan for other split_tokens, head
- * counts or num_seqs is ignored (nothing is written), other mismatches give
- * unspecified results.
+ * same context_lens, num_seqs, max_blocks_per_seq, max_context_len and
+ * split_tokens; a plan for another split_tokens, num_seqs or length bound is
+ * ignored (nothing is written), other mismatches give unspecified results.
  *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (PA_F32/PA_BF16)
  *   k_cache, ...   pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
  *                  (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and

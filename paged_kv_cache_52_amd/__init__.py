@@ -102,12 +102,10 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
 
 @dataclasses.dataclass
 class Plan:
-    """Work list of one decode step (see paged_attn_plan); reusable by every
-    layer of the step."""
+    """Split list of one decode step (see paged_attn_plan); it depends only on
+    the lengths and bounds, so every layer of the step can reuse it."""
     sched: torch.Tensor         # int32 scratch, pa_sched_bytes(num_seqs, max_splits)
     context_lens: torch.Tensor  # [B] int32 the plan was made from
-    num_q_heads: int
-    num_kv_heads: int
     max_blocks_per_seq: int
     max_context_len: int
     split_tokens: int
@@ -152,26 +150,30 @@ def _max_len(context_lens, max_context_len):
     return int(max_context_len)
 
 
-def paged_attn_plan(context_lens, num_q_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
-                    *, max_context_len=None, split_tokens=None,
-                    sched: Optional[torch.Tensor] = None) -> Plan:
-    """Plan kernel: list every split of the batch (device side, from
-    context_lens) for the split kernel."""
-    lib = _lib.load()
+def _plan_sizes(context_lens, max_context_len, split_tokens, sched):
     B = context_lens.shape[0]
     mcl = _max_len(context_lens, max_context_len)
-    T = int(split_tokens) if split_tokens else default_split_tokens(B, num_kv_heads, mcl)
+    T = int(split_tokens) if split_tokens else default_split_tokens(B, 1, mcl)
     S = max(1, num_splits(mcl, T))
     need = sched_bytes(B, S)
     if sched is None or sched.numel() * sched.element_size() < need:
         sched = torch.empty(max(need, 16) // 4, dtype=torch.int32, device=context_lens.device)
-    _check(lib.paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B, num_q_heads,
-                               num_kv_heads, max_blocks_per_seq, mcl, T,
-                               _dev(sched, "sched", torch.int32), _stream(context_lens.device)))
-    return Plan(sched, context_lens, num_q_heads, num_kv_heads, max_blocks_per_seq, mcl, T, S)
+    return B, mcl, T, S, sched
 
 
-def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens, num_q_heads: int,
+def paged_attn_plan(context_lens, max_blocks_per_seq: int, *, max_context_len=None,
+                    split_tokens=None, sched: Optional[torch.Tensor] = None) -> Plan:
+    """Plan kernel: list every split of the batch (on the device, from
+    context_lens) for the split kernel."""
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched)
+    _check(_lib.load().paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B,
+                                       max_blocks_per_seq, mcl, T,
+                                       _dev(sched, "sched", torch.int32),
+                                       _stream(context_lens.device)))
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S)
+
+
+def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
                          max_blocks_per_seq: int, k_scale=None, v_scale=None, *,
                          max_context_len=None, split_tokens=None,
                          sched: Optional[torch.Tensor] = None) -> Plan:
@@ -184,21 +186,15 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens, num
         raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
     if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
         raise PagedAttnError("an int8 cache needs k_scale and v_scale")
-    B = context_lens.shape[0]
-    mcl = _max_len(context_lens, max_context_len)
-    T = int(split_tokens) if split_tokens else default_split_tokens(B, Hkv, mcl)
-    S = max(1, num_splits(mcl, T))
-    need = sched_bytes(B, S)
-    if sched is None or sched.numel() * sched.element_size() < need:
-        sched = torch.empty(max(need, 16) // 4, dtype=torch.int32, device=context_lens.device)
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched)
     _check(_lib.load().paged_decode_prepare(
         _dev(k, "k"), _dev(v, "v", k.dtype), _code(k),
         _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), NB, _code(k_cache),
-        _dev(context_lens, "context_lens", torch.int32), B, num_q_heads, max_blocks_per_seq,
-        mcl, T, _dev(sched, "sched", torch.int32), _stream(k.device)))
-    return Plan(sched, context_lens, num_q_heads, Hkv, max_blocks_per_seq, mcl, T, S)
+        _dev(context_lens, "context_lens", torch.int32), B, max_blocks_per_seq, mcl, T,
+        _dev(sched, "sched", torch.int32), _stream(k.device)))
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S)
 
 
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -211,10 +207,10 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     if plan is None:
-        plan = paged_attn_plan(context_lens, Hq, Hkv, block_tables.shape[1],
+        plan = paged_attn_plan(context_lens, block_tables.shape[1],
                                max_context_len=max_context_len, split_tokens=split_tokens)
-    elif ((plan.num_q_heads, plan.num_kv_heads, plan.max_blocks_per_seq) !=
-          (Hq, Hkv, block_tables.shape[1]) or plan.context_lens is not context_lens or
+    elif (plan.max_blocks_per_seq != block_tables.shape[1] or
+          plan.context_lens is not context_lens or
           (split_tokens and int(split_tokens) != plan.split_tokens) or
           (max_context_len is not None and int(max_context_len) != plan.max_context_len)):
         raise PagedAttnError("plan was made for other arguments")

@@ -97,22 +97,18 @@ int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *s
 }
 
 // Argument checks of the plan; fills `out` on success.
-int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-               int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
-               int32_t split_tokens, int32_t *sched, pa::PlanParams *out) {
-  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      max_blocks_per_seq <= 0 || max_context_len < 0)
+int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+               int32_t max_context_len, int32_t split_tokens, int32_t *sched,
+               pa::PlanParams *out) {
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
-    return PA_ERR_SHAPE;
-  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, 1, max_context_len);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
-  const int group = num_q_heads / num_kv_heads;
   *out = pa::PlanParams{
       context_lens, sched, num_seqs,
       (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE),
-      split_tokens, num_kv_heads * (group > 8 ? group / 8 : 1)};
+      split_tokens};
   return PA_OK;
 }
 
@@ -131,12 +127,12 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
   return launch_status(pa::launch_kv_write(w, stream));
 }
 
-int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
-                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int32_t split_tokens, int32_t *sched,
+                    hipStream_t stream) {
   pa::PlanParams pl;
-  const int st = check_plan(context_lens, num_seqs, num_q_heads, num_kv_heads,
-                            max_blocks_per_seq, max_context_len, split_tokens, sched, &pl);
+  const int st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
+                            split_tokens, sched, &pl);
   if (st != PA_OK || num_seqs == 0) return st;
   return launch_status(pa::launch_plan(pl, stream));
 }
@@ -145,7 +141,7 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         const int32_t *context_lens, int32_t num_seqs,
                          int32_t max_blocks_per_seq, int32_t max_context_len,
                          int32_t split_tokens, int32_t *sched, hipStream_t stream) {
   pa::WriteParams w;
@@ -153,8 +149,8 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
                        v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK) return st;
-  st = check_plan(context_lens, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
-                  max_context_len, split_tokens, sched, &pl);
+  st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, split_tokens,
+                  sched, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
   return launch_status(pa::launch_prepare(w, pl, stream));
@@ -268,8 +264,8 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   float *m = (float *)base;
   float *l = (float *)(base + align256(rows * sizeof(float)));
   float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
-  int st = paged_attn_plan(context_lens, num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
-                           max_context_len, split_tokens, sched, stream);
+  int st = paged_attn_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
+                           split_tokens, sched, stream);
   if (st != PA_OK) return st;
   st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_q_heads, head_dim, k_cache,
                                      v_cache, k_scale, v_scale, cache_dtype, num_blocks,

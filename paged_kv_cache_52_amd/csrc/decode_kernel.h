@@ -54,8 +54,8 @@ struct DecodeParams {
 constexpr int kPrefetch = PA_PREFETCH;
 
 // Layout of the scheduling scratch written by the plan kernel:
-//   [0] number of work items (splits x KV-head groups)
-//   [1] split_tokens, [2] KV-head groups, [3] num_seqs the plan was made for
+//   [0] number of splits of the batch
+//   [1] split_tokens, [2] num_seqs, [3] clamped max length the plan was made for
 //   then two words per split, full splits first: (sequence << 16 | split) and
 //   the sequence's clamped context length.
 constexpr int kSchedHeader = 4;
@@ -276,30 +276,200 @@ struct DecodeWave {
   }
 };
 
-// One work item: split j of sequence s for KV head kvh (query-head group hg).
-// The NW waves of the workgroup share the split's tiles, merge their states in
-// LDS and write the split's partials. Contains one workgroup barrier.
+// ---------------------------------------------------------------------------
+// MFMA engine (bf16 cache and bf16 q, head_dim 128, any group size g <= 16).
+//
+// The g query heads of a KV head make q.k^T and P.V small dense products, so
+// one wave computes them on the matrix cores:
+//   S[16 tokens][16 heads] = K_tile . q^T   4 x v_mfma_f32_16x16x32_bf16
+//   O[16 heads][128 dims] += P . V_tile     8 x 2 x v_mfma_f32_16x16x16_bf16
+// with the query heads padded to 16 (zero q). Lane l (c = l % 16, g = l / 16):
+//   - K operand: token c, dims 32i + 8g .. +8 (load i of the tile, i < 4); one
+//     load instruction reads 64 contiguous bytes of each of the 16 rows;
+//   - q operand: head c, the same dims;
+//   - S: head c, tokens 4g .. 4g+3 -- which is exactly how P must be laid out
+//     as the A operand of P.V (rows heads, k = tokens 4g..4g+3), so P never
+//     moves between lanes;
+//   - V: rows 4g .. 4g+3, dims 8c .. 8c+7 (load i reads rows i, 4+i, 8+i,
+//     12+i, 256 contiguous bytes each); v_perm gathers, for output column
+//     block jj, element jj of the four rows into the B operand;
+//   - O: heads 4g .. 4g+3, dims 8c + jj.
+// P is split into bf16 hi + lo parts (two MFMAs) so that the softmax weights
+// keep ~16 significant bits. The running max is shared by the four lane groups
+// of a head (two cross-row max steps per tile) and is only moved when a tile's
+// max exceeds it by more than kRescaleSlack (exp2 arguments stay <= that
+// slack); the true max is tracked on the side and the state is renormalised
+// to it once, at the end of the split.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay below 2^8
+
+template <int CT, int D>
+struct MfmaEligible {
+  static constexpr bool value = CT == PA_BF16 && D == 128;
+};
+
+struct MfmaTile {
+  u32x4 k[4];  // K operand fragments
+  u32x4 v[4];  // V rows 4g + i
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <int G>
+struct MfmaWave {
+  static constexpr int ROW = 256;        // bytes per token row (128 bf16)
+  static constexpr int TILE = kBlock * ROW;
+  u32x4 qB[4];  // q operand: head c (zero beyond the group), dims 32i + 8g .. +8
+  f32x4 acc[8];  // O: heads 4g + r, dims 8c + jj
+  float m;       // reference max (log2 units) of head c
+  float mtrue;   // true running max of head c
+  float l;       // sum of exp2(z - m) over this lane's tokens of head c
+
+  __device__ __forceinline__ void load_tile(MfmaTile &t, const DecodeParams &p, int blk, int kvh,
+                                            int koff, int voff) {
+    const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc((const char *)p.k_cache + tile * TILE, TILE);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc((const char *)p.v_cache + tile * TILE, TILE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * i, 0, kStreamPolicy);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, kStreamPolicy);
+  }
+
+  __device__ __forceinline__ void consume(MfmaTile &t, int valid_rows, int g, float scale_log2) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]),
+                                                  __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0, 0);
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
+    if (valid_rows < kBlock) {  // uniform: the last tile of the split
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 4 * g + r < valid_rows;
+        z[r] = ok ? z[r] : -INFINITY;
+        if (!ok) t.v[r] = u32x4{0u, 0u, 0u, 0u};  // NaN * 0 would leak: select, not scale
+      }
+    }
+    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    mtrue = fmaxf(mtrue, bm);
+    const bool grow = bm > m + kRescaleSlack;
+    if (__any(grow)) rescale(grow ? bm : m, g);
+    float pz[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
+    l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+    // P = hi + lo, both bf16.
+    const uint32_t h01 = pack_bf16(pz[0], pz[1]), h23 = pack_bf16(pz[2], pz[3]);
+    const uint32_t l01 = pack_bf16(pz[0] - bf16_lo(h01), pz[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16(pz[2] - bf16_lo(h23), pz[3] - bf16_hi(h23));
+    const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+    const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t w0 = t.v[0][jj >> 1], w1 = t.v[1][jj >> 1];
+      const uint32_t w2 = t.v[2][jj >> 1], w3 = t.v[3][jj >> 1];
+      const uint32_t b01 = __builtin_amdgcn_perm(w1, w0, sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(w3, w2, sel);
+      const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{b01, b23});
+      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[jj], 0, 0, 0);
+      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[jj], 0, 0, 0);
+    }
+  }
+
+  // Move the reference max of head c to mnew (per lane) and rescale l and the
+  // O rows (heads 4g + r get the factor computed in lane 4g + r). All lanes of
+  // the wave must call it together.
+  __device__ __forceinline__ void rescale(float mnew, int g) {
+    const float alpha = fast_exp2(m - mnew);
+    l *= alpha;
+    m = mnew;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[jj][r] *= ar;
+    }
+  }
+};
+
+// Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split; leaves
+// the wave's (m, l, acc) for heads < G in LDS row `wave`.
 template <int QT, int CT, int D, int G, int NW>
-__device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
-                                              int kvh, int hg, int lane, int wave,
-                                              float (&sm_m)[NW][G],
-                                              float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
+__device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int hq0,
+                                               int b0, int t1, int wb0, int wb1, int lane,
+                                               int wave, float (&sm_m)[NW][G],
+                                               float (&sm_l)[NW][G],
+                                               float (&sm_acc)[NW][G][D]) {
+  MfmaWave<G> st;
+  const int c = lane % 16, g = lane / 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.qB[i] = u32x4{0u, 0u, 0u, 0u};
+    if (c < G)
+      st.qB[i] = *(const u32x4 *)((const uint16_t *)p.q +
+                                  ((int64_t)s * p.num_q_heads + hq0 + c) * D + 32 * i + 8 * g);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) st.acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegBig;
+  st.mtrue = kNegBig;
+  st.l = 0.f;
+
+  int my_id = 0;
+  if (lane < wb1 - wb0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
+  const int last_block = (int)(p.num_blocks - 1);
+  const int koff = c * MfmaWave<G>::ROW + 16 * g;
+  const int voff = 4 * g * MfmaWave<G>::ROW + 16 * c;
+  MfmaTile t;
+  for (int n = wb0; n < wb1; ++n) {
+    const int blk = min(max(__builtin_amdgcn_readlane(my_id, n - wb0), 0), last_block);
+    st.load_tile(t, p, blk, kvh, koff, voff);
+    st.consume(t, min(kBlock, t1 - (b0 + n) * kBlock), g, p.scale_log2);
+  }
+  // Renormalise to the true max (every lane takes part: rescale reads other
+  // lanes' factors), then sum l over the four lane groups.
+  st.rescale(fmaxf(st.mtrue, st.m), g);
+  float lt = st.l + __shfl_xor(st.l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (lane < G) {
+    sm_m[wave][lane] = st.m;
+    sm_l[wave][lane] = lt;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    if (h < G) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sm_acc[wave][h][8 * c + jj] = st.acc[jj][r];
+    }
+  }
+}
+
+// Per-wave pass of the VALU engine (every dtype and head_dim); same contract.
+template <int QT, int CT, int D, int G, int NW>
+__device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int kvh, int hq0,
+                                               int b0, int t1, int wb0, int wb1, int lane,
+                                               int wave, float (&sm_m)[NW][G],
+                                               float (&sm_l)[NW][G],
+                                               float (&sm_acc)[NW][G][D]) {
   using S = DecodeShape<QT, CT, D, G>;
   using W = DecodeWave<QT, CT, D, G, NW>;
-  // Context length, clamped so that no read leaves the table or the pool.
-  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
-  const int L = max(0, min(len, lmax));
-  const int nsplit = max(1, (L + p.split_tokens - 1) / p.split_tokens);
-  if (j >= nsplit) return;  // never for planned items; uniform across the workgroup
-  const int t0 = j * p.split_tokens;
-  const int t1 = min(t0 + p.split_tokens, L);
-  const int b0 = t0 / kBlock;
-  const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;
-  const int per = (nb + NW - 1) / NW;
-  const int wb0 = min(nb, wave * per);
-  const int wb1 = min(nb, wb0 + per);
-  const int hq0 = kvh * (p.num_q_heads / p.num_kv_heads) + hg * G;
-
   W st;
   // q slice for this lane's dims.
   {
@@ -338,10 +508,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 
   // Physical block ids of this wave's blocks, one per lane (per <= 64).
   int my_id = 0;
-  {
-    const int cnt = wb1 - wb0;
-    if (lane < cnt) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
-  }
+  if (lane < wb1 - wb0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
   const int last_block = (int)(p.num_blocks - 1);  // the host checks 0 < num_blocks < 2^31
   auto block_id = [&](int n) {
     int b = __builtin_amdgcn_readlane(my_id, n - wb0);
@@ -402,6 +569,36 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
       sm_l[wave][h] = st.l[h];
     }
   }
+}
+
+// One work item: split j of sequence s for KV head kvh (query-head group hg).
+// The NW waves of the workgroup share the split's tiles, merge their states in
+// LDS and write the split's partials. Contains one workgroup barrier.
+template <int QT, int CT, int D, int G, int NW>
+__device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
+                                              int kvh, int hg, int lane, int wave,
+                                              float (&sm_m)[NW][G],
+                                              float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
+  // Context length, clamped so that no read leaves the table or the pool.
+  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  const int L = max(0, min(len, lmax));
+  const int nsplit = max(1, (L + p.split_tokens - 1) / p.split_tokens);
+  if (j >= nsplit) return;  // never for planned items; uniform across the workgroup
+  const int t0 = j * p.split_tokens;
+  const int t1 = min(t0 + p.split_tokens, L);
+  const int b0 = t0 / kBlock;
+  const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;
+  const int per = (nb + NW - 1) / NW;
+  const int wb0 = min(nb, wave * per);
+  const int wb1 = min(nb, wb0 + per);
+  const int hq0 = kvh * (p.num_q_heads / p.num_kv_heads) + hg * G;
+
+  if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value)
+    wave_pass_mfma<QT, CT, D, G, NW>(p, s, kvh, hq0, b0, t1, wb0, wb1, lane, wave, sm_m, sm_l,
+                                     sm_acc);
+  else
+    wave_pass_valu<QT, CT, D, G, NW>(p, s, kvh, hq0, b0, t1, wb0, wb1, lane, wave, sm_m, sm_l,
+                                     sm_acc);
   __syncthreads();
 
   // Merge the waves and write the split's partials.
@@ -428,11 +625,12 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 
 // Split kernel. Work item k is split sched[kSchedHeader + 2*(k / heff)]
 // (packed sequence << 16 | split, followed by the sequence's context length)
-// for KV-head group k % heff, from the list the plan kernel wrote (full splits
-// first, the shortest last splits at the end). Workgroup k processes item k;
-// the grid is an upper bound on the number of items and the workgroups past
-// the end of the list, all at the end of the grid, exit at once. A plan made
-// for other parameters counts as an empty list.
+// for KV-head group k % heff (heff = KV heads x query-head groups), from the
+// list the plan kernel wrote (full splits first, the shortest last splits at
+// the end). Workgroup k processes item k; the grid is an upper bound on the
+// number of items and the workgroups past the end of the list, all at the end
+// of the grid, exit at once. A plan made for another split size, batch or
+// length bound counts as an empty list.
 template <int QT, int CT, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodeParams p) {
   __shared__ float sm_m[NW][G];
@@ -440,9 +638,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodePa
   __shared__ float sm_acc[NW][G][D];
 
   const int heff = p.num_kv_heads * p.head_groups;
-  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == heff &&
-                       p.sched[3] == p.num_seqs;
-  const int n_items = plan_ok ? p.sched[0] : 0;
+  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
+                       p.sched[3] == lmax;
+  const int n_items = plan_ok ? p.sched[0] * heff : 0;
   const int k = blockIdx.x;
   if (k >= n_items) return;
   const int lane = lane_id();
@@ -477,16 +676,30 @@ hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t str
   return hipGetLastError();
 }
 
-// Dispatch on (head_dim, group size) for one (q dtype, cache dtype) pair.
+// Dispatch on (head_dim, group size) for one (q dtype, cache dtype) pair. The
+// MFMA engine takes all g <= 16 heads of a KV head in one workgroup; the VALU
+// engine takes at most 8 (g = 16 runs as two query-head groups).
 template <int QT, int CT>
-hipError_t dispatch_decode(const DecodeParams &p, int group, int grid_splits, hipStream_t stream) {
+hipError_t dispatch_decode(DecodeParams p, int group, int grid_splits, hipStream_t stream) {
   auto by_group = [&](auto dtag) -> hipError_t {
     constexpr int D = decltype(dtag)::value;
-    switch (group) {
-      case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
-      case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
-      case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
-      default: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);  // 8, and 16 as 2 x 8
+    if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
+      p.head_groups = 1;
+      switch (group) {
+        case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
+        case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
+        case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
+        case 8: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);
+        default: return launch_decode<QT, CT, D, 16>(p, grid_splits, stream);
+      }
+    } else {
+      p.head_groups = group > 8 ? group / 8 : 1;
+      switch (group) {
+        case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
+        case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
+        case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
+        default: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);  // 8, and 16 as 2 x 8
+      }
     }
   };
   if (p.head_dim == 64) return by_group(std::integral_constant<int, 64>{});

@@ -35,7 +35,7 @@ constexpr int kPlanThreads = 256;  // threads of the plan workgroup (and write w
 struct PlanParams {
   const int32_t *context_lens;
   int32_t *sched;
-  int32_t num_seqs, max_len, split_tokens, heff;
+  int32_t num_seqs, max_len, split_tokens;
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);

@@ -5,8 +5,9 @@
 // splits the split kernel works through [EchoLLMServing notes, section 2:
 // split count derived from the context length, max(1, ceil(L/T))]. It writes
 // into the scheduling scratch:
-//   sched[0]  = (#splits) * heff       work items (heff = KV heads x head groups)
-//   sched[1..3] = split_tokens, heff, num_seqs   (checked by the split kernel)
+//   sched[0]  = number of splits of the batch
+//   sched[1..3] = split_tokens, num_seqs, clamped max length (checked by the
+//                 split kernel)
 //   sched[4+2i], sched[5+2i] = (s << 16) | j, L_s   split i, in this order:
 //     1. all splits but the last of each sequence (full T-token splits),
 //        sequence by sequence;
@@ -116,10 +117,10 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     }
   }
   if (tid == 0) {
-    p.sched[0] = (n_full + p.num_seqs) * p.heff;
+    p.sched[0] = n_full + p.num_seqs;
     p.sched[1] = T;
-    p.sched[2] = p.heff;
-    p.sched[3] = p.num_seqs;
+    p.sched[2] = p.num_seqs;
+    p.sched[3] = p.max_len;
   }
 }
 

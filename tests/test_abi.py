@@ -90,19 +90,33 @@ def test_kv_write_validation(lib):
 def test_prepare_validation(lib):
     def prep(**kw):
         a = dict(k=FAKE, v=FAKE, idt=BF16, slots=FAKE, T=4, Hkv=8, D=128, kc=FAKE, vc=FAKE,
-                 NB=100, cdt=BF16, cl=FAKE, B=4, Hq=32, mb=8, mcl=128, split=512, sched=FAKE)
+                 NB=100, cdt=BF16, cl=FAKE, B=4, mb=8, mcl=128, split=512, sched=FAKE)
         a.update(kw)
         return lib.paged_decode_prepare(a["k"], a["v"], a["idt"], a["slots"], a["T"], a["Hkv"],
                                         a["D"], a["kc"], a["vc"], None, None, a["NB"], a["cdt"],
-                                        a["cl"], a["B"], a["Hq"], a["mb"], a["mcl"], a["split"],
+                                        a["cl"], a["B"], a["mb"], a["mcl"], a["split"],
                                         a["sched"], None)
     assert prep(D=96) == ERR_SHAPE
-    assert prep(Hq=24) == ERR_SHAPE
+    assert prep(mb=0) == ERR_SHAPE
+    assert prep(B=65536) == ERR_SHAPE
     assert prep(split=40) == ERR_SPLIT
     assert prep(sched=None) == ERR_NULL
     assert prep(k=None) == ERR_NULL
     assert prep(kc=FAKE_ODD) == ERR_ALIGN
     assert prep(T=0, B=0, k=None, cl=None) == OK
+
+
+def test_plan_validation(lib):
+    def plan(**kw):
+        a = dict(cl=FAKE, B=4, mb=8, mcl=128, split=512, sched=FAKE)
+        a.update(kw)
+        return lib.paged_attn_plan(a["cl"], a["B"], a["mb"], a["mcl"], a["split"], a["sched"],
+                                   None)
+    assert plan(mb=0) == ERR_SHAPE
+    assert plan(mcl=-1) == ERR_SHAPE
+    assert plan(split=8) == ERR_SPLIT
+    assert plan(sched=None) == ERR_NULL
+    assert plan(B=0, cl=None, sched=None) == OK
 
 
 def _partial(lib, **kw):

@@ -337,15 +337,13 @@ def test_plan_lists_every_split_once(T):
                              ctx_range=(1024, 1024))
     b.context_lens = torch.tensor(lens, dtype=torch.int32)
     g = _to(b, "cuda")
-    plan = pa().paged_attn_plan(g.context_lens, g.q.shape[1], g.k_cache.shape[1],
-                                g.block_tables.shape[1], max_context_len=g.max_context_len,
-                                split_tokens=T)
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=T)
     torch.cuda.synchronize()
     sched = plan.sched.cpu().numpy()
-    heff = b.k_cache.shape[1]
     nsplit = [max(1, -(-L // T)) for L in lens]
     n = sum(nsplit)
-    assert list(sched[:4]) == [n * heff, T, heff, len(lens)]
+    assert list(sched[:4]) == [n, T, len(lens), min(g.max_context_len, 16 * b.block_tables.shape[1])]
     entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[4:4 + 2 * n:2]]
     assert list(sched[5:5 + 2 * n:2]) == [lens[s] for s, _ in entries]
     assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
@@ -362,9 +360,8 @@ def test_plan_is_shared_and_mismatch_is_ignored():
     b = workloads.make_batch("llama8b_bf16", 161, "cpu", num_seqs=5, ctx_range=(1, 900))
     g = _to(b, "cuda")
     ref = _oracle_decode(b)
-    plan = pa().paged_attn_plan(g.context_lens, g.q.shape[1], g.k_cache.shape[1],
-                                g.block_tables.shape[1], max_context_len=g.max_context_len,
-                                split_tokens=64)
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=64)
     for _ in range(2):
         parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
                                                g.context_lens, g.scale, plan=plan)
@@ -404,17 +401,17 @@ def test_prepare_equals_write_then_plan(name):
     Hq, mb = b.q.shape[1], b.block_tables.shape[1]
     pa().paged_kv_write(g1.new_k, g1.new_v, g1.slot_mapping, g1.k_cache, g1.v_cache, g1.k_scale,
                         g1.v_scale)
-    p1 = pa().paged_attn_plan(g1.context_lens, Hq, b.k_cache.shape[1], mb,
-                              max_context_len=b.max_context_len, split_tokens=64)
+    p1 = pa().paged_attn_plan(g1.context_lens, mb, max_context_len=b.max_context_len,
+                              split_tokens=64)
     p2 = pa().paged_decode_prepare(g2.new_k, g2.new_v, g2.slot_mapping, g2.k_cache, g2.v_cache,
-                                   g2.context_lens, Hq, mb, g2.k_scale, g2.v_scale,
+                                   g2.context_lens, mb, g2.k_scale, g2.v_scale,
                                    max_context_len=b.max_context_len, split_tokens=64)
     torch.cuda.synchronize()
     for a, c in [(g1.k_cache, g2.k_cache), (g1.v_cache, g2.v_cache)]:
         assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
     if b.k_scale is not None:
         assert torch.equal(g1.k_scale, g2.k_scale) and torch.equal(g1.v_scale, g2.v_scale)
-    n = int(p1.sched[0].item()) // b.k_cache.shape[1]
+    n = int(p1.sched[0].item())
     s1, s2 = p1.sched[:4 + 2 * n].cpu(), p2.sched[:4 + 2 * n].cpu()
     assert torch.equal(s1[:4], s2[:4])
     # Entries within one tile-count bucket may come in any order.
