@@ -277,22 +277,23 @@ struct DecodeWave {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA engine (bf16 cache and bf16 q, head_dim 128, any group size g <= 16).
+// MFMA engine (bf16 q; bf16 or INT8 cache; head_dim 128; any group g <= 16).
 //
 // The g query heads of a KV head make q.k^T and P.V small dense products, so
 // one wave computes them on the matrix cores:
 //   S[16 tokens][16 heads] = K_tile . q^T   4 x v_mfma_f32_16x16x32_bf16
 //   O[16 heads][128 dims] += P . V_tile     8 x 2 x v_mfma_f32_16x16x16_bf16
 // with the query heads padded to 16 (zero q). Lane l (c = l % 16, g = l / 16):
-//   - K operand: token c, dims 32i + 8g .. +8 (load i of the tile, i < 4); one
+//   - K operand: token c, 8 dims per MFMA (bf16: dims 32i + 8g .. +8, so one
 //     load instruction reads 64 contiguous bytes of each of the 16 rows;
-//   - q operand: head c, the same dims;
-//   - S: head c, tokens 4g .. 4g+3 -- which is exactly how P must be laid out
-//     as the A operand of P.V (rows heads, k = tokens 4g..4g+3), so P never
-//     moves between lanes;
-//   - V: rows 4g .. 4g+3, dims 8c .. 8c+7 (load i reads rows i, 4+i, 8+i,
-//     12+i, 256 contiguous bytes each); v_perm gathers, for output column
-//     block jj, element jj of the four rows into the B operand;
+//     INT8: dims 32g + 8i .. +8, two 16-byte loads per lane);
+//   - q operand: head c, the same dims as K;
+//   - S: head c, tokens 4g .. 4g+3 -- exactly how P must be laid out as the A
+//     operand of P.V (rows heads, k = tokens 4g..4g+3), so P never moves
+//     between lanes;
+//   - V: rows 4g .. 4g+3, dims 8c .. 8c+7; v_perm (bf16) or byte conversion
+//     (INT8) gathers, for output column block jj, element jj of the four rows
+//     into the B operand;
 //   - O: heads 4g .. 4g+3, dims 8c + jj.
 // P is split into bf16 hi + lo parts (two MFMAs) so that the softmax weights
 // keep ~16 significant bits. The running max is shared by the four lane groups
@@ -300,6 +301,11 @@ struct DecodeWave {
 // max exceeds it by more than kRescaleSlack (exp2 arguments stay <= that
 // slack); the true max is tracked on the side and the state is renormalised
 // to it once, at the end of the split.
+//
+// INT8 codes x are fed as u = x + 128 (x ^ 0x80 per byte), which bf16 holds
+// exactly, and the bias is removed algebraically: q.x = q.u - 128 sum(q) per
+// head, and sum_t w_t x_t = sum_t w_t u_t - 128 sum_t w_t with w_t = p_t *
+// vscale_t; the per-token K scale multiplies the finished logit.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -310,12 +316,22 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay below 2^8
 
 template <int CT, int D>
 struct MfmaEligible {
-  static constexpr bool value = CT == PA_BF16 && D == 128;
+  static constexpr bool value = (CT == PA_BF16 || CT == PA_I8) && D == 128;
 };
 
-struct MfmaTile {
+template <int CT>
+struct MfmaTile;
+template <>
+struct MfmaTile<PA_BF16> {
   u32x4 k[4];  // K operand fragments
-  u32x4 v[4];  // V rows 4g + i
+  u32x4 v[4];  // V rows 4g + i, dims 8c .. 8c+7
+};
+template <>
+struct MfmaTile<PA_I8> {
+  u32x4 k[2];  // K codes: token c, dims 32g .. 32g+31
+  u32x2 v[4];  // V codes: rows 4g + i, dims 8c .. 8c+7
+  f32x4 ks;    // K scales of tokens 4g .. 4g+3
+  f32x4 vs;    // V scales of tokens 4g .. 4g+3
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -323,44 +339,104 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int G>
+// Unsigned byte k of w as fp32 (selected as v_cvt_f32_ubyte<k>).
+template <int K>
+__device__ __forceinline__ float ubyte_f32(uint32_t w) {
+  return (float)((w >> (8 * K)) & 0xffu);
+}
+
+// Biased INT8 codes (u = x + 128) of bytes 2h and 2h+1 of w, as a bf16 pair.
+template <int H>
+__device__ __forceinline__ uint32_t u8pair_to_bf16(uint32_t w) {
+  return pack_bf16(ubyte_f32<2 * H>(w), ubyte_f32<2 * H + 1>(w));
+}
+
+// Byte K of each of two words, as biased codes, packed as a bf16 pair.
+template <int K>
+__device__ __forceinline__ uint32_t u8col_to_bf16(uint32_t w0, uint32_t w1) {
+  return pack_bf16(ubyte_f32<K>(w0), ubyte_f32<K>(w1));
+}
+
+template <int CT, int G>
 struct MfmaWave {
-  static constexpr int ROW = 256;        // bytes per token row (128 bf16)
+  static constexpr int ELT = DtypeBytes<CT>::value;
+  static constexpr int ROW = 128 * ELT;  // bytes per token row
   static constexpr int TILE = kBlock * ROW;
-  u32x4 qB[4];  // q operand: head c (zero beyond the group), dims 32i + 8g .. +8
+  u32x4 qB[4];   // q operand: head c (zero beyond the group), the K operand's dims
   f32x4 acc[8];  // O: heads 4g + r, dims 8c + jj
   float m;       // reference max (log2 units) of head c
   float mtrue;   // true running max of head c
   float l;       // sum of exp2(z - m) over this lane's tokens of head c
+  float wsum;    // INT8: sum of exp2(z - m) * vscale over this lane's tokens
+  float qbias;   // INT8: 128 * sum_d q[c][d]
 
-  __device__ __forceinline__ void load_tile(MfmaTile &t, const DecodeParams &p, int blk, int kvh,
-                                            int koff, int voff) {
+  __device__ __forceinline__ void load_tile(MfmaTile<CT> &t, const DecodeParams &p, int blk,
+                                            int kvh, int koff, int voff, int soff) {
     const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc((const char *)p.k_cache + tile * TILE, TILE);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc((const char *)p.v_cache + tile * TILE, TILE);
+    if constexpr (CT == PA_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * i, 0, kStreamPolicy);
+      for (int i = 0; i < 4; ++i)
+        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * i, 0, kStreamPolicy);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, kStreamPolicy);
+      for (int i = 0; i < 4; ++i)
+        t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, kStreamPolicy);
+    } else {
+      const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, kBlock * 4);
+      const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, kBlock * 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16 * i, 0, kStreamPolicy);
+      t.ks = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ksr, soff, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        t.v[i] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + ROW * i, 0, kStreamPolicy);
+      t.vs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vsr, soff, 0, 0));
+    }
   }
 
-  __device__ __forceinline__ void consume(MfmaTile &t, int valid_rows, int g, float scale_log2) {
+  __device__ __forceinline__ void consume(MfmaTile<CT> &t, int valid_rows, int g,
+                                          float scale_log2) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (CT == PA_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]),
-                                                  __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]),
+                                                    __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0,
+                                                    0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // 8 codes: dims 32g + 8i .. +8 = bytes 8i .. 8i+7 of the lane's 32.
+        const uint32_t w0 = t.k[i / 2][2 * (i % 2)] ^ 0x80808080u;
+        const uint32_t w1 = t.k[i / 2][2 * (i % 2) + 1] ^ 0x80808080u;
+        const u32x4 kb = {u8pair_to_bf16<0>(w0), u8pair_to_bf16<1>(w0), u8pair_to_bf16<0>(w1),
+                          u8pair_to_bf16<1>(w1)};
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb),
+                                                    __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0,
+                                                    0);
+      }
+    }
     float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CT == PA_BF16)
+        z[r] = sc[r] * scale_log2;
+      else
+        z[r] = (sc[r] - qbias) * t.ks[r] * scale_log2;
+    }
     if (valid_rows < kBlock) {  // uniform: the last tile of the split
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = 4 * g + r < valid_rows;
         z[r] = ok ? z[r] : -INFINITY;
-        if (!ok) t.v[r] = u32x4{0u, 0u, 0u, 0u};  // NaN * 0 would leak: select, not scale
+        // NaN * 0 would leak: rows past the end are removed by select.
+        if constexpr (CT == PA_BF16) {
+          if (!ok) t.v[r] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+          if (!ok) t.vs[r] = 0.f;
+        }
       }
     }
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -373,7 +449,12 @@ struct MfmaWave {
 #pragma unroll
     for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
     l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
-    // P = hi + lo, both bf16.
+    if constexpr (CT == PA_I8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pz[r] *= t.vs[r];
+      wsum += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+    }
+    // P (INT8: the V-scaled weights) = hi + lo, both bf16.
     const uint32_t h01 = pack_bf16(pz[0], pz[1]), h23 = pack_bf16(pz[2], pz[3]);
     const uint32_t l01 = pack_bf16(pz[0] - bf16_lo(h01), pz[1] - bf16_hi(h01));
     const uint32_t l23 = pack_bf16(pz[2] - bf16_lo(h23), pz[3] - bf16_hi(h23));
@@ -381,23 +462,35 @@ struct MfmaWave {
     const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t w0 = t.v[0][jj >> 1], w1 = t.v[1][jj >> 1];
-      const uint32_t w2 = t.v[2][jj >> 1], w3 = t.v[3][jj >> 1];
-      const uint32_t b01 = __builtin_amdgcn_perm(w1, w0, sel);
-      const uint32_t b23 = __builtin_amdgcn_perm(w3, w2, sel);
+      uint32_t b01, b23;
+      if constexpr (CT == PA_BF16) {
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        b01 = __builtin_amdgcn_perm(t.v[1][jj >> 1], t.v[0][jj >> 1], sel);
+        b23 = __builtin_amdgcn_perm(t.v[3][jj >> 1], t.v[2][jj >> 1], sel);
+      } else {
+        const int w = jj >> 2;  // dims 8c + jj live in byte jj % 4 of word jj / 4
+        const uint32_t v0 = t.v[0][w] ^ 0x80808080u, v1 = t.v[1][w] ^ 0x80808080u;
+        const uint32_t v2 = t.v[2][w] ^ 0x80808080u, v3 = t.v[3][w] ^ 0x80808080u;
+        switch (jj & 3) {
+          case 0: b01 = u8col_to_bf16<0>(v0, v1); b23 = u8col_to_bf16<0>(v2, v3); break;
+          case 1: b01 = u8col_to_bf16<1>(v0, v1); b23 = u8col_to_bf16<1>(v2, v3); break;
+          case 2: b01 = u8col_to_bf16<2>(v0, v1); b23 = u8col_to_bf16<2>(v2, v3); break;
+          default: b01 = u8col_to_bf16<3>(v0, v1); b23 = u8col_to_bf16<3>(v2, v3); break;
+        }
+      }
       const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{b01, b23});
       acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[jj], 0, 0, 0);
       acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[jj], 0, 0, 0);
     }
   }
 
-  // Move the reference max of head c to mnew (per lane) and rescale l and the
-  // O rows (heads 4g + r get the factor computed in lane 4g + r). All lanes of
-  // the wave must call it together.
+  // Move the reference max of head c to mnew (per lane) and rescale l (and
+  // wsum) and the O rows (heads 4g + r get the factor computed in lane 4g + r).
+  // All lanes of the wave must call it together.
   __device__ __forceinline__ void rescale(float mnew, int g) {
     const float alpha = fast_exp2(m - mnew);
     l *= alpha;
+    wsum *= alpha;
     m = mnew;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -416,30 +509,45 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
                                                int wave, float (&sm_m)[NW][G],
                                                float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D]) {
-  MfmaWave<G> st;
+  using Wv = MfmaWave<CT, G>;
+  Wv st;
   const int c = lane % 16, g = lane / 16;
+  float qs = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     st.qB[i] = u32x4{0u, 0u, 0u, 0u};
-    if (c < G)
+    if (c < G) {
+      const int dim0 = CT == PA_BF16 ? 32 * i + 8 * g : 32 * g + 8 * i;
       st.qB[i] = *(const u32x4 *)((const uint16_t *)p.q +
-                                  ((int64_t)s * p.num_q_heads + hq0 + c) * D + 32 * i + 8 * g);
+                                  ((int64_t)s * p.num_q_heads + hq0 + c) * D + dim0);
+    }
+    if constexpr (CT == PA_I8) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qs += bf16_lo(st.qB[i][k]) + bf16_hi(st.qB[i][k]);
+    }
   }
+  if constexpr (CT == PA_I8) {
+    qs += __shfl_xor(qs, 16);
+    qs += __shfl_xor(qs, 32);
+  }
+  st.qbias = 128.f * qs;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) st.acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = kNegBig;
   st.mtrue = kNegBig;
   st.l = 0.f;
+  st.wsum = 0.f;
 
   int my_id = 0;
   if (lane < wb1 - wb0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
   const int last_block = (int)(p.num_blocks - 1);
-  const int koff = c * MfmaWave<G>::ROW + 16 * g;
-  const int voff = 4 * g * MfmaWave<G>::ROW + 16 * c;
-  MfmaTile t;
+  const int koff = CT == PA_BF16 ? c * Wv::ROW + 16 * g : c * Wv::ROW + 32 * g;
+  const int voff = 4 * g * Wv::ROW + 8 * Wv::ELT * c;
+  const int soff = 16 * g;  // scales of tokens 4g .. 4g+3
+  MfmaTile<CT> t;
   for (int n = wb0; n < wb1; ++n) {
     const int blk = min(max(__builtin_amdgcn_readlane(my_id, n - wb0), 0), last_block);
-    st.load_tile(t, p, blk, kvh, koff, voff);
+    st.load_tile(t, p, blk, kvh, koff, voff, soff);
     st.consume(t, min(kBlock, t1 - (b0 + n) * kBlock), g, p.scale_log2);
   }
   // Renormalise to the true max (every lane takes part: rescale reads other
@@ -447,6 +555,17 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   st.rescale(fmaxf(st.mtrue, st.m), g);
   float lt = st.l + __shfl_xor(st.l, 16);
   lt += __shfl_xor(lt, 32);
+  if constexpr (CT == PA_I8) {
+    // Remove the code bias from O: row 4g + r loses 128 * (its head's wsum).
+    float wt = st.wsum + __shfl_xor(st.wsum, 16);
+    wt += __shfl_xor(wt, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float bias = 128.f * __shfl(wt, 4 * g + r);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) st.acc[jj][r] -= bias;
+    }
+  }
   if (lane < G) {
     sm_m[wave][lane] = st.m;
     sm_l[wave][lane] = lt;
@@ -631,8 +750,20 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 // number of items and the workgroups past the end of the list, all at the end
 // of the grid, exit at once. A plan made for another split size, batch or
 // length bound counts as an empty list.
+// Minimum waves per SIMD the compiler must fit the split kernel's registers
+// to (0: its own choice).
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 0
+#endif
+#if PA_WAVES_PER_EU > 0
+#define PA_OCCUPANCY_ATTR __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_OCCUPANCY_ATTR
+#endif
+
 template <int QT, int CT, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_kernel(
+    const DecodeParams p) {
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ float sm_acc[NW][G][D];
