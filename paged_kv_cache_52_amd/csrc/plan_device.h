@@ -41,6 +41,8 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   __shared__ int wave_sum[kPlanThreads / kWave];
   __shared__ int bucket[kMaxTileBuckets + 1];  // count, then start offset, of each tile count
   __shared__ int carry;
+  __shared__ int chunk_first[kPlanThreads];  // first entry of each sequence of the chunk
+  __shared__ int chunk_len[kPlanThreads];
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
@@ -50,8 +52,11 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   if (tid == 0) carry = 0;
   __syncthreads();
 
-  // Pass 1: the full splits, with a workgroup-wide exclusive scan of their
-  // per-sequence counts; also histogram the last splits by tile count.
+  // Pass 1: the full splits. Per chunk of kPlanThreads sequences, a
+  // workgroup-wide exclusive scan of their counts gives each sequence's first
+  // entry; all threads then write the chunk's entries together (each finds its
+  // sequence by binary search over the chunk's offsets). The last splits are
+  // histogrammed by tile count on the way.
   for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
     const int s = base + tid;
     const bool valid = s < p.num_seqs;
@@ -66,16 +71,27 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     if (lane == kWave - 1) wave_sum[wave] = incl;
     if (valid) atomicAdd(&bucket[last_tiles(L, T)], 1);
     __syncthreads();
-    int before = carry, total = 0;
+    int before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < kPlanThreads / kWave; ++w) {
       if (w < wave) before += wave_sum[w];
       total += wave_sum[w];
     }
-    const int first = before + incl - f;
-    for (int q = 0; q < f; ++q) {
-      p.sched[kSchedHeader + 2 * (first + q)] = (s << 16) | q;
-      p.sched[kSchedHeader + 2 * (first + q) + 1] = L;
+    chunk_first[tid] = before + incl - f;  // offset inside the chunk
+    chunk_len[tid] = L;
+    __syncthreads();
+    const int base_entry = carry;
+    for (int e = tid; e < total; e += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;  // last i with chunk_first[i] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_first[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      // Sequences with no full split share their offset with the next one;
+      // the search lands on the last of them, which is the one that owns e.
+      const int q = e - chunk_first[lo];
+      p.sched[kSchedHeader + 2 * (base_entry + e)] = ((base + lo) << 16) | q;
+      p.sched[kSchedHeader + 2 * (base_entry + e) + 1] = chunk_len[lo];
     }
     __syncthreads();
     if (tid == 0) carry += total;

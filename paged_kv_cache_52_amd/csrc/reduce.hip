@@ -6,18 +6,29 @@
 
 namespace pa {
 
-// One wavefront per (query head, sequence). Lane j first turns split j's
-// (m_j, l_j) into its weight w_j = exp(m_j - M) (0 for an empty split, so the
-// contents of its acc never matter), then the splits' acc rows are summed with
-// those weights, each lane owning head_dim / 64 output dims. The row loads do
-// not depend on each other, so the compiler can keep several in flight.
-template <int OT, int D>
-__global__ __launch_bounds__(kWave) void reduce_kernel(const ReduceParams p) {
+constexpr int kReduceWaves = 4;       // waves per workgroup
+constexpr int kReduceManySplits = 32;  // from this many splits, 4 waves share one head
+
+// Every workgroup has kReduceWaves waves. WPH waves work on one (query head,
+// sequence): WPH = 1 gives four heads per workgroup (few splits per head),
+// WPH = 4 one head whose splits the waves divide (long contexts). Each wave
+// finds the maximum M of the split maxima (lane-parallel), then sums a
+// contiguous range of splits: lane j of a 64-split chunk turns split j's
+// (m_j, l_j) into w_j = exp(m_j - M) (0 for an empty split, so the contents of
+// its acc never matter), and the chunk's acc rows are added with those weights,
+// each lane owning head_dim / 64 output dims, four rows loaded at a time. With
+// WPH > 1 the waves' sums meet in LDS.
+template <int OT, int D, int WPH>
+__global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const ReduceParams p) {
   constexpr int DPL = D / kWave;  // dims per lane
   constexpr int U = 4;            // splits whose rows are loaded together
-  const int hq = blockIdx.x;
-  const int s = blockIdx.y;
+  constexpr int HPW = kReduceWaves / WPH;  // heads per workgroup
   const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int part = wave % WPH;
+  const int hq = blockIdx.x * HPW + wave / WPH;
+  const int s = blockIdx.y;
+  if (WPH == 1 && hq >= p.num_q_heads) return;  // no barrier below in that case
   const int L = max(0, p.context_lens[s]);
   const int ns = min(max(1, (L + p.split_tokens - 1) / p.split_tokens), p.max_splits);
   const int64_t row0 = ((int64_t)s * p.num_q_heads + hq) * p.max_splits;
@@ -28,19 +39,21 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(const ReduceParams p) {
   }
   M = group_max<kWave>(M);
 
+  const int per = (ns + WPH - 1) / WPH;
+  const int j0 = min(ns, part * per), j1 = min(ns, j0 + per);
   float acc[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
   float den = 0.f;
-  for (int base = 0; base < ns; base += kWave) {
+  for (int base = j0; base < j1; base += kWave) {
     const int j = base + lane;
     float w = 0.f, lj = 0.f;
-    if (j < ns) {
+    if (j < j1) {
       lj = p.part_l[row0 + j];
       w = lj > 0.f ? __expf(p.part_m[row0 + j] - M) : 0.f;
     }
     den += group_sum<kWave>(w * lj);
-    const int cnt = min(kWave, ns - base);
+    const int cnt = min(kWave, j1 - base);
     const float *rows = p.part_acc + (row0 + base) * D + lane;
     int i = 0;
     for (; i + U <= cnt; i += U) {
@@ -65,31 +78,63 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(const ReduceParams p) {
                                                   acc[k]);
     }
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t orow = ((int64_t)s * p.num_q_heads + hq) * D;
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) {
-    const float o = acc[k] * inv;
+
+  auto store = [&](int64_t idx, float o) {
     if constexpr (OT == PA_BF16) {
-      ((uint16_t *)p.out)[orow + lane + k * kWave] = (uint16_t)f32_to_bf16_rne(o);
+      ((uint16_t *)p.out)[idx] = (uint16_t)f32_to_bf16_rne(o);
     } else {
-      ((float *)p.out)[orow + lane + k * kWave] = o;
+      ((float *)p.out)[idx] = o;
+    }
+  };
+  if constexpr (WPH == 1) {
+    const int64_t orow = ((int64_t)s * p.num_q_heads + hq) * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) store(orow + lane + k * kWave, den > 0.f ? acc[k] / den : 0.f);
+  } else {
+    __shared__ float sm_acc[kReduceWaves][D];
+    __shared__ float sm_den[kReduceWaves];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) sm_acc[wave][lane + k * kWave] = acc[k];
+    if (lane == 0) sm_den[wave] = den;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < HPW * D; idx += kReduceWaves * kWave) {
+      const int h = idx / D, d = idx % D;
+      const int hh = blockIdx.x * HPW + h;
+      if (hh >= p.num_q_heads) continue;
+      float a = 0.f, dn = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPH; ++w) {
+        a += sm_acc[h * WPH + w][d];
+        dn += sm_den[h * WPH + w];
+      }
+      store(((int64_t)s * p.num_q_heads + hh) * D + d, dn > 0.f ? a / dn : 0.f);
     }
   }
 }
 
-hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream) {
-  dim3 grid(p.num_q_heads, p.num_seqs);
-  if (p.out_dtype == PA_BF16) {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((reduce_kernel<PA_BF16, 64>), grid, dim3(kWave), 0, stream, p);
-    else
-      hipLaunchKernelGGL((reduce_kernel<PA_BF16, 128>), grid, dim3(kWave), 0, stream, p);
+namespace {
+
+template <int OT, int D>
+void launch_reduce_t(const ReduceParams &p, hipStream_t stream) {
+  const dim3 block(kReduceWaves * kWave);
+  if (p.max_splits >= kReduceManySplits) {
+    hipLaunchKernelGGL((reduce_kernel<OT, D, kReduceWaves>), dim3(p.num_q_heads, p.num_seqs),
+                       block, 0, stream, p);
   } else {
-    if (p.head_dim == 64)
-      hipLaunchKernelGGL((reduce_kernel<PA_F32, 64>), grid, dim3(kWave), 0, stream, p);
-    else
-      hipLaunchKernelGGL((reduce_kernel<PA_F32, 128>), grid, dim3(kWave), 0, stream, p);
+    const dim3 grid((p.num_q_heads + kReduceWaves - 1) / kReduceWaves, p.num_seqs);
+    hipLaunchKernelGGL((reduce_kernel<OT, D, 1>), grid, block, 0, stream, p);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream) {
+  if (p.out_dtype == PA_BF16) {
+    if (p.head_dim == 64) launch_reduce_t<PA_BF16, 64>(p, stream);
+    else launch_reduce_t<PA_BF16, 128>(p, stream);
+  } else {
+    if (p.head_dim == 64) launch_reduce_t<PA_F32, 64>(p, stream);
+    else launch_reduce_t<PA_F32, 128>(p, stream);
   }
   return hipGetLastError();
 }

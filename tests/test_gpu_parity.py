@@ -290,7 +290,7 @@ def test_edge_lengths():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (16, 2), (32, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (6, 6), (4, 4), (8, 4), (16, 4), (16, 2), (32, 2)])
 def test_gqa_group_sizes(Hq, Hkv, D, dtype):
     print(f"[case] gqa Hq={Hq} Hkv={Hkv} D={D} {dtype}", flush=True)
     name = "tiny_fp32" if dtype == "fp32" else "llama8b_bf16"
