@@ -146,7 +146,8 @@ def main():
                           b.v_scale)
         b.fill_k = b.fill_v = None
     B, Hq, D = b.q.shape
-    T = args.split_tokens or pa.default_split_tokens(B, w.num_kv_heads, b.max_context_len)
+    T = args.split_tokens or pa.default_split_tokens(B, w.num_kv_heads, w.head_dim,
+                                                       b.k_cache.dtype, b.max_context_len)
     S = pa.num_splits(b.max_context_len, T)
     out = torch.empty_like(b.q)
     parts = pa.Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),

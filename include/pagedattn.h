@@ -87,11 +87,17 @@ const char *pa_strerror(int status);
  * [EchoLLMServing notes, section 2, FlashDecoding split heuristic.] */
 int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
 
-/* Split size (tokens, a multiple of 16) the library picks when the caller
- * passes split_tokens = 0, tuned on MI355X; it depends only on the batch size
- * and the length bound (num_kv_heads is accepted for future tuning and
- * ignored). Host-only arithmetic. */
-int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
+/* Split size T (tokens) the library uses when a caller passes
+ * split_tokens = 0 [EchoLLMServing notes, section 2: the split count follows
+ * the context length, one split per 512 tokens in the notes' setting].
+ * T starts at 256 KiB of K and V per (split, KV head), i.e. 262144 /
+ * (2 * head_dim * element bytes): 512 tokens for a 16-bit 128-dim cache, 1024
+ * for an INT8 one, capped at 4096. It is then halved, down to 64, while
+ * num_seqs * num_kv_heads * pa_num_splits(max_context_len, T) is below 1024
+ * work items (small batches still fill the device). Returns 0 for a head_dim
+ * other than 64 or 128 or an unknown cache_dtype. Host-only arithmetic. */
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t cache_dtype, int32_t max_context_len);
 
 /* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
  * a small header). */
@@ -132,7 +138,9 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  * T and the length bounds, so one plan serves every attention layer of a step.
  *   context_lens     [num_seqs] int32 (device)
  *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
- *   split_tokens     T as for paged_attn_decode_partial (0: default)
+ *   split_tokens     T, a positive multiple of 16 <= 4096 (the plan knows no
+ *                    cache, so there is no default here: pass what the decode
+ *                    call will use, e.g. pa_default_split_tokens())
  *   sched            device scratch of pa_sched_bytes(num_seqs, max_splits) bytes
  *                    with max_splits >= pa_num_splits(max_context_len, T)
  */
@@ -143,7 +151,8 @@ int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_b
 /*
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
  * depend on each other, so one kernel does both (its last workgroup plans, the
- * others write). Arguments, layouts and errors are those of the two calls; the
+ * others write). Arguments, layouts and errors are those of the two calls
+ * (split_tokens = 0 here picks pa_default_split_tokens() for this cache); the
  * results are identical to calling them in turn. Serves the start of a decode
  * step, where the new tokens are written and the batch's splits are listed.
  */

@@ -66,8 +66,15 @@ def num_splits(context_len: int, split_tokens: int) -> int:
     return int(_lib.load().pa_num_splits(int(context_len), int(split_tokens)))
 
 
-def default_split_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int) -> int:
-    return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len))
+def default_split_tokens(num_seqs: int, num_kv_heads: int, head_dim: int, cache_dtype,
+                         max_context_len: int) -> int:
+    """Split size the library picks for split_tokens=None (cache_dtype: a torch
+    dtype or a PA_* code)."""
+    code = _DTYPE_CODES.get(cache_dtype, cache_dtype)
+    if not isinstance(code, int):
+        raise PagedAttnError(f"unsupported cache dtype {cache_dtype}")
+    return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, code,
+                                                   max_context_len))
 
 
 def sched_bytes(num_seqs: int, max_splits: int) -> int:
@@ -150,10 +157,17 @@ def _max_len(context_lens, max_context_len):
     return int(max_context_len)
 
 
-def _plan_sizes(context_lens, max_context_len, split_tokens, sched):
+def _plan_sizes(context_lens, max_context_len, split_tokens, sched, cache=None):
+    """cache = (num_kv_heads, head_dim, cache dtype) picks the default split
+    size when split_tokens is None; without it split_tokens is required."""
     B = context_lens.shape[0]
     mcl = _max_len(context_lens, max_context_len)
-    T = int(split_tokens) if split_tokens else default_split_tokens(B, 1, mcl)
+    if split_tokens:
+        T = int(split_tokens)
+    elif cache is not None:
+        T = default_split_tokens(B, cache[0], cache[1], cache[2], mcl)
+    else:
+        raise PagedAttnError("paged_attn_plan needs split_tokens (see default_split_tokens)")
     S = max(1, num_splits(mcl, T))
     need = sched_bytes(B, S)
     if sched is None or sched.numel() * sched.element_size() < need:
@@ -162,10 +176,11 @@ def _plan_sizes(context_lens, max_context_len, split_tokens, sched):
 
 
 def paged_attn_plan(context_lens, max_blocks_per_seq: int, *, max_context_len=None,
-                    split_tokens=None, sched: Optional[torch.Tensor] = None) -> Plan:
+                    split_tokens=None, sched: Optional[torch.Tensor] = None,
+                    _cache=None) -> Plan:
     """Plan kernel: list every split of the batch (on the device, from
-    context_lens) for the split kernel."""
-    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched)
+    context_lens) for the split kernel. split_tokens is required."""
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched, _cache)
     _check(_lib.load().paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B,
                                        max_blocks_per_seq, mcl, T,
                                        _dev(sched, "sched", torch.int32),
@@ -186,7 +201,8 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
         raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
     if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
         raise PagedAttnError("an int8 cache needs k_scale and v_scale")
-    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched)
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched,
+                                      (Hkv, D, k_cache.dtype))
     _check(_lib.load().paged_decode_prepare(
         _dev(k, "k"), _dev(v, "v", k.dtype), _code(k),
         _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
@@ -208,7 +224,8 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
     Hkv = k_cache.shape[1]
     if plan is None:
         plan = paged_attn_plan(context_lens, block_tables.shape[1],
-                               max_context_len=max_context_len, split_tokens=split_tokens)
+                               max_context_len=max_context_len, split_tokens=split_tokens,
+                               _cache=(Hkv, D, k_cache.dtype))
     elif (plan.max_blocks_per_seq != block_tables.shape[1] or
           plan.context_lens is not context_lens or
           (split_tokens and int(split_tokens) != plan.split_tokens) or
@@ -258,7 +275,8 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise PagedAttnError("out must match q's shape and dtype")
     mcl = _max_len(context_lens, max_context_len)
-    T = int(split_tokens) if split_tokens else default_split_tokens(B, k_cache.shape[1], mcl)
+    T = (int(split_tokens) if split_tokens else
+         default_split_tokens(B, k_cache.shape[1], D, k_cache.dtype, mcl))
     need = workspace_bytes(B, Hq, D, max(1, num_splits(mcl, T)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -21,6 +21,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Packed fp32 VALU ops stay off: the compiler emits only scalar fp32 forms.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with AGPRs the register allocator
+    # copies the whole O tile out and back every iteration around the (rare)
+    # rescale branch, which multiplies it with VALU ops.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

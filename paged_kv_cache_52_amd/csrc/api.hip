@@ -24,6 +24,9 @@ int check_split_tokens(int32_t split_tokens) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+constexpr int32_t kMinDefaultSplit = 64;  // smallest split the default picks
+constexpr int64_t kMinWorkItems = 1024;   // (split, KV head) items the default aims for
+
 }  // namespace
 
 extern "C" {
@@ -49,11 +52,26 @@ int32_t pa_num_splits(int32_t context_len, int32_t split_tokens) {
   return (int32_t)(n < 1 ? 1 : n);
 }
 
-int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_context_len;
-  return 512;
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t cache_dtype, int32_t max_context_len) {
+  int elt;
+  switch (cache_dtype) {
+    case PA_F32: elt = 4; break;
+    case PA_BF16: elt = 2; break;
+    case PA_I8: elt = 1; break;
+    default: return 0;
+  }
+  if (head_dim != 64 && head_dim != 128) return 0;
+  // 256 KiB of K and V codes per (split, KV head): 512 tokens of a 16-bit
+  // 128-dim cache, 1024 of an INT8 one.
+  const int64_t kv_bytes_per_token = 2LL * head_dim * elt;
+  int32_t t = (int32_t)std::min<int64_t>(PA_MAX_SPLIT_TOKENS, (256 << 10) / kv_bytes_per_token);
+  // Halve while the batch has too few (split, KV head) work items to fill the
+  // device (a workgroup per item, 256 compute units).
+  const int64_t heads = (int64_t)std::max(num_seqs, 0) * std::max(num_kv_heads, 0);
+  while (t > kMinDefaultSplit && heads * pa_num_splits(max_context_len, t) < kMinWorkItems)
+    t /= 2;
+  return t;
 }
 
 size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits) {
@@ -102,7 +120,6 @@ int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks
                pa::PlanParams *out) {
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
-  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, 1, max_context_len);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
   *out = pa::PlanParams{
@@ -149,6 +166,9 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
                        v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK) return st;
+  if (split_tokens == 0)
+    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
+                                           max_context_len);
   st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, split_tokens,
                   sched, &pl);
   if (st != PA_OK) return st;
@@ -176,7 +196,9 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                      (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
                      ((q_dtype == PA_BF16 || q_dtype == PA_F32) && cache_dtype == PA_I8);
   if (!dt_ok) return PA_ERR_DTYPE;
-  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
+  if (split_tokens == 0)
+    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
+                                           max_context_len);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   const int32_t grid_splits = pa_num_splits(max_context_len, split_tokens);
   if (max_splits < grid_splits) return PA_ERR_SPLIT;
@@ -246,11 +268,16 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       int32_t max_blocks_per_seq, const int32_t *context_lens,
                       int32_t max_context_len, float scale, int32_t split_tokens, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (split_tokens == 0) split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, max_context_len);
-  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0)
+  if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
+      num_kv_heads <= 0)
     return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_I8)
+    return PA_ERR_DTYPE;
+  if (split_tokens == 0)
+    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
+                                           max_context_len);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   const int32_t ns = pa_num_splits(max_context_len, split_tokens);
   const size_t need = pa_workspace_bytes(num_seqs, num_q_heads, head_dim, ns);
   if (num_seqs == 0) return PA_OK;

@@ -48,6 +48,11 @@ struct DecodeParams {
 };
 
 // Tiles a wave keeps in flight beyond the one it is consuming (0 or 1).
+// Software pipeline of the MFMA engine: 1 keeps the next tile's loads in
+// flight while the current tile is consumed.
+#ifndef PA_MFMA_PREFETCH
+#define PA_MFMA_PREFETCH 0
+#endif
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 0
 #endif
@@ -370,11 +375,15 @@ struct MfmaWave {
   float wsum;    // INT8: sum of exp2(z - m) * vscale over this lane's tokens
   float qbias;   // INT8: 128 * sum_d q[c][d]
 
+  // Loads one tile. With live == false the descriptors have size 0: every
+  // load is out of range, returns zeros and reads no memory.
   __device__ __forceinline__ void load_tile(MfmaTile<CT> &t, const DecodeParams &p, int blk,
-                                            int kvh, int koff, int voff, int soff) {
+                                            int kvh, int koff, int voff, int soff,
+                                            bool live = true) {
     const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc((const char *)p.k_cache + tile * TILE, TILE);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc((const char *)p.v_cache + tile * TILE, TILE);
+    const int tb = live ? TILE : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc((const char *)p.k_cache + tile * TILE, tb);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc((const char *)p.v_cache + tile * TILE, tb);
     if constexpr (CT == PA_BF16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -383,8 +392,9 @@ struct MfmaWave {
       for (int i = 0; i < 4; ++i)
         t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, kStreamPolicy);
     } else {
-      const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, kBlock * 4);
-      const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, kBlock * 4);
+      const int sb = live ? kBlock * 4 : 0;
+      const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, sb);
+      const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, sb);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16 * i, 0, kStreamPolicy);
@@ -544,12 +554,34 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   const int koff = CT == PA_BF16 ? c * Wv::ROW + 16 * g : c * Wv::ROW + 32 * g;
   const int voff = 4 * g * Wv::ROW + 8 * Wv::ELT * c;
   const int soff = 16 * g;  // scales of tokens 4g .. 4g+3
+  // Physical block of tile n of the wave (clamped: a corrupt table entry reads
+  // a wrong but existing block instead of faulting).
+  auto block_of = [&](int n) {
+    return min(max(__builtin_amdgcn_readlane(my_id, min(n - wb0, kWave - 1)), 0), last_block);
+  };
+  auto rows_of = [&](int n) { return min(kBlock, t1 - (b0 + n) * kBlock); };
+#if PA_MFMA_PREFETCH
+  // Two tiles in flight: tile n + 1 is requested before tile n is consumed.
+  // The look-ahead load is unconditional (a dead one reads nothing), so the
+  // wait before each consume is the same on every path.
+  MfmaTile<CT> ta, tb;
+  st.load_tile(ta, p, block_of(wb0), kvh, koff, voff, soff, wb0 < wb1);
+  for (int n = wb0; n < wb1; n += 2) {
+    st.load_tile(tb, p, block_of(n + 1), kvh, koff, voff, soff, n + 1 < wb1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead ahead of the wait
+    st.consume(ta, rows_of(n), g, p.scale_log2);
+    if (n + 1 >= wb1) break;
+    st.load_tile(ta, p, block_of(n + 2), kvh, koff, voff, soff, n + 2 < wb1);
+    __builtin_amdgcn_sched_barrier(0);
+    st.consume(tb, rows_of(n + 1), g, p.scale_log2);
+  }
+#else
   MfmaTile<CT> t;
   for (int n = wb0; n < wb1; ++n) {
-    const int blk = min(max(__builtin_amdgcn_readlane(my_id, n - wb0), 0), last_block);
-    st.load_tile(t, p, blk, kvh, koff, voff, soff);
-    st.consume(t, min(kBlock, t1 - (b0 + n) * kBlock), g, p.scale_log2);
+    st.load_tile(t, p, block_of(n), kvh, koff, voff, soff);
+    st.consume(t, rows_of(n), g, p.scale_log2);
   }
+#endif
   // Renormalise to the true max (every lane takes part: rescale reads other
   // lanes' factors), then sum l over the four lane groups.
   st.rescale(fmaxf(st.mtrue, st.m), g);

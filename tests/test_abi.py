@@ -52,9 +52,33 @@ def test_num_splits(lib, L, T, n):
 
 
 def test_default_split_tokens_is_valid(lib):
-    for B, Hkv, L in [(64, 8, 4096), (8, 8, 131072), (256, 4, 18385), (4, 2, 128), (1, 1, 1)]:
-        T = lib.pa_default_split_tokens(B, Hkv, L)
-        assert 16 <= T <= 4096 and T % 16 == 0
+    for B, Hkv, L in [(64, 8, 4096), (8, 8, 131072), (256, 4, 18385), (4, 2, 128), (1, 1, 1),
+                      (0, 8, 100)]:
+        for D in (64, 128):
+            for dt in (F32, BF16, I8):
+                T = lib.pa_default_split_tokens(B, Hkv, D, dt, L)
+                assert 64 <= T <= 4096 and T % 16 == 0, (B, Hkv, L, D, dt, T)
+
+
+@pytest.mark.parametrize("B,Hkv,D,dt,L,T", [
+    (64, 8, 128, BF16, 4096, 512),      # 8B-shaped bf16 batch: one split per 512 tokens
+    (8, 8, 128, BF16, 131072, 512),     # long contexts: ceil(L / 512) splits
+    (128, 8, 128, I8, 8192, 1024),      # INT8: the same 256 KiB per split is 1024 tokens
+    (256, 4, 128, BF16, 18385, 512),    # shared-prefix batch
+    (64, 8, 64, F32, 4096, 512),        # 64-dim fp32: 512 B per token, like bf16 x 128
+    (64, 8, 128, F32, 4096, 256),
+    (64, 8, 64, I8, 4096, 2048),
+    (1, 8, 128, BF16, 4096, 64),        # 8 heads x 64 splits = 512 items < 1024: floor 64
+    (2, 8, 128, BF16, 8192, 128),       # 16 heads x 64 splits = 1024 items
+    (4, 2, 64, F32, 128, 64),
+])
+def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
+    assert lib.pa_default_split_tokens(B, Hkv, D, dt, L) == T
+
+
+def test_default_split_tokens_rejects_unknown(lib):
+    assert lib.pa_default_split_tokens(4, 8, 96, BF16, 100) == 0
+    assert lib.pa_default_split_tokens(4, 8, 128, 7, 100) == 0
 
 
 def test_workspace_bytes(lib):
@@ -100,6 +124,7 @@ def test_prepare_validation(lib):
     assert prep(mb=0) == ERR_SHAPE
     assert prep(B=65536) == ERR_SHAPE
     assert prep(split=40) == ERR_SPLIT
+    assert prep(split=0, mcl=100000, mb=8000, B=4, sched=None) == ERR_NULL  # default T accepted
     assert prep(sched=None) == ERR_NULL
     assert prep(k=None) == ERR_NULL
     assert prep(kc=FAKE_ODD) == ERR_ALIGN
@@ -115,6 +140,7 @@ def test_plan_validation(lib):
     assert plan(mb=0) == ERR_SHAPE
     assert plan(mcl=-1) == ERR_SHAPE
     assert plan(split=8) == ERR_SPLIT
+    assert plan(split=0) == ERR_SPLIT                  # no default without the cache
     assert plan(sched=None) == ERR_NULL
     assert plan(B=0, cl=None, sched=None) == OK
 

@@ -437,8 +437,10 @@ def test_graph_capture_replays_match_eager():
     eager = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
                                    g.scale, max_context_len=g.max_context_len).clone()
     out = torch.empty_like(g.q)
+    T = pa().default_split_tokens(8, g.k_cache.shape[1], g.q.shape[2], g.k_cache.dtype,
+                                  g.max_context_len)
     ws = torch.empty(pa().workspace_bytes(8, g.q.shape[1], g.q.shape[2],
-                                          pa().num_splits(g.max_context_len, 512)),
+                                          pa().num_splits(g.max_context_len, T)),
                      dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
