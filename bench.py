@@ -10,9 +10,12 @@ Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
 head_dim 128, block 16, context lengths uniform in [512, 4096], random
 non-contiguous block tables over a pool of 1.1x the tokens).
 
-Prints ONE JSON line. `value` is tokens/s for the whole step (B / t_step);
-the split kernel's roofline uses its own average duration measured with HIP
-events on the launch stream in a second pass with identical launches.
+Prints ONE JSON line. `value` is tokens/s for the whole step (B / t_step).
+The split kernel's roofline uses its own duration: HIP events on the launch
+stream around `steps` back-to-back launches of it after the timed region.
+Per-kernel p10/p50/p90 come from a pass with events between the kernels of
+each step. The line also carries the practical HBM read ceiling measured by
+the library's read probe on the same device.
 """
 import argparse
 import hashlib
@@ -27,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("decode attention tokens/s and achieved KV-read GB/s (% of HBM peak), 1 MI355X")
 HBM_PEAK_GBPS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_llama8b_bf16_counters.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -45,6 +48,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--ctx-range", type=int, nargs=2, default=None, metavar=("LO", "HI"),
                     help="override the workload's context-length range (inclusive)")
+    ap.add_argument("--probe-mib", type=int, default=1024,
+                    help="measure the practical HBM read ceiling with the library's read probe "
+                         "over a buffer of this many MiB (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -111,17 +117,41 @@ def cpu_baseline(b, seconds):
     }
 
 
-def load_counters():
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources."""
+def load_counters(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs on this
+    workload, if they were taken on the current kernel sources."""
     try:
-        with open(PROFILE_COUNTERS) as f:
+        with open(os.path.join(PROFILES, f"decode_{workload}_counters.json")) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None
     return c
+
+
+def pct(sorted_vals, q):
+    """Nearest-rank percentile of an ascending list."""
+    i = min(len(sorted_vals) - 1, max(0, math.ceil(q * len(sorted_vals)) - 1))
+    return sorted_vals[i]
+
+
+def hbm_probe(pa, torch, dev, stream, mib, reps=10):
+    """Practical HBM read ceiling: the library's read probe over a `mib` MiB
+    buffer, `reps` back-to-back launches after one warm-up, timed like the
+    split kernel (GB/s)."""
+    buf = torch.ones((mib << 20) // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    pa.hbm_read_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        pa.hbm_read_probe(buf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf, sink
+    return (mib << 20) / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -202,17 +232,30 @@ def main():
         e[2].record(stream); reduce()
         e[3].record(stream)
     torch.cuda.synchronize()
-    t_prep = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_red = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    per = {k: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+           for i, k in enumerate(("write_and_plan", "decode_split", "reduce"))}
+    t_prep, t_dec, t_red = (sum(per[k]) / args.steps
+                            for k in ("write_and_plan", "decode_split", "reduce"))
+
+    # The split kernel's own duration: `steps` back-to-back launches on the
+    # same stream (each waits for the previous), no events or other kernels
+    # in between; this is what a kernel trace reports as its duration.
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
+        decode()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    t_dec_b2b = d0.elapsed_time(d1) / args.steps
 
     kv_bytes, alg_bytes = algorithmic_bytes(b)
-    dec_gbps = alg_bytes / (t_dec * 1e-3) / 1e9
+    dec_gbps = alg_bytes / (t_dec_b2b * 1e-3) / 1e9
     kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
-    counters = load_counters()
+    counters = load_counters(w.name)
     traffic = None
     if counters is not None:
         traffic = counters["fetch_bytes_per_launch"] + counters["write_bytes_per_launch"]
+    probe_gbps = hbm_probe(pa, torch, dev, stream, args.probe_mib) if args.probe_mib else None
 
     line = {
         "metric": METRIC,
@@ -240,11 +283,17 @@ def main():
         "kv_read_gbps": kv_gbps_step,
         "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
         "decode_reduce_tokens_per_s": B / ((t_dec + t_red) * 1e-3),
-        "kernel_ms": {"write_and_plan": t_prep, "decode_split": t_dec, "reduce": t_red},
+        "kernel_ms": {"write_and_plan": t_prep, "decode_split": t_dec, "reduce": t_red,
+                      "decode_split_back_to_back": t_dec_b2b},
+        "kernel_us_p10_p50_p90": {k: [round(1e3 * pct(v, q), 2) for q in (0.1, 0.5, 0.9)]
+                                  for k, v in per.items()},
         "roofline": {
             "kernel": "decode_split_kernel", "bound": "hbm", "achieved": dec_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
-            "algorithmic_bytes_per_launch": alg_bytes, "traffic": traffic,
+            "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
+            "duration_us": 1e3 * t_dec_b2b,
+            "read_probe_gbps": probe_gbps,
+            "frac_of_read_probe": dec_gbps / probe_gbps if probe_gbps else None,
         },
         "wall_s_timed": wall,
     }

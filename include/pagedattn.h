@@ -235,10 +235,11 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
 
 /*
  * Measurement aid (not part of the attention path): read `bytes` (a multiple
- * of 16) from device buffer `src` once with 16-byte loads, using
- * sink_words / 256 workgroups of 256 threads; each thread writes one word of
- * its XOR to sink[sink_words]. Used to measure the device's practical HBM
- * read bandwidth next to the decode kernel's.
+ * of 16) from device buffer `src` once, using sink_words / 256 workgroups of
+ * 256 threads (four waves; each wave reads whole 8 KiB chunks, two in flight);
+ * each thread writes one word of its XOR to sink[sink_words]. Used to measure
+ * the device's practical HBM read bandwidth next to the decode kernel's
+ * (about 1024 to 3072 workgroups suit MI355X).
  */
 int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,
                       hipStream_t stream);

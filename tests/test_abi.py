@@ -198,3 +198,11 @@ def test_decode_workspace_validation(lib):
     assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
     assert lib.paged_attn_decode(*args, FAKE + 16, need, None) == ERR_ALIGN  # 256-byte rule
     assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
+
+
+def test_read_probe_validation(lib):
+    assert lib.pa_hbm_read_probe(None, 1024, FAKE, 256, None) == ERR_NULL
+    assert lib.pa_hbm_read_probe(FAKE, 1024, None, 256, None) == ERR_NULL
+    assert lib.pa_hbm_read_probe(FAKE_ODD, 1024, FAKE, 256, None) == ERR_ALIGN
+    assert lib.pa_hbm_read_probe(FAKE, 1000, FAKE, 256, None) == ERR_SHAPE
+    assert lib.pa_hbm_read_probe(FAKE, 1024, FAKE, 255, None) == ERR_SHAPE

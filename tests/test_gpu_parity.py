@@ -495,3 +495,19 @@ def test_full_size_sampled_rows(name):
     _check_out(out32[seqs, heads], ref, TOL_BF16, f"{name}/fp32-out")
     _check_bf16_out(out[torch.from_numpy(seqs).long(), torch.from_numpy(heads).long()].cpu(),
                     ref, f"{name}/bf16-out")
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(1 << 20, 4), ((1 << 20) + 48, 4), (8192 * 7 + 16, 3),
+                                           (48, 1), (64 << 20, 1024)])
+def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
+    """The probe's sink, XORed together, equals the XOR of every word of the
+    buffer: each 16-byte word (whole chunks and the ragged tail) is read once."""
+    print(f"[case] probe bytes={nbytes} blocks={blocks}", flush=True)
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda")
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    pa().hbm_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
