@@ -8,7 +8,9 @@ Arrays are NumPy arrays on the host. dtype codes follow the element type:
 ``np.float32`` is fp32, ``np.uint16``/``np.int16`` hold bf16 bit patterns and
 ``np.int8`` is the INT8 cache. Shapes:
 
-* q            [num_seqs][num_q_heads][head_dim]
+* q            [num_seqs][num_q_heads][head_dim], or
+               [num_seqs][num_query_tokens][num_q_heads][head_dim] (several query
+               tokens per sequence: the last num_query_tokens tokens of its context)
 * k/v cache    [num_blocks][num_kv_heads][16][head_dim]
 * k/v scale    [num_blocks][num_kv_heads][16] float32 (INT8 cache only)
 * block_tables [num_seqs][max_blocks_per_seq] int32
@@ -41,15 +43,18 @@ def _load():
         P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_kv_write.argtypes = [P, P, I, P, L, I, I, P, P, P, P, L, I]
         lib.oracle_kv_write.restype = I
-        lib.oracle_decode.argtypes = [P, I, I, P, P, P, P, I, I, I, P, I, P, D, P, P, L, P]
+        lib.oracle_decode.argtypes = [P, I, I, I, I, P, P, P, P, I, I, I, P, I, P, D, P, P, P,
+                                      L, P]
         lib.oracle_decode.restype = None
-        lib.oracle_decode_split.argtypes = [P, I, I, I, P, P, P, P, I, I, I, P, I, P, D, I, I,
-                                            P, P, P]
+        lib.oracle_decode_split.argtypes = [P, I, I, I, I, I, P, P, P, P, I, I, I, P, I, P, D, I,
+                                            I, P, P, P]
         lib.oracle_decode_split.restype = None
         lib.oracle_merge.argtypes = [P, P, P, L, I, I, P]
         lib.oracle_merge.restype = None
         lib.oracle_num_splits.argtypes = [I, I]
         lib.oracle_num_splits.restype = I
+        lib.oracle_split_base.argtypes = [I, I, I]
+        lib.oracle_split_base.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -84,8 +89,16 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def num_splits(context_len: int, split_tokens: int) -> int:
-    return int(_load().oracle_num_splits(int(context_len), int(split_tokens)))
+def split_base(context_len: int, num_query_tokens: int = 1, window: int = 0) -> int:
+    """First token of a sequence's split range (0 without a window)."""
+    return int(_load().oracle_split_base(int(context_len), int(num_query_tokens), int(window)))
+
+
+def num_splits(context_len: int, split_tokens: int, num_query_tokens: int = 1,
+               window: int = 0) -> int:
+    """max(1, ceil((L - base) / T)) with base = split_base(L, Q, W)."""
+    base = split_base(context_len, num_query_tokens, window)
+    return int(_load().oracle_num_splits(int(context_len) - base, int(split_tokens)))
 
 
 def kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
@@ -104,64 +117,79 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
         raise ValueError("oracle_kv_write rejected its arguments")
 
 
-def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window):
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
     block_tables, context_lens = _c(block_tables, np.int32), _c(context_lens, np.int32)
-    num_seqs, num_q_heads, head_dim = q.shape
+    if q.ndim == 3:
+        q = q.reshape(q.shape[0], 1, q.shape[1], q.shape[2])
+    num_seqs, nqt, num_q_heads, head_dim = q.shape
     num_blocks, num_kv_heads, bs, hd = k_cache.shape
     assert bs == BLOCK_SIZE and hd == head_dim and num_q_heads % num_kv_heads == 0
+    assert nqt >= 1 and window >= 0
     if _code(k_cache) == I8:
         assert k_scale is not None and v_scale is not None
-    # Every block the definition will read must exist in the pool.
+    # Every block the definition will read must exist in the pool (blocks
+    # before a sliding window's reach are never read).
     for s in range(num_seqs):
-        nb = -(-int(context_lens[s]) // BLOCK_SIZE)
+        L = int(context_lens[s])
+        nb = -(-L // BLOCK_SIZE)
         assert nb <= block_tables.shape[1]
-        ids = block_tables[s, :nb]
+        ids = block_tables[s, split_base(L, nqt, window) // BLOCK_SIZE:nb]
         assert (ids >= 0).all() and (ids < num_blocks).all()
     return q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None,
-           rows=None):
+           rows=None, window=0):
     """Decode attention by definition, in fp64.
 
-    rows: optional (seq_ids, head_ids) pair of equal-length int arrays; the
-    result is then [n_rows][head_dim]. Without rows it is [B][Hq][D].
+    q is [B][Hq][D] (one query token per sequence) or [B][Q][Hq][D]; window
+    is the sliding window in tokens (0: none). rows: optional (seq_ids,
+    head_ids) pair, or (seq_ids, query_token_ids, head_ids) triple, of
+    equal-length int arrays; the result is then [n_rows][head_dim]. Without
+    rows it has q's shape.
     """
+    shape = np.shape(q)
     q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
-        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
-    num_seqs, num_q_heads, head_dim = q.shape
+        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window)
+    num_seqs, nqt, num_q_heads, head_dim = q.shape
     if rows is None:
-        seq_ids = np.repeat(np.arange(num_seqs, dtype=np.int32), num_q_heads)
-        head_ids = np.tile(np.arange(num_q_heads, dtype=np.int32), num_seqs)
-    else:
+        seq_ids = np.repeat(np.arange(num_seqs, dtype=np.int32), nqt * num_q_heads)
+        tok_ids = np.tile(np.repeat(np.arange(nqt, dtype=np.int32), num_q_heads), num_seqs)
+        head_ids = np.tile(np.arange(num_q_heads, dtype=np.int32), num_seqs * nqt)
+    elif len(rows) == 2:
         seq_ids, head_ids = _c(rows[0], np.int32), _c(rows[1], np.int32)
+        tok_ids = np.zeros_like(seq_ids)
+    else:
+        seq_ids, tok_ids, head_ids = (_c(r, np.int32) for r in rows)
     out = np.zeros((len(seq_ids), head_dim), dtype=np.float64)
-    _load().oracle_decode(_ptr(q), _code(q), num_q_heads, _ptr(k_cache), _ptr(v_cache),
-                          _ptr(k_scale), _ptr(v_scale), _code(k_cache), k_cache.shape[1],
-                          head_dim, _ptr(block_tables), block_tables.shape[1],
-                          _ptr(context_lens), float(scale), _ptr(seq_ids), _ptr(head_ids),
-                          len(seq_ids), _ptr(out))
+    _load().oracle_decode(_ptr(q), _code(q), num_q_heads, nqt, int(window), _ptr(k_cache),
+                          _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _code(k_cache),
+                          k_cache.shape[1], head_dim, _ptr(block_tables), block_tables.shape[1],
+                          _ptr(context_lens), float(scale), _ptr(seq_ids), _ptr(tok_ids),
+                          _ptr(head_ids), len(seq_ids), _ptr(out))
     if rows is None:
-        out = out.reshape(num_seqs, num_q_heads, head_dim)
+        out = out.reshape(shape[:-1] + (head_dim,))
     return out
 
 
 def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, split_tokens,
-                 max_splits=None, k_scale=None, v_scale=None):
-    """Split-K partials (m, l, acc) in fp64; acc is not divided by l."""
+                 max_splits=None, k_scale=None, v_scale=None, window=0):
+    """Split-K partials (m, l, acc) in fp64; acc is not divided by l. Shapes:
+    m, l [B](+[Q])[Hq][S], acc [B](+[Q])[Hq][S][D], following q."""
+    lead = np.shape(q)[:-1]
     q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
-        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
-    num_seqs, num_q_heads, head_dim = q.shape
+        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window)
+    num_seqs, nqt, num_q_heads, head_dim = q.shape
     if max_splits is None:
-        max_splits = max(num_splits(int(L), split_tokens) for L in context_lens)
-    m = np.zeros((num_seqs, num_q_heads, max_splits), dtype=np.float64)
+        max_splits = max(num_splits(int(L), split_tokens, nqt, window) for L in context_lens)
+    m = np.zeros(lead + (max_splits,), dtype=np.float64)
     l = np.zeros_like(m)
-    acc = np.zeros((num_seqs, num_q_heads, max_splits, head_dim), dtype=np.float64)
-    _load().oracle_decode_split(_ptr(q), _code(q), num_seqs, num_q_heads, _ptr(k_cache),
-                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _code(k_cache),
-                                k_cache.shape[1], head_dim, _ptr(block_tables),
+    acc = np.zeros(lead + (max_splits, head_dim), dtype=np.float64)
+    _load().oracle_decode_split(_ptr(q), _code(q), num_seqs, num_q_heads, nqt, int(window),
+                                _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                _code(k_cache), k_cache.shape[1], head_dim, _ptr(block_tables),
                                 block_tables.shape[1], _ptr(context_lens), float(scale),
                                 int(split_tokens), int(max_splits), _ptr(m), _ptr(l), _ptr(acc))
     return m, l, acc

@@ -22,6 +22,14 @@
  *                 kernel merges them.
  *   [Echo 3]      same notes, section 3, "KV Cache INT8 quantisation": INT8
  *                 cache with per-token scales, dequantised right after loading.
+ *   [ATOM 4.2]    "AMD ATOM Inference Engine" article, section 4.2 (decode
+ *                 scheduling): with MTP speculative decoding every decode step
+ *                 of a sequence carries mtp_k + 1 new tokens (the target token
+ *                 and the draft tokens), each with its own KV slot.
+ *   [Echo 4]      EchoLLMServing notes, section 4 (design trade-offs): sliding
+ *                 window attention as an algorithm-level way to bound decode
+ *                 cost; the ATOM article's model table lists it for GPT-OSS
+ *                 and MiMo.
  *
  * Readings where the pages are silent (each one is listed with its reason in
  * the design notes of the repository):
@@ -32,8 +40,16 @@
  *   - logits are scale * q.k with a natural-exponent softmax over all tokens
  *     t < context_len (the token written this step included);
  *   - context_len 0 gives a zero output and empty partials (m=-inf, l=0, acc=0);
- *   - split j of a sequence holds tokens [j*T, min((j+1)*T, L)), T =
- *     split_tokens, and there are max(1, ceil(L/T)) splits;
+ *   - Q = num_query_tokens >= 1 query tokens per sequence (Q = mtp_k + 1): they
+ *     are the last Q tokens of the context, query token i at position
+ *     p = L - Q + i, and it attends the tokens t <= p (causal among the new
+ *     tokens); with a sliding window of W > 0 tokens only p - W < t <= p
+ *     (the W most recent positions, its own included); W = 0 means no window.
+ *     A query with p < 0 attends nothing and gives a zero output;
+ *   - splits cover [base, L) with base = the start of the block holding the
+ *     earliest attended token (0 without a window); split j holds tokens
+ *     [base + j*T, min(base + (j+1)*T, L)), T = split_tokens, and there are
+ *     max(1, ceil((L - base)/T)) splits (max(1, ceil(L/T)) without a window);
  *   - partials: m = max logit of the split, l = sum exp(z - m), acc =
  *     sum exp(z - m) * v, NOT divided by l;
  *   - INT8 quantiser per (token, KV head): a = max |x| in fp32, sc = a/127 (IEEE
@@ -149,15 +165,29 @@ int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *s
 
 /* Everything the decode definition reads. */
 typedef struct {
-  const void *q;          /* [num_seqs][num_q_heads][head_dim] of q_dtype */
-  int q_dtype, num_q_heads;
+  const void *q; /* [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype */
+  int q_dtype, num_q_heads, num_query_tokens;
   const void *k, *v;      /* pool, [num_blocks][num_kv_heads][16][head_dim] */
   const float *k_scale, *v_scale; /* [num_blocks][num_kv_heads][16], INT8 only */
   int cache_dtype, num_kv_heads, head_dim;
   const int32_t *block_tables; /* [num_seqs][max_blocks_per_seq] */
   int max_blocks_per_seq;
   double scale;
+  int window; /* sliding window in tokens, 0 = none */
 } decode_args;
+
+/* Tokens [*t0, *t1) that query token i of a sequence of length L attends
+ * [ATOM 4.2, Echo 4]: its position is p = L - Q + i; t <= p, and with a
+ * window W > 0 also t > p - W. */
+static void query_range(int L, int Q, int W, int i, int *t0, int *t1) {
+  int p = L - Q + i;
+  if (p < 0) {
+    *t0 = *t1 = 0;
+    return;
+  }
+  *t1 = p + 1;
+  *t0 = (W > 0 && p - W + 1 > 0) ? p - W + 1 : 0;
+}
 
 /* Dequantised element d of the K (which=0) or V (which=1) row of logical
  * token t of sequence s in KV head kv, reached through the block table. */
@@ -173,22 +203,23 @@ static double kv_elem(const decode_args *a, int which, int s, int kv, int t, int
   return x;
 }
 
-/* Logit z_t = scale * q[s][h] . k_t. */
-static double logit(const decode_args *a, int s, int h, int t) {
+/* Logit z_t = scale * q[s][i][h] . k_t. */
+static double logit(const decode_args *a, int s, int i, int h, int t) {
   int kv = h / (a->num_q_heads / a->num_kv_heads);
+  int64_t row = ((int64_t)s * a->num_query_tokens + i) * a->num_q_heads + h;
   double dot = 0.0;
   for (int d = 0; d < a->head_dim; ++d) {
-    double qd = load_elem(a->q, a->q_dtype, ((int64_t)s * a->num_q_heads + h) * a->head_dim + d);
+    double qd = load_elem(a->q, a->q_dtype, row * a->head_dim + d);
     dot += qd * kv_elem(a, 0, s, kv, t, d);
   }
   return a->scale * dot;
 }
 
-/* Softmax-weighted sums over tokens [t0, t1) of sequence s, head h, taken
- * relative to the maximum logit of that range:
+/* Softmax-weighted sums over tokens [t0, t1) of sequence s, query token i,
+ * head h, taken relative to the maximum logit of that range:
  *   *m = max z_t,  *l = sum exp(z_t - m),  acc[d] = sum exp(z_t - m) v_t[d].
  * An empty range gives m = -inf, l = 0, acc = 0. */
-static void weighted_sums(const decode_args *a, int s, int h, int t0, int t1, double *m,
+static void weighted_sums(const decode_args *a, int s, int i, int h, int t0, int t1, double *m,
                           double *l, double *acc) {
   int kv = h / (a->num_q_heads / a->num_kv_heads);
   for (int d = 0; d < a->head_dim; ++d) acc[d] = 0.0;
@@ -198,7 +229,7 @@ static void weighted_sums(const decode_args *a, int s, int h, int t0, int t1, do
   double *z = (double *)malloc(sizeof(double) * (size_t)(t1 - t0));
   double mx = -INFINITY;
   for (int t = t0; t < t1; ++t) {
-    z[t - t0] = logit(a, s, h, t);
+    z[t - t0] = logit(a, s, i, h, t);
     if (z[t - t0] > mx) mx = z[t - t0];
   }
   double sum = 0.0;
@@ -214,26 +245,31 @@ static void weighted_sums(const decode_args *a, int s, int h, int t0, int t1, do
 
 /*
  * Decode attention by definition [Primer 8.1, Echo 2]: for each requested
- * (sequence, query head) row,
- *   out = sum_t softmax_t(scale * q.k_t) v_t   over t < context_lens[s],
- * with K and V gathered token by token through the block table and the whole
- * context taken at once (no splitting). Rows are given as index lists so that
- * a caller can check a sample of a large batch; out is [n_rows][head_dim].
+ * (sequence, query token, query head) row,
+ *   out = sum_t softmax_t(scale * q.k_t) v_t   over the tokens t the query
+ * token attends (query_range), with K and V gathered token by token through
+ * the block table and the whole range taken at once (no splitting). Rows are
+ * given as index lists so that a caller can check a sample of a large batch;
+ * out is [n_rows][head_dim].
  */
-void oracle_decode(const void *q, int q_dtype, int num_q_heads, const void *k_cache,
-                   const void *v_cache, const float *k_scale, const float *v_scale,
-                   int cache_dtype, int num_kv_heads, int head_dim,
+void oracle_decode(const void *q, int q_dtype, int num_q_heads, int num_query_tokens,
+                   int window, const void *k_cache, const void *v_cache, const float *k_scale,
+                   const float *v_scale, int cache_dtype, int num_kv_heads, int head_dim,
                    const int32_t *block_tables, int max_blocks_per_seq,
                    const int32_t *context_lens, double scale, const int32_t *row_seq,
-                   const int32_t *row_head, int64_t n_rows, double *out) {
-  decode_args a = {q, q_dtype, num_q_heads, k_cache, v_cache, k_scale, v_scale, cache_dtype,
-                   num_kv_heads, head_dim, block_tables, max_blocks_per_seq, scale};
+                   const int32_t *row_tok, const int32_t *row_head, int64_t n_rows,
+                   double *out) {
+  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, k_cache, v_cache, k_scale,
+                   v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
+                   max_blocks_per_seq, scale, window};
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
-    int s = row_seq[r], h = row_head[r];
+    int s = row_seq[r], i = row_tok[r], h = row_head[r];
+    int t0, t1;
+    query_range(context_lens[s], num_query_tokens, window, i, &t0, &t1);
     double m, l;
     double *o = out + r * head_dim;
-    weighted_sums(&a, s, h, 0, context_lens[s], &m, &l, o);
+    weighted_sums(&a, s, i, h, t0, t1, &m, &l, o);
     for (int d = 0; d < head_dim; ++d) o[d] = l > 0.0 ? o[d] / l : 0.0;
   }
 }
@@ -244,32 +280,54 @@ int oracle_num_splits(int context_len, int split_tokens) {
   return n < 1 ? 1 : n;
 }
 
+/* First token of the split range of a sequence of length L with Q query
+ * tokens and window W: the start of the block that holds the earliest token
+ * any of its query tokens attends (0 without a window). */
+int oracle_split_base(int context_len, int num_query_tokens, int window) {
+  if (window <= 0) return 0;
+  int first = context_len - num_query_tokens - window + 1;
+  if (first < 0) first = 0;
+  return first / OR_BLOCK * OR_BLOCK;
+}
+
 /*
  * Split-K partials [Echo 2, FlashDecoding]: split j of sequence s covers
- * tokens [j*split_tokens, min((j+1)*split_tokens, L)) and yields (m_j, l_j,
- * acc_j) as defined for weighted_sums. Splits j >= num_splits(L) are empty.
- * Layout: m, l [num_seqs][num_q_heads][max_splits];
- *         acc  [num_seqs][num_q_heads][max_splits][head_dim].
+ * tokens [base + j*T, min(base + (j+1)*T, L)), base = oracle_split_base, and
+ * yields, for every (query token i, head h), (m_j, l_j, acc_j) as defined
+ * for weighted_sums over the tokens of the split that query token attends.
+ * Splits j >= max(1, ceil((L - base)/T)) are empty.
+ * Layout: m, l [num_seqs][num_query_tokens][num_q_heads][max_splits];
+ *         acc  [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim].
  */
 void oracle_decode_split(const void *q, int q_dtype, int num_seqs, int num_q_heads,
-                         const void *k_cache, const void *v_cache, const float *k_scale,
-                         const float *v_scale, int cache_dtype, int num_kv_heads, int head_dim,
+                         int num_query_tokens, int window, const void *k_cache,
+                         const void *v_cache, const float *k_scale, const float *v_scale,
+                         int cache_dtype, int num_kv_heads, int head_dim,
                          const int32_t *block_tables, int max_blocks_per_seq,
                          const int32_t *context_lens, double scale, int split_tokens,
                          int max_splits, double *m, double *l, double *acc) {
-  decode_args a = {q, q_dtype, num_q_heads, k_cache, v_cache, k_scale, v_scale, cache_dtype,
-                   num_kv_heads, head_dim, block_tables, max_blocks_per_seq, scale};
-  int64_t jobs = (int64_t)num_seqs * num_q_heads * max_splits;
+  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, k_cache, v_cache, k_scale,
+                   v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
+                   max_blocks_per_seq, scale, window};
+  int64_t rows_per_seq = (int64_t)num_query_tokens * num_q_heads;
+  int64_t jobs = (int64_t)num_seqs * rows_per_seq * max_splits;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < jobs; ++r) {
     int j = (int)(r % max_splits);
-    int s = (int)(r / max_splits / num_q_heads);
-    int h = (int)(r / max_splits % num_q_heads);
+    int64_t row = r / max_splits; /* (s, i, h) */
+    int s = (int)(row / rows_per_seq);
+    int i = (int)(row % rows_per_seq / num_q_heads);
+    int h = (int)(row % num_q_heads);
     int L = context_lens[s];
-    int t0 = j * split_tokens;
+    int base = oracle_split_base(L, num_query_tokens, window);
+    int t0 = base + j * split_tokens;
     int t1 = t0 + split_tokens < L ? t0 + split_tokens : L;
-    if (j >= oracle_num_splits(L, split_tokens)) t1 = t0; /* empty split */
-    weighted_sums(&a, s, h, t0, t1, &m[r], &l[r], acc + r * head_dim);
+    if (j >= oracle_num_splits(L - base, split_tokens)) t1 = t0; /* empty split */
+    int q0, q1; /* the query token's own range */
+    query_range(L, num_query_tokens, window, i, &q0, &q1);
+    if (q0 > t0) t0 = q0;
+    if (q1 < t1) t1 = q1;
+    weighted_sums(&a, s, i, h, t0, t1, &m[r], &l[r], acc + r * head_dim);
   }
 }
 
@@ -279,7 +337,7 @@ void oracle_decode_split(const void *q, int q_dtype, int num_seqs, int num_q_hea
  *   out = sum_j w_j acc_j / sum_j w_j l_j.
  * Empty splits (l_j == 0) are skipped; no non-empty split gives out = 0.
  * Layouts as for oracle_decode_split; out is [num_rows][head_dim] where a row is
- * one (sequence, head) pair, num_rows = num_seqs * num_q_heads.
+ * one (sequence, query token, head) triple.
  */
 void oracle_merge(const double *m, const double *l, const double *acc, int64_t num_rows,
                   int max_splits, int head_dim, double *out) {

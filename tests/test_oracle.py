@@ -441,3 +441,146 @@ def test_fragmentation_one_tail_block():
     waste = (-(-L // 16)) * 16 - L
     assert workloads.fragmentation(L) == pytest.approx(waste.sum() / ((-(-L // 16)) * 16).sum())
     assert np.all(waste < 16)
+
+
+# ------------------------------------------------ several query tokens, windows
+#
+# [ATOM 4.2]: with MTP speculative decoding a decode step carries mtp_k + 1 new
+# tokens per sequence; read as the last Q tokens of the context, each attending
+# causally. [Echo 4] / ATOM's model table: sliding-window attention, read as
+# "the W most recent positions, the query's own included".
+
+def _mtp(Q, W=0, seed=21, **kw):
+    kw.setdefault("num_seqs", 4)
+    kw.setdefault("ctx_range", (Q, 150))
+    return _small("llama8b_bf16", seed, query_tokens=Q, window=W, **kw)
+
+
+@pytest.mark.parametrize("Q", [2, 4])
+def test_multi_token_rows_equal_prefix_decodes(Q):
+    """Query token i of a sequence of length L is an ordinary one-token decode
+    of the length-(L - Q + i + 1) prefix: same tokens in the same order, so the
+    outputs agree bitwise."""
+    b = _mtp(Q)
+    out = _decode(b)
+    assert out.shape == tuple(b.q.shape)
+    L = _np(b.context_lens)
+    for i in range(Q):
+        prefix = (L - Q + i + 1).astype(np.int32)
+        ref = oracle.decode(_np(b.q)[:, i], _np(b.k_cache), _np(b.v_cache), _np(b.block_tables),
+                            prefix, b.scale)
+        assert np.array_equal(out[:, i], ref), i
+
+
+def _dense(b, s):
+    """K, V of sequence s as [Hkv][L][D] fp64 tensors, gathered with NumPy."""
+    L = int(b.context_lens[s])
+    t = np.arange(L)
+    tab = b.block_tables.numpy()[s]
+    k = torch.from_numpy(_f64(b.k_cache)[tab[t // 16], :, t % 16]).permute(1, 0, 2)
+    v = torch.from_numpy(_f64(b.v_cache)[tab[t // 16], :, t % 16]).permute(1, 0, 2)
+    return k, v
+
+
+@pytest.mark.parametrize("Q,W", [(4, 0), (1, 37), (4, 37), (3, 16), (2, 1)])
+def test_query_ranges_match_masked_sdpa(Q, W):
+    """Textbook masked attention: torch SDPA in fp64 with a boolean mask that
+    lets query i (position p = L - Q + i) see t <= p and, with a window W,
+    t > p - W."""
+    b = _mtp(Q, W, seed=23, ctx_range=(max(Q, 1), 120))
+    out = _decode(b, window=W)
+    q = _f64(b.q).reshape(b.num_seqs, Q, b.q.shape[-2], -1)
+    Hq, Hkv = q.shape[2], b.k_cache.shape[1]
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        k, v = _dense(b, s)
+        p = L - Q + np.arange(Q)
+        t = np.arange(L)
+        mask = t[None, :] <= p[:, None]
+        if W:
+            mask &= t[None, :] > (p[:, None] - W)
+        qs = torch.from_numpy(q[s]).permute(1, 0, 2).unsqueeze(0)       # [1][Hq][Q][D]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qs, k.unsqueeze(0).contiguous(), v.unsqueeze(0).contiguous(),
+            attn_mask=torch.from_numpy(mask), scale=b.scale, enable_gqa=(Hq != Hkv))
+        np.testing.assert_allclose(out[s].reshape(Q, Hq, -1), ref[0].permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_window_at_least_the_context_changes_nothing():
+    b = _mtp(1, seed=25, ctx_range=(1, 200))
+    ref = _decode(b)
+    for W in (200, 201, 10 ** 6):
+        assert np.array_equal(_decode(b, window=W), ref)
+
+
+def test_window_of_one_returns_own_value():
+    """W = 1: each query token sees only its own position, so out = that
+    token's V row exactly (bf16 values are exact in fp64)."""
+    b = _mtp(3, W=1, seed=27, ctx_range=(3, 90))
+    out = _decode(b, window=1)
+    L = _np(b.context_lens)
+    tab, v = b.block_tables.numpy(), _f64(b.v_cache)
+    g = b.q.shape[2] // b.k_cache.shape[1]
+    for s in range(b.num_seqs):
+        for i in range(3):
+            p = int(L[s]) - 3 + i
+            row = v[tab[s, p // 16], :, p % 16]                         # [Hkv][D]
+            assert np.array_equal(out[s, i], np.repeat(row, g, axis=0))
+
+
+def test_query_before_the_sequence_start_is_zero():
+    """L < Q: query tokens at negative positions attend nothing (zero output);
+    the others are ordinary."""
+    b = _small("llama8b_bf16", 29, lengths=[2, 1, 5], query_tokens=4)
+    out = _decode(b)
+    assert np.all(out[0, :2] == 0) and np.all(out[1, :3] == 0)
+    assert np.all(np.isfinite(out)) and np.any(out[2] != 0) and np.any(out[0, 2:] != 0)
+
+
+@pytest.mark.parametrize("Q,W", [(4, 0), (1, 100), (4, 100), (2, 33)])
+def test_split_invariance_with_query_ranges(Q, W):
+    b = _mtp(Q, W, seed=31, ctx_range=(Q, 400))
+    ref = _decode(b, window=W)
+    for T in (16, 32, 64, 512):
+        m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
+                                        _np(b.block_tables), _np(b.context_lens), b.scale, T,
+                                        window=W)
+        np.testing.assert_allclose(oracle.merge(m, l, acc), ref, rtol=0, atol=1e-12)
+
+
+def test_poison_outside_the_reach_changes_nothing():
+    """NaN in every slot no query token attends (before the window, in the
+    first block's leading rows, past L) and freed table entries (-1) before
+    the window leave the result unchanged."""
+    kw = dict(num_seqs=5, ctx_range=(40, 300))
+    clean = _mtp(4, 45, seed=33, **kw)
+    dirty = _mtp(4, 45, seed=33, poison=True, **kw)
+    assert (dirty.block_tables.numpy() == -1).any()
+    assert np.array_equal(_decode(dirty, window=45), _decode(clean, window=45))
+    m, l, acc = oracle.decode_split(_np(dirty.q), _np(dirty.k_cache), _np(dirty.v_cache),
+                                    _np(dirty.block_tables), _np(dirty.context_lens),
+                                    dirty.scale, 16, window=45)
+    assert np.all(np.isfinite(acc)) and np.all(np.isfinite(l))
+
+
+def test_split_layout_with_windows_hand_worked():
+    """Hand-worked split layouts: base = start of the block holding
+    max(0, L - Q - W + 1); splits = max(1, ceil((L - base) / T))."""
+    cases = json.load(open(os.path.join(GOLDEN, "split_layout.json")))["cases"]
+    for c in cases:
+        assert oracle.split_base(c["L"], c["Q"], c["W"]) == c["base"], c
+        assert oracle.num_splits(c["L"], c["T"], c["Q"], c["W"]) == c["splits"], c
+
+
+def test_empty_splits_and_rows_in_multi_token_partials():
+    """With Q = 4 and T = 16 the last split of a sequence whose length is
+    16k + 1 holds only position L - 1: query tokens 0..2 attend none of it and
+    get (-inf, 0, 0) there, token 3 gets one token with l = 1."""
+    b = _small("llama8b_bf16", 35, lengths=[33, 17], query_tokens=4)
+    m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
+                                    _np(b.block_tables), _np(b.context_lens), b.scale, 16)
+    for s, last in ((0, 2), (1, 1)):
+        assert np.all(m[s, :3, :, last] == -np.inf) and np.all(l[s, :3, :, last] == 0)
+        assert np.all(acc[s, :3, :, last] == 0)
+        assert np.all(l[s, 3, :, last] == 1.0)

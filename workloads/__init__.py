@@ -20,9 +20,16 @@ Recipe (every draw is seeded):
   physically scattered; one more block is the "pad" block. Table entries past a
   sequence's last block point at the pad block.
 * The decode step's new token of sequence s sits at position L_s - 1; its slot
-  is ``slot_mapping[s]`` and its K/V rows are ``new_k[s]``/``new_v[s]``.
+  is ``slot_mapping[s]`` and its K/V rows are ``new_k[s]``/``new_v[s]``. With
+  Q = ``query_tokens`` > 1 (multi-token decode) the step's Q new tokens are
+  positions L_s - Q .. L_s - 1, q is [B][Q][Hq][D] and slot_mapping, new_k,
+  new_v hold B*Q rows, sequence-major.
+* With a sliding window W > 0 only the blocks from the one holding token
+  max(0, L_s - Q - W + 1) on are allocated (as a cache that frees blocks
+  behind the window would); earlier table entries are -1.
 * ``poison=True`` fills every pool slot that no sequence attends (tail slots of
-  last blocks, unused blocks, the pad block) with NaN (INT8 pools: NaN scales).
+  last blocks, tokens before a window's reach, unused blocks, the pad block)
+  with NaN (INT8 pools: NaN scales).
 
 Workloads (block size 16 throughout):
 
@@ -40,6 +47,10 @@ Workloads (block size 16 throughout):
   head_dim 128, bf16. Each group's 2000-token prefix (125 full blocks) is
   mapped to the same physical blocks; each sample's private suffix length is
   clip(rint(exp(N(ln 300, 1))), 1, 16384) and L = 2000 + suffix + 1.
+* ``mtp4_llama8b_bf16``: the 8B-shaped batch with 4 query tokens per sequence
+  (3 draft tokens and the target token of MTP speculative decoding).
+* ``swa4k_bf16``: 64 seqs, 32 q / 8 KV heads, head_dim 128, bf16, L uniform in
+  [8192, 65536], sliding window of 4096 tokens.
 """
 from __future__ import annotations
 
@@ -66,6 +77,8 @@ class Workload:
     ctx_hi: int = 0
     fixed_pool_blocks: int = 0  # 0: 1.1x the attended tokens
     split_tokens: int = 512
+    query_tokens: int = 1      # query tokens per sequence (mtp_k + 1)
+    window: int = 0            # sliding window in tokens, 0 = none
     # shared-prefix workloads
     groups: int = 0
     samples: int = 0
@@ -84,6 +97,9 @@ WORKLOADS = {
         Workload("int8_kv", 128, 32, 8, 128, "bf16", "int8", 1024, 8192),
         Workload("shared_prefix_bf16", 256, 64, 4, 128, "bf16", "bf16", groups=32, samples=8,
                  prefix_len=2000, suffix_median=300.0, suffix_sigma=1.0, suffix_max=16384),
+        Workload("mtp4_llama8b_bf16", 64, 32, 8, 128, "bf16", "bf16", 512, 4096,
+                 query_tokens=4),
+        Workload("swa4k_bf16", 64, 32, 8, 128, "bf16", "bf16", 8192, 65536, window=4096),
     ]
 }
 
@@ -93,15 +109,15 @@ TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "int8": torch.int
 @dataclasses.dataclass
 class Batch:
     workload: Workload
-    q: torch.Tensor               # [B][Hq][D]
+    q: torch.Tensor               # [B][Hq][D], or [B][Q][Hq][D] with Q query tokens
     k_cache: torch.Tensor         # [NB][Hkv][16][D]
     v_cache: torch.Tensor
     k_scale: Optional[torch.Tensor]  # [NB][Hkv][16] float32 (INT8 only)
     v_scale: Optional[torch.Tensor]
     block_tables: torch.Tensor    # [B][max_blocks] int32
     context_lens: torch.Tensor    # [B] int32
-    slot_mapping: torch.Tensor    # [B] int64, slot of position L-1
-    new_k: torch.Tensor           # [B][Hkv][D]
+    slot_mapping: torch.Tensor    # [B*Q] int64, slots of positions L-Q .. L-1
+    new_k: torch.Tensor           # [B*Q][Hkv][D]
     new_v: torch.Tensor
     scale: float
     max_context_len: int
@@ -111,6 +127,8 @@ class Batch:
     fill_slots: Optional[torch.Tensor] = None
     num_blocks_shared: int = 0    # physical blocks referenced (shared counted once)
     num_blocks_logical: int = 0   # sum over seqs of ceil(L/16)
+    query_tokens: int = 1
+    window: int = 0
 
     @property
     def num_seqs(self) -> int:
@@ -126,13 +144,23 @@ def _lengths(w: Workload, rng: np.random.Generator, num_seqs: int, ctx_lo: int, 
     return rng.integers(ctx_lo, ctx_hi + 1, size=num_seqs).astype(np.int64), None
 
 
-def _attended_slots(tables: np.ndarray, L: np.ndarray) -> np.ndarray:
-    """Physical slot of every (sequence, position < L) pair, sequence-major."""
+def reach_start(L, query_tokens: int = 1, window: int = 0):
+    """Earliest position any query token of a sequence attends (elementwise)."""
+    L = np.asarray(L, dtype=np.int64)
+    if window <= 0:
+        return np.zeros_like(L)
+    return np.maximum(L - query_tokens - window + 1, 0)
+
+
+def _attended_slots(tables: np.ndarray, L: np.ndarray, lo: Optional[np.ndarray] = None):
+    """Physical slot of every (sequence, lo <= position < L) pair, sequence-major."""
     if len(L) == 0:
         return np.zeros(0, np.int64)
-    seq = np.repeat(np.arange(len(L)), L)
-    starts = np.cumsum(L) - L
-    pos = np.arange(int(L.sum())) - np.repeat(starts, L)
+    lo = np.zeros_like(L) if lo is None else lo
+    n = L - lo
+    seq = np.repeat(np.arange(len(L)), n)
+    starts = np.cumsum(n) - n
+    pos = np.arange(int(n.sum())) - np.repeat(starts, n) + np.repeat(lo, n)
     return tables[seq, pos // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + pos % BLOCK_SIZE
 
 
@@ -144,17 +172,24 @@ def _randn(shape, gen: torch.Generator, device, dtype: torch.dtype) -> torch.Ten
 def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
                ctx_range: Optional[tuple] = None, poison: bool = False,
                contiguous_tables: bool = False, groups: Optional[int] = None,
-               suffix_max: Optional[int] = None) -> Batch:
+               suffix_max: Optional[int] = None, query_tokens: Optional[int] = None,
+               window: Optional[int] = None, lengths=None) -> Batch:
     """Draw one decode batch of workload ``name`` (a key of WORKLOADS or a
     Workload).
 
     num_seqs / ctx_range / groups / suffix_max shrink a workload for tests;
-    contiguous_tables assigns physical blocks in logical order instead of a
-    random permutation (the "contiguous slice" layout).
+    query_tokens / window override the workload's; lengths fixes the context
+    lengths (one per sequence); contiguous_tables assigns physical blocks in
+    logical order instead of a random permutation (the "contiguous slice"
+    layout).
     """
     w = name if isinstance(name, Workload) else WORKLOADS[name]
     if groups is not None or suffix_max is not None:
         w = dataclasses.replace(w, groups=groups or w.groups, suffix_max=suffix_max or w.suffix_max)
+    if query_tokens is not None or window is not None:
+        w = dataclasses.replace(w, query_tokens=w.query_tokens if query_tokens is None else query_tokens,
+                                window=w.window if window is None else window)
+    Q, W = w.query_tokens, w.window
     rng = np.random.default_rng(seed)
     gen = torch.Generator(device=device).manual_seed(seed)
     if w.groups:
@@ -163,8 +198,13 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         B = num_seqs or w.num_seqs
     lo, hi = ctx_range if ctx_range is not None else (w.ctx_lo, w.ctx_hi)
     L, suffix = _lengths(w, rng, B, lo, hi)
+    if lengths is not None:
+        L = np.asarray(lengths, dtype=np.int64)
+        B = len(L)
     nblk = -(-L // BLOCK_SIZE)
     max_blocks = int(nblk.max()) if B else 1
+    first_blk = reach_start(L, Q, W) // BLOCK_SIZE  # blocks before it are never read
+    nalloc = nblk - first_blk
 
     # Physical block assignment.
     if w.groups:
@@ -174,8 +214,8 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         needed = w.groups * pre_blocks + int(priv.sum())
         unique_tokens = w.groups * w.prefix_len + int((L - w.prefix_len).sum())
     else:
-        needed = int(nblk.sum())
-        unique_tokens = int(L.sum())
+        needed = int(nalloc.sum())
+        unique_tokens = int((L - first_blk * BLOCK_SIZE).sum())
     if w.fixed_pool_blocks:
         num_blocks = w.fixed_pool_blocks
         assert num_blocks >= needed + 1
@@ -184,6 +224,8 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
     order = np.arange(num_blocks) if contiguous_tables else rng.permutation(num_blocks)
     pad_block = int(order[needed])
     tables = np.full((B, max_blocks), pad_block, dtype=np.int32)
+    for s in range(B):
+        tables[s, :first_blk[s]] = -1  # freed behind the window
     cursor = 0
     if w.groups:
         prefix_ids = []
@@ -197,18 +239,23 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
             cursor += priv[s]
     else:
         for s in range(B):
-            tables[s, :nblk[s]] = order[cursor:cursor + nblk[s]]
-            cursor += nblk[s]
+            tables[s, first_blk[s]:nblk[s]] = order[cursor:cursor + nalloc[s]]
+            cursor += nalloc[s]
     assert cursor == needed
 
     D, Hq, Hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
     in_dt = TORCH_DTYPES[w.dtype]
-    q = _randn((B, Hq, D), gen, device, in_dt)
-    new_k = _randn((B, Hkv, D), gen, device, in_dt)
-    new_v = _randn((B, Hkv, D), gen, device, in_dt)
-    last = L - 1
-    slot_mapping = (tables[np.arange(B), last // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE
-                    + last % BLOCK_SIZE)
+    q = _randn((B, Hq, D) if Q == 1 else (B, Q, Hq, D), gen, device, in_dt)
+    new_k = _randn((B * Q, Hkv, D), gen, device, in_dt)
+    new_v = _randn((B * Q, Hkv, D), gen, device, in_dt)
+    # Positions L-Q .. L-1 of every sequence, sequence-major (negative
+    # positions, for L < Q, get slot -1: nothing to write).
+    pos = (L[:, None] - Q + np.arange(Q)[None, :]).reshape(-1)
+    seq = np.repeat(np.arange(B), Q)
+    ok = pos >= 0
+    pos_c = np.maximum(pos, 0)
+    slot_mapping = np.where(ok, tables[seq, pos_c // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE
+                            + pos_c % BLOCK_SIZE, -1).astype(np.int64)
 
     k_scale = v_scale = fill_k = fill_v = fill_slots = None
     cache_shape = (num_blocks, Hkv, BLOCK_SIZE, D)
@@ -219,7 +266,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         k_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         v_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         # Every attended token's K/V, to be written through the KV write.
-        fill_slots_np = np.unique(_attended_slots(tables, L))
+        fill_slots_np = np.unique(_attended_slots(tables, L, reach_start(L, Q, W)))
         fill_slots = torch.from_numpy(fill_slots_np).to(device)
         fill_k = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
         fill_v = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
@@ -229,7 +276,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         v_cache = _randn(cache_shape, gen, device, cdt)
         if poison:
             live = torch.zeros(num_blocks * BLOCK_SIZE, dtype=torch.bool)
-            live[torch.from_numpy(_attended_slots(tables, L))] = True
+            live[torch.from_numpy(_attended_slots(tables, L, reach_start(L, Q, W)))] = True
             dead = (~live).view(num_blocks, 1, BLOCK_SIZE, 1).expand(cache_shape).to(device)
             k_cache.masked_fill_(dead, float("nan"))
             v_cache.masked_fill_(dead, float("nan"))
@@ -243,7 +290,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         new_k=new_k, new_v=new_v, scale=1.0 / math.sqrt(D),
         max_context_len=int(L.max()) if B else 0, pad_block=pad_block,
         fill_k=fill_k, fill_v=fill_v, fill_slots=fill_slots,
-        num_blocks_shared=needed, num_blocks_logical=logical)
+        num_blocks_shared=needed, num_blocks_logical=logical, query_tokens=Q, window=W)
 
 
 def kv_token_slots(prefix_len: int, gen_lens, shared: bool) -> int:
