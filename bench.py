@@ -10,7 +10,9 @@ Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
 head_dim 128, block 16, context lengths uniform in [512, 4096], random
 non-contiguous block tables over a pool of 1.1x the tokens).
 
-Prints ONE JSON line. `value` is tokens/s for the whole step (B / t_step).
+Prints ONE JSON line. `value` is tokens/s for the whole step (B * Q / t_step:
+one new token per sequence, Q query tokens per sequence for multi-token
+decode).
 The split kernel's roofline uses its own duration: HIP events on the launch
 stream around `steps` back-to-back launches of it after the timed region.
 Per-kernel p10/p50/p90 come from a pass with events between the kernels of
@@ -68,15 +70,18 @@ def kernel_source_hash():
 
 
 def algorithmic_bytes(b):
-    """Bytes the split kernel must read by definition: every attended token's
-    K and V rows (plus INT8 scales), q, and the block-table entries used."""
+    """Bytes the split kernel must read by definition: the K and V rows (plus
+    INT8 scales) of every token some query token attends (with a sliding
+    window only the tokens it reaches), q, and the block-table entries used."""
+    import numpy as np
     import workloads
-    L = b.context_lens.to("cpu").long()
+    L = b.context_lens.to("cpu").numpy().astype(np.int64)
+    lo = workloads.reach_start(L, b.query_tokens, b.window)
     w = b.workload
     per_token = workloads.kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.cache_dtype)
-    kv = int(L.sum()) * per_token
+    kv = int((L - lo).sum()) * per_token
     q = b.q.numel() * b.q.element_size()
-    tables = int(((L + 15) // 16).sum()) * 4 + L.numel() * 4
+    tables = int(((L + 15) // 16 - lo // 16).sum()) * 4 + L.size * 4
     return kv, kv + q + tables
 
 
@@ -97,23 +102,25 @@ def cpu_baseline(b, seconds):
     ks = None if b.k_scale is None else host(b.k_scale)
     vs = None if b.v_scale is None else host(b.v_scale)
     bt, cl = host(b.block_tables), host(b.context_lens)
-    B, Hq = q.shape[:2]
-    h = np.arange(Hq, dtype=np.int32)
+    B, Q, Hq = q.shape[0], b.query_tokens, q.shape[-2]
+    tok = np.repeat(np.arange(Q, dtype=np.int32), Hq)
+    h = np.tile(np.arange(Hq, dtype=np.int32), Q)
     done, tokens, t0 = 0, 0, time.perf_counter()
     elapsed = 0.0
     # Whole sequences in batch order, wrapping around, until the time budget.
     while elapsed < seconds:
         s = done % B
-        oracle.decode(q, kc, vc, bt, cl, b.scale, ks, vs, rows=(np.full(Hq, s, np.int32), h))
+        oracle.decode(q, kc, vc, bt, cl, b.scale, ks, vs,
+                      rows=(np.full(Q * Hq, s, np.int32), tok, h), window=b.window)
         tokens += int(cl[s])
         done += 1
         elapsed = time.perf_counter() - t0
     return {
-        "value": done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+        "value": done * Q / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{done} sequence decodes ({done / B:.2f} passes over the {B}-sequence "
-                  f"batch, all {Hq} q heads, {tokens} context tokens), fp64 block-table "
-                  f"walk, {elapsed:.1f} s",
+                  f"batch, {Q} query token(s) x {Hq} q heads, {tokens} context tokens), fp64 "
+                  f"block-table walk, {elapsed:.1f} s",
     }
 
 
@@ -175,15 +182,17 @@ def main():
         pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
                           b.v_scale)
         b.fill_k = b.fill_v = None
-    B, Hq, D = b.q.shape
+    B, Hq, D = b.q.shape[0], b.q.shape[-2], b.q.shape[-1]
+    Q, W = b.query_tokens, b.window
+    mb = b.block_tables.shape[1]
     T = args.split_tokens or pa.default_split_tokens(B, w.num_kv_heads, w.head_dim,
-                                                       b.k_cache.dtype, b.max_context_len)
-    S = pa.num_splits(b.max_context_len, T)
+                                                       b.k_cache.dtype, b.max_context_len, Q, W)
+    S = pa.max_splits(min(b.max_context_len, mb * 16), T, Q, W)
     out = torch.empty_like(b.q)
-    parts = pa.Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
-                        l=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
-                        acc=torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev),
-                        context_lens=b.context_lens, split_tokens=T)
+    parts = pa.Partials(m=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=dev),
+                        l=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=dev),
+                        acc=torch.empty((B, Q, Hq, S, D), dtype=torch.float32, device=dev),
+                        context_lens=b.context_lens, split_tokens=T, sliding_window=W)
     sched = torch.empty(pa.sched_bytes(B, S) // 4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     plan = [None]
@@ -191,16 +200,15 @@ def main():
     def prepare():
         # KV write of the step's new tokens and the split plan, one launch.
         plan[0] = pa.paged_decode_prepare(b.new_k, b.new_v, b.slot_mapping, b.k_cache,
-                                          b.v_cache, b.context_lens,
-                                          b.block_tables.shape[1], b.k_scale, b.v_scale,
+                                          b.v_cache, b.context_lens, mb, b.k_scale, b.v_scale,
                                           max_context_len=b.max_context_len, split_tokens=T,
-                                          sched=sched)
+                                          num_query_tokens=Q, sliding_window=W, sched=sched)
 
     def decode():
         pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
                                      b.scale, b.k_scale, b.v_scale,
                                      max_context_len=b.max_context_len, split_tokens=T,
-                                     plan=plan[0], partials=parts)
+                                     sliding_window=W, plan=plan[0], partials=parts)
 
     def reduce():
         pa.paged_attn_reduce(parts, out)
@@ -259,7 +267,7 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": B / (ms_step * 1e-3),
+        "value": B * Q / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -275,6 +283,7 @@ def main():
             "head_dim": D, "block_size": 16, "cache_dtype": w.cache_dtype,
             "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
+            "query_tokens": Q, "sliding_window": W,
             "tables": "contiguous" if args.contiguous_tables else "permuted",
             "context_range": list(args.ctx_range) if args.ctx_range else
             [b.workload.ctx_lo, b.workload.ctx_hi],
@@ -282,7 +291,7 @@ def main():
         },
         "kv_read_gbps": kv_gbps_step,
         "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
-        "decode_reduce_tokens_per_s": B / ((t_dec + t_red) * 1e-3),
+        "decode_reduce_tokens_per_s": B * Q / ((t_dec + t_red) * 1e-3),
         "kernel_ms": {"write_and_plan": t_prep, "decode_split": t_dec, "reduce": t_red,
                       "decode_split_back_to_back": t_dec_b2b},
         "kernel_us_p10_p50_p90": {k: [round(1e3 * pct(v, q), 2) for q in (0.1, 0.5, 0.9)]

@@ -16,7 +16,11 @@
  *     a second reduce kernel, and a split count that follows the context length
  *     (split_num = context_len / chunk, chunk 256 or 512 from profiling);
  *     section 3 (KV Cache INT8): INT8 cache with per-token scales, dequantised
- *     inside the attention kernel right after loading.
+ *     inside the attention kernel right after loading; section 4: sliding
+ *     window attention as a way to bound decode cost.
+ *   - "AMD ATOM Inference Engine" article, section 4.2 (decode scheduling):
+ *     with MTP speculative decoding each decode step of a sequence carries
+ *     mtp_k + 1 new tokens, each with its own KV slot.
  *
  * Conventions shared by every entry point:
  *   - Pool layout: k_cache, v_cache are [num_blocks][num_kv_heads][16][head_dim]
@@ -26,15 +30,30 @@
  *   - Token t of sequence s lives in block block_tables[s][t / 16], row t % 16.
  *     A slot is block * 16 + row.
  *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
- *   - Logits are scale * q.k; softmax uses the natural exponent over every
- *     token t < context_lens[s]. context_lens[s] == 0 gives a zero output.
- *   - Split j of sequence s covers tokens [j*T, min((j+1)*T, L)), T =
- *     split_tokens (a positive multiple of 16, at most 4096), and a sequence of
- *     length L has max(1, ceil(L / T)) splits.
- *   - Partials: m[s][h][j] is the split's maximum logit (natural-log units),
- *     l[s][h][j] = sum exp(z - m), acc[s][h][j][:] = sum exp(z - m) v (not
- *     divided by l). A split with no tokens stores m = -inf, l = 0, acc = 0.
- *     Entries for j >= max(1, ceil(L / T)) are not written.
+ *   - Query tokens: each sequence carries Q = num_query_tokens (1 to 16) query
+ *     tokens, its last Q positions: query token i sits at p = L - Q + i
+ *     (L = context_lens[s], the new tokens already written) and attends the
+ *     tokens t <= p (causal among the new tokens). With a sliding window of
+ *     W = sliding_window > 0 tokens it attends only p - W < t <= p (its W most
+ *     recent positions, its own included); W = 0 means no window. A query
+ *     token with p < 0, or a sequence with L == 0, gives a zero output.
+ *     q and out are [num_seqs][Q][num_q_heads][head_dim] (for Q = 1 the same
+ *     memory as [num_seqs][num_q_heads][head_dim]).
+ *   - Logits are scale * q.k; softmax uses the natural exponent over the
+ *     tokens a query token attends.
+ *   - Splits cover [base, L), base = 16 * floor(max(0, L - Q - W + 1) / 16)
+ *     with a window (the block holding the earliest attended token), else 0.
+ *     Split j covers [base + j*T, min(base + (j+1)*T, L)), T = split_tokens (a
+ *     positive multiple of 16, at most 4096); a sequence has
+ *     max(1, ceil((L - base) / T)) splits (max(1, ceil(L / T)) without a
+ *     window). Blocks before base are never read: their table entries may be
+ *     anything (a cache may free them).
+ *   - Partials: rows are (sequence, query token, query head), laid out
+ *     [num_seqs][Q][num_q_heads]; m[row][j] is the maximum logit over the
+ *     tokens of split j the row's query token attends (natural-log units),
+ *     l[row][j] = sum exp(z - m), acc[row][j][:] = sum exp(z - m) v (not
+ *     divided by l). A split with no such token stores m = -inf, l = 0,
+ *     acc = 0. Entries past the sequence's split count are not written.
  *   - Pointers: every array argument is a device pointer owned by the caller;
  *     the library never allocates, frees or synchronises. q, k/v, k_cache,
  *     v_cache must be 16-byte aligned and contiguous in the layouts above.
@@ -63,6 +82,7 @@ extern "C" {
 #define PA_BLOCK_SIZE 16
 #define PA_MAX_SPLIT_TOKENS 4096
 #define PA_MAX_SEQS 65535
+#define PA_MAX_QUERY_TOKENS 16
 
 /* Element types. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
@@ -87,26 +107,36 @@ const char *pa_strerror(int status);
  * [EchoLLMServing notes, section 2, FlashDecoding split heuristic.] */
 int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
 
+/* Splits of the longest split range a sequence of length <= max_context_len
+ * can have with num_query_tokens query tokens and the given window: the
+ * max_splits the partials need. Without a window this is
+ * pa_num_splits(max_context_len, split_tokens); with one the range is at
+ * most min(max_context_len, Q + W + 14) tokens. 0 for bad arguments. */
+int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
+                      int32_t split_tokens);
+
 /* Split size T (tokens) the library uses when a caller passes
  * split_tokens = 0 [EchoLLMServing notes, section 2: the split count follows
  * the context length, one split per 512 tokens in the notes' setting].
  * T starts at 256 KiB of K and V per (split, KV head), i.e. 262144 /
  * (2 * head_dim * element bytes): 512 tokens for a 16-bit 128-dim cache, 1024
  * for an INT8 one, capped at 4096. It is then halved, down to 64, while
- * num_seqs * num_kv_heads * pa_num_splits(max_context_len, T) is below 1024
- * work items (small batches still fill the device). Returns 0 for a head_dim
- * other than 64 or 128 or an unknown cache_dtype. Host-only arithmetic. */
+ * num_seqs * num_kv_heads * pa_max_splits(max_context_len, Q, W, T) is below
+ * 1024 work items (small batches still fill the device). Returns 0 for a
+ * head_dim other than 64 or 128, an unknown cache_dtype or bad Q / W.
+ * Host-only arithmetic. */
 int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t cache_dtype, int32_t max_context_len);
+                                int32_t cache_dtype, int32_t max_context_len,
+                                int32_t num_query_tokens, int32_t sliding_window);
 
 /* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
  * a small header). */
 size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits);
 
 /* Bytes of workspace paged_attn_decode needs: scheduling scratch plus the
- * partials (m, l, acc). */
-size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                          int32_t max_splits);
+ * partials (m, l, acc) of num_seqs * num_query_tokens * num_q_heads rows. */
+size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                          int32_t head_dim, int32_t max_splits);
 
 /*
  * KV write ("reshape and cache") [ATOM article 5.1; Primer 8.1]: for every
@@ -133,20 +163,23 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  * Plan of a decode step [EchoLLMServing notes, section 2: the split count of a
  * sequence follows its context length]: one small kernel reads context_lens on
  * the device and writes into `sched` the list of every split of the batch,
- * max(1, ceil(L_s / T)) per sequence, full splits first and then the last
- * split of each sequence, longest first. The list depends only on the lengths,
- * T and the length bounds, so one plan serves every attention layer of a step.
- *   context_lens     [num_seqs] int32 (device)
+ * max(1, ceil((L_s - base_s) / T)) per sequence (see the split range above),
+ * full splits first and then the last split of each sequence, longest first.
+ * The list depends only on the lengths, Q, W, T and the length bounds, so one
+ * plan serves every attention layer of a step that uses the same window.
+ *   context_lens       [num_seqs] int32 (device)
  *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
- *   split_tokens     T, a positive multiple of 16 <= 4096 (the plan knows no
- *                    cache, so there is no default here: pass what the decode
- *                    call will use, e.g. pa_default_split_tokens())
- *   sched            device scratch of pa_sched_bytes(num_seqs, max_splits) bytes
- *                    with max_splits >= pa_num_splits(max_context_len, T)
+ *   num_query_tokens   Q, 1 .. PA_MAX_QUERY_TOKENS
+ *   sliding_window     W >= 0 (0: none)
+ *   split_tokens       T, a positive multiple of 16 <= 4096 (the plan knows no
+ *                      cache, so there is no default here: pass what the
+ *                      decode call will use, e.g. pa_default_split_tokens())
+ *   sched              device scratch of pa_sched_bytes(num_seqs, max_splits)
+ *                      bytes, max_splits >= pa_max_splits(max_context_len, Q, W, T)
  */
 int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t split_tokens, int32_t *sched,
-                    hipStream_t stream);
+                    int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
+                    int32_t split_tokens, int32_t *sched, hipStream_t stream);
 
 /*
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
@@ -154,7 +187,8 @@ int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_b
  * others write). Arguments, layouts and errors are those of the two calls
  * (split_tokens = 0 here picks pa_default_split_tokens() for this cache); the
  * results are identical to calling them in turn. Serves the start of a decode
- * step, where the new tokens are written and the batch's splits are listed.
+ * step, where the new tokens (num_seqs * Q of them with several query tokens)
+ * are written and the batch's splits are listed.
  */
 int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
@@ -162,75 +196,84 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
                          const int32_t *context_lens, int32_t num_seqs,
                          int32_t max_blocks_per_seq, int32_t max_context_len,
-                         int32_t split_tokens, int32_t *sched, hipStream_t stream);
+                         int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
+                         int32_t *sched, hipStream_t stream);
 
 /*
  * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
- * s, query head h and split j < max(1, ceil(L_s / T)), write the partials
- * (m, l, acc) of that split. The g = Hq/Hkv query heads of a KV head share
- * every K/V load. Works through the split list of `sched`, which
+ * s, query token i, query head h and split j of s, write the partials
+ * (m, l, acc) of that split. The Q*g rows (query tokens x query heads) of a KV
+ * head share every K/V load. Works through the split list of `sched`, which
  * paged_attn_plan must have written (on this stream, before this call) for the
- * same context_lens, num_seqs, max_blocks_per_seq, max_context_len and
- * split_tokens; a plan for another split_tokens, num_seqs or length bound is
- * ignored (nothing is written), other mismatches give unspecified results.
- *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (PA_F32/PA_BF16)
- *   k_cache, ...   pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
- *                  (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and
- *                  v_scale required). num_blocks < 2^31.
- *   block_tables   [num_seqs][max_blocks_per_seq] int32
- *   context_lens   [num_seqs] int32, each <= max_context_len
- *   max_context_len  host bound on context_lens, sizes the launch grid
- *   scale          logit scale (commonly 1/sqrt(head_dim))
- *   split_tokens   T, a positive multiple of 16 <= 4096, or 0 for
- *                  pa_default_split_tokens()
- *   max_splits     leading stride of the partials; >= pa_num_splits(max_context_len, T)
- *   part_m, part_l [num_seqs][num_q_heads][max_splits] fp32
- *   part_acc       [num_seqs][num_q_heads][max_splits][head_dim] fp32
- *   sched          the plan (read only)
+ * same context_lens, num_seqs, max_blocks_per_seq, max_context_len, Q, W and
+ * split_tokens; a plan for another split_tokens, num_seqs, length bound, Q or
+ * W is ignored (nothing is written), other mismatches give unspecified results.
+ *   q                 [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype
+ *                     (PA_F32/PA_BF16)
+ *   k_cache, ...      pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
+ *                     (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and
+ *                     v_scale required). num_blocks < 2^31.
+ *   block_tables      [num_seqs][max_blocks_per_seq] int32
+ *   context_lens      [num_seqs] int32, each <= max_context_len
+ *   max_context_len   host bound on context_lens, sizes the launch grid
+ *   sliding_window    W >= 0 (0: none)
+ *   scale             logit scale (commonly 1/sqrt(head_dim))
+ *   split_tokens      T, a positive multiple of 16 <= 4096, or 0 for
+ *                     pa_default_split_tokens()
+ *   max_splits        leading stride of the partials;
+ *                     >= pa_max_splits(max_context_len, Q, W, T)
+ *   part_m, part_l    [num_seqs][num_query_tokens][num_q_heads][max_splits] fp32
+ *   part_acc          [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim] fp32
+ *   sched             the plan (read only)
  * head_dim must be 64 or 128, num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16,
- * and num_seqs at most PA_MAX_SEQS.
+ * num_query_tokens 1 .. PA_MAX_QUERY_TOKENS and num_seqs at most PA_MAX_SEQS.
  */
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
-                              int32_t num_q_heads, int32_t head_dim, const void *k_cache,
-                              const void *v_cache, const float *k_scale, const float *v_scale,
-                              int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
-                              const int32_t *block_tables, int32_t max_blocks_per_seq,
-                              const int32_t *context_lens, int32_t max_context_len, float scale,
+                              int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                              const void *k_cache, const void *v_cache, const float *k_scale,
+                              const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
+                              int32_t num_kv_heads, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t max_context_len, int32_t sliding_window, float scale,
                               int32_t split_tokens, int32_t max_splits, float *part_m,
                               float *part_l, float *part_acc, const int32_t *sched,
                               hipStream_t stream);
 
 /*
  * Reduce kernel [EchoLLMServing notes, section 2]: merge the partials of every
- * (sequence, query head) over its splits j < max(1, ceil(L_s / T)):
+ * row (sequence, query token, query head) over the splits of its sequence:
  *   M = max_j m_j over splits with l_j > 0, w_j = exp(m_j - M),
  *   out = sum_j w_j acc_j / sum_j w_j l_j   (0 when no split holds a token),
  * written as out_dtype (PA_F32, or PA_BF16 rounded to nearest even).
- *   part_*        as written by paged_attn_decode_partial with the same
- *                 split_tokens (T > 0) and max_splits
- *   context_lens  [num_seqs] int32 (lengths are clamped to >= 0)
- *   out           [num_seqs][num_q_heads][head_dim]
+ *   part_*         as written by paged_attn_decode_partial with the same
+ *                  num_query_tokens, sliding_window, split_tokens (T > 0) and
+ *                  max_splits
+ *   context_lens   [num_seqs] int32 (lengths are clamped to >= 0)
+ *   out            [num_seqs][num_query_tokens][num_q_heads][head_dim]
  */
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
-                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t head_dim, int32_t split_tokens, int32_t max_splits, void *out,
-                      int32_t out_dtype, hipStream_t stream);
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_query_tokens,
+                      int32_t num_q_heads, int32_t head_dim, int32_t sliding_window,
+                      int32_t split_tokens, int32_t max_splits, void *out, int32_t out_dtype,
+                      hipStream_t stream);
 
 /*
  * Whole decode step of one attention layer: paged_attn_plan and
  * paged_attn_decode_partial into the caller's workspace, then
  * paged_attn_reduce into out (dtype = q_dtype).
- * The split count is pa_num_splits(max_context_len, T) with T = split_tokens
- * (0: pa_default_split_tokens()). workspace must hold
- * pa_workspace_bytes(num_seqs, num_q_heads, head_dim, that split count)
+ * The split count is pa_max_splits(max_context_len', Q, W, T) with
+ * max_context_len' = min(max_context_len, 16 * max_blocks_per_seq) and
+ * T = split_tokens (0: pa_default_split_tokens()). workspace must hold
+ * pa_workspace_bytes(num_seqs, Q, num_q_heads, head_dim, that split count)
  * bytes, 256-byte aligned.
  */
-int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t head_dim, const void *k_cache, const void *v_cache,
-                      const float *k_scale, const float *v_scale, int32_t cache_dtype,
-                      int64_t num_blocks, int32_t num_kv_heads, const int32_t *block_tables,
-                      int32_t max_blocks_per_seq, const int32_t *context_lens,
-                      int32_t max_context_len, float scale, int32_t split_tokens, void *out,
+int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_query_tokens,
+                      int32_t num_q_heads, int32_t head_dim, const void *k_cache,
+                      const void *v_cache, const float *k_scale, const float *v_scale,
+                      int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t max_context_len,
+                      int32_t sliding_window, float scale, int32_t split_tokens, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -7,12 +7,17 @@ library must be built (``__graft_entry__.build()``); there is no fallback.
 
 Tensor layouts (block size 16):
 
-* q, out          [num_seqs][num_q_heads][head_dim], fp32 or bf16
+* q, out          [num_seqs][num_q_heads][head_dim] (one query token per
+                  sequence) or [num_seqs][Q][num_q_heads][head_dim] (Q query
+                  tokens: the sequence's last Q positions), fp32 or bf16
 * k_cache, v_cache [num_blocks][num_kv_heads][16][head_dim], fp32/bf16/int8
 * k_scale, v_scale [num_blocks][num_kv_heads][16] fp32 (int8 caches only)
 * block_tables    [num_seqs][max_blocks_per_seq] int32
 * context_lens    [num_seqs] int32
 * slot_mapping    [num_tokens] int64 (negative = skip)
+
+``sliding_window`` (tokens, 0 = none) limits each query token to its W most
+recent positions.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ import torch
 from . import _lib
 
 BLOCK_SIZE = 16
+MAX_QUERY_TOKENS = 16
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 _DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
 
@@ -66,23 +72,34 @@ def num_splits(context_len: int, split_tokens: int) -> int:
     return int(_lib.load().pa_num_splits(int(context_len), int(split_tokens)))
 
 
+def max_splits(max_context_len: int, split_tokens: int, num_query_tokens: int = 1,
+               sliding_window: int = 0) -> int:
+    """Splits of the longest split range under the bound (the partials' stride)."""
+    return int(_lib.load().pa_max_splits(int(max_context_len), int(num_query_tokens),
+                                         int(sliding_window), int(split_tokens)))
+
+
 def default_split_tokens(num_seqs: int, num_kv_heads: int, head_dim: int, cache_dtype,
-                         max_context_len: int) -> int:
+                         max_context_len: int, num_query_tokens: int = 1,
+                         sliding_window: int = 0) -> int:
     """Split size the library picks for split_tokens=None (cache_dtype: a torch
     dtype or a PA_* code)."""
     code = _DTYPE_CODES.get(cache_dtype, cache_dtype)
     if not isinstance(code, int):
         raise PagedAttnError(f"unsupported cache dtype {cache_dtype}")
     return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, code,
-                                                   max_context_len))
+                                                   max_context_len, num_query_tokens,
+                                                   sliding_window))
 
 
 def sched_bytes(num_seqs: int, max_splits: int) -> int:
     return int(_lib.load().pa_sched_bytes(num_seqs, max_splits))
 
 
-def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_splits: int) -> int:
-    return int(_lib.load().pa_workspace_bytes(num_seqs, num_q_heads, head_dim, max_splits))
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_splits: int,
+                    num_query_tokens: int = 1) -> int:
+    return int(_lib.load().pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim,
+                                              max_splits))
 
 
 def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None) -> None:
@@ -110,54 +127,57 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
 @dataclasses.dataclass
 class Plan:
     """Split list of one decode step (see paged_attn_plan); it depends only on
-    the lengths and bounds, so every layer of the step can reuse it."""
+    the lengths, bounds, query-token count and window, so every layer of the
+    step with the same window can reuse it."""
     sched: torch.Tensor         # int32 scratch, pa_sched_bytes(num_seqs, max_splits)
     context_lens: torch.Tensor  # [B] int32 the plan was made from
     max_blocks_per_seq: int
     max_context_len: int
     split_tokens: int
     max_splits: int
+    num_query_tokens: int = 1
+    sliding_window: int = 0
 
 
 @dataclasses.dataclass
 class Partials:
     """Split-K partials of one decode call (see paged_attn_decode_partial)."""
-    m: torch.Tensor             # [B][Hq][max_splits] fp32, natural-log units
-    l: torch.Tensor             # [B][Hq][max_splits] fp32
-    acc: torch.Tensor           # [B][Hq][max_splits][D] fp32, not divided by l
+    m: torch.Tensor             # [B][Q][Hq][max_splits] fp32, natural-log units
+    l: torch.Tensor             # [B][Q][Hq][max_splits] fp32
+    acc: torch.Tensor           # [B][Q][Hq][max_splits][D] fp32, not divided by l
     context_lens: torch.Tensor  # [B] int32
     split_tokens: int
+    sliding_window: int = 0
 
     @property
     def max_splits(self) -> int:
         return self.m.shape[-1]
 
+    @property
+    def num_query_tokens(self) -> int:
+        return self.m.shape[1]
 
-def _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
-    B, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_cache.shape
-    if bs != BLOCK_SIZE or Dk != D or v_cache.shape != k_cache.shape:
-        raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
-        raise PagedAttnError("block_tables must be [B][max_blocks], context_lens [B]")
-    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
-        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
-    return (_dev(q, "q"), _code(q), B, Hq, D, _dev(k_cache, "k_cache"),
-            _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
-            _dev(v_scale, "v_scale", torch.float32), _code(k_cache), NB, Hkv,
-            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
-            _dev(context_lens, "context_lens", torch.int32))
+
+def _q_shape(q):
+    """(B, Q, Hq, D) of a [B][Hq][D] or [B][Q][Hq][D] query tensor."""
+    if q.dim() == 3:
+        return q.shape[0], 1, q.shape[1], q.shape[2]
+    if q.dim() == 4:
+        B, Q, Hq, D = q.shape
+        if not 1 <= Q <= MAX_QUERY_TOKENS:
+            raise PagedAttnError(f"1..{MAX_QUERY_TOKENS} query tokens per sequence, got {Q}")
+        return B, Q, Hq, D
+    raise PagedAttnError("q must be [B][Hq][D] or [B][Q][Hq][D]")
 
 
 def _max_len(context_lens, max_context_len):
-    # Passing max_context_len avoids a device->host sync (and keeps the call
-    # capturable in a graph).
     if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+        return int(context_lens.max().item()) if context_lens.numel() else 0
     return int(max_context_len)
 
 
-def _plan_sizes(context_lens, max_context_len, split_tokens, sched, cache=None):
+def _plan_sizes(context_lens, max_blocks_per_seq, max_context_len, split_tokens, sched, Q, W,
+                cache=None):
     """cache = (num_kv_heads, head_dim, cache dtype) picks the default split
     size when split_tokens is None; without it split_tokens is required."""
     B = context_lens.shape[0]
@@ -165,10 +185,10 @@ def _plan_sizes(context_lens, max_context_len, split_tokens, sched, cache=None):
     if split_tokens:
         T = int(split_tokens)
     elif cache is not None:
-        T = default_split_tokens(B, cache[0], cache[1], cache[2], mcl)
+        T = default_split_tokens(B, cache[0], cache[1], cache[2], mcl, Q, W)
     else:
         raise PagedAttnError("paged_attn_plan needs split_tokens (see default_split_tokens)")
-    S = max(1, num_splits(mcl, T))
+    S = max(1, max_splits(min(mcl, int(max_blocks_per_seq) * BLOCK_SIZE), T, Q, W))
     need = sched_bytes(B, S)
     if sched is None or sched.numel() * sched.element_size() < need:
         sched = torch.empty(max(need, 16) // 4, dtype=torch.int32, device=context_lens.device)
@@ -176,21 +196,24 @@ def _plan_sizes(context_lens, max_context_len, split_tokens, sched, cache=None):
 
 
 def paged_attn_plan(context_lens, max_blocks_per_seq: int, *, max_context_len=None,
-                    split_tokens=None, sched: Optional[torch.Tensor] = None,
-                    _cache=None) -> Plan:
+                    split_tokens=None, num_query_tokens: int = 1, sliding_window: int = 0,
+                    sched: Optional[torch.Tensor] = None, _cache=None) -> Plan:
     """Plan kernel: list every split of the batch (on the device, from
     context_lens) for the split kernel. split_tokens is required."""
-    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched, _cache)
+    Q, W = int(num_query_tokens), int(sliding_window)
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_blocks_per_seq, max_context_len,
+                                      split_tokens, sched, Q, W, _cache)
     _check(_lib.load().paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B,
-                                       max_blocks_per_seq, mcl, T,
+                                       max_blocks_per_seq, mcl, Q, W, T,
                                        _dev(sched, "sched", torch.int32),
                                        _stream(context_lens.device)))
-    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S)
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W)
 
 
 def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
                          max_blocks_per_seq: int, k_scale=None, v_scale=None, *,
-                         max_context_len=None, split_tokens=None,
+                         max_context_len=None, split_tokens=None, num_query_tokens: int = 1,
+                         sliding_window: int = 0,
                          sched: Optional[torch.Tensor] = None) -> Plan:
     """paged_kv_write + paged_attn_plan in one launch; returns the plan."""
     T_tok, Hkv, D = k.shape
@@ -201,48 +224,71 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
         raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
     if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
         raise PagedAttnError("an int8 cache needs k_scale and v_scale")
-    B, mcl, T, S, sched = _plan_sizes(context_lens, max_context_len, split_tokens, sched,
-                                      (Hkv, D, k_cache.dtype))
+    Q, W = int(num_query_tokens), int(sliding_window)
+    B, mcl, T, S, sched = _plan_sizes(context_lens, max_blocks_per_seq, max_context_len,
+                                      split_tokens, sched, Q, W, (Hkv, D, k_cache.dtype))
     _check(_lib.load().paged_decode_prepare(
         _dev(k, "k"), _dev(v, "v", k.dtype), _code(k),
         _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), NB, _code(k_cache),
-        _dev(context_lens, "context_lens", torch.int32), B, max_blocks_per_seq, mcl, T,
+        _dev(context_lens, "context_lens", torch.int32), B, max_blocks_per_seq, mcl, Q, W, T,
         _dev(sched, "sched", torch.int32), _stream(k.device)))
-    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S)
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W)
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
+    B, Q, Hq, D = _q_shape(q)
+    NB, Hkv, bs, Dk = k_cache.shape
+    if bs != BLOCK_SIZE or Dk != D or v_cache.shape != k_cache.shape:
+        raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise PagedAttnError("block_tables must be [B][max_blocks], context_lens [B]")
+    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    return (_dev(q, "q"), _code(q), B, Q, Hq, D, _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
+            _dev(v_scale, "v_scale", torch.float32), _code(k_cache), NB, Hkv,
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32))
 
 
 def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, scale,
                               k_scale=None, v_scale=None, *, max_context_len=None,
-                              split_tokens=None, plan: Optional[Plan] = None,
+                              split_tokens=None, sliding_window: int = 0,
+                              plan: Optional[Plan] = None,
                               partials: Optional[Partials] = None) -> Partials:
     """Split kernel: returns the per-split (m, l, acc). Without `plan`, the
     plan kernel runs first."""
     lib = _lib.load()
-    B, Hq, D = q.shape
+    B, Q, Hq, D = _q_shape(q)
     Hkv = k_cache.shape[1]
+    W = int(sliding_window)
+    mb = block_tables.shape[1]
     if plan is None:
-        plan = paged_attn_plan(context_lens, block_tables.shape[1],
-                               max_context_len=max_context_len, split_tokens=split_tokens,
+        plan = paged_attn_plan(context_lens, mb, max_context_len=max_context_len,
+                               split_tokens=split_tokens, num_query_tokens=Q, sliding_window=W,
                                _cache=(Hkv, D, k_cache.dtype))
-    elif (plan.max_blocks_per_seq != block_tables.shape[1] or
-          plan.context_lens is not context_lens or
+    elif (plan.max_blocks_per_seq != mb or plan.context_lens is not context_lens or
           (split_tokens and int(split_tokens) != plan.split_tokens) or
-          (max_context_len is not None and int(max_context_len) != plan.max_context_len)):
+          (max_context_len is not None and int(max_context_len) != plan.max_context_len) or
+          plan.num_query_tokens != Q or plan.sliding_window != W):
         raise PagedAttnError("plan was made for other arguments")
     T, S = plan.split_tokens, plan.max_splits
     if partials is None:
-        partials = Partials(m=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
-                            l=torch.empty((B, Hq, S), dtype=torch.float32, device=q.device),
-                            acc=torch.empty((B, Hq, S, D), dtype=torch.float32,
+        partials = Partials(m=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=q.device),
+                            l=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=q.device),
+                            acc=torch.empty((B, Q, Hq, S, D), dtype=torch.float32,
                                             device=q.device),
-                            context_lens=context_lens, split_tokens=T)
+                            context_lens=context_lens, split_tokens=T, sliding_window=W)
     else:
+        if partials.m.shape[:3] != (B, Q, Hq):
+            raise PagedAttnError("partials must be [B][Q][Hq][max_splits](...)")
         partials.context_lens, partials.split_tokens = context_lens, T
+        partials.sliding_window = W
     args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
     _check(lib.paged_attn_decode_partial(
-        *args, plan.max_context_len, float(scale), T, partials.max_splits,
+        *args, plan.max_context_len, W, float(scale), T, partials.max_splits,
         _dev(partials.m, "m", torch.float32), _dev(partials.l, "l", torch.float32),
         _dev(partials.acc, "acc", torch.float32), _dev(plan.sched, "sched", torch.int32),
         _stream(q.device)))
@@ -250,38 +296,43 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
 
 
 def paged_attn_reduce(partials: Partials, out: torch.Tensor) -> torch.Tensor:
-    """Reduce kernel: merge the partials into out [B][Hq][D] (fp32 or bf16)."""
+    """Reduce kernel: merge the partials into out ([B][Hq][D] or [B][Q][Hq][D],
+    fp32 or bf16)."""
     lib = _lib.load()
-    B, Hq, S = partials.m.shape
+    B, Q, Hq, S = partials.m.shape
     D = partials.acc.shape[-1]
-    if out.shape != (B, Hq, D):
-        raise PagedAttnError("out must be [B][Hq][D]")
+    if out.shape not in ((B, Q, Hq, D),) + (((B, Hq, D),) if Q == 1 else ()):
+        raise PagedAttnError("out must be [B][Hq][D] or [B][Q][Hq][D]")
     _check(lib.paged_attn_reduce(
         _dev(partials.m, "m", torch.float32), _dev(partials.l, "l", torch.float32),
         _dev(partials.acc, "acc", torch.float32),
-        _dev(partials.context_lens, "context_lens", torch.int32), B, Hq, D,
-        partials.split_tokens, S, _dev(out, "out"), _code(out), _stream(out.device)))
+        _dev(partials.context_lens, "context_lens", torch.int32), B, Q, Hq, D,
+        partials.sliding_window, partials.split_tokens, S, _dev(out, "out"), _code(out),
+        _stream(out.device)))
     return out
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
                       k_scale=None, v_scale=None, *, max_context_len=None, split_tokens=None,
+                      sliding_window: int = 0,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Whole decode step: split kernel then reduce kernel, out in q's dtype."""
+    """Whole decode step: split kernel then reduce kernel, out in q's dtype and shape."""
     lib = _lib.load()
-    B, Hq, D = q.shape
+    B, Q, Hq, D = _q_shape(q)
+    W = int(sliding_window)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise PagedAttnError("out must match q's shape and dtype")
     mcl = _max_len(context_lens, max_context_len)
+    mb = block_tables.shape[1]
     T = (int(split_tokens) if split_tokens else
-         default_split_tokens(B, k_cache.shape[1], D, k_cache.dtype, mcl))
-    need = workspace_bytes(B, Hq, D, max(1, num_splits(mcl, T)))
+         default_split_tokens(B, k_cache.shape[1], D, k_cache.dtype, mcl, Q, W))
+    need = workspace_bytes(B, Hq, D, max(1, max_splits(min(mcl, mb * BLOCK_SIZE), T, Q, W)), Q)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale)
-    _check(lib.paged_attn_decode(*args, mcl, float(scale), T, _dev(out, "out"),
+    _check(lib.paged_attn_decode(*args, mcl, W, float(scale), T, _dev(out, "out"),
                                  _dev(workspace, "workspace"), workspace.numel(),
                                  _stream(q.device)))
     return out
@@ -297,7 +348,8 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
 
 
 __all__ = [
-    "BLOCK_SIZE", "PagedAttnError", "Plan", "Partials", "num_splits", "default_split_tokens",
-    "sched_bytes", "workspace_bytes", "paged_kv_write", "paged_attn_plan", "paged_decode_prepare", "paged_attn_decode_partial", "paged_attn_reduce",
+    "BLOCK_SIZE", "MAX_QUERY_TOKENS", "PagedAttnError", "Plan", "Partials", "num_splits",
+    "max_splits", "default_split_tokens", "sched_bytes", "workspace_bytes", "paged_kv_write",
+    "paged_attn_plan", "paged_decode_prepare", "paged_attn_decode_partial", "paged_attn_reduce",
     "paged_attn_decode", "hbm_read_probe",
 ]

@@ -20,23 +20,25 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "pa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_num_splits": (_I32, [_I32, _I32]),
-    "pa_default_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_max_splits": (_I32, [_I32, _I32, _I32, _I32]),
+    "pa_default_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_sched_bytes": (_SZ, [_I32, _I32]),
-    "pa_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "pa_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_kv_write": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _I64,
                                       _I32, _P]),
-    "paged_attn_decode_partial": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P,
-                                                 _I32, _I64, _I32, _P, _I32, _P, _I32, _F32,
-                                                 _I32, _I32, _P, _P, _P, _P, _P]),
-    "paged_attn_plan": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+    "paged_attn_decode_partial": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                                 _P, _I32, _I64, _I32, _P, _I32, _P, _I32, _I32,
+                                                 _F32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "paged_attn_plan": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "paged_decode_prepare": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P,
-                                            _I64, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
-    "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P,
-                                         _I32, _P]),
+                                            _I64, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _P, _P]),
+    "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                         _I32, _P, _I32, _P]),
     "pa_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),
-    "paged_attn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
-                                         _I64, _I32, _P, _I32, _P, _I32, _F32, _I32, _P, _P,
-                                         _SZ, _P]),
+    "paged_attn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
+                                         _I64, _I32, _P, _I32, _P, _I32, _I32, _F32, _I32, _P,
+                                         _P, _SZ, _P]),
 }
 
 _lib = None

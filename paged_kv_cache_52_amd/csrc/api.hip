@@ -22,7 +22,16 @@ int check_split_tokens(int32_t split_tokens) {
   return PA_OK;
 }
 
+bool bad_query_shape(int32_t num_query_tokens, int32_t sliding_window) {
+  return num_query_tokens < 1 || num_query_tokens > PA_MAX_QUERY_TOKENS || sliding_window < 0;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+// The length bound the kernels clamp every context length to.
+int32_t clamped_bound(int32_t max_context_len, int32_t max_blocks_per_seq) {
+  return (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE);
+}
 
 constexpr int32_t kMinDefaultSplit = 64;  // smallest split the default picks
 constexpr int64_t kMinWorkItems = 1024;   // (split, KV head) items the default aims for
@@ -36,8 +45,8 @@ const char *pa_strerror(int status) {
     case PA_OK: return "success";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_DTYPE: return "unsupported dtype or dtype combination";
-    case PA_ERR_SHAPE: return "unsupported sizes (head_dim 64/128, Hq/Hkv in {1,2,4,8,16}, counts >= 0)";
-    case PA_ERR_SPLIT: return "split_tokens must be a positive multiple of 16 up to 4096, and max_splits must cover max_context_len";
+    case PA_ERR_SHAPE: return "unsupported sizes (head_dim 64/128, Hq/Hkv in {1,2,4,8,16}, 1..16 query tokens, window >= 0, counts >= 0)";
+    case PA_ERR_SPLIT: return "split_tokens must be a positive multiple of 16 up to 4096, and max_splits must cover the longest split range";
     case PA_ERR_WORKSPACE: return "workspace smaller than pa_workspace_bytes()";
     case PA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case PA_ERR_LAUNCH: return "kernel launch failed";
@@ -52,8 +61,16 @@ int32_t pa_num_splits(int32_t context_len, int32_t split_tokens) {
   return (int32_t)(n < 1 ? 1 : n);
 }
 
+int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
+                      int32_t split_tokens) {
+  if (split_tokens <= 0 || bad_query_shape(num_query_tokens, sliding_window)) return 0;
+  return pa_num_splits(pa::max_span(std::max(max_context_len, 0), num_query_tokens, sliding_window),
+                       split_tokens);
+}
+
 int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t cache_dtype, int32_t max_context_len) {
+                                int32_t cache_dtype, int32_t max_context_len,
+                                int32_t num_query_tokens, int32_t sliding_window) {
   int elt;
   switch (cache_dtype) {
     case PA_F32: elt = 4; break;
@@ -62,6 +79,7 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t 
     default: return 0;
   }
   if (head_dim != 64 && head_dim != 128) return 0;
+  if (bad_query_shape(num_query_tokens, sliding_window)) return 0;
   // 256 KiB of K and V codes per (split, KV head): 512 tokens of a 16-bit
   // 128-dim cache, 1024 of an INT8 one.
   const int64_t kv_bytes_per_token = 2LL * head_dim * elt;
@@ -69,7 +87,9 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   // Halve while the batch has too few (split, KV head) work items to fill the
   // device (a workgroup per item, 256 compute units).
   const int64_t heads = (int64_t)std::max(num_seqs, 0) * std::max(num_kv_heads, 0);
-  while (t > kMinDefaultSplit && heads * pa_num_splits(max_context_len, t) < kMinWorkItems)
+  while (t > kMinDefaultSplit &&
+         heads * pa_max_splits(max_context_len, num_query_tokens, sliding_window, t) <
+             kMinWorkItems)
     t /= 2;
   return t;
 }
@@ -80,10 +100,11 @@ size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits) {
                   sizeof(int32_t));
 }
 
-size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                          int32_t max_splits) {
-  if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_splits < 0) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_splits;
+size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                          int32_t head_dim, int32_t max_splits) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads < 0 || head_dim < 0 || max_splits < 0)
+    return 0;
+  const size_t rows = (size_t)num_seqs * num_query_tokens * num_q_heads * max_splits;
   return pa_sched_bytes(num_seqs, max_splits) + 2 * align256(rows * sizeof(float)) +
          align256(rows * head_dim * sizeof(float));
 }
@@ -116,16 +137,16 @@ int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *s
 
 // Argument checks of the plan; fills `out` on success.
 int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-               int32_t max_context_len, int32_t split_tokens, int32_t *sched,
-               pa::PlanParams *out) {
+               int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
+               int32_t split_tokens, int32_t *sched, pa::PlanParams *out) {
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
+  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
-  *out = pa::PlanParams{
-      context_lens, sched, num_seqs,
-      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE),
-      split_tokens};
+  *out = pa::PlanParams{context_lens, sched, num_seqs,
+                        clamped_bound(max_context_len, max_blocks_per_seq), split_tokens,
+                        num_query_tokens, sliding_window};
   return PA_OK;
 }
 
@@ -145,11 +166,11 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
 }
 
 int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t split_tokens, int32_t *sched,
-                    hipStream_t stream) {
+                    int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
+                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
   pa::PlanParams pl;
   const int st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
-                            split_tokens, sched, &pl);
+                            num_query_tokens, sliding_window, split_tokens, sched, &pl);
   if (st != PA_OK || num_seqs == 0) return st;
   return launch_status(pa::launch_plan(pl, stream));
 }
@@ -160,7 +181,8 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
                          const int32_t *context_lens, int32_t num_seqs,
                          int32_t max_blocks_per_seq, int32_t max_context_len,
-                         int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+                         int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
+                         int32_t *sched, hipStream_t stream) {
   pa::WriteParams w;
   pa::PlanParams pl;
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
@@ -168,26 +190,28 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
   if (st != PA_OK) return st;
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len);
-  st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, split_tokens,
-                  sched, &pl);
+                                           max_context_len, num_query_tokens, sliding_window);
+  st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, num_query_tokens,
+                  sliding_window, split_tokens, sched, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
   return launch_status(pa::launch_prepare(w, pl, stream));
 }
 
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
-                              int32_t num_q_heads, int32_t head_dim, const void *k_cache,
-                              const void *v_cache, const float *k_scale, const float *v_scale,
-                              int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
-                              const int32_t *block_tables, int32_t max_blocks_per_seq,
-                              const int32_t *context_lens, int32_t max_context_len, float scale,
+                              int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                              const void *k_cache, const void *v_cache, const float *k_scale,
+                              const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
+                              int32_t num_kv_heads, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t max_context_len, int32_t sliding_window, float scale,
                               int32_t split_tokens, int32_t max_splits, float *part_m,
                               float *part_l, float *part_acc, const int32_t *sched,
                               hipStream_t stream) {
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
+  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
     return PA_ERR_SHAPE;
@@ -198,9 +222,12 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   if (!dt_ok) return PA_ERR_DTYPE;
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len);
+                                           max_context_len, num_query_tokens, sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  const int32_t grid_splits = pa_num_splits(max_context_len, split_tokens);
+  // Splits of the longest range any sequence can have under the clamped bound.
+  const int32_t grid_splits =
+      pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq), num_query_tokens,
+                    sliding_window, split_tokens);
   if (max_splits < grid_splits) return PA_ERR_SPLIT;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !part_m || !part_l ||
@@ -209,7 +236,6 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
 
-  const int group = num_q_heads / num_kv_heads;
   pa::DecodeParams p{};
   p.q = q;
   p.k_cache = k_cache;
@@ -230,61 +256,69 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   p.max_context_len = max_context_len;
   p.split_tokens = split_tokens;
   p.max_splits = max_splits;
+  p.num_query_tokens = num_query_tokens;
+  p.window = sliding_window;
+  p.group = num_q_heads / num_kv_heads;
   p.sched = sched;
-  p.head_groups = group > 8 ? group / 8 : 1;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   hipError_t e;
   if (q_dtype == PA_BF16 && cache_dtype == PA_BF16)
-    e = pa::decode_bf16_bf16(p, group, grid_splits, stream);
+    e = pa::decode_bf16_bf16(p, grid_splits, stream);
   else if (q_dtype == PA_F32 && cache_dtype == PA_F32)
-    e = pa::decode_f32_f32(p, group, grid_splits, stream);
+    e = pa::decode_f32_f32(p, grid_splits, stream);
   else if (q_dtype == PA_BF16)
-    e = pa::decode_bf16_i8(p, group, grid_splits, stream);
+    e = pa::decode_bf16_i8(p, grid_splits, stream);
   else
-    e = pa::decode_f32_i8(p, group, grid_splits, stream);
+    e = pa::decode_f32_i8(p, grid_splits, stream);
   return launch_status(e);
 }
 
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
-                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t head_dim, int32_t split_tokens, int32_t max_splits, void *out,
-                      int32_t out_dtype, hipStream_t stream) {
-  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_query_tokens,
+                      int32_t num_q_heads, int32_t head_dim, int32_t sliding_window,
+                      int32_t split_tokens, int32_t max_splits, void *out, int32_t out_dtype,
+                      hipStream_t stream) {
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (check_split_tokens(split_tokens) != PA_OK || max_splits <= 0) return PA_ERR_SPLIT;
   if (num_seqs == 0) return PA_OK;
   if (!part_m || !part_l || !part_acc || !context_lens || !out) return PA_ERR_NULL;
   pa::ReduceParams p{part_m, part_l, part_acc, context_lens, out, num_seqs, num_q_heads,
-                     head_dim, split_tokens, max_splits, out_dtype};
+                     head_dim, split_tokens, max_splits, out_dtype, num_query_tokens,
+                     sliding_window};
   return launch_status(pa::launch_reduce(p, stream));
 }
 
-int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t head_dim, const void *k_cache, const void *v_cache,
-                      const float *k_scale, const float *v_scale, int32_t cache_dtype,
-                      int64_t num_blocks, int32_t num_kv_heads, const int32_t *block_tables,
-                      int32_t max_blocks_per_seq, const int32_t *context_lens,
-                      int32_t max_context_len, float scale, int32_t split_tokens, void *out,
+int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_query_tokens,
+                      int32_t num_q_heads, int32_t head_dim, const void *k_cache,
+                      const void *v_cache, const float *k_scale, const float *v_scale,
+                      int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t max_context_len,
+                      int32_t sliding_window, float scale, int32_t split_tokens, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
-      num_kv_heads <= 0)
+      num_kv_heads <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
+  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_I8)
     return PA_ERR_DTYPE;
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len);
+                                           max_context_len, num_query_tokens, sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  const int32_t ns = pa_num_splits(max_context_len, split_tokens);
-  const size_t need = pa_workspace_bytes(num_seqs, num_q_heads, head_dim, ns);
+  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
+                                   num_query_tokens, sliding_window, split_tokens);
+  const size_t need = pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim, ns);
   if (num_seqs == 0) return PA_OK;
   if (!workspace || !out) return PA_ERR_NULL;
   if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t rows = (size_t)num_seqs * num_q_heads * ns;
+  const size_t rows = (size_t)num_seqs * num_query_tokens * num_q_heads * ns;
   char *base = (char *)workspace;
   int32_t *sched = (int32_t *)base;
   base += pa_sched_bytes(num_seqs, ns);
@@ -292,16 +326,16 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   float *l = (float *)(base + align256(rows * sizeof(float)));
   float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
   int st = paged_attn_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
-                           split_tokens, sched, stream);
+                           num_query_tokens, sliding_window, split_tokens, sched, stream);
   if (st != PA_OK) return st;
-  st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_q_heads, head_dim, k_cache,
-                                     v_cache, k_scale, v_scale, cache_dtype, num_blocks,
-                                     num_kv_heads, block_tables, max_blocks_per_seq,
-                                     context_lens, max_context_len, scale, split_tokens, ns, m,
-                                     l, acc, sched, stream);
+  st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_query_tokens, num_q_heads, head_dim,
+                                 k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks,
+                                 num_kv_heads, block_tables, max_blocks_per_seq, context_lens,
+                                 max_context_len, sliding_window, scale, split_tokens, ns, m, l,
+                                 acc, sched, stream);
   if (st != PA_OK) return st;
-  return paged_attn_reduce(m, l, acc, context_lens, num_seqs, num_q_heads, head_dim,
-                           split_tokens, ns, out, q_dtype, stream);
+  return paged_attn_reduce(m, l, acc, context_lens, num_seqs, num_query_tokens, num_q_heads,
+                           head_dim, sliding_window, split_tokens, ns, out, q_dtype, stream);
 }
 
 int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,

@@ -43,8 +43,49 @@ struct DecodeParams {
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, max_context_len;
   int32_t split_tokens, max_splits;
-  int32_t head_groups;  // query-head groups per KV head handled by separate workgroups
+  int32_t num_query_tokens;  // Q query tokens per sequence (its last Q positions)
+  int32_t window;            // sliding window in tokens, 0 = none
+  int32_t group;             // g = num_q_heads / num_kv_heads
+  int32_t head_groups;  // row groups per KV head (Q*g rows) handled by separate workgroups
   float scale_log2;     // scale * log2(e)
+};
+
+// Row R (0 <= R < Q*g) of KV head kvh is query token R / g, query head
+// kvh*g + R % g; its q, out and partials row in [num_seqs][Q][Hq].
+__device__ __forceinline__ int64_t query_row(const DecodeParams &p, int s, int kvh, int R) {
+  const int g = p.group;
+  return ((int64_t)s * p.num_query_tokens + R / g) * p.num_q_heads + kvh * g + R % g;
+}
+
+// Token ranges of the rows a workgroup handles. Query token i of the sequence
+// attends [lo(i), hi(i)] (empty when its position is negative); the group's
+// rows together attend [ulo, uhi], and a 16-token tile inside
+// [lo_max, hi_min] is attended in full by every row (no mask needed).
+struct RowRanges {
+  int q0;      // position of query token 0: L - Q
+  int window;  // W, 0 = none
+  int ulo, uhi, lo_max, hi_min;
+
+  __device__ __forceinline__ int lo(int i) const {
+    const int pos = q0 + i;
+    return window > 0 ? max(0, pos - window + 1) : 0;
+  }
+  __device__ __forceinline__ int hi(int i) const { return q0 + i; }
+  __device__ __forceinline__ bool needs_mask(int tb) const {
+    return tb < lo_max || tb + kBlock - 1 > hi_min;
+  }
+  // Rows [R0, R0 + nrows) with g query heads per KV head.
+  __device__ __forceinline__ static RowRanges make(int L, int Q, int W, int g, int R0, int nrows) {
+    RowRanges r;
+    r.q0 = L - Q;
+    r.window = W;
+    const int i0 = R0 / g, i1 = (R0 + nrows - 1) / g;
+    r.ulo = r.lo(i0);
+    r.uhi = r.hi(i1);
+    r.lo_max = r.lo(i1);
+    r.hi_min = r.hi(i0);
+    return r;
+  }
 };
 
 // Tiles a wave keeps in flight beyond the one it is consuming (0 or 1).
@@ -60,10 +101,11 @@ constexpr int kPrefetch = PA_PREFETCH;
 
 // Layout of the scheduling scratch written by the plan kernel:
 //   [0] number of splits of the batch
-//   [1] split_tokens, [2] num_seqs, [3] clamped max length the plan was made for
+//   [1] split_tokens, [2] num_seqs, [3] clamped max length, [4] query tokens,
+//   [5] window the plan was made for, [6..7] unused
 //   then two words per split, full splits first: (sequence << 16 | split) and
 //   the sequence's clamped context length.
-constexpr int kSchedHeader = 4;
+constexpr int kSchedHeader = 8;
 
 template <int QT, int CT, int D, int G>
 struct DecodeShape {
@@ -145,10 +187,12 @@ struct DecodeWave {
     }
   }
 
-  // Fold one tile into the running state. `valid_rows` is the number of
-  // leading token rows of the tile inside the split (16 except at the end).
-  __device__ __forceinline__ void consume(const Tile<S> &t, int valid_rows, int lane,
-                                         float scale_log2) {
+  // Fold one tile (first token tb) into the running state. With need_mask,
+  // row h keeps only the tokens in [lo[h], hi[h]] and the V rows of tokens
+  // outside the group's [ulo, uhi] are dropped by select.
+  __device__ __forceinline__ void consume(const Tile<S> &t, bool need_mask, int tb,
+                                         const int (&lo)[G], const int (&hi)[G], int ulo,
+                                         int uhi, int lane, float scale_log2) {
     const int r0 = lane / S::LPR;
     float z[S::NI][G];
     // q . k over this lane's E dims, for each owned token row and query head.
@@ -205,15 +249,18 @@ struct DecodeWave {
 #pragma unroll
         for (int h = 0; h < G; ++h) z[i][h] *= t.ks[i];
     }
-    const bool tail = valid_rows < kBlock;  // uniform
-    bool valid[S::NI];
+    bool valid[S::NI];  // token inside the group's union
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) valid[i] = !tail || (r0 + i * S::RPI) < valid_rows;
-    if (tail) {
+    for (int i = 0; i < S::NI; ++i) valid[i] = true;
+    if (need_mask) {  // uniform
 #pragma unroll
-      for (int i = 0; i < S::NI; ++i)
+      for (int i = 0; i < S::NI; ++i) {
+        const int tok = tb + r0 + i * S::RPI;
+        valid[i] = tok >= ulo && tok <= uhi;
 #pragma unroll
-        for (int h = 0; h < G; ++h) z[i][h] = valid[i] ? z[i][h] : -INFINITY;
+        for (int h = 0; h < G; ++h)
+          z[i][h] = (tok >= lo[h] && tok <= hi[h]) ? z[i][h] : -INFINITY;
+      }
     }
 
     // Online softmax update of this row group.
@@ -269,7 +316,7 @@ struct DecodeWave {
         const float vs = valid[i] ? t.vs[i] : 0.f;  // a poisoned scale must not leak
 #pragma unroll
         for (int h = 0; h < G; ++h) w[h] *= vs;
-      } else if (tail && !valid[i]) {
+      } else if (need_mask && !valid[i]) {
 #pragma unroll
         for (int e = 0; e < S::E; ++e) vf[e] = 0.f;  // NaN * 0 would leak: select, not scale
       }
@@ -406,8 +453,11 @@ struct MfmaWave {
     }
   }
 
-  __device__ __forceinline__ void consume(MfmaTile<CT> &t, int valid_rows, int g,
-                                          float scale_log2) {
+  // Fold one tile (first token tb) into the running state. With need_mask,
+  // this lane's row keeps only tokens in [lo, hi], and V rows of tokens
+  // outside the group's [ulo, uhi] are dropped by select.
+  __device__ __forceinline__ void consume(MfmaTile<CT> &t, bool need_mask, int tb, int lo,
+                                          int hi, int ulo, int uhi, int g, float scale_log2) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (CT == PA_BF16) {
 #pragma unroll
@@ -436,16 +486,17 @@ struct MfmaWave {
       else
         z[r] = (sc[r] - qbias) * t.ks[r] * scale_log2;
     }
-    if (valid_rows < kBlock) {  // uniform: the last tile of the split
+    if (need_mask) {  // uniform: a tile at an edge of some row's range
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = 4 * g + r < valid_rows;
-        z[r] = ok ? z[r] : -INFINITY;
-        // NaN * 0 would leak: rows past the end are removed by select.
+        const int tok = tb + 4 * g + r;
+        z[r] = (tok >= lo && tok <= hi) ? z[r] : -INFINITY;
+        // NaN * 0 would leak: tokens no row attends are removed by select.
+        const bool used = tok >= ulo && tok <= uhi;
         if constexpr (CT == PA_BF16) {
-          if (!ok) t.v[r] = u32x4{0u, 0u, 0u, 0u};
+          if (!used) t.v[r] = u32x4{0u, 0u, 0u, 0u};
         } else {
-          if (!ok) t.vs[r] = 0.f;
+          if (!used) t.vs[r] = 0.f;
         }
       }
     }
@@ -511,25 +562,31 @@ struct MfmaWave {
   }
 };
 
-// Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split; leaves
-// the wave's (m, l, acc) for heads < G in LDS row `wave`.
+// Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split (tile n
+// starts at token (b0 + n) * 16); leaves the wave's (m, l, acc) for the rows
+// R0 .. R0 + nrows - 1 in LDS row `wave`.
 template <int QT, int CT, int D, int G, int NW>
-__device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int hq0,
-                                               int b0, int t1, int wb0, int wb1, int lane,
-                                               int wave, float (&sm_m)[NW][G],
-                                               float (&sm_l)[NW][G],
+__device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int R0,
+                                               int nrows, const RowRanges &rr, int b0, int wb0,
+                                               int wb1, int lane, int wave,
+                                               float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D]) {
   using Wv = MfmaWave<CT, G>;
   Wv st;
   const int c = lane % 16, g = lane / 16;
+  // This lane's S row: row R0 + c (padding rows beyond nrows keep zero q and
+  // the group's token range).
+  const bool row_ok = c < G && c < nrows;
+  const int qi = (R0 + c) / p.group;
+  const int lo = row_ok ? rr.lo(qi) : rr.ulo, hi = row_ok ? rr.hi(qi) : rr.uhi;
+  const int64_t qrow = row_ok ? query_row(p, s, kvh, R0 + c) : 0;
   float qs = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     st.qB[i] = u32x4{0u, 0u, 0u, 0u};
-    if (c < G) {
+    if (row_ok) {
       const int dim0 = CT == PA_BF16 ? 32 * i + 8 * g : 32 * g + 8 * i;
-      st.qB[i] = *(const u32x4 *)((const uint16_t *)p.q +
-                                  ((int64_t)s * p.num_q_heads + hq0 + c) * D + dim0);
+      st.qB[i] = *(const u32x4 *)((const uint16_t *)p.q + qrow * D + dim0);
     }
     if constexpr (CT == PA_I8) {
 #pragma unroll
@@ -559,7 +616,10 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   auto block_of = [&](int n) {
     return min(max(__builtin_amdgcn_readlane(my_id, min(n - wb0, kWave - 1)), 0), last_block);
   };
-  auto rows_of = [&](int n) { return min(kBlock, t1 - (b0 + n) * kBlock); };
+  auto eat = [&](MfmaTile<CT> &t, int n) {
+    const int tb = (b0 + n) * kBlock;
+    st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
+  };
 #if PA_MFMA_PREFETCH
   // Two tiles in flight: tile n + 1 is requested before tile n is consumed.
   // The look-ahead load is unconditional (a dead one reads nothing), so the
@@ -569,17 +629,17 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   for (int n = wb0; n < wb1; n += 2) {
     st.load_tile(tb, p, block_of(n + 1), kvh, koff, voff, soff, n + 1 < wb1);
     __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead ahead of the wait
-    st.consume(ta, rows_of(n), g, p.scale_log2);
+    eat(ta, n);
     if (n + 1 >= wb1) break;
     st.load_tile(ta, p, block_of(n + 2), kvh, koff, voff, soff, n + 2 < wb1);
     __builtin_amdgcn_sched_barrier(0);
-    st.consume(tb, rows_of(n + 1), g, p.scale_log2);
+    eat(tb, n + 1);
   }
 #else
   MfmaTile<CT> t;
   for (int n = wb0; n < wb1; ++n) {
     st.load_tile(t, p, block_of(n), kvh, koff, voff, soff);
-    st.consume(t, rows_of(n), g, p.scale_log2);
+    eat(t, n);
   }
 #endif
   // Renormalise to the true max (every lane takes part: rescale reads other
@@ -614,21 +674,32 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
 
 // Per-wave pass of the VALU engine (every dtype and head_dim); same contract.
 template <int QT, int CT, int D, int G, int NW>
-__device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int kvh, int hq0,
-                                               int b0, int t1, int wb0, int wb1, int lane,
-                                               int wave, float (&sm_m)[NW][G],
-                                               float (&sm_l)[NW][G],
+__device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int kvh, int R0,
+                                               int nrows, const RowRanges &rr, int b0, int wb0,
+                                               int wb1, int lane, int wave,
+                                               float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D]) {
   using S = DecodeShape<QT, CT, D, G>;
   using W = DecodeWave<QT, CT, D, G, NW>;
   W st;
-  // q slice for this lane's dims.
+  // Token range of each row (padding rows past nrows take the group's).
+  int lo[G], hi[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int qi = (R0 + h) / p.group;
+    lo[h] = h < nrows ? rr.lo(qi) : rr.ulo;
+    hi[h] = h < nrows ? rr.hi(qi) : rr.uhi;
+  }
+  // q slice for this lane's dims (zero for padding rows).
   {
     const int c = lane % S::LPR;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t row = ((int64_t)s * p.num_q_heads + hq0 + h) * D;
-      if constexpr (S::DOT2) {
+      const int64_t row = (h < nrows ? query_row(p, s, kvh, R0 + h) : 0) * D;
+      if (h >= nrows) {
+#pragma unroll
+        for (int k = 0; k < S::QW; ++k) st.qr[h][k] = 0.f;
+      } else if constexpr (S::DOT2) {
         const u32x4 w = *(const u32x4 *)((const uint16_t *)p.q + row + c * S::E);
 #pragma unroll
         for (int k = 0; k < S::E / 2; ++k) st.qr[h][k] = __uint_as_float(w[k]);
@@ -665,7 +736,10 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
     int b = __builtin_amdgcn_readlane(my_id, n - wb0);
     return min(max(b, 0), last_block);
   };
-  auto rows_in = [&](int n) { return min(kBlock, t1 - (b0 + n) * kBlock); };
+  auto eat = [&](const Tile<S> &t, int n) {
+    const int tb = (b0 + n) * kBlock;
+    st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, lane, p.scale_log2);
+  };
 
   const int lane_off = (lane / S::LPR) * S::ROW_BYTES + (lane % S::LPR) * 16;
   const int scale_off = (lane / S::LPR) * 4;
@@ -677,23 +751,23 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   if constexpr (kPrefetch == 0) {
     for (int n = wb0; n < wb1; ++n) {
       st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
-      st.consume(ta, rows_in(n), lane, p.scale_log2);
+      eat(ta, n);
     }
   } else if (wb0 < wb1) {
     int n = wb0;
     st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
     for (; n + 2 < wb1; n += 2) {
       st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
-      st.consume(ta, rows_in(n), lane, p.scale_log2);
+      eat(ta, n);
       st.load_tile(ta, p, block_id(n + 2), kvh, lane_off, scale_off);
-      st.consume(tb, rows_in(n + 1), lane, p.scale_log2);
+      eat(tb, n + 1);
     }
     if (n + 1 < wb1) {
       st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
-      st.consume(ta, rows_in(n), lane, p.scale_log2);
-      st.consume(tb, rows_in(n + 1), lane, p.scale_log2);
+      eat(ta, n);
+      eat(tb, n + 1);
     } else {
-      st.consume(ta, rows_in(n), lane, p.scale_log2);
+      eat(ta, n);
     }
   }
 
@@ -722,9 +796,10 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   }
 }
 
-// One work item: split j of sequence s for KV head kvh (query-head group hg).
-// The NW waves of the workgroup share the split's tiles, merge their states in
-// LDS and write the split's partials. Contains one workgroup barrier.
+// One work item: split j of sequence s for KV head kvh, row group hg (rows
+// hg*G .. of the Q*g rows of the KV head). The NW waves of the workgroup share
+// the split's tiles, merge their states in LDS and write the split's partials.
+// Contains one workgroup barrier.
 template <int QT, int CT, int D, int G, int NW>
 __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
                                               int kvh, int hg, int lane, int wave,
@@ -733,27 +808,30 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
   const int L = max(0, min(len, lmax));
-  const int nsplit = max(1, (L + p.split_tokens - 1) / p.split_tokens);
-  if (j >= nsplit) return;  // never for planned items; uniform across the workgroup
-  const int t0 = j * p.split_tokens;
+  const int Q = p.num_query_tokens, W = p.window;
+  const int base = split_base(L, Q, W);
+  if (j >= splits_of(L, Q, W, p.split_tokens)) return;  // never for planned items; uniform
+  const int t0 = base + j * p.split_tokens;  // a multiple of 16
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
   const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;
   const int per = (nb + NW - 1) / NW;
   const int wb0 = min(nb, wave * per);
   const int wb1 = min(nb, wb0 + per);
-  const int hq0 = kvh * (p.num_q_heads / p.num_kv_heads) + hg * G;
+  const int R0 = hg * G;
+  const int nrows = min(G, Q * p.group - R0);
+  const RowRanges rr = RowRanges::make(L, Q, W, p.group, R0, nrows);
 
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value)
-    wave_pass_mfma<QT, CT, D, G, NW>(p, s, kvh, hq0, b0, t1, wb0, wb1, lane, wave, sm_m, sm_l,
-                                     sm_acc);
+    wave_pass_mfma<QT, CT, D, G, NW>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave, sm_m,
+                                     sm_l, sm_acc);
   else
-    wave_pass_valu<QT, CT, D, G, NW>(p, s, kvh, hq0, b0, t1, wb0, wb1, lane, wave, sm_m, sm_l,
-                                     sm_acc);
+    wave_pass_valu<QT, CT, D, G, NW>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave, sm_m,
+                                     sm_l, sm_acc);
   __syncthreads();
 
   // Merge the waves and write the split's partials.
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+  for (int idx = threadIdx.x; idx < nrows * D; idx += NW * kWave) {
     const int h = idx / D, d = idx % D;
     float M = sm_m[0][h];
 #pragma unroll
@@ -765,7 +843,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
       a = fmaf(f, sm_acc[w][h][d], a);
       lsum = fmaf(f, sm_l[w][h], lsum);
     }
-    const int64_t row = ((int64_t)s * p.num_q_heads + hq0 + h) * p.max_splits + j;
+    const int64_t row = query_row(p, s, kvh, R0 + h) * p.max_splits + j;
     p.part_acc[row * D + d] = a;
     if (d == 0) {
       p.part_l[row] = lsum;
@@ -776,12 +854,12 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 
 // Split kernel. Work item k is split sched[kSchedHeader + 2*(k / heff)]
 // (packed sequence << 16 | split, followed by the sequence's context length)
-// for KV-head group k % heff (heff = KV heads x query-head groups), from the
+// for (KV head, row group) k % heff (heff = KV heads x row groups), from the
 // list the plan kernel wrote (full splits first, the shortest last splits at
 // the end). Workgroup k processes item k; the grid is an upper bound on the
 // number of items and the workgroups past the end of the list, all at the end
 // of the grid, exit at once. A plan made for another split size, batch or
-// length bound counts as an empty list.
+// length bound, query-token count or window counts as an empty list.
 // Minimum waves per SIMD the compiler must fit the split kernel's registers
 // to (0: its own choice).
 #ifndef PA_WAVES_PER_EU
@@ -803,7 +881,8 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
   const int heff = p.num_kv_heads * p.head_groups;
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
   const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
-                       p.sched[3] == lmax;
+                       p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
+                       p.sched[5] == p.window;
   const int n_items = plan_ok ? p.sched[0] * heff : 0;
   const int k = blockIdx.x;
   if (k >= n_items) return;
@@ -839,34 +918,36 @@ hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t str
   return hipGetLastError();
 }
 
-// Dispatch on (head_dim, group size) for one (q dtype, cache dtype) pair. The
-// MFMA engine takes all g <= 16 heads of a KV head in one workgroup; the VALU
-// engine takes at most 8 (g = 16 runs as two query-head groups).
+// Dispatch on (head_dim, rows per KV head) for one (q dtype, cache dtype)
+// pair. A KV head has Q*g query rows (query tokens x the heads of its group).
+// The MFMA engine takes up to 16 rows per workgroup, the VALU engine up to 8;
+// more rows are split into row groups handled by separate workgroups.
+inline int pow2_at_least(int x) {
+  int r = 1;
+  while (r < x) r <<= 1;
+  return r;
+}
+
 template <int QT, int CT>
-hipError_t dispatch_decode(DecodeParams p, int group, int grid_splits, hipStream_t stream) {
-  auto by_group = [&](auto dtag) -> hipError_t {
+hipError_t dispatch_decode(DecodeParams p, int grid_splits, hipStream_t stream) {
+  const int rows = p.num_query_tokens * p.group;
+  auto by_rows = [&](auto dtag) -> hipError_t {
     constexpr int D = decltype(dtag)::value;
-    if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
-      p.head_groups = 1;
-      switch (group) {
-        case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
-        case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
-        case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
-        case 8: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);
-        default: return launch_decode<QT, CT, D, 16>(p, grid_splits, stream);
-      }
-    } else {
-      p.head_groups = group > 8 ? group / 8 : 1;
-      switch (group) {
-        case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
-        case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
-        case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
-        default: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);  // 8, and 16 as 2 x 8
-      }
+    constexpr int kMaxRows = (QT == PA_BF16 && MfmaEligible<CT, D>::value) ? 16 : 8;
+    const int G = min(kMaxRows, pow2_at_least(rows));
+    p.head_groups = (rows + G - 1) / G;
+    switch (G) {
+      case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
+      case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
+      case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
+      case 8: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);
+      default:
+        if constexpr (kMaxRows >= 16) return launch_decode<QT, CT, D, 16>(p, grid_splits, stream);
+        return hipErrorInvalidValue;
     }
   };
-  if (p.head_dim == 64) return by_group(std::integral_constant<int, 64>{});
-  return by_group(std::integral_constant<int, 128>{});
+  if (p.head_dim == 64) return by_rows(std::integral_constant<int, 64>{});
+  return by_rows(std::integral_constant<int, 128>{});
 }
 
 }  // namespace pa

@@ -104,4 +104,34 @@ constexpr int kStreamPolicy = PA_STREAM_POLICY;
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf, 1 for 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Split geometry of one sequence, shared by the host checks, the plan, the
+// split kernel and the reduce. A sequence of length L carries Q query tokens
+// (its last Q positions; query token i sits at L - Q + i and attends the
+// positions up to its own) and, with a sliding window of W > 0 tokens, each
+// query token attends only its W most recent positions [ATOM 4.2 for the Q
+// new tokens of an MTP step; EchoLLMServing notes, section 4, for the
+// window]. The splits cover [split_base, L).
+// ---------------------------------------------------------------------------
+
+// Start of the block holding the earliest token any query token attends.
+__host__ __device__ inline int split_base(int L, int Q, int W) {
+  if (W <= 0) return 0;
+  const int first = L - Q - W + 1;
+  return first > 0 ? first / kBlock * kBlock : 0;
+}
+
+// max(1, ceil((L - split_base) / T)).
+__host__ __device__ inline int splits_of(int L, int Q, int W, int T) {
+  const int n = (L - split_base(L, Q, W) + T - 1) / T;
+  return n > 1 ? n : 1;
+}
+
+// Largest L - split_base(L) over 0 <= L <= lmax: the longest split range.
+__host__ __device__ inline int max_span(int lmax, int Q, int W) {
+  if (W <= 0) return lmax;
+  const int cap = Q + W + kBlock - 2;  // (Q + W - 1) + up to 15 leading tokens of a block
+  return lmax < cap ? lmax : cap;
+}
+
 }  // namespace pa

@@ -15,6 +15,7 @@ struct ReduceParams {
   const int32_t *context_lens;
   void *out;
   int32_t num_seqs, num_q_heads, head_dim, split_tokens, max_splits, out_dtype;
+  int32_t num_query_tokens, window;  // rows per sequence: num_query_tokens * num_q_heads
 };
 
 struct WriteParams {
@@ -36,6 +37,7 @@ struct PlanParams {
   const int32_t *context_lens;
   int32_t *sched;
   int32_t num_seqs, max_len, split_tokens;
+  int32_t num_query_tokens, window;
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
@@ -46,10 +48,10 @@ hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int blocks,
                              hipStream_t stream);
 
-// One per (q dtype, cache dtype) pair; group is Hq / Hkv in {1, 2, 4, 8, 16}.
-hipError_t decode_bf16_bf16(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
-hipError_t decode_f32_f32(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
-hipError_t decode_bf16_i8(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
-hipError_t decode_f32_i8(const DecodeParams &p, int group, int grid_splits, hipStream_t s);
+// One per (q dtype, cache dtype) pair; p.group = Hq / Hkv in {1, 2, 4, 8, 16}.
+hipError_t decode_bf16_bf16(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_f32_f32(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_bf16_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_f32_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
 
 }  // namespace pa

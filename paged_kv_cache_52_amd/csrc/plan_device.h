@@ -3,11 +3,12 @@
 //
 // One workgroup of kPlanThreads threads turns context_lens into the list of
 // splits the split kernel works through [EchoLLMServing notes, section 2:
-// split count derived from the context length, max(1, ceil(L/T))]. It writes
+// split count derived from the context length, max(1, ceil(L/T)); with a
+// sliding window, of the span the window reaches]. It writes
 // into the scheduling scratch:
 //   sched[0]  = number of splits of the batch
-//   sched[1..3] = split_tokens, num_seqs, clamped max length (checked by the
-//                 split kernel)
+//   sched[1..5] = split_tokens, num_seqs, clamped max length, query tokens,
+//                 window (checked by the split kernel); sched[6..7] = 0
 //   sched[4+2i], sched[5+2i] = (s << 16) | j, L_s   split i, in this order:
 //     1. all splits but the last of each sequence (full T-token splits),
 //        sequence by sequence;
@@ -28,12 +29,15 @@ __device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
   return max(0, min(p.context_lens[s], p.max_len));
 }
 
-__device__ __forceinline__ int num_splits_of(int L, int T) { return max(1, (L + T - 1) / T); }
+__device__ __forceinline__ int seq_splits(const PlanParams &p, int L) {
+  return splits_of(L, p.num_query_tokens, p.window, p.split_tokens);
+}
 
-// Tiles of the last split (1 for an empty sequence, which sorts last).
-__device__ __forceinline__ int last_tiles(int L, int T) {
-  if (L <= 0) return 1;
-  const int rest = L - (num_splits_of(L, T) - 1) * T;
+// Tiles of the last split (1 for an empty split range, which sorts last).
+__device__ __forceinline__ int last_tiles(const PlanParams &p, int L) {
+  const int span = L - split_base(L, p.num_query_tokens, p.window);
+  if (span <= 0) return 1;
+  const int rest = span - (seq_splits(p, L) - 1) * p.split_tokens;
   return (rest + kBlock - 1) / kBlock;
 }
 
@@ -61,7 +65,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     const int s = base + tid;
     const bool valid = s < p.num_seqs;
     const int L = valid ? clamp_len(p, s) : 0;
-    const int f = valid ? num_splits_of(L, T) - 1 : 0;
+    const int f = valid ? seq_splits(p, L) - 1 : 0;
     int incl = f;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -69,7 +73,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
       if (lane >= o) incl += y;
     }
     if (lane == kWave - 1) wave_sum[wave] = incl;
-    if (valid) atomicAdd(&bucket[last_tiles(L, T)], 1);
+    if (valid) atomicAdd(&bucket[last_tiles(p, L)], 1);
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
@@ -127,8 +131,8 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     const int s = base + tid;
     if (s < p.num_seqs) {
       const int L = clamp_len(p, s);
-      const int pos = atomicAdd(&bucket[last_tiles(L, T)], 1);
-      p.sched[kSchedHeader + 2 * pos] = (s << 16) | (num_splits_of(L, T) - 1);
+      const int pos = atomicAdd(&bucket[last_tiles(p, L)], 1);
+      p.sched[kSchedHeader + 2 * pos] = (s << 16) | (seq_splits(p, L) - 1);
       p.sched[kSchedHeader + 2 * pos + 1] = L;
     }
   }
@@ -137,6 +141,10 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     p.sched[1] = T;
     p.sched[2] = p.num_seqs;
     p.sched[3] = p.max_len;
+    p.sched[4] = p.num_query_tokens;
+    p.sched[5] = p.window;
+    p.sched[6] = 0;
+    p.sched[7] = 0;
   }
 }
 

@@ -9,8 +9,8 @@ namespace pa {
 constexpr int kReduceWaves = 4;       // waves per workgroup
 constexpr int kReduceManySplits = 32;  // from this many splits, 4 waves share one head
 
-// Every workgroup has kReduceWaves waves. WPH waves work on one (query head,
-// sequence): WPH = 1 gives four heads per workgroup (few splits per head),
+// Every workgroup has kReduceWaves waves. WPH waves work on one row (query
+// token, query head) of a sequence: WPH = 1 gives four heads per workgroup (few splits per head),
 // WPH = 4 one head whose splits the waves divide (long contexts). Each wave
 // finds the maximum M of the split maxima (lane-parallel), then sums a
 // contiguous range of splits: lane j of a 64-split chunk turns split j's
@@ -26,12 +26,13 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int part = wave % WPH;
+  const int rows = p.num_query_tokens * p.num_q_heads;  // (query token, head) rows per sequence
   const int hq = blockIdx.x * HPW + wave / WPH;
   const int s = blockIdx.y;
-  if (WPH == 1 && hq >= p.num_q_heads) return;  // no barrier below in that case
+  if (WPH == 1 && hq >= rows) return;  // no barrier below in that case
   const int L = max(0, p.context_lens[s]);
-  const int ns = min(max(1, (L + p.split_tokens - 1) / p.split_tokens), p.max_splits);
-  const int64_t row0 = ((int64_t)s * p.num_q_heads + hq) * p.max_splits;
+  const int ns = min(splits_of(L, p.num_query_tokens, p.window, p.split_tokens), p.max_splits);
+  const int64_t row0 = ((int64_t)s * rows + hq) * p.max_splits;
 
   float M = -INFINITY;
   for (int j = lane; j < ns; j += kWave) {
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
     }
   };
   if constexpr (WPH == 1) {
-    const int64_t orow = ((int64_t)s * p.num_q_heads + hq) * D;
+    const int64_t orow = ((int64_t)s * rows + hq) * D;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) store(orow + lane + k * kWave, den > 0.f ? acc[k] / den : 0.f);
   } else {
@@ -100,14 +101,14 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
     for (int idx = threadIdx.x; idx < HPW * D; idx += kReduceWaves * kWave) {
       const int h = idx / D, d = idx % D;
       const int hh = blockIdx.x * HPW + h;
-      if (hh >= p.num_q_heads) continue;
+      if (hh >= rows) continue;
       float a = 0.f, dn = 0.f;
 #pragma unroll
       for (int w = 0; w < WPH; ++w) {
         a += sm_acc[h * WPH + w][d];
         dn += sm_den[h * WPH + w];
       }
-      store(((int64_t)s * p.num_q_heads + hh) * D + d, dn > 0.f ? a / dn : 0.f);
+      store(((int64_t)s * rows + hh) * D + d, dn > 0.f ? a / dn : 0.f);
     }
   }
 }
@@ -117,11 +118,12 @@ namespace {
 template <int OT, int D>
 void launch_reduce_t(const ReduceParams &p, hipStream_t stream) {
   const dim3 block(kReduceWaves * kWave);
+  const int rows = p.num_query_tokens * p.num_q_heads;
   if (p.max_splits >= kReduceManySplits) {
-    hipLaunchKernelGGL((reduce_kernel<OT, D, kReduceWaves>), dim3(p.num_q_heads, p.num_seqs),
-                       block, 0, stream, p);
+    hipLaunchKernelGGL((reduce_kernel<OT, D, kReduceWaves>), dim3(rows, p.num_seqs), block, 0,
+                       stream, p);
   } else {
-    const dim3 grid((p.num_q_heads + kReduceWaves - 1) / kReduceWaves, p.num_seqs);
+    const dim3 grid((rows + kReduceWaves - 1) / kReduceWaves, p.num_seqs);
     hipLaunchKernelGGL((reduce_kernel<OT, D, 1>), grid, block, 0, stream, p);
   }
 }

@@ -56,8 +56,9 @@ def test_default_split_tokens_is_valid(lib):
                       (0, 8, 100)]:
         for D in (64, 128):
             for dt in (F32, BF16, I8):
-                T = lib.pa_default_split_tokens(B, Hkv, D, dt, L)
-                assert 64 <= T <= 4096 and T % 16 == 0, (B, Hkv, L, D, dt, T)
+                for Q, W in ((1, 0), (4, 0), (1, 4096), (16, 128)):
+                    T = lib.pa_default_split_tokens(B, Hkv, D, dt, L, Q, W)
+                    assert 64 <= T <= 4096 and T % 16 == 0, (B, Hkv, L, D, dt, Q, W, T)
 
 
 @pytest.mark.parametrize("B,Hkv,D,dt,L,T", [
@@ -73,21 +74,48 @@ def test_default_split_tokens_is_valid(lib):
     (4, 2, 64, F32, 128, 64),
 ])
 def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
-    assert lib.pa_default_split_tokens(B, Hkv, D, dt, L) == T
+    assert lib.pa_default_split_tokens(B, Hkv, D, dt, L, 1, 0) == T
+
+
+def test_default_split_tokens_with_window(lib):
+    # 64 seqs x 8 heads, window 4096: ranges of at most 4111 tokens, 9 splits of
+    # 512 -> 4608 items, so T stays 512; a 128-token window on 8 seqs shrinks T.
+    assert lib.pa_default_split_tokens(64, 8, 128, BF16, 65536, 1, 4096) == 512
+    assert lib.pa_default_split_tokens(8, 8, 128, BF16, 65536, 1, 128) == 64
 
 
 def test_default_split_tokens_rejects_unknown(lib):
-    assert lib.pa_default_split_tokens(4, 8, 96, BF16, 100) == 0
-    assert lib.pa_default_split_tokens(4, 8, 128, 7, 100) == 0
+    assert lib.pa_default_split_tokens(4, 8, 96, BF16, 100, 1, 0) == 0
+    assert lib.pa_default_split_tokens(4, 8, 128, 7, 100, 1, 0) == 0
+    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 0, 0) == 0
+    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 17, 0) == 0
+    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 1, -1) == 0
+
+
+@pytest.mark.parametrize("L,Q,W,T,n", [
+    (4096, 1, 0, 512, 8),         # no window: ceil(L / T)
+    (131072, 1, 0, 512, 256),
+    (65536, 1, 4096, 512, 9),     # range <= 4096 + 15 tokens
+    (65536, 4, 4096, 512, 9),     # 4099 + 15 = 4114 -> 9
+    (65536, 1, 4081, 512, 8),     # 4081 + 15 = 4096 -> 8
+    (100, 1, 4096, 16, 7),        # window longer than the bound: ceil(100 / 16)
+    (0, 1, 0, 512, 1),
+    (100, 0, 0, 16, 0),           # bad Q
+    (100, 1, -1, 16, 0),          # bad W
+    (100, 1, 0, 0, 0),            # bad T
+])
+def test_max_splits(lib, L, Q, W, T, n):
+    assert lib.pa_max_splits(L, Q, W, T) == n
 
 
 def test_workspace_bytes(lib):
-    rows = 64 * 32 * 8
-    sched = -(-(2 + 2 * 64 * 8) * 4 // 256) * 256
+    sched = -(-(8 + 2 * 64 * 8) * 4 // 256) * 256
     assert lib.pa_sched_bytes(64, 8) == sched
-    expect = sched + 2 * (-(-rows * 4 // 256) * 256) + (-(-rows * 128 * 4 // 256) * 256)
-    assert lib.pa_workspace_bytes(64, 32, 128, 8) == expect
-    assert lib.pa_workspace_bytes(-1, 32, 128, 8) == 0
+    for Q in (1, 4):
+        rows = 64 * Q * 32 * 8
+        expect = sched + 2 * (-(-rows * 4 // 256) * 256) + (-(-rows * 128 * 4 // 256) * 256)
+        assert lib.pa_workspace_bytes(64, Q, 32, 128, 8) == expect
+    assert lib.pa_workspace_bytes(-1, 1, 32, 128, 8) == 0
     assert lib.pa_sched_bytes(-1, 8) == 0
 
 
@@ -114,17 +142,20 @@ def test_kv_write_validation(lib):
 def test_prepare_validation(lib):
     def prep(**kw):
         a = dict(k=FAKE, v=FAKE, idt=BF16, slots=FAKE, T=4, Hkv=8, D=128, kc=FAKE, vc=FAKE,
-                 NB=100, cdt=BF16, cl=FAKE, B=4, mb=8, mcl=128, split=512, sched=FAKE)
+                 NB=100, cdt=BF16, cl=FAKE, B=4, mb=8, mcl=128, Q=1, W=0, split=512, sched=FAKE)
         a.update(kw)
         return lib.paged_decode_prepare(a["k"], a["v"], a["idt"], a["slots"], a["T"], a["Hkv"],
                                         a["D"], a["kc"], a["vc"], None, None, a["NB"], a["cdt"],
-                                        a["cl"], a["B"], a["mb"], a["mcl"], a["split"],
-                                        a["sched"], None)
+                                        a["cl"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
+                                        a["split"], a["sched"], None)
     assert prep(D=96) == ERR_SHAPE
     assert prep(mb=0) == ERR_SHAPE
     assert prep(B=65536) == ERR_SHAPE
     assert prep(split=40) == ERR_SPLIT
     assert prep(split=0, mcl=100000, mb=8000, B=4, sched=None) == ERR_NULL  # default T accepted
+    assert prep(Q=0) == ERR_SHAPE
+    assert prep(Q=17) == ERR_SHAPE
+    assert prep(W=-1) == ERR_SHAPE
     assert prep(sched=None) == ERR_NULL
     assert prep(k=None) == ERR_NULL
     assert prep(kc=FAKE_ODD) == ERR_ALIGN
@@ -133,27 +164,31 @@ def test_prepare_validation(lib):
 
 def test_plan_validation(lib):
     def plan(**kw):
-        a = dict(cl=FAKE, B=4, mb=8, mcl=128, split=512, sched=FAKE)
+        a = dict(cl=FAKE, B=4, mb=8, mcl=128, Q=1, W=0, split=512, sched=FAKE)
         a.update(kw)
-        return lib.paged_attn_plan(a["cl"], a["B"], a["mb"], a["mcl"], a["split"], a["sched"],
-                                   None)
+        return lib.paged_attn_plan(a["cl"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
+                                   a["split"], a["sched"], None)
     assert plan(mb=0) == ERR_SHAPE
     assert plan(mcl=-1) == ERR_SHAPE
     assert plan(split=8) == ERR_SPLIT
     assert plan(split=0) == ERR_SPLIT                  # no default without the cache
     assert plan(sched=None) == ERR_NULL
+    assert plan(Q=0) == ERR_SHAPE
+    assert plan(Q=17) == ERR_SHAPE
+    assert plan(W=-5) == ERR_SHAPE
     assert plan(B=0, cl=None, sched=None) == OK
 
 
 def _partial(lib, **kw):
-    a = dict(q=FAKE, qdt=BF16, B=4, Hq=32, D=128, kc=FAKE, vc=FAKE, ks=None, vs=None, cdt=BF16,
-             NB=100, Hkv=8, bt=FAKE, mb=8, cl=FAKE, mcl=128, scale=0.1, T=512, S=1, m=FAKE,
-             l=FAKE, acc=FAKE, sched=FAKE)
+    a = dict(q=FAKE, qdt=BF16, B=4, Q=1, Hq=32, D=128, kc=FAKE, vc=FAKE, ks=None, vs=None,
+             cdt=BF16, NB=100, Hkv=8, bt=FAKE, mb=8, cl=FAKE, mcl=128, W=0, scale=0.1, T=512,
+             S=1, m=FAKE, l=FAKE, acc=FAKE, sched=FAKE)
     a.update(kw)
-    return lib.paged_attn_decode_partial(a["q"], a["qdt"], a["B"], a["Hq"], a["D"], a["kc"],
-                                         a["vc"], a["ks"], a["vs"], a["cdt"], a["NB"], a["Hkv"],
-                                         a["bt"], a["mb"], a["cl"], a["mcl"], a["scale"], a["T"],
-                                         a["S"], a["m"], a["l"], a["acc"], a["sched"], None)
+    return lib.paged_attn_decode_partial(a["q"], a["qdt"], a["B"], a["Q"], a["Hq"], a["D"],
+                                         a["kc"], a["vc"], a["ks"], a["vs"], a["cdt"], a["NB"],
+                                         a["Hkv"], a["bt"], a["mb"], a["cl"], a["mcl"], a["W"],
+                                         a["scale"], a["T"], a["S"], a["m"], a["l"], a["acc"],
+                                         a["sched"], None)
 
 
 def test_decode_partial_validation(lib):
@@ -167,7 +202,11 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, qdt=I8, cdt=I8) == ERR_DTYPE
     assert _partial(lib, T=24) == ERR_SPLIT
     assert _partial(lib, T=8192) == ERR_SPLIT
-    assert _partial(lib, mcl=1025, S=2) == ERR_SPLIT    # needs 3 splits
+    assert _partial(lib, mcl=1025, S=2, mb=100) == ERR_SPLIT  # needs 3 splits
+    assert _partial(lib, mcl=100000, mb=8000, W=500, S=1) == ERR_SPLIT  # 515 tokens: 2 splits
+    assert _partial(lib, Q=0) == ERR_SHAPE
+    assert _partial(lib, Q=17) == ERR_SHAPE
+    assert _partial(lib, W=-1) == ERR_SHAPE
     assert _partial(lib, q=None) == ERR_NULL
     assert _partial(lib, sched=None) == ERR_NULL
     assert _partial(lib, B=65536) == ERR_SHAPE
@@ -178,23 +217,25 @@ def test_decode_partial_validation(lib):
 
 def test_reduce_validation(lib):
     def red(**kw):
-        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, B=4, Hq=32, D=128, T=512, S=2, out=FAKE,
-                 odt=BF16)
+        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, B=4, Q=1, Hq=32, D=128, W=0, T=512, S=2,
+                 out=FAKE, odt=BF16)
         a.update(kw)
-        return lib.paged_attn_reduce(a["m"], a["l"], a["acc"], a["cl"], a["B"], a["Hq"], a["D"],
-                                     a["T"], a["S"], a["out"], a["odt"], None)
+        return lib.paged_attn_reduce(a["m"], a["l"], a["acc"], a["cl"], a["B"], a["Q"], a["Hq"],
+                                     a["D"], a["W"], a["T"], a["S"], a["out"], a["odt"], None)
     assert red(D=32) == ERR_SHAPE
     assert red(odt=I8) == ERR_DTYPE
     assert red(T=0) == ERR_SPLIT
     assert red(S=0) == ERR_SPLIT
     assert red(out=None) == ERR_NULL
+    assert red(Q=0) == ERR_SHAPE
+    assert red(W=-1) == ERR_SHAPE
     assert red(B=0, out=None) == OK
 
 
 def test_decode_workspace_validation(lib):
-    need = lib.pa_workspace_bytes(4, 32, 128, lib.pa_num_splits(1000, 512))
-    args = [FAKE, BF16, 4, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE, 1000,
-            ctypes.c_float(0.1), 512, FAKE]
+    need = lib.pa_workspace_bytes(4, 1, 32, 128, lib.pa_num_splits(1000, 512))
+    args = [FAKE, BF16, 4, 1, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE, 1000,
+            0, ctypes.c_float(0.1), 512, FAKE]
     assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
     assert lib.paged_attn_decode(*args, FAKE + 16, need, None) == ERR_ALIGN  # 256-byte rule
     assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
@@ -206,3 +247,14 @@ def test_read_probe_validation(lib):
     assert lib.pa_hbm_read_probe(FAKE_ODD, 1024, FAKE, 256, None) == ERR_ALIGN
     assert lib.pa_hbm_read_probe(FAKE, 1000, FAKE, 256, None) == ERR_SHAPE
     assert lib.pa_hbm_read_probe(FAKE, 1024, FAKE, 255, None) == ERR_SHAPE
+
+
+def test_decode_workspace_with_query_tokens_and_window(lib):
+    # Q = 4, window 100 on a 100000-token bound: splits of at most 100+4+14 = 118 tokens
+    S = lib.pa_max_splits(100000, 4, 100, 64)
+    assert S == 2
+    need = lib.pa_workspace_bytes(4, 4, 32, 128, S)
+    args = [FAKE, BF16, 4, 4, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 8000, FAKE,
+            100000, 100, ctypes.c_float(0.1), 64, FAKE]
+    assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
+    assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL

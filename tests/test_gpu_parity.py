@@ -51,7 +51,8 @@ def _oracle_decode(b, rows=None):
     return oracle.decode(_np(b.q), _np(b.k_cache), _np(b.v_cache), _np(b.block_tables),
                          _np(b.context_lens), b.scale,
                          None if b.k_scale is None else _np(b.k_scale),
-                         None if b.v_scale is None else _np(b.v_scale), rows=rows)
+                         None if b.v_scale is None else _np(b.v_scale), rows=rows,
+                         window=b.window)
 
 
 def _tol(b):
@@ -63,7 +64,7 @@ def _gpu_fp32_out(g, split_tokens=None):
     parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
                                            g.context_lens, g.scale, g.k_scale, g.v_scale,
                                            max_context_len=g.max_context_len,
-                                           split_tokens=split_tokens)
+                                           split_tokens=split_tokens, sliding_window=g.window)
     out = torch.empty(g.q.shape, dtype=torch.float32, device=g.q.device)
     pa().paged_attn_reduce(parts, out)
     torch.cuda.synchronize()
@@ -221,9 +222,9 @@ def test_partials_match_oracle_splits(name):
     m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
                                     _np(b.block_tables), _np(b.context_lens), b.scale, T,
                                     max_splits=parts.max_splits)
-    gm = parts.m.cpu().double().numpy()
-    gl = parts.l.cpu().double().numpy()
-    ga = parts.acc.cpu().double().numpy()
+    gm = parts.m.cpu().double().numpy().reshape(m.shape)
+    gl = parts.l.cpu().double().numpy().reshape(l.shape)
+    ga = parts.acc.cpu().double().numpy().reshape(acc.shape)
     for s, L in enumerate(b.context_lens.tolist()):
         n = oracle.num_splits(L, T)
         np.testing.assert_allclose(gm[s, :, :n], m[s, :, :n], rtol=0, atol=1e-4)
@@ -242,9 +243,9 @@ def test_reduce_alone_against_oracle_merge():
     m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
                                     _np(b.block_tables), _np(b.context_lens), b.scale, T)
     ref = oracle.merge(m, l, acc)
-    parts = pa().Partials(m=torch.from_numpy(m).float().cuda(),
-                          l=torch.from_numpy(l).float().cuda(),
-                          acc=torch.from_numpy(acc).float().cuda(),
+    parts = pa().Partials(m=torch.from_numpy(m).float().cuda().unsqueeze(1),
+                          l=torch.from_numpy(l).float().cuda().unsqueeze(1),
+                          acc=torch.from_numpy(acc).float().cuda().unsqueeze(1),
                           context_lens=b.context_lens.cuda(), split_tokens=T)
     out = torch.empty(b.q.shape, dtype=torch.float32, device="cuda")
     pa().paged_attn_reduce(parts, out)
@@ -343,9 +344,10 @@ def test_plan_lists_every_split_once(T):
     sched = plan.sched.cpu().numpy()
     nsplit = [max(1, -(-L // T)) for L in lens]
     n = sum(nsplit)
-    assert list(sched[:4]) == [n, T, len(lens), min(g.max_context_len, 16 * b.block_tables.shape[1])]
-    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[4:4 + 2 * n:2]]
-    assert list(sched[5:5 + 2 * n:2]) == [lens[s] for s, _ in entries]
+    assert list(sched[:8]) == [n, T, len(lens), min(g.max_context_len, 16 * b.block_tables.shape[1]),
+                               1, 0, 0, 0]
+    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
+    assert list(sched[9:9 + 2 * n:2]) == [lens[s] for s, _ in entries]
     assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
     n_full = n - len(lens)
     assert all(j < nsplit[s] - 1 for s, j in entries[:n_full])
@@ -377,10 +379,10 @@ def test_plan_is_shared_and_mismatch_is_ignored():
     l = torch.full_like(m, 7.0)
     acc = torch.full((5, g.q.shape[1], S, 128), 7.0, device="cuda")
     rc = lib.paged_attn_decode_partial(
-        g.q.data_ptr(), 1, 5, g.q.shape[1], 128, g.k_cache.data_ptr(), g.v_cache.data_ptr(),
+        g.q.data_ptr(), 1, 5, 1, g.q.shape[1], 128, g.k_cache.data_ptr(), g.v_cache.data_ptr(),
         None, None, 1, g.k_cache.shape[0], g.k_cache.shape[1], g.block_tables.data_ptr(),
-        g.block_tables.shape[1], g.context_lens.data_ptr(), g.max_context_len, g.scale, 32, S,
-        m.data_ptr(), l.data_ptr(), acc.data_ptr(), plan.sched.data_ptr(),
+        g.block_tables.shape[1], g.context_lens.data_ptr(), g.max_context_len, 0, g.scale, 32,
+        S, m.data_ptr(), l.data_ptr(), acc.data_ptr(), plan.sched.data_ptr(),
         torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0
@@ -412,11 +414,11 @@ def test_prepare_equals_write_then_plan(name):
     if b.k_scale is not None:
         assert torch.equal(g1.k_scale, g2.k_scale) and torch.equal(g1.v_scale, g2.v_scale)
     n = int(p1.sched[0].item())
-    s1, s2 = p1.sched[:4 + 2 * n].cpu(), p2.sched[:4 + 2 * n].cpu()
-    assert torch.equal(s1[:4], s2[:4])
+    s1, s2 = p1.sched[:8 + 2 * n].cpu(), p2.sched[:8 + 2 * n].cpu()
+    assert torch.equal(s1[:8], s2[:8])
     # Entries within one tile-count bucket may come in any order.
-    e1 = sorted(zip(s1[4::2].tolist(), s1[5::2].tolist()))
-    e2 = sorted(zip(s2[4::2].tolist(), s2[5::2].tolist()))
+    e1 = sorted(zip(s1[8::2].tolist(), s1[9::2].tolist()))
+    e2 = sorted(zip(s2[8::2].tolist(), s2[9::2].tolist()))
     assert e1 == e2
 
 
@@ -460,20 +462,23 @@ def test_graph_capture_replays_match_eager():
 
 # ------------------------------------------------------------------ full size
 
-def _sample_rows(B, Hq, n, seed):
+def _sample_rows(B, Q, Hq, n, seed):
     rng = np.random.default_rng(seed)
     seqs = rng.integers(0, B, size=n).astype(np.int32)
+    toks = rng.integers(0, Q, size=n).astype(np.int32)
     heads = rng.integers(0, Hq, size=n).astype(np.int32)
-    seqs[0], heads[0] = 0, 0
-    seqs[1], heads[1] = B - 1, Hq - 1
-    return seqs, heads
+    seqs[0], toks[0], heads[0] = 0, 0, 0
+    seqs[1], toks[1], heads[1] = B - 1, Q - 1, Hq - 1
+    return seqs, toks, heads
 
 
-@pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "shared_prefix_bf16"])
+@pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "shared_prefix_bf16",
+                                  "mtp4_llama8b_bf16", "swa4k_bf16"])
 def test_full_size_sampled_rows(name):
     """Full workload sizes, the launch the benchmark times (default split),
-    checked on sampled (sequence, head) rows; every output must be finite.
-    The oracle reads only its own copy of the inputs and its own writes."""
+    checked on sampled (sequence, query token, head) rows; every output must
+    be finite. The oracle reads only its own copy of the inputs and its own
+    writes."""
     print(f"[case] full-size {name}", flush=True)
     g = workloads.make_batch(name, 1, "cuda")
     b = workloads.Batch(**{f: getattr(g, f) for f in g.__dataclass_fields__})
@@ -486,15 +491,152 @@ def test_full_size_sampled_rows(name):
     _write_new_tokens(b, g)
     out = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
                                  g.scale, k_scale=g.k_scale, v_scale=g.v_scale,
-                                 max_context_len=g.max_context_len)
+                                 max_context_len=g.max_context_len, sliding_window=g.window)
     out32, _ = _gpu_fp32_out(g)
     assert torch.isfinite(out).all()
-    B, Hq = g.q.shape[:2]
-    seqs, heads = _sample_rows(B, Hq, 24, 7)
-    ref = _oracle_decode(b, rows=(seqs, heads))
-    _check_out(out32[seqs, heads], ref, TOL_BF16, f"{name}/fp32-out")
-    _check_bf16_out(out[torch.from_numpy(seqs).long(), torch.from_numpy(heads).long()].cpu(),
-                    ref, f"{name}/bf16-out")
+    B, Q, Hq = g.q.shape[0], g.query_tokens, g.q.shape[-2]
+    seqs, toks, heads = _sample_rows(B, Q, Hq, 24, 7)
+    ref = _oracle_decode(b, rows=(seqs, toks, heads))
+    o32 = out32.reshape(B, Q, Hq, -1)
+    ob = out.reshape(B, Q, Hq, -1)
+    _check_out(o32[seqs, toks, heads], ref, TOL_BF16, f"{name}/fp32-out")
+    idx = [torch.from_numpy(a).long() for a in (seqs, toks, heads)]
+    _check_bf16_out(ob[idx[0], idx[1], idx[2]].cpu(), ref, f"{name}/bf16-out")
+
+
+# ------------------------------------------------ several query tokens, windows
+
+MTP_CASES = [
+    # (workload, Q, window)
+    ("llama8b_bf16", 4, 0),     # 16 rows per KV head: one full MFMA tile
+    ("llama8b_bf16", 3, 0),     # 12 rows, 4 padding
+    ("llama8b_bf16", 2, 0),
+    ("llama8b_bf16", 8, 0),     # 32 rows: two row groups
+    ("tiny_fp32", 4, 0),        # VALU engine: 16 rows as two groups of 8
+    ("tiny_fp32", 3, 0),
+    ("llama8b_bf16", 1, 37),
+    ("llama8b_bf16", 4, 37),
+    ("llama8b_bf16", 1, 1),
+    ("llama8b_bf16", 4, 300),
+    ("tiny_fp32", 1, 20),
+    ("tiny_fp32", 4, 16),
+    ("int8_kv", 4, 0),
+    ("int8_kv", 1, 50),
+    ("int8_kv", 4, 50),
+]
+
+
+def _mtp_batch(name, Q, W, seed, **kw):
+    small = name == "tiny_fp32"  # its pool is fixed at 64 blocks
+    kw.setdefault("num_seqs", 4 if small else 6)
+    kw.setdefault("ctx_range", (Q, 128 if small else 700))
+    return workloads.make_batch(name, seed, "cpu", query_tokens=Q, window=W, **kw)
+
+
+@pytest.mark.parametrize("split_tokens", [16, 64, 512])
+@pytest.mark.parametrize("name,Q,W", MTP_CASES)
+def test_query_tokens_and_windows_match_oracle(name, Q, W, split_tokens):
+    """Q query tokens per sequence (causal among them) and sliding windows,
+    with NaN in every slot no query token attends and -1 table entries behind
+    the window; the new tokens are written first (Q per sequence)."""
+    print(f"[case] query rows {name} Q={Q} W={W} T={split_tokens}", flush=True)
+    b = _mtp_batch(name, Q, W, 201, poison=True)
+    g = _to(b, "cuda")
+    if b.k_cache.dtype == torch.int8:
+        _fill_int8(b, g)
+    _write_new_tokens(b, g)
+    ref = _oracle_decode(b)
+    assert np.isfinite(ref).all()
+    out32, _ = _gpu_fp32_out(g, split_tokens)
+    _check_out(out32, ref, _tol(b), f"{name} Q={Q} W={W}")
+    out = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
+                                 g.scale, k_scale=g.k_scale, v_scale=g.v_scale,
+                                 max_context_len=g.max_context_len, split_tokens=split_tokens,
+                                 sliding_window=W)
+    torch.cuda.synchronize()
+    assert out.shape == g.q.shape
+    if b.q.dtype == torch.bfloat16:
+        _check_bf16_out(out, ref, f"{name} Q={Q} W={W}/bf16-out")
+    else:
+        _check_out(out.cpu().double().numpy(), ref, TOL_F32, f"{name} Q={Q} W={W}/out")
+
+
+def test_query_tokens_before_the_sequence_start():
+    """L < Q: query tokens at negative positions give zeros; L = 0 too."""
+    print("[case] query rows L < Q", flush=True)
+    b = workloads.make_batch("llama8b_bf16", 211, "cpu", lengths=[0, 1, 2, 3, 4, 5, 40],
+                             query_tokens=4)
+    g = _to(b, "cuda")
+    ref = _oracle_decode(b)
+    for T in (16, 512):
+        out32, _ = _gpu_fp32_out(g, T)
+        _check_out(out32, ref, TOL_BF16, f"L<Q T={T}")
+        assert np.all(out32[0] == 0) and np.all(out32[1, :3] == 0) and np.all(out32[2, :2] == 0)
+
+
+@pytest.mark.parametrize("Q,W", [(4, 0), (1, 37), (4, 37)])
+def test_partials_with_query_ranges(Q, W):
+    """Per-split partials with empty per-row splits (m = -inf, l = 0)."""
+    print(f"[case] partials Q={Q} W={W}", flush=True)
+    b = _mtp_batch("llama8b_bf16", Q, W, 221, ctx_range=(Q, 300))
+    g = _to(b, "cuda")
+    T = 16
+    _, parts = _gpu_fp32_out(g, T)
+    m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
+                                    _np(b.block_tables), _np(b.context_lens), b.scale, T,
+                                    max_splits=parts.max_splits, window=W)
+    rows = tuple(parts.m.shape[:3])  # (B, Q, Hq); the oracle's follow q's shape
+    m, l = m.reshape(rows + m.shape[-1:]), l.reshape(rows + l.shape[-1:])
+    acc = acc.reshape(rows + acc.shape[-2:])
+    gm, gl, ga = (t.cpu().double().numpy() for t in (parts.m, parts.l, parts.acc))
+    for s, L in enumerate(b.context_lens.tolist()):
+        n = oracle.num_splits(L, T, Q, W)
+        empty = l[s, :, :, :n] == 0
+        assert np.all(gl[s, :, :, :n][empty] == 0) and np.all(gm[s, :, :, :n][empty] == -np.inf)
+        full = ~empty
+        np.testing.assert_allclose(gm[s, :, :, :n][full], m[s, :, :, :n][full], rtol=0, atol=1e-4)
+        np.testing.assert_allclose((gl * np.exp(gm))[s, :, :, :n][full],
+                                   (l * np.exp(m))[s, :, :, :n][full], rtol=1e-4)
+        np.testing.assert_allclose((ga / np.where(gl > 0, gl, 1)[..., None])[s, :, :, :n][full],
+                                   (acc / np.where(l > 0, l, 1)[..., None])[s, :, :, :n][full],
+                                   rtol=0, atol=TOL_BF16)
+
+
+def test_reduce_alone_with_query_rows():
+    print("[case] reduce alone Q=3 W=40", flush=True)
+    b = _mtp_batch("llama8b_bf16", 3, 40, 231, num_seqs=5, ctx_range=(3, 600))
+    T = 16
+    m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
+                                    _np(b.block_tables), _np(b.context_lens), b.scale, T,
+                                    window=40)
+    ref = oracle.merge(m, l, acc)
+    parts = pa().Partials(m=torch.from_numpy(m).float().cuda(), l=torch.from_numpy(l).float().cuda(),
+                          acc=torch.from_numpy(acc).float().cuda(),
+                          context_lens=b.context_lens.cuda(), split_tokens=T, sliding_window=40)
+    out = torch.empty(b.q.shape, dtype=torch.float32, device="cuda")
+    pa().paged_attn_reduce(parts, out)
+    torch.cuda.synchronize()
+    _check_out(out.cpu().double().numpy(), ref, 1e-5, "reduce Q=3 W=40")
+
+
+@pytest.mark.parametrize("Q,W,T", [(1, 100, 16), (4, 100, 64), (4, 0, 16), (2, 33, 512)])
+def test_plan_with_query_ranges(Q, W, T):
+    """The plan lists max(1, ceil((L - base) / T)) splits per sequence and
+    records Q and W in its header."""
+    print(f"[case] plan Q={Q} W={W} T={T}", flush=True)
+    lens = [4, 5, 16, 17, 100, 101, 116, 117, 500, 1000, 1023, 37]
+    b = workloads.make_batch("llama8b_bf16", 241, "cpu", lengths=lens, query_tokens=Q, window=W)
+    g = _to(b, "cuda")
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=T,
+                                num_query_tokens=Q, sliding_window=W)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    nsplit = [oracle.num_splits(L, T, Q, W) for L in lens]
+    n = sum(nsplit)
+    assert list(sched[:8]) == [n, T, len(lens), g.max_context_len, Q, W, 0, 0]
+    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
+    assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
 
 
 @pytest.mark.parametrize("nbytes,blocks", [(1 << 20, 4), ((1 << 20) + 48, 4), (8192 * 7 + 16, 3),
