@@ -5,14 +5,15 @@ smoke check and the benchmark's CPU-baseline leg may import this package; the
 HIP library never does, and this package never imports the HIP library.
 
 Arrays are NumPy arrays on the host. dtype codes follow the element type:
-``np.float32`` is fp32, ``np.uint16``/``np.int16`` hold bf16 bit patterns and
-``np.int8`` is the INT8 cache. Shapes:
+``np.float32`` is fp32, ``np.uint16``/``np.int16`` hold bf16 bit patterns,
+``np.int8`` is the INT8 cache and ``np.uint8`` holds OCP FP8 E4M3 codes.
+Shapes:
 
 * q            [num_seqs][num_q_heads][head_dim], or
                [num_seqs][num_query_tokens][num_q_heads][head_dim] (several query
                tokens per sequence: the last num_query_tokens tokens of its context)
 * k/v cache    [num_blocks][num_kv_heads][16][head_dim]
-* k/v scale    [num_blocks][num_kv_heads][16] float32 (INT8 cache only)
+* k/v scale    [num_blocks][num_kv_heads][16] float32 (INT8 / FP8 caches only)
 * block_tables [num_seqs][max_blocks_per_seq] int32
 * context_lens [num_seqs] int32
 * slot_mapping [num_tokens] int64 (negative = skip)
@@ -30,7 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 BLOCK_SIZE = 16
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, FP8 = 0, 1, 2, 3
 
 
 def _load():
@@ -55,6 +56,10 @@ def _load():
         lib.oracle_num_splits.restype = I
         lib.oracle_split_base.argtypes = [I, I, I]
         lib.oracle_split_base.restype = I
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = D
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -68,6 +73,8 @@ def _code(a):
         return BF16
     if a.dtype == np.int8:
         return I8
+    if a.dtype == np.uint8:
+        return FP8
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -82,6 +89,16 @@ def _c(a, dtype=None):
     if dtype is not None and a.dtype != dtype:
         a = a.astype(dtype)
     return np.ascontiguousarray(a)
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code."""
+    return float(_load().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    """E4M3 code of an fp32 value (nearest, ties to even, saturating at 448)."""
+    return int(_load().oracle_e4m3_encode(float(np.float32(x))))
 
 
 def num_threads() -> int:
@@ -127,7 +144,7 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
     num_blocks, num_kv_heads, bs, hd = k_cache.shape
     assert bs == BLOCK_SIZE and hd == head_dim and num_q_heads % num_kv_heads == 0
     assert nqt >= 1 and window >= 0
-    if _code(k_cache) == I8:
+    if _code(k_cache) in (I8, FP8):
         assert k_scale is not None and v_scale is not None
     # Every block the definition will read must exist in the pool (blocks
     # before a sliding window's reach are never read).

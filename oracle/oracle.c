@@ -22,6 +22,8 @@
  *                 kernel merges them.
  *   [Echo 3]      same notes, section 3, "KV Cache INT8 quantisation": INT8
  *                 cache with per-token scales, dequantised right after loading.
+ *   [ATOM 3]      same article, quick start: every example runs with
+ *                 --kv_cache_dtype fp8 (an FP8 KV cache).
  *   [ATOM 4.2]    "AMD ATOM Inference Engine" article, section 4.2 (decode
  *                 scheduling): with MTP speculative decoding every decode step
  *                 of a sequence carries mtp_k + 1 new tokens (the target token
@@ -54,7 +56,11 @@
  *     sum exp(z - m) * v, NOT divided by l;
  *   - INT8 quantiser per (token, KV head): a = max |x| in fp32, sc = a/127 (IEEE
  *     fp32 divide), q = clamp(round-half-even(x/sc), -127, 127), a = 0 -> q = 0;
- *     its input is the bf16/fp32 source widened exactly to fp32.
+ *     its input is the bf16/fp32 source widened exactly to fp32;
+ *   - FP8 cache [ATOM 3]: OCP FP8 E4M3 (bias 7, no infinities, 0x7F/0xFF NaN,
+ *     largest finite 448) with the same per-(token, KV head) fp32 scale,
+ *     sc = a/448, code = e4m3(x/sc) rounded to nearest (ties to even),
+ *     a = 0 -> codes 0; dequantised as e4m3 value * sc.
  *
  * Floating point: every attention quantity is computed in double. Build with
  * -ffp-contract=off and without -ffast-math (the INT8 quantiser relies on IEEE
@@ -66,7 +72,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3 };
 enum { OR_BLOCK = 16 };
 
 /* bf16 is the top half of an IEEE binary32: widening is a 16-bit shift. */
@@ -77,10 +83,43 @@ static float bf16_bits_to_float(uint16_t b) {
   return f;
 }
 
+/* Value of an OCP FP8 E4M3 code: sign, 4 exponent bits (bias 7), 3
+ * mantissa bits; exponent 0 holds the subnormals m * 2^-9; S.1111.111 is NaN
+ * (the format has no infinities). */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* The E4M3 code nearest to x (ties to the even mantissa); finite values past
+ * the largest code, 448, saturate to +-448; NaN gives 0x7F. */
+uint8_t oracle_e4m3_encode(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return 0x7F;
+  float a = fabsf(x);
+  if (a >= 448.0f) return sign | 0x7E;
+  if (a < 0.015625f) { /* below 2^-6: subnormal codes m * 2^-9 (m = 8 is 2^-6) */
+    float q = rintf(a * 512.0f);
+    return sign | (uint8_t)q;
+  }
+  int e;
+  frexpf(a, &e); /* a = f * 2^e with f in [0.5, 1) */
+  e -= 1;        /* a = 1.xxx * 2^e, e in [-6, 8] */
+  float q = rintf(ldexpf(a, 3 - e)); /* 8 .. 16: 1.xxx in eighths */
+  if (q == 16.0f) {
+    q = 8.0f;
+    e += 1;
+  }
+  return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
 /* Element idx of an array of `dtype` values, widened exactly to double. */
 static double load_elem(const void *base, int dtype, int64_t idx) {
   if (dtype == OR_F32) return (double)((const float *)base)[idx];
   if (dtype == OR_BF16) return (double)bf16_bits_to_float(((const uint16_t *)base)[idx]);
+  if (dtype == OR_FP8) return oracle_e4m3_decode(((const uint8_t *)base)[idx]);
   return (double)((const int8_t *)base)[idx];
 }
 
@@ -100,6 +139,21 @@ static int64_t cache_index(int64_t b, int h, int o, int d, int num_kv_heads, int
 /* Flat index of the per-token scale of (block b, kv head h, offset o). */
 static int64_t scale_index(int64_t b, int h, int o, int num_kv_heads) {
   return (b * num_kv_heads + h) * OR_BLOCK + o;
+}
+
+/* FP8 quantiser of one row [ATOM 3]: the INT8 recipe with 448 (the largest
+ * E4M3 value) in place of 127 and E4M3 rounding in place of integer rounding. */
+static void quantise_row_fp8(const void *src, int src_dtype, int64_t row_off, int head_dim,
+                             uint8_t *dst, float *scale_out) {
+  float a = 0.0f;
+  for (int d = 0; d < head_dim; ++d) {
+    float ax = fabsf(load_elem_f32(src, src_dtype, row_off + d));
+    if (ax > a) a = ax;
+  }
+  float sc = a / 448.0f;
+  for (int d = 0; d < head_dim; ++d)
+    dst[d] = a == 0.0f ? 0 : oracle_e4m3_encode(load_elem_f32(src, src_dtype, row_off + d) / sc);
+  *scale_out = sc;
 }
 
 /* INT8 quantiser of one row of head_dim values [Echo 3]. */
@@ -131,7 +185,8 @@ static void quantise_row(const void *src, int src_dtype, int64_t row_off, int he
  *   k, v        [num_tokens][num_kv_heads][head_dim] of in_dtype (0 fp32, 1 bf16)
  *   k_cache,... [num_blocks][num_kv_heads][16][head_dim] of cache_dtype
  *   k_scale,... [num_blocks][num_kv_heads][16] fp32, used when cache_dtype is INT8
- * Non-INT8 caches need in_dtype == cache_dtype and receive an exact copy.
+ * INT8 and FP8 caches are quantised per (token, KV head); other caches need
+ * in_dtype == cache_dtype and receive an exact copy.
  * Returns 0, or -1 on an unsupported combination or a slot outside the pool.
  */
 int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *slot_mapping,
@@ -139,7 +194,7 @@ int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *s
                     void *v_cache, float *k_scale, float *v_scale, int64_t num_blocks,
                     int cache_dtype) {
   if (in_dtype != OR_F32 && in_dtype != OR_BF16) return -1;
-  if (cache_dtype != OR_I8 && cache_dtype != in_dtype) return -1;
+  if (cache_dtype != OR_I8 && cache_dtype != OR_FP8 && cache_dtype != in_dtype) return -1;
   for (int64_t t = 0; t < num_tokens; ++t) {
     int64_t slot = slot_mapping[t];
     if (slot < 0) continue;
@@ -153,6 +208,12 @@ int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *s
         int64_t si = scale_index(b, h, o, num_kv_heads);
         quantise_row(k, in_dtype, src_off, head_dim, (int8_t *)k_cache + dst_off, &k_scale[si]);
         quantise_row(v, in_dtype, src_off, head_dim, (int8_t *)v_cache + dst_off, &v_scale[si]);
+      } else if (cache_dtype == OR_FP8) {
+        int64_t si = scale_index(b, h, o, num_kv_heads);
+        quantise_row_fp8(k, in_dtype, src_off, head_dim, (uint8_t *)k_cache + dst_off,
+                         &k_scale[si]);
+        quantise_row_fp8(v, in_dtype, src_off, head_dim, (uint8_t *)v_cache + dst_off,
+                         &v_scale[si]);
       } else {
         size_t es = dtype_size(cache_dtype);
         memcpy((char *)k_cache + dst_off * es, (const char *)k + src_off * es, es * head_dim);
@@ -168,7 +229,7 @@ typedef struct {
   const void *q; /* [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype */
   int q_dtype, num_q_heads, num_query_tokens;
   const void *k, *v;      /* pool, [num_blocks][num_kv_heads][16][head_dim] */
-  const float *k_scale, *v_scale; /* [num_blocks][num_kv_heads][16], INT8 only */
+  const float *k_scale, *v_scale; /* [num_blocks][num_kv_heads][16], INT8 / FP8 only */
   int cache_dtype, num_kv_heads, head_dim;
   const int32_t *block_tables; /* [num_seqs][max_blocks_per_seq] */
   int max_blocks_per_seq;
@@ -196,7 +257,7 @@ static double kv_elem(const decode_args *a, int which, int s, int kv, int t, int
   int o = t % OR_BLOCK;
   const void *base = which ? a->v : a->k;
   double x = load_elem(base, a->cache_dtype, cache_index(b, kv, o, d, a->num_kv_heads, a->head_dim));
-  if (a->cache_dtype == OR_I8) {
+  if (a->cache_dtype == OR_I8 || a->cache_dtype == OR_FP8) {
     const float *sc = which ? a->v_scale : a->k_scale;
     x *= (double)sc[scale_index(b, kv, o, a->num_kv_heads)];
   }

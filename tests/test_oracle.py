@@ -19,10 +19,13 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _np(t):
-    """Host NumPy view of a batch tensor (bf16 as its uint16 bit pattern)."""
+    """Host NumPy view of a batch tensor (bf16 as its uint16 bit pattern, FP8
+    as its uint8 codes)."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
@@ -398,6 +401,127 @@ def test_int8_dequant_uses_per_token_scales():
     assert np.array_equal(out_i8, out_32)
 
 
+# ---------------------------------------------------------------- FP8 (E4M3)
+#
+# [ATOM 3] runs with --kv_cache_dtype fp8. Read as OCP FP8 E4M3 (bias 7, no
+# infinities, S.1111.111 = NaN, largest finite 448) with the INT8 recipe's
+# per-(token, KV head) scale, absmax / 448.
+
+def test_e4m3_decoding_worked_values():
+    """Codes worked by hand from the OCP E4M3 layout (tests/golden/fp8_e4m3.json)."""
+    fx = json.load(open(os.path.join(GOLDEN, "fp8_e4m3.json")))
+    for c in fx["codes"]:
+        v = oracle.e4m3_decode(int(c["code"], 16))
+        if c["value"] == "nan":
+            assert math.isnan(v), c
+        else:
+            assert v == float(c["value"]) and math.copysign(1, v) == math.copysign(1, float(c["value"])), c
+
+
+def test_e4m3_decoding_matches_torch_float8():
+    """Every code decodes as torch's float8_e4m3fn (a library rendering of
+    the same OCP format), NaN codes included."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def test_e4m3_encoding_round_trip_ties_and_saturation():
+    # Every finite code is its own value's code.
+    for c in range(256):
+        if (c & 0x7F) != 0x7F:
+            assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c
+    # Midpoints between neighbouring codes go to the even mantissa.
+    for c in range(0, 0x7E):
+        lo, hi = oracle.e4m3_decode(c), oracle.e4m3_decode(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2  # exact in fp32
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == want, hex(c)
+        assert oracle.e4m3_encode(-mid) == want | 0x80
+    # Past the largest code: saturation; NaN stays NaN.
+    for x in (448.0, 463.9, 464.0, 1e6, 3.4e38, float("inf")):
+        assert oracle.e4m3_encode(x) == 0x7E and oracle.e4m3_encode(-x) == 0xFE
+    assert oracle.e4m3_encode(float("nan")) & 0x7F == 0x7F
+
+
+def test_e4m3_encoding_matches_torch_float8_in_range():
+    """Inside the finite range torch's float8_e4m3fn conversion rounds to
+    nearest even too: agreement on random fp32 values of every magnitude."""
+    rng = np.random.default_rng(13)
+    x = (rng.uniform(-1, 1, 20000) * np.exp2(rng.uniform(-12, 8.8, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(v) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def _quantise_rows_fp8(x_bf16_bits):
+    """Run rows [T][D] through the oracle's FP8 write (one KV head)."""
+    T, D = x_bf16_bits.shape
+    nblocks = -(-T // 16)
+    kc = np.zeros((nblocks, 1, 16, D), np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.full((nblocks, 1, 16), np.nan, np.float32)
+    vs = np.full_like(ks, np.nan)
+    src = np.ascontiguousarray(x_bf16_bits.reshape(T, 1, D))
+    oracle.kv_write(src, src, np.arange(T, dtype=np.int64), kc, vc, ks, vs)
+    return kc.reshape(-1, D)[:T], ks.reshape(-1)[:T]
+
+
+def test_fp8_quantiser_properties_and_independent_implementation():
+    """The FP8 write against an independent quantiser (NumPy fp32 scale and
+    divide, torch's float8_e4m3fn rounding): bitwise; the absmax element is
+    +-448; the error is within half an E4M3 step of the scaled value."""
+    rng = np.random.default_rng(17)
+    x = rng.normal(size=(300, 128)).astype(np.float32)
+    x[7] = 0.0
+    x[8] *= 1e-30
+    x[9] *= 1e30
+    x[10, :4] = [3.0, -3.0, 1.5, 0.0]  # ties after scaling
+    x[10, 4:] = 0.0
+    bits = _bf16_bits(x)
+    codes, scales = _quantise_rows_fp8(bits)
+    xw = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    a = np.max(np.abs(xw), axis=1)
+    sc = (a / np.float32(448.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        y = (xw / sc[:, None]).astype(np.float32)
+    ref = torch.from_numpy(np.where(a[:, None] == 0, 0, y).astype(np.float32))
+    ref = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(scales, sc) and np.array_equal(codes, ref)
+    nz = a > 0
+    am = np.argmax(np.abs(xw), axis=1)
+    assert np.all(codes[nz, am[nz]] & 0x7F == 0x7E)
+    val = np.vectorize(oracle.e4m3_decode)(codes)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3)
+    assert np.all(np.abs(y - val)[nz] <= 0.5 * ulp[nz] * (1 + 1e-6))
+    assert np.all(codes[~nz] == 0) and np.all(scales[~nz] == 0)
+
+
+def test_fp8_dequant_uses_per_token_scales():
+    """An FP8 pool whose per-token scales are powers of two equals, exactly,
+    an fp32 pool holding value(code) * scale."""
+    b = workloads.make_batch("fp8_kv", 3, "cpu", num_seqs=4, ctx_range=(1, 70))
+    kc, vc = _np(b.k_cache).copy(), _np(b.v_cache).copy()
+    ks, vs = _np(b.k_scale).copy(), _np(b.v_scale).copy()
+    oracle.kv_write(_np(b.fill_k), _np(b.fill_v), _np(b.fill_slots), kc, vc, ks, vs)
+    rng = np.random.default_rng(1)
+    ks = np.ldexp(1.0, rng.integers(-6, 6, size=ks.shape)).astype(np.float32)
+    vs = np.ldexp(1.0, rng.integers(-6, 6, size=vs.shape)).astype(np.float32)
+    dec = np.vectorize(oracle.e4m3_decode)
+    k32 = (dec(kc) * ks[..., None]).astype(np.float32)
+    v32 = (dec(vc) * vs[..., None]).astype(np.float32)
+    q32 = torch.from_numpy(_np(b.q)).view(torch.bfloat16).float().numpy()
+    out_8 = oracle.decode(_np(b.q), kc, vc, _np(b.block_tables), _np(b.context_lens), b.scale, ks, vs)
+    out_32 = oracle.decode(q32, k32, v32, _np(b.block_tables), _np(b.context_lens), b.scale)
+    assert np.array_equal(out_8, out_32)
+
+
 # ---------------------------------------------------------------- harness pins
 
 def test_prefix_sharing_example():
@@ -433,6 +557,7 @@ def test_kv_bytes_per_token_matches_page_size_example():
     assert abs(total / 1e9 - fx["page_gigabytes"]) / fx["page_gigabytes"] <= fx["rel_tol"]
     assert workloads.kv_bytes_per_token(8, 128, "bf16") == 4096
     assert workloads.kv_bytes_per_token(8, 128, "int8") == 2112
+    assert workloads.kv_bytes_per_token(8, 128, "fp8") == 2112
 
 
 def test_fragmentation_one_tail_block():

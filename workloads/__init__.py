@@ -47,6 +47,8 @@ Workloads (block size 16 throughout):
   head_dim 128, bf16. Each group's 2000-token prefix (125 full blocks) is
   mapped to the same physical blocks; each sample's private suffix length is
   clip(rint(exp(N(ln 300, 1))), 1, 16384) and L = 2000 + suffix + 1.
+* ``fp8_kv``: the INT8 batch's shape with an FP8 (OCP E4M3) cache, per-token
+  fp32 scales, filled through the KV write.
 * ``mtp4_llama8b_bf16``: the 8B-shaped batch with 4 query tokens per sequence
   (3 draft tokens and the target token of MTP speculative decoding).
 * ``swa4k_bf16``: 64 seqs, 32 q / 8 KV heads, head_dim 128, bf16, L uniform in
@@ -72,7 +74,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     dtype: str                 # q / out / source K,V: "fp32" | "bf16"
-    cache_dtype: str           # "fp32" | "bf16" | "int8"
+    cache_dtype: str           # "fp32" | "bf16" | "int8" | "fp8" (OCP E4M3)
     ctx_lo: int = 0
     ctx_hi: int = 0
     fixed_pool_blocks: int = 0  # 0: 1.1x the attended tokens
@@ -97,13 +99,16 @@ WORKLOADS = {
         Workload("int8_kv", 128, 32, 8, 128, "bf16", "int8", 1024, 8192),
         Workload("shared_prefix_bf16", 256, 64, 4, 128, "bf16", "bf16", groups=32, samples=8,
                  prefix_len=2000, suffix_median=300.0, suffix_sigma=1.0, suffix_max=16384),
+        Workload("fp8_kv", 128, 32, 8, 128, "bf16", "fp8", 1024, 8192),
         Workload("mtp4_llama8b_bf16", 64, 32, 8, 128, "bf16", "bf16", 512, 4096,
                  query_tokens=4),
         Workload("swa4k_bf16", 64, 32, 8, 128, "bf16", "bf16", 8192, 65536, window=4096),
     ]
 }
 
-TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "int8": torch.int8}
+TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16, "int8": torch.int8,
+                "fp8": torch.float8_e4m3fn}
+QUANTISED = ("int8", "fp8")  # caches filled through the quantising KV write
 
 
 @dataclasses.dataclass
@@ -112,7 +117,7 @@ class Batch:
     q: torch.Tensor               # [B][Hq][D], or [B][Q][Hq][D] with Q query tokens
     k_cache: torch.Tensor         # [NB][Hkv][16][D]
     v_cache: torch.Tensor
-    k_scale: Optional[torch.Tensor]  # [NB][Hkv][16] float32 (INT8 only)
+    k_scale: Optional[torch.Tensor]  # [NB][Hkv][16] float32 (INT8 / FP8 only)
     v_scale: Optional[torch.Tensor]
     block_tables: torch.Tensor    # [B][max_blocks] int32
     context_lens: torch.Tensor    # [B] int32
@@ -259,9 +264,10 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
 
     k_scale = v_scale = fill_k = fill_v = fill_slots = None
     cache_shape = (num_blocks, Hkv, BLOCK_SIZE, D)
-    if w.cache_dtype == "int8":
-        k_cache = torch.zeros(cache_shape, dtype=torch.int8, device=device)
-        v_cache = torch.zeros(cache_shape, dtype=torch.int8, device=device)
+    if w.cache_dtype in QUANTISED:
+        cdt = TORCH_DTYPES[w.cache_dtype]
+        k_cache = torch.zeros(cache_shape, dtype=cdt, device=device)
+        v_cache = torch.zeros(cache_shape, dtype=cdt, device=device)
         fill = torch.nan if poison else 0.0
         k_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         v_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
@@ -315,9 +321,9 @@ def kv_blocks(prefix_len: int, gen_lens, shared: bool, block_size: int = BLOCK_S
 
 
 def kv_bytes_per_token(num_kv_heads: int, head_dim: int, cache_dtype: str) -> int:
-    """KV bytes one token occupies in the pool (K and V rows, plus INT8 scales)."""
-    elt = {"fp32": 4, "bf16": 2, "int8": 1}[cache_dtype]
-    extra = 2 * num_kv_heads * 4 if cache_dtype == "int8" else 0
+    """KV bytes one token occupies in the pool (K and V rows, plus INT8/FP8 scales)."""
+    elt = {"fp32": 4, "bf16": 2, "int8": 1, "fp8": 1}[cache_dtype]
+    extra = 2 * num_kv_heads * 4 if cache_dtype in QUANTISED else 0
     return 2 * num_kv_heads * head_dim * elt + extra
 
 
