@@ -96,6 +96,8 @@ def cpu_baseline(b, seconds):
         t = t.detach().cpu().contiguous()
         if t.dtype == torch.bfloat16:
             return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
         return t.numpy()
 
     q, kc, vc = host(b.q), host(b.k_cache), host(b.v_cache)
@@ -178,7 +180,7 @@ def main():
                              contiguous_tables=args.contiguous_tables,
                              ctx_range=tuple(args.ctx_range) if args.ctx_range else None)
     w = b.workload
-    if b.k_cache.dtype == torch.int8:
+    if b.fill_k is not None:  # quantised pools are filled through the KV write
         pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
                           b.v_scale)
         b.fill_k = b.fill_v = None
@@ -276,7 +278,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16"}[w.dtype] + ("+i8kv" if w.cache_dtype == "int8" else ""),
+        "dtype": {"fp32": "f32", "bf16": "bf16"}[w.dtype] +
+                 {"int8": "+i8kv", "fp8": "+fp8kv"}.get(w.cache_dtype, ""),
         "data": "synthetic",
         "config": {
             "workload": w.name, "num_seqs": B, "q_heads": Hq, "kv_heads": w.num_kv_heads,

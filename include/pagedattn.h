@@ -18,15 +18,17 @@
  *     section 3 (KV Cache INT8): INT8 cache with per-token scales, dequantised
  *     inside the attention kernel right after loading; section 4: sliding
  *     window attention as a way to bound decode cost.
- *   - "AMD ATOM Inference Engine" article, section 4.2 (decode scheduling):
+ *   - "AMD ATOM Inference Engine" article, quick start (section 3): an FP8 KV
+ *     cache (--kv_cache_dtype fp8); section 4.2 (decode scheduling):
  *     with MTP speculative decoding each decode step of a sequence carries
  *     mtp_k + 1 new tokens, each with its own KV slot.
  *
  * Conventions shared by every entry point:
  *   - Pool layout: k_cache, v_cache are [num_blocks][num_kv_heads][16][head_dim]
  *     of the cache dtype, so one (block, KV head) tile is 16*head_dim contiguous
- *     elements. INT8 pools carry k_scale, v_scale [num_blocks][num_kv_heads][16]
- *     fp32, one scale per (token, KV head).
+ *     elements. INT8 and FP8 pools carry k_scale, v_scale
+ *     [num_blocks][num_kv_heads][16] fp32, one scale per (token, KV head); an
+ *     element's value is code * scale (FP8: the E4M3 value of the code).
  *   - Token t of sequence s lives in block block_tables[s][t / 16], row t % 16.
  *     A slot is block * 16 + row.
  *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -84,8 +86,9 @@ extern "C" {
 #define PA_MAX_SEQS 65535
 #define PA_MAX_QUERY_TOKENS 16
 
-/* Element types. */
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+/* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
+ * NaN, largest finite 448). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8 = 3 } pa_dtype;
 
 /* Status codes. */
 enum {
@@ -149,7 +152,10 @@ size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t nu
  *                 (token, head) a = max|x| (x widened to fp32), scale = a/127
  *                 (IEEE fp32 division), code = clamp(rint_half_even(x/scale),
  *                 -127, 127), a == 0 gives scale 0 and codes 0; the scale goes
- *                 to k_scale / v_scale (required for PA_I8, ignored otherwise).
+ *                 to k_scale / v_scale (required for PA_I8 and PA_FP8, ignored
+ *                 otherwise). cache_dtype == PA_FP8 [ATOM article, section 3]:
+ *                 the same with scale = a/448 and code = the OCP E4M3 value
+ *                 nearest to x/scale (ties to even, saturating at +-448).
  *   head_dim      64 or 128.
  * Duplicate slots in one call race (unspecified winner). Writing into a block
  * shared by several sequences is the caller's decision.
@@ -211,8 +217,8 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
  *   q                 [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype
  *                     (PA_F32/PA_BF16)
  *   k_cache, ...      pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
- *                     (q PA_BF16) or PA_I8 (q PA_BF16 or PA_F32; k_scale and
- *                     v_scale required). num_blocks < 2^31.
+ *                     (q PA_BF16), PA_I8 or PA_FP8 (q PA_BF16 or PA_F32;
+ *                     k_scale and v_scale required). num_blocks < 2^31.
  *   block_tables      [num_seqs][max_blocks_per_seq] int32
  *   context_lens      [num_seqs] int32, each <= max_context_len
  *   max_context_len   host bound on context_lens, sizes the launch grid

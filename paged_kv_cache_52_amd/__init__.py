@@ -10,8 +10,9 @@ Tensor layouts (block size 16):
 * q, out          [num_seqs][num_q_heads][head_dim] (one query token per
                   sequence) or [num_seqs][Q][num_q_heads][head_dim] (Q query
                   tokens: the sequence's last Q positions), fp32 or bf16
-* k_cache, v_cache [num_blocks][num_kv_heads][16][head_dim], fp32/bf16/int8
-* k_scale, v_scale [num_blocks][num_kv_heads][16] fp32 (int8 caches only)
+* k_cache, v_cache [num_blocks][num_kv_heads][16][head_dim], fp32/bf16/int8/
+                  float8_e4m3fn (OCP FP8 E4M3)
+* k_scale, v_scale [num_blocks][num_kv_heads][16] fp32 (int8 and fp8 caches only)
 * block_tables    [num_seqs][max_blocks_per_seq] int32
 * context_lens    [num_seqs] int32
 * slot_mapping    [num_tokens] int64 (negative = skip)
@@ -30,8 +31,10 @@ from . import _lib
 
 BLOCK_SIZE = 16
 MAX_QUERY_TOKENS = 16
-PA_F32, PA_BF16, PA_I8 = 0, 1, 2
-_DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+PA_F32, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3
+_DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
+                torch.float8_e4m3fn: PA_FP8}
+_QUANTISED = (torch.int8, torch.float8_e4m3fn)  # caches that carry per-token scales
 
 
 class PagedAttnError(RuntimeError):
@@ -110,8 +113,8 @@ def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=N
         raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
     if v.shape != k.shape or slot_mapping.shape != (T,):
         raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
-    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
-        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    if k_cache.dtype in _QUANTISED and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 or fp8 cache needs k_scale and v_scale")
     for sc in (k_scale, v_scale):
         if sc is not None and sc.shape != (NB, Hkv, BLOCK_SIZE):
             raise PagedAttnError("scales must be [num_blocks][num_kv_heads][16]")
@@ -222,8 +225,8 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
         raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
     if v.shape != k.shape or slot_mapping.shape != (T_tok,):
         raise PagedAttnError("k, v must be [T][Hkv][D] and slot_mapping [T]")
-    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
-        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    if k_cache.dtype in _QUANTISED and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 or fp8 cache needs k_scale and v_scale")
     Q, W = int(num_query_tokens), int(sliding_window)
     B, mcl, T, S, sched = _plan_sizes(context_lens, max_blocks_per_seq, max_context_len,
                                       split_tokens, sched, Q, W, (Hkv, D, k_cache.dtype))
@@ -244,8 +247,8 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_sca
         raise PagedAttnError("cache shape must be [num_blocks][num_kv_heads][16][head_dim]")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise PagedAttnError("block_tables must be [B][max_blocks], context_lens [B]")
-    if k_cache.dtype == torch.int8 and (k_scale is None or v_scale is None):
-        raise PagedAttnError("an int8 cache needs k_scale and v_scale")
+    if k_cache.dtype in _QUANTISED and (k_scale is None or v_scale is None):
+        raise PagedAttnError("an int8 or fp8 cache needs k_scale and v_scale")
     return (_dev(q, "q"), _code(q), B, Q, Hq, D, _dev(k_cache, "k_cache"),
             _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
             _dev(v_scale, "v_scale", torch.float32), _code(k_cache), NB, Hkv,

@@ -16,6 +16,9 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
+// Caches of 8-bit codes with per-(token, KV head) scales.
+bool quantised(int32_t cache_dtype) { return cache_dtype == PA_I8 || cache_dtype == PA_FP8; }
+
 int check_split_tokens(int32_t split_tokens) {
   if (split_tokens <= 0 || split_tokens % PA_BLOCK_SIZE != 0 || split_tokens > PA_MAX_SPLIT_TOKENS)
     return PA_ERR_SPLIT;
@@ -75,7 +78,8 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   switch (cache_dtype) {
     case PA_F32: elt = 4; break;
     case PA_BF16: elt = 2; break;
-    case PA_I8: elt = 1; break;
+    case PA_I8:
+    case PA_FP8: elt = 1; break;
     default: return 0;
   }
   if (head_dim != 64 && head_dim != 128) return 0;
@@ -121,12 +125,13 @@ int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *s
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (in_dtype != PA_F32 && in_dtype != PA_BF16) return PA_ERR_DTYPE;
-  if (cache_dtype != PA_I8 && cache_dtype != in_dtype) return PA_ERR_DTYPE;
+  if (cache_dtype != PA_I8 && cache_dtype != PA_FP8 && cache_dtype != in_dtype)
+    return PA_ERR_DTYPE;
   if (num_blocks > INT64_MAX / (PA_BLOCK_SIZE * (int64_t)num_kv_heads * head_dim * 4))
     return PA_ERR_SHAPE;
   if (num_tokens > 0) {
     if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
     if (misaligned16(k) || misaligned16(v) || misaligned16(k_cache) || misaligned16(v_cache))
       return PA_ERR_ALIGN;
   }
@@ -218,7 +223,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   if (num_blocks <= 0 || num_blocks > INT_MAX) return PA_ERR_SHAPE;
   const bool dt_ok = (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
                      (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
-                     ((q_dtype == PA_BF16 || q_dtype == PA_F32) && cache_dtype == PA_I8);
+                     ((q_dtype == PA_BF16 || q_dtype == PA_F32) && quantised(cache_dtype));
   if (!dt_ok) return PA_ERR_DTYPE;
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
@@ -233,7 +238,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !part_m || !part_l ||
       !part_acc || !sched)
     return PA_ERR_NULL;
-  if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
 
   pa::DecodeParams p{};
@@ -267,10 +272,14 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
     e = pa::decode_bf16_bf16(p, grid_splits, stream);
   else if (q_dtype == PA_F32 && cache_dtype == PA_F32)
     e = pa::decode_f32_f32(p, grid_splits, stream);
-  else if (q_dtype == PA_BF16)
+  else if (q_dtype == PA_BF16 && cache_dtype == PA_I8)
     e = pa::decode_bf16_i8(p, grid_splits, stream);
-  else
+  else if (cache_dtype == PA_I8)
     e = pa::decode_f32_i8(p, grid_splits, stream);
+  else if (q_dtype == PA_BF16)
+    e = pa::decode_bf16_fp8(p, grid_splits, stream);
+  else
+    e = pa::decode_f32_fp8(p, grid_splits, stream);
   return launch_status(e);
 }
 
@@ -305,7 +314,7 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
     return PA_ERR_SHAPE;
   if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
-  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_I8)
+  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && !quantised(cache_dtype))
     return PA_ERR_DTYPE;
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,

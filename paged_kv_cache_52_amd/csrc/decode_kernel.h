@@ -155,7 +155,7 @@ struct DecodeWave {
     for (int i = 0; i < S::NI; ++i)
       t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
                                                      kStreamPolicy);
-    if constexpr (CT == PA_I8) {
+    if constexpr (Quantised<CT>::value) {
       const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, kBlock * 4);
 #pragma unroll
       for (int i = 0; i < S::NI; ++i)
@@ -166,7 +166,7 @@ struct DecodeWave {
     for (int i = 0; i < S::NI; ++i)
       t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
                                                      kStreamPolicy);
-    if constexpr (CT == PA_I8) {
+    if constexpr (Quantised<CT>::value) {
       const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, kBlock * 4);
 #pragma unroll
       for (int i = 0; i < S::NI; ++i)
@@ -175,15 +175,26 @@ struct DecodeWave {
     }
   }
 
-  // 16 dims of an INT8 row chunk, widened to fp32.
-  __device__ __forceinline__ static void widen_i8(const u32x4 &w, float (&x)[16]) {
+  // 16 dims of an 8-bit row chunk (INT8 codes, or FP8 E4M3 codes decoded by
+  // v_cvt_pk_f32_fp8), widened to fp32.
+  __device__ __forceinline__ static void widen8(const u32x4 &w, float (&x)[16]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int32_t v = (int32_t)w[k];
-      x[4 * k + 0] = (float)((v << 24) >> 24);
-      x[4 * k + 1] = (float)((v << 16) >> 24);
-      x[4 * k + 2] = (float)((v << 8) >> 24);
-      x[4 * k + 3] = (float)(v >> 24);
+      if constexpr (CT == PA_FP8) {
+        const uint32_t wk = w[k];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wk, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wk, true);
+        x[4 * k + 0] = lo[0];
+        x[4 * k + 1] = lo[1];
+        x[4 * k + 2] = hi[0];
+        x[4 * k + 3] = hi[1];
+      } else {
+        const int32_t v = (int32_t)w[k];
+        x[4 * k + 0] = (float)((v << 24) >> 24);
+        x[4 * k + 1] = (float)((v << 16) >> 24);
+        x[4 * k + 2] = (float)((v << 8) >> 24);
+        x[4 * k + 3] = (float)(v >> 24);
+      }
     }
   }
 
@@ -221,9 +232,9 @@ struct DecodeWave {
           for (int e = 0; e < S::E; ++e) a = fmaf(qr[h][e], __uint_as_float(t.k[i][e]), a);
           z[i][h] = a;
         }
-      } else {  // INT8 codes; the per-token scale multiplies the finished sum
+      } else {  // 8-bit codes; the per-token scale multiplies the finished sum
         float x[16];
-        widen_i8(t.k[i], x);
+        widen8(t.k[i], x);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float a = 0.f;
@@ -243,7 +254,7 @@ struct DecodeWave {
 #pragma unroll
         for (int h = 0; h < G; ++h) z[i][h] *= scale_log2;
     }
-    if constexpr (CT == PA_I8) {
+    if constexpr (Quantised<CT>::value) {
 #pragma unroll
       for (int i = 0; i < S::NI; ++i)
 #pragma unroll
@@ -307,18 +318,20 @@ struct DecodeWave {
 #pragma unroll
         for (int e = 0; e < S::E; ++e) vf[e] = __uint_as_float(t.v[i][e]);
       } else {
-        widen_i8(t.v[i], vf);
+        widen8(t.v[i], vf);
       }
       float w[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) w[h] = pr[i][h];
-      if constexpr (CT == PA_I8) {
+      if constexpr (Quantised<CT>::value) {
         const float vs = valid[i] ? t.vs[i] : 0.f;  // a poisoned scale must not leak
 #pragma unroll
         for (int h = 0; h < G; ++h) w[h] *= vs;
-      } else if (need_mask && !valid[i]) {
+      }
+      // NaN * 0 would leak (an FP8 code can be NaN): select, not scale.
+      if (CT != PA_I8 && need_mask && !valid[i]) {
 #pragma unroll
-        for (int e = 0; e < S::E; ++e) vf[e] = 0.f;  // NaN * 0 would leak: select, not scale
+        for (int e = 0; e < S::E; ++e) vf[e] = 0.f;
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -359,16 +372,12 @@ struct DecodeWave {
 // head, and sum_t w_t x_t = sum_t w_t u_t - 128 sum_t w_t with w_t = p_t *
 // vscale_t; the per-token K scale multiplies the finished logit.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay below 2^8
 
 template <int CT, int D>
 struct MfmaEligible {
-  static constexpr bool value = (CT == PA_BF16 || CT == PA_I8) && D == 128;
+  static constexpr bool value = (CT == PA_BF16 || CT == PA_I8 || CT == PA_FP8) && D == 128;
 };
 
 template <int CT>
@@ -385,6 +394,8 @@ struct MfmaTile<PA_I8> {
   f32x4 ks;    // K scales of tokens 4g .. 4g+3
   f32x4 vs;    // V scales of tokens 4g .. 4g+3
 };
+template <>
+struct MfmaTile<PA_FP8> : MfmaTile<PA_I8> {};  // same layout, E4M3 codes
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2 v = {a, b};
@@ -395,6 +406,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 template <int K>
 __device__ __forceinline__ float ubyte_f32(uint32_t w) {
   return (float)((w >> (8 * K)) & 0xffu);
+}
+
+// E4M3 codes in bytes 0, 1 (HI = false) or 2, 3 (HI = true) of w as a bf16
+// pair (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, E4M3 fits bf16).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8pair_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // Biased INT8 codes (u = x + 128) of bytes 2h and 2h+1 of w, as a bf16 pair.
@@ -469,10 +487,17 @@ struct MfmaWave {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // 8 codes: dims 32g + 8i .. +8 = bytes 8i .. 8i+7 of the lane's 32.
-        const uint32_t w0 = t.k[i / 2][2 * (i % 2)] ^ 0x80808080u;
-        const uint32_t w1 = t.k[i / 2][2 * (i % 2) + 1] ^ 0x80808080u;
-        const u32x4 kb = {u8pair_to_bf16<0>(w0), u8pair_to_bf16<1>(w0), u8pair_to_bf16<0>(w1),
-                          u8pair_to_bf16<1>(w1)};
+        u32x4 kb;
+        if constexpr (CT == PA_I8) {
+          const uint32_t w0 = t.k[i / 2][2 * (i % 2)] ^ 0x80808080u;
+          const uint32_t w1 = t.k[i / 2][2 * (i % 2) + 1] ^ 0x80808080u;
+          kb = u32x4{u8pair_to_bf16<0>(w0), u8pair_to_bf16<1>(w0), u8pair_to_bf16<0>(w1),
+                     u8pair_to_bf16<1>(w1)};
+        } else {  // E4M3 values are exact in bf16
+          const uint32_t w0 = t.k[i / 2][2 * (i % 2)], w1 = t.k[i / 2][2 * (i % 2) + 1];
+          kb = u32x4{fp8pair_to_bf16<false>(w0), fp8pair_to_bf16<true>(w0),
+                     fp8pair_to_bf16<false>(w1), fp8pair_to_bf16<true>(w1)};
+        }
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb),
                                                     __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0,
                                                     0);
@@ -483,8 +508,10 @@ struct MfmaWave {
     for (int r = 0; r < 4; ++r) {
       if constexpr (CT == PA_BF16)
         z[r] = sc[r] * scale_log2;
-      else
+      else if constexpr (CT == PA_I8)
         z[r] = (sc[r] - qbias) * t.ks[r] * scale_log2;
+      else
+        z[r] = sc[r] * t.ks[r] * scale_log2;
     }
     if (need_mask) {  // uniform: a tile at an edge of some row's range
 #pragma unroll
@@ -497,6 +524,9 @@ struct MfmaWave {
           if (!used) t.v[r] = u32x4{0u, 0u, 0u, 0u};
         } else {
           if (!used) t.vs[r] = 0.f;
+          if constexpr (CT == PA_FP8) {  // a NaN code must not meet a zero weight
+            if (!used) t.v[r] = u32x2{0u, 0u};
+          }
         }
       }
     }
@@ -510,10 +540,10 @@ struct MfmaWave {
 #pragma unroll
     for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
     l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
-    if constexpr (CT == PA_I8) {
+    if constexpr (Quantised<CT>::value) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) pz[r] *= t.vs[r];
-      wsum += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+      if constexpr (CT == PA_I8) wsum += (pz[0] + pz[1]) + (pz[2] + pz[3]);
     }
     // P (INT8: the V-scaled weights) = hi + lo, both bf16.
     const uint32_t h01 = pack_bf16(pz[0], pz[1]), h23 = pack_bf16(pz[2], pz[3]);
@@ -521,10 +551,32 @@ struct MfmaWave {
     const uint32_t l23 = pack_bf16(pz[2] - bf16_lo(h23), pz[3] - bf16_hi(h23));
     const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
     const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+    // FP8: V bytes of rows (0, 1) and (2, 3) interleaved per column pair, so
+    // that one conversion yields a column's bf16 pair of two rows.
+    [[maybe_unused]] uint32_t x01[4], x23[4];
+    if constexpr (CT == PA_FP8) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        x01[2 * w] = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x05010400u);
+        x01[2 * w + 1] = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], 0x07030602u);
+        x23[2 * w] = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x05010400u);
+        x23[2 * w + 1] = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x07030602u);
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       uint32_t b01, b23;
-      if constexpr (CT == PA_BF16) {
+      if constexpr (CT == PA_FP8) {
+        // column jj = byte jj % 4 of word jj / 4; x*[jj / 2] holds columns
+        // 2(jj/2) and 2(jj/2) + 1 in its low and high halves.
+        if (jj & 1) {
+          b01 = fp8pair_to_bf16<true>(x01[jj >> 1]);
+          b23 = fp8pair_to_bf16<true>(x23[jj >> 1]);
+        } else {
+          b01 = fp8pair_to_bf16<false>(x01[jj >> 1]);
+          b23 = fp8pair_to_bf16<false>(x23[jj >> 1]);
+        }
+      } else if constexpr (CT == PA_BF16) {
         const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
         b01 = __builtin_amdgcn_perm(t.v[1][jj >> 1], t.v[0][jj >> 1], sel);
         b23 = __builtin_amdgcn_perm(t.v[3][jj >> 1], t.v[2][jj >> 1], sel);

@@ -1,7 +1,10 @@
 // KV write ("reshape and cache") kernels [AMD ATOM article, section 5.1;
 // LLM Primer ch. 8, 8.1]: each new token's K and V rows go to the physical slot
 // its slot_mapping entry names; an INT8 pool quantises per (token, KV head)
-// with one fp32 scale [EchoLLMServing notes, section 3].
+// with one fp32 scale [EchoLLMServing notes, section 3], and an FP8 pool
+// (OCP E4M3, the ATOM article's FP8 KV cache) likewise.
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 #include "plan_device.h"
@@ -27,16 +30,31 @@ __device__ __forceinline__ void kv_copy_thread(const WriteParams &p, int row_byt
   *(u32x4 *)((char *)p.v_cache + dst) = *(const u32x4 *)((const char *)p.v + src);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void kv_copy_kernel(const WriteParams p, int row_bytes) {
-  kv_copy_thread(p, row_bytes, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+// OCP E4M3 code of x: the nearest value (ties to the even mantissa) among
+// +-m * 2^-9 (subnormals, m < 8) and +-(8 + m) * 2^(e - 10) (e = 1 .. 15, not
+// e = 15 with m = 7, which is NaN); finite values beyond 448 saturate to +-448.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // m * 2^-9; m = 8 is 2^-6
+  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;         // a = 1.f * 2^e, e in [-6, 8]
+  int q = (int)rintf(a * __uint_as_float((uint32_t)(127 + 3 - e) << 23));  // 8 .. 16 eighths
+  if (q == 16) {
+    q = 8;
+    e += 1;
+  }
+  return sign | (uint32_t)(((e + 7) << 3) | (q - 8));
 }
 
-// INT8 quantiser: a group of D/8 lanes owns one (token, head) row, 8 values
-// per lane. absmax is combined across the group with DPP; the division by the
-// scale is IEEE fp32 (correctly rounded) and rintf rounds half to even.
-template <int IT, int D>
+// INT8 / FP8 quantiser: a group of D/8 lanes owns one (token, head) row, 8
+// values per lane. absmax is combined across the group with DPP; the scale is
+// absmax / 127 (INT8) or absmax / 448 (FP8), the division by it is IEEE fp32
+// (correctly rounded), and both roundings are to nearest, ties to even.
+template <int CT, int IT, int D>
 __device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, int part,
-                                             int8_t *dst, float *scale_dst, bool write_scale) {
+                                             uint8_t *dst, float *scale_dst, bool write_scale) {
   constexpr int LPG = D / 8;
   float x[8];
   if constexpr (IT == PA_BF16) {
@@ -60,16 +78,19 @@ __device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, i
 #pragma unroll
   for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
   a = group_max<LPG>(a);
-  const float sc = a / 127.0f;
+  const float sc = a / (CT == PA_FP8 ? 448.0f : 127.0f);
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    float r = 0.f;
+    uint32_t code = 0u;
     if (a != 0.f) {
-      r = rintf(x[k] / sc);
-      r = fminf(fmaxf(r, -127.f), 127.f);
+      if constexpr (CT == PA_FP8) {
+        code = e4m3_code(x[k] / sc);
+      } else {
+        const float r = fminf(fmaxf(rintf(x[k] / sc), -127.f), 127.f);
+        code = (uint32_t)((int32_t)r) & 0xffu;
+      }
     }
-    const uint32_t code = (uint32_t)((int32_t)r) & 0xffu;
     packed[k / 4] |= code << (8 * (k % 4));
   }
   u32x2 out;
@@ -79,7 +100,7 @@ __device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, i
   if (write_scale) *scale_dst = sc;
 }
 
-template <int IT, int D>
+template <int CT, int IT, int D>
 __device__ __forceinline__ void kv_quant_thread(const WriteParams &p, int64_t gid) {
   constexpr int LPG = D / 8;
   const int64_t total = p.num_tokens * p.num_kv_heads * LPG;
@@ -93,18 +114,34 @@ __device__ __forceinline__ void kv_quant_thread(const WriteParams &p, int64_t gi
   const int64_t b = slot / kBlock;
   const int o = (int)(slot - b * kBlock);
   const int64_t srow = (b * p.num_kv_heads + h) * kBlock + o;  // scale index
-  quantise_row<IT, D>(p.k, row, part, (int8_t *)p.k_cache + srow * D, p.k_scale + srow, part == 0);
-  quantise_row<IT, D>(p.v, row, part, (int8_t *)p.v_cache + srow * D, p.v_scale + srow, part == 0);
+  quantise_row<CT, IT, D>(p.k, row, part, (uint8_t *)p.k_cache + srow * D, p.k_scale + srow,
+                          part == 0);
+  quantise_row<CT, IT, D>(p.v, row, part, (uint8_t *)p.v_cache + srow * D, p.v_scale + srow,
+                          part == 0);
 }
 
-template <int IT, int D>
-__global__ __launch_bounds__(kPlanThreads) void kv_quant_kernel(const WriteParams p) {
-  kv_quant_thread<IT, D>(p, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+// Write variants: 0 copies; 1..4 quantise to INT8 and 5..8 to FP8, each for
+// ({bf16, fp32} input) x (head_dim {64, 128}).
+template <int VARIANT>
+__device__ __forceinline__ void write_variant(const WriteParams &w, int row_bytes, int64_t gid) {
+  constexpr int CT = VARIANT >= 5 ? PA_FP8 : PA_I8;
+  constexpr int V = VARIANT >= 5 ? VARIANT - 4 : VARIANT;
+  constexpr int IT = V <= 2 ? PA_BF16 : PA_F32;
+  constexpr int D = (V % 2) ? 64 : 128;
+  if constexpr (VARIANT == 0)
+    kv_copy_thread(w, row_bytes, gid);
+  else
+    kv_quant_thread<CT, IT, D>(w, gid);
+}
+
+template <int VARIANT>
+__global__ __launch_bounds__(kPlanThreads) void kv_write_kernel(const WriteParams p,
+                                                                int row_bytes) {
+  write_variant<VARIANT>(p, row_bytes, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // KV write and plan of one decode step in one launch (they do not depend on
-// each other): the last workgroup plans, the others write. Variant 0 copies,
-// variants 1..4 quantise ({bf16, fp32} input x head_dim {64, 128}).
+// each other): the last workgroup plans, the others write.
 template <int VARIANT>
 __global__ __launch_bounds__(kPlanThreads) void prepare_kernel(const WriteParams w,
                                                                const PlanParams pl,
@@ -113,12 +150,7 @@ __global__ __launch_bounds__(kPlanThreads) void prepare_kernel(const WriteParams
     plan_workgroup(pl);
     return;
   }
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if constexpr (VARIANT == 0) kv_copy_thread(w, row_bytes, gid);
-  if constexpr (VARIANT == 1) kv_quant_thread<PA_BF16, 64>(w, gid);
-  if constexpr (VARIANT == 2) kv_quant_thread<PA_BF16, 128>(w, gid);
-  if constexpr (VARIANT == 3) kv_quant_thread<PA_F32, 64>(w, gid);
-  if constexpr (VARIANT == 4) kv_quant_thread<PA_F32, 128>(w, gid);
+  write_variant<VARIANT>(w, row_bytes, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 namespace {
@@ -130,13 +162,14 @@ struct WriteShape {
 };
 
 WriteShape write_shape(const WriteParams &p) {
-  if (p.cache_dtype != PA_I8) {
+  if (p.cache_dtype != PA_I8 && p.cache_dtype != PA_FP8) {
     const int row_bytes = p.head_dim * (p.cache_dtype == PA_F32 ? 4 : 2);
     const int64_t total = p.num_tokens * p.num_kv_heads * (row_bytes / 16);
     return {0, row_bytes, (total + kPlanThreads - 1) / kPlanThreads};
   }
   const int64_t total = p.num_tokens * p.num_kv_heads * (p.head_dim / 8);
-  const int variant = (p.in_dtype == PA_BF16 ? 1 : 3) + (p.head_dim == 128 ? 1 : 0);
+  const int variant = (p.cache_dtype == PA_FP8 ? 4 : 0) + (p.in_dtype == PA_BF16 ? 1 : 3) +
+                      (p.head_dim == 64 ? 0 : 1);
   return {variant, 0, (total + kPlanThreads - 1) / kPlanThreads};
 }
 
@@ -145,12 +178,20 @@ WriteShape write_shape(const WriteParams &p) {
 hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream) {
   const WriteShape ws = write_shape(p);
   const dim3 grid((unsigned)ws.blocks), block(kPlanThreads);
+  auto go = [&](auto v) {
+    hipLaunchKernelGGL(kv_write_kernel<decltype(v)::value>, grid, block, 0, stream, p,
+                       ws.row_bytes);
+  };
   switch (ws.variant) {
-    case 0: hipLaunchKernelGGL(kv_copy_kernel, grid, block, 0, stream, p, ws.row_bytes); break;
-    case 1: hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 64>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((kv_quant_kernel<PA_BF16, 128>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 64>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((kv_quant_kernel<PA_F32, 128>), grid, block, 0, stream, p); break;
+    case 0: go(std::integral_constant<int, 0>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
   }
   return hipGetLastError();
 }
@@ -158,12 +199,20 @@ hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream) {
 hipError_t launch_prepare(const WriteParams &w, const PlanParams &pl, hipStream_t stream) {
   const WriteShape ws = write_shape(w);
   const dim3 grid((unsigned)(ws.blocks + 1)), block(kPlanThreads);
+  auto go = [&](auto v) {
+    hipLaunchKernelGGL(prepare_kernel<decltype(v)::value>, grid, block, 0, stream, w, pl,
+                       ws.row_bytes);
+  };
   switch (ws.variant) {
-    case 0: hipLaunchKernelGGL(prepare_kernel<0>, grid, block, 0, stream, w, pl, ws.row_bytes); break;
-    case 1: hipLaunchKernelGGL(prepare_kernel<1>, grid, block, 0, stream, w, pl, 0); break;
-    case 2: hipLaunchKernelGGL(prepare_kernel<2>, grid, block, 0, stream, w, pl, 0); break;
-    case 3: hipLaunchKernelGGL(prepare_kernel<3>, grid, block, 0, stream, w, pl, 0); break;
-    default: hipLaunchKernelGGL(prepare_kernel<4>, grid, block, 0, stream, w, pl, 0); break;
+    case 0: go(std::integral_constant<int, 0>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
   }
   return hipGetLastError();
 }

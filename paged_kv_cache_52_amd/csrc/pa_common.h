@@ -14,6 +14,10 @@ constexpr int kWave = 64;              // CDNA wavefront width
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -24,6 +28,13 @@ template <int DT> struct DtypeBytes;
 template <> struct DtypeBytes<PA_F32> { static constexpr int value = 4; };
 template <> struct DtypeBytes<PA_BF16> { static constexpr int value = 2; };
 template <> struct DtypeBytes<PA_I8> { static constexpr int value = 1; };
+template <> struct DtypeBytes<PA_FP8> { static constexpr int value = 1; };
+
+// Caches stored as 8-bit codes with a per-(token, KV head) fp32 scale.
+template <int CT>
+struct Quantised {
+  static constexpr bool value = CT == PA_I8 || CT == PA_FP8;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }

@@ -53,5 +53,7 @@ hipError_t decode_bf16_bf16(const DecodeParams &p, int grid_splits, hipStream_t 
 hipError_t decode_f32_f32(const DecodeParams &p, int grid_splits, hipStream_t s);
 hipError_t decode_bf16_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
 hipError_t decode_f32_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_bf16_fp8(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_f32_fp8(const DecodeParams &p, int grid_splits, hipStream_t s);
 
 }  // namespace pa

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_SPLIT, ERR_WS, ERR_ALIGN, ERR_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, FP8 = 0, 1, 2, 3
 FAKE = 0x10000       # non-null, 16-byte aligned, never dereferenced
 FAKE_ODD = 0x10008   # non-null, not 16-byte aligned
 
@@ -69,6 +69,7 @@ def test_default_split_tokens_is_valid(lib):
     (64, 8, 64, F32, 4096, 512),        # 64-dim fp32: 512 B per token, like bf16 x 128
     (64, 8, 128, F32, 4096, 256),
     (64, 8, 64, I8, 4096, 2048),
+    (128, 8, 128, FP8, 8192, 1024),     # FP8: same bytes per token as INT8
     (1, 8, 128, BF16, 4096, 64),        # 8 heads x 64 splits = 512 items < 1024: floor 64
     (2, 8, 128, BF16, 8192, 128),       # 16 heads x 64 splits = 1024 items
     (4, 2, 64, F32, 128, 64),
@@ -135,6 +136,9 @@ def test_kv_write_validation(lib):
     assert _write(lib, in_dtype=F32, cache_dtype=BF16) == ERR_DTYPE
     assert _write(lib, k=None) == ERR_NULL
     assert _write(lib, cache_dtype=I8) == ERR_NULL  # INT8 needs scales
+    assert _write(lib, cache_dtype=FP8) == ERR_NULL  # so does FP8
+    assert _write(lib, in_dtype=FP8, cache_dtype=FP8) == ERR_DTYPE
+    assert _write(lib, cache_dtype=4) == ERR_DTYPE
     assert _write(lib, kc=FAKE_ODD) == ERR_ALIGN
     assert _write(lib, T=0, k=None) == OK            # nothing to do, nothing enqueued
 
@@ -211,6 +215,9 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, sched=None) == ERR_NULL
     assert _partial(lib, B=65536) == ERR_SHAPE
     assert _partial(lib, cdt=I8) == ERR_NULL            # INT8 needs scales
+    assert _partial(lib, cdt=FP8) == ERR_NULL           # so does FP8
+    assert _partial(lib, qdt=FP8, cdt=FP8) == ERR_DTYPE
+    assert _partial(lib, qdt=F32, cdt=FP8) == ERR_NULL  # fp32 q on an FP8 cache is fine
     assert _partial(lib, q=FAKE_ODD) == ERR_ALIGN
     assert _partial(lib, B=0, q=None) == OK
 

@@ -34,6 +34,8 @@ def _np(t):
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
@@ -99,8 +101,9 @@ def _write_new_tokens(b, g):
         assert np.array_equal(_np(g.v_scale).view(np.uint32), vs.view(np.uint32))
 
 
-def _fill_int8(b, g):
-    """Fill the INT8 pool through the KV write on both sides; check bit-exact."""
+def _fill_quantised(b, g):
+    """Fill an INT8 / FP8 pool through the KV write on both sides; check
+    bit-exact."""
     kc, vc = _np(b.k_cache).copy(), _np(b.v_cache).copy()
     ks, vs = _np(b.k_scale).copy(), _np(b.v_scale).copy()
     oracle.kv_write(_np(b.fill_k), _np(b.fill_v), _np(b.fill_slots), kc, vc, ks, vs)
@@ -146,8 +149,10 @@ def test_kv_write_bit_exact(name, kw):
     assert not np.array_equal(_np(b.k_cache).view(np.uint8), before.view(np.uint8))
 
 
-def test_kv_write_int8_bit_exact_with_edge_rows():
-    print("[case] kv_write int8 edge rows", flush=True)
+@pytest.mark.parametrize("cache", ["int8", "fp8"])
+def test_kv_write_quantised_bit_exact_with_edge_rows(cache):
+    print(f"[case] kv_write {cache} edge rows", flush=True)
+    np_dt, t_dt = {"int8": (np.int8, torch.int8), "fp8": (np.uint8, torch.float8_e4m3fn)}[cache]
     rng = np.random.default_rng(3)
     D, Hkv, T = 128, 2, 64
     x = rng.normal(size=(T, Hkv, D)).astype(np.float32)
@@ -157,6 +162,8 @@ def test_kv_write_int8_bit_exact_with_edge_rows():
     x[2] *= 1e-36                        # subnormal scales
     x[3] *= 1e30                         # large values
     x[4, 1] = -7.0                       # constant row
+    x[5, 0, :4] = [448.0, 3.0, 1.5, -0.75]  # FP8 ties after scaling by 1
+    x[5, 0, 4:] = 0.0
     k = torch.from_numpy(x).to(torch.bfloat16)
     v = torch.from_numpy(-x[::-1].copy()).to(torch.bfloat16)
     for dt in (torch.bfloat16, torch.float32):
@@ -164,12 +171,12 @@ def test_kv_write_int8_bit_exact_with_edge_rows():
         NB = 6
         slots = torch.from_numpy(rng.permutation(NB * 16)[:T].astype(np.int64))
         slots[5] = -1
-        kc = np.zeros((NB, Hkv, 16, D), np.int8)
+        kc = np.zeros((NB, Hkv, 16, D), np_dt)
         vc = np.zeros_like(kc)
         ks = np.zeros((NB, Hkv, 16), np.float32)
         vs = np.zeros_like(ks)
         oracle.kv_write(_np(kk), _np(vv), _np(slots), kc, vc, ks, vs)
-        gk = torch.zeros(kc.shape, dtype=torch.int8, device="cuda")
+        gk = torch.zeros(kc.shape, dtype=t_dt, device="cuda")
         gv = torch.zeros_like(gk)
         gks = torch.zeros(ks.shape, dtype=torch.float32, device="cuda")
         gvs = torch.zeros_like(gks)
@@ -304,18 +311,20 @@ def test_gqa_group_sizes(Hq, Hkv, D, dtype):
     _check_out(out32, ref, _tol(b), f"gqa {Hq}/{Hkv}/{D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float32])
-def test_int8_decode_matches_oracle(qdt):
-    print(f"[case] int8 decode q={qdt}", flush=True)
-    b = workloads.make_batch("int8_kv", 111, "cpu", num_seqs=6, ctx_range=(1, 900),
-                             poison=True)
+@pytest.mark.parametrize("name", ["int8_kv", "fp8_kv"])
+def test_quantised_decode_matches_oracle(name, qdt, D):
+    print(f"[case] {name} decode q={qdt} D={D}", flush=True)
+    w = dataclasses.replace(workloads.WORKLOADS[name], head_dim=D)
+    b = workloads.make_batch(w, 111, "cpu", num_seqs=6, ctx_range=(1, 900), poison=True)
     b.q = b.q.to(qdt)
     g = _to(b, "cuda")
-    _fill_int8(b, g)
+    _fill_quantised(b, g)
     ref = _oracle_decode(b)
     for T in (16, 512):
         out32, _ = _gpu_fp32_out(g, T)
-        _check_out(out32, ref, TOL_BF16, f"int8/{T}")
+        _check_out(out32, ref, TOL_BF16, f"{name}/{T}")
 
 
 def test_identity_and_permuted_tables_agree():
@@ -389,14 +398,14 @@ def test_plan_is_shared_and_mismatch_is_ignored():
     assert bool((m == 7.0).all()) and bool((acc == 7.0).all())
 
 
-@pytest.mark.parametrize("name", ["llama8b_bf16", "int8_kv"])
+@pytest.mark.parametrize("name", ["llama8b_bf16", "int8_kv", "fp8_kv"])
 def test_prepare_equals_write_then_plan(name):
     """The fused write-and-plan launch gives the same pool bytes and the same
     plan as the two separate calls."""
     print(f"[case] prepare {name}", flush=True)
     b = workloads.make_batch(name, 171, "cpu", num_seqs=9, ctx_range=(1, 700))
     g1, g2 = _to(b, "cuda"), _to(b, "cuda")
-    if b.k_cache.dtype == torch.int8:
+    if b.fill_k is not None:
         for g in (g1, g2):
             pa().paged_kv_write(g.fill_k, g.fill_v, g.fill_slots, g.k_cache, g.v_cache,
                                 g.k_scale, g.v_scale)
@@ -472,8 +481,8 @@ def _sample_rows(B, Q, Hq, n, seed):
     return seqs, toks, heads
 
 
-@pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "shared_prefix_bf16",
-                                  "mtp4_llama8b_bf16", "swa4k_bf16"])
+@pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "fp8_kv",
+                                  "shared_prefix_bf16", "mtp4_llama8b_bf16", "swa4k_bf16"])
 def test_full_size_sampled_rows(name):
     """Full workload sizes, the launch the benchmark times (default split),
     checked on sampled (sequence, query token, head) rows; every output must
@@ -486,8 +495,8 @@ def test_full_size_sampled_rows(name):
         v = getattr(g, f)
         if isinstance(v, torch.Tensor):
             setattr(b, f, v.cpu())
-    if g.k_cache.dtype == torch.int8:
-        _fill_int8(b, g)
+    if g.fill_k is not None:
+        _fill_quantised(b, g)
     _write_new_tokens(b, g)
     out = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
                                  g.scale, k_scale=g.k_scale, v_scale=g.v_scale,
@@ -523,6 +532,8 @@ MTP_CASES = [
     ("int8_kv", 4, 0),
     ("int8_kv", 1, 50),
     ("int8_kv", 4, 50),
+    ("fp8_kv", 4, 0),
+    ("fp8_kv", 1, 50),
 ]
 
 
@@ -542,8 +553,8 @@ def test_query_tokens_and_windows_match_oracle(name, Q, W, split_tokens):
     print(f"[case] query rows {name} Q={Q} W={W} T={split_tokens}", flush=True)
     b = _mtp_batch(name, Q, W, 201, poison=True)
     g = _to(b, "cuda")
-    if b.k_cache.dtype == torch.int8:
-        _fill_int8(b, g)
+    if b.fill_k is not None:
+        _fill_quantised(b, g)
     _write_new_tokens(b, g)
     ref = _oracle_decode(b)
     assert np.isfinite(ref).all()
