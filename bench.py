@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("decode attention tokens/s and achieved KV-read GB/s (% of HBM peak), 1 MI355X")
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -67,6 +68,19 @@ def kernel_source_hash():
             h.update(open(os.path.join(csrc, f), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "pagedattn.h"), "rb").read())
     return h.hexdigest()[:16]
+
+
+def algorithmic_flops(b):
+    """Useful flops of the split kernel: per (query token, query head) and
+    attended token, q.k and p.v are 2 * head_dim multiply-adds each."""
+    import numpy as np
+    L = b.context_lens.to("cpu").numpy().astype(np.int64)
+    Q, W = b.query_tokens, b.window
+    pos = L[:, None] - Q + np.arange(Q)[None, :]          # query positions
+    lo = np.maximum(pos - W + 1, 0) if W > 0 else np.zeros_like(pos)
+    attended = np.clip(pos + 1 - lo, 0, None)
+    w = b.workload
+    return int(attended.sum()) * w.num_q_heads * 4 * w.head_dim
 
 
 def algorithmic_bytes(b):
@@ -187,7 +201,7 @@ def main():
     B, Hq, D = b.q.shape[0], b.q.shape[-2], b.q.shape[-1]
     Q, W = b.query_tokens, b.window
     mb = b.block_tables.shape[1]
-    T = args.split_tokens or pa.default_split_tokens(B, w.num_kv_heads, w.head_dim,
+    T = args.split_tokens or pa.default_split_tokens(B, Hq, w.num_kv_heads, w.head_dim,
                                                        b.k_cache.dtype, b.max_context_len, Q, W)
     S = pa.max_splits(min(b.max_context_len, mb * 16), T, Q, W)
     out = torch.empty_like(b.q)
@@ -259,7 +273,12 @@ def main():
     t_dec_b2b = d0.elapsed_time(d1) / args.steps
 
     kv_bytes, alg_bytes = algorithmic_bytes(b)
+    alg_flops = algorithmic_flops(b)
     dec_gbps = alg_bytes / (t_dec_b2b * 1e-3) / 1e9
+    dec_tflops = alg_flops / (t_dec_b2b * 1e-3) / 1e12
+    # The kernel's bound: matrix cores once its arithmetic intensity passes
+    # the ridge point of the two peaks (dense bf16 MFMA / HBM).
+    mfma_bound = alg_flops / alg_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
     counters = load_counters(w.name)
     traffic = None
@@ -299,14 +318,20 @@ def main():
                       "decode_split_back_to_back": t_dec_b2b},
         "kernel_us_p10_p50_p90": {k: [round(1e3 * pct(v, q), 2) for q in (0.1, 0.5, 0.9)]
                                   for k, v in per.items()},
-        "roofline": {
+        "roofline": ({
+            "kernel": "decode_split_kernel", "bound": "mfma", "achieved": dec_tflops,
+            "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": dec_tflops / MFMA_PEAK_TFLOPS,
+            "traffic": traffic, "algorithmic_flops_per_launch": alg_flops,
+            "algorithmic_bytes_per_launch": alg_bytes, "kv_read_gbps": dec_gbps,
+            "duration_us": 1e3 * t_dec_b2b,
+        } if mfma_bound else {
             "kernel": "decode_split_kernel", "bound": "hbm", "achieved": dec_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
             "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
-            "duration_us": 1e3 * t_dec_b2b,
+            "algorithmic_flops_per_launch": alg_flops, "duration_us": 1e3 * t_dec_b2b,
             "read_probe_gbps": probe_gbps,
             "frac_of_read_probe": dec_gbps / probe_gbps if probe_gbps else None,
-        },
+        }),
         "wall_s_timed": wall,
     }
     if args.copy_probe_mib:

@@ -32,7 +32,7 @@
  *   - Token t of sequence s lives in block block_tables[s][t / 16], row t % 16.
  *     A slot is block * 16 + row.
  *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
- *   - Query tokens: each sequence carries Q = num_query_tokens (1 to 16) query
+ *   - Query tokens: each sequence carries Q = num_query_tokens (1 to 4096) query
  *     tokens, its last Q positions: query token i sits at p = L - Q + i
  *     (L = context_lens[s], the new tokens already written) and attends the
  *     tokens t <= p (causal among the new tokens). With a sliding window of
@@ -40,7 +40,9 @@
  *     recent positions, its own included); W = 0 means no window. A query
  *     token with p < 0, or a sequence with L == 0, gives a zero output.
  *     q and out are [num_seqs][Q][num_q_heads][head_dim] (for Q = 1 the same
- *     memory as [num_seqs][num_q_heads][head_dim]).
+ *     memory as [num_seqs][num_q_heads][head_dim]). Q = 1 is a decode step,
+ *     Q = mtp_k + 1 an MTP verification step, a larger Q a chunk of prefill
+ *     over the cache.
  *   - Logits are scale * q.k; softmax uses the natural exponent over the
  *     tokens a query token attends.
  *   - Splits cover [base, L), base = 16 * floor(max(0, L - Q - W + 1) / 16)
@@ -84,7 +86,7 @@ extern "C" {
 #define PA_BLOCK_SIZE 16
 #define PA_MAX_SPLIT_TOKENS 4096
 #define PA_MAX_SEQS 65535
-#define PA_MAX_QUERY_TOKENS 16
+#define PA_MAX_QUERY_TOKENS 4096
 
 /* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
  * NaN, largest finite 448). */
@@ -123,13 +125,15 @@ int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t
  * the context length, one split per 512 tokens in the notes' setting].
  * T starts at 256 KiB of K and V per (split, KV head), i.e. 262144 /
  * (2 * head_dim * element bytes): 512 tokens for a 16-bit 128-dim cache, 1024
- * for an INT8 one, capped at 4096. It is then halved, down to 64, while
- * num_seqs * num_kv_heads * pa_max_splits(max_context_len, Q, W, T) is below
- * 1024 work items (small batches still fill the device). Returns 0 for a
- * head_dim other than 64 or 128, an unknown cache_dtype or bad Q / W.
- * Host-only arithmetic. */
-int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t cache_dtype, int32_t max_context_len,
+ * for an INT8 one, capped at 4096. With items = num_seqs * num_kv_heads *
+ * ceil(Q * g / 64) * pa_max_splits(max_context_len, Q, W, T) (g = num_q_heads /
+ * num_kv_heads): T is halved, down to 64, while items < 1024 (small batches
+ * still fill the device); with more than 64 query rows per KV head it is then
+ * doubled, up to 4096, while items stay >= 1024 (fewer partials to write).
+ * Returns 0 for a head_dim other than 64 or 128, an unknown cache_dtype, bad
+ * head counts or bad Q / W. Host-only arithmetic. */
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t cache_dtype, int32_t max_context_len,
                                 int32_t num_query_tokens, int32_t sliding_window);
 
 /* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
@@ -191,8 +195,8 @@ int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_b
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
  * depend on each other, so one kernel does both (its last workgroup plans, the
  * others write). Arguments, layouts and errors are those of the two calls
- * (split_tokens = 0 here picks pa_default_split_tokens() for this cache); the
- * results are identical to calling them in turn. Serves the start of a decode
+ * (split_tokens is required, as for the plan); the results are identical to
+ * calling them in turn. Serves the start of a decode
  * step, where the new tokens (num_seqs * Q of them with several query tokens)
  * are written and the batch's splits are listed.
  */
@@ -229,7 +233,8 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
  *   max_splits        leading stride of the partials;
  *                     >= pa_max_splits(max_context_len, Q, W, T)
  *   part_m, part_l    [num_seqs][num_query_tokens][num_q_heads][max_splits] fp32
- *   part_acc          [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim] fp32
+ *   part_acc          [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim] fp32,
+ *                     16-byte aligned
  *   sched             the plan (read only)
  * head_dim must be 64 or 128, num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16,
  * num_query_tokens 1 .. PA_MAX_QUERY_TOKENS and num_seqs at most PA_MAX_SEQS.

@@ -30,7 +30,7 @@ import torch
 from . import _lib
 
 BLOCK_SIZE = 16
-MAX_QUERY_TOKENS = 16
+MAX_QUERY_TOKENS = 4096
 PA_F32, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3
 _DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
                 torch.float8_e4m3fn: PA_FP8}
@@ -82,16 +82,16 @@ def max_splits(max_context_len: int, split_tokens: int, num_query_tokens: int = 
                                          int(sliding_window), int(split_tokens)))
 
 
-def default_split_tokens(num_seqs: int, num_kv_heads: int, head_dim: int, cache_dtype,
-                         max_context_len: int, num_query_tokens: int = 1,
+def default_split_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                         cache_dtype, max_context_len: int, num_query_tokens: int = 1,
                          sliding_window: int = 0) -> int:
     """Split size the library picks for split_tokens=None (cache_dtype: a torch
     dtype or a PA_* code)."""
     code = _DTYPE_CODES.get(cache_dtype, cache_dtype)
     if not isinstance(code, int):
         raise PagedAttnError(f"unsupported cache dtype {cache_dtype}")
-    return int(_lib.load().pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, code,
-                                                   max_context_len, num_query_tokens,
+    return int(_lib.load().pa_default_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                   code, max_context_len, num_query_tokens,
                                                    sliding_window))
 
 
@@ -181,14 +181,15 @@ def _max_len(context_lens, max_context_len):
 
 def _plan_sizes(context_lens, max_blocks_per_seq, max_context_len, split_tokens, sched, Q, W,
                 cache=None):
-    """cache = (num_kv_heads, head_dim, cache dtype) picks the default split
-    size when split_tokens is None; without it split_tokens is required."""
+    """cache = (num_q_heads, num_kv_heads, head_dim, cache dtype) picks the
+    default split size when split_tokens is None; without it split_tokens is
+    required."""
     B = context_lens.shape[0]
     mcl = _max_len(context_lens, max_context_len)
     if split_tokens:
         T = int(split_tokens)
     elif cache is not None:
-        T = default_split_tokens(B, cache[0], cache[1], cache[2], mcl, Q, W)
+        T = default_split_tokens(B, cache[0], cache[1], cache[2], cache[3], mcl, Q, W)
     else:
         raise PagedAttnError("paged_attn_plan needs split_tokens (see default_split_tokens)")
     S = max(1, max_splits(min(mcl, int(max_blocks_per_seq) * BLOCK_SIZE), T, Q, W))
@@ -216,9 +217,10 @@ def paged_attn_plan(context_lens, max_blocks_per_seq: int, *, max_context_len=No
 def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
                          max_blocks_per_seq: int, k_scale=None, v_scale=None, *,
                          max_context_len=None, split_tokens=None, num_query_tokens: int = 1,
-                         sliding_window: int = 0,
+                         sliding_window: int = 0, num_q_heads: Optional[int] = None,
                          sched: Optional[torch.Tensor] = None) -> Plan:
-    """paged_kv_write + paged_attn_plan in one launch; returns the plan."""
+    """paged_kv_write + paged_attn_plan in one launch; returns the plan.
+    Without split_tokens the default is taken for num_q_heads query heads."""
     T_tok, Hkv, D = k.shape
     NB = k_cache.shape[0]
     if k_cache.shape != (NB, Hkv, BLOCK_SIZE, D) or v_cache.shape != k_cache.shape:
@@ -228,8 +230,9 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
     if k_cache.dtype in _QUANTISED and (k_scale is None or v_scale is None):
         raise PagedAttnError("an int8 or fp8 cache needs k_scale and v_scale")
     Q, W = int(num_query_tokens), int(sliding_window)
+    cache = None if num_q_heads is None else (int(num_q_heads), Hkv, D, k_cache.dtype)
     B, mcl, T, S, sched = _plan_sizes(context_lens, max_blocks_per_seq, max_context_len,
-                                      split_tokens, sched, Q, W, (Hkv, D, k_cache.dtype))
+                                      split_tokens, sched, Q, W, cache)
     _check(_lib.load().paged_decode_prepare(
         _dev(k, "k"), _dev(v, "v", k.dtype), _code(k),
         _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
@@ -271,7 +274,7 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
     if plan is None:
         plan = paged_attn_plan(context_lens, mb, max_context_len=max_context_len,
                                split_tokens=split_tokens, num_query_tokens=Q, sliding_window=W,
-                               _cache=(Hkv, D, k_cache.dtype))
+                               _cache=(Hq, Hkv, D, k_cache.dtype))
     elif (plan.max_blocks_per_seq != mb or plan.context_lens is not context_lens or
           (split_tokens and int(split_tokens) != plan.split_tokens) or
           (max_context_len is not None and int(max_context_len) != plan.max_context_len) or
@@ -330,7 +333,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     mcl = _max_len(context_lens, max_context_len)
     mb = block_tables.shape[1]
     T = (int(split_tokens) if split_tokens else
-         default_split_tokens(B, k_cache.shape[1], D, k_cache.dtype, mcl, Q, W))
+         default_split_tokens(B, Hq, k_cache.shape[1], D, k_cache.dtype, mcl, Q, W))
     need = workspace_bytes(B, Hq, D, max(1, max_splits(min(mcl, mb * BLOCK_SIZE), T, Q, W)), Q)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

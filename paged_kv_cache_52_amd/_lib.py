@@ -21,7 +21,7 @@ SIGNATURES = {
     "pa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_num_splits": (_I32, [_I32, _I32]),
     "pa_max_splits": (_I32, [_I32, _I32, _I32, _I32]),
-    "pa_default_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_default_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_sched_bytes": (_SZ, [_I32, _I32]),
     "pa_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_kv_write": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _I64,

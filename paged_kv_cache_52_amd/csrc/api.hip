@@ -71,8 +71,8 @@ int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t
                        split_tokens);
 }
 
-int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t cache_dtype, int32_t max_context_len,
+int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t cache_dtype, int32_t max_context_len,
                                 int32_t num_query_tokens, int32_t sliding_window) {
   int elt;
   switch (cache_dtype) {
@@ -84,17 +84,24 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   }
   if (head_dim != 64 && head_dim != 128) return 0;
   if (bad_query_shape(num_query_tokens, sliding_window)) return 0;
+  if (num_kv_heads <= 0 || num_q_heads < num_kv_heads) return 0;
   // 256 KiB of K and V codes per (split, KV head): 512 tokens of a 16-bit
   // 128-dim cache, 1024 of an INT8 one.
   const int64_t kv_bytes_per_token = 2LL * head_dim * elt;
   int32_t t = (int32_t)std::min<int64_t>(PA_MAX_SPLIT_TOKENS, (256 << 10) / kv_bytes_per_token);
-  // Halve while the batch has too few (split, KV head) work items to fill the
-  // device (a workgroup per item, 256 compute units).
-  const int64_t heads = (int64_t)std::max(num_seqs, 0) * std::max(num_kv_heads, 0);
-  while (t > kMinDefaultSplit &&
-         heads * pa_max_splits(max_context_len, num_query_tokens, sliding_window, t) <
-             kMinWorkItems)
-    t /= 2;
+  // Work items: (split, KV head, set of up to 64 query rows); a decode step
+  // has one row set per KV head, a prefill chunk many.
+  const int64_t rows = (int64_t)num_query_tokens * (num_q_heads / num_kv_heads);
+  const int64_t per_split = (int64_t)std::max(num_seqs, 0) * num_kv_heads * ((rows + 63) / 64);
+  auto items = [&](int32_t tt) {
+    return per_split * pa_max_splits(max_context_len, num_query_tokens, sliding_window, tt);
+  };
+  // Halve while the batch has too few work items to fill the device (a
+  // workgroup per item, 256 compute units); with many query rows, double
+  // while it keeps enough (longer splits write fewer partials).
+  while (t > kMinDefaultSplit && items(t) < kMinWorkItems) t /= 2;
+  if (rows > 64)
+    while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kMinWorkItems) t *= 2;
   return t;
 }
 
@@ -193,9 +200,6 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
                        v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK) return st;
-  if (split_tokens == 0)
-    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len, num_query_tokens, sliding_window);
   st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, num_query_tokens,
                   sliding_window, split_tokens, sched, &pl);
   if (st != PA_OK) return st;
@@ -226,8 +230,9 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                      ((q_dtype == PA_BF16 || q_dtype == PA_F32) && quantised(cache_dtype));
   if (!dt_ok) return PA_ERR_DTYPE;
   if (split_tokens == 0)
-    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len, num_query_tokens, sliding_window);
+    split_tokens = pa_default_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           cache_dtype, max_context_len, num_query_tokens,
+                                           sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   // Splits of the longest range any sequence can have under the clamped bound.
   const int32_t grid_splits =
@@ -239,7 +244,8 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
       !part_acc || !sched)
     return PA_ERR_NULL;
   if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
-  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(part_acc))
+    return PA_ERR_ALIGN;
 
   pa::DecodeParams p{};
   p.q = q;
@@ -310,15 +316,16 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       int32_t sliding_window, float scale, int32_t split_tokens, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || max_blocks_per_seq <= 0)
+      num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0)
     return PA_ERR_SHAPE;
   if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && !quantised(cache_dtype))
     return PA_ERR_DTYPE;
   if (split_tokens == 0)
-    split_tokens = pa_default_split_tokens(num_seqs, num_kv_heads, head_dim, cache_dtype,
-                                           max_context_len, num_query_tokens, sliding_window);
+    split_tokens = pa_default_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           cache_dtype, max_context_len, num_query_tokens,
+                                           sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
                                    num_query_tokens, sliding_window, split_tokens);

@@ -88,16 +88,11 @@ struct RowRanges {
   }
 };
 
-// Tiles a wave keeps in flight beyond the one it is consuming (0 or 1).
 // Software pipeline of the MFMA engine: 1 keeps the next tile's loads in
 // flight while the current tile is consumed.
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 0
 #endif
-#ifndef PA_PREFETCH
-#define PA_PREFETCH 0
-#endif
-constexpr int kPrefetch = PA_PREFETCH;
 
 // Layout of the scheduling scratch written by the plan kernel:
 //   [0] number of splits of the batch
@@ -142,6 +137,7 @@ struct DecodeWave {
   // Tile loads go through buffer descriptors built per tile in SGPRs: the
   // lane offset stays a 32-bit VGPR (no 64-bit address pairs), and the record
   // count is the tile size, so an offset outside the tile reads zeros.
+  template <int POL>
   __device__ __forceinline__ void load_tile(Tile<S> &t, const DecodeParams &p, int blk, int kvh,
                                             int lane_off, int scale_off) {
     const int64_t tile = (int64_t)blk * p.num_kv_heads + kvh;
@@ -154,7 +150,7 @@ struct DecodeWave {
 #pragma unroll
     for (int i = 0; i < S::NI; ++i)
       t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
-                                                     kStreamPolicy);
+                                                     POL);
     if constexpr (Quantised<CT>::value) {
       const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, kBlock * 4);
 #pragma unroll
@@ -165,7 +161,7 @@ struct DecodeWave {
 #pragma unroll
     for (int i = 0; i < S::NI; ++i)
       t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + i * S::RPI * S::ROW_BYTES, 0,
-                                                     kStreamPolicy);
+                                                     POL);
     if constexpr (Quantised<CT>::value) {
       const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, kBlock * 4);
 #pragma unroll
@@ -442,6 +438,7 @@ struct MfmaWave {
 
   // Loads one tile. With live == false the descriptors have size 0: every
   // load is out of range, returns zeros and reads no memory.
+  template <int POL>
   __device__ __forceinline__ void load_tile(MfmaTile<CT> &t, const DecodeParams &p, int blk,
                                             int kvh, int koff, int voff, int soff,
                                             bool live = true) {
@@ -452,21 +449,21 @@ struct MfmaWave {
     if constexpr (CT == PA_BF16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * i, 0, kStreamPolicy);
+        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * i, 0, POL);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, kStreamPolicy);
+        t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + ROW * i, 0, POL);
     } else {
       const int sb = live ? kBlock * 4 : 0;
       const __amdgpu_buffer_rsrc_t ksr = make_rsrc(p.k_scale + tile * kBlock, sb);
       const __amdgpu_buffer_rsrc_t vsr = make_rsrc(p.v_scale + tile * kBlock, sb);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16 * i, 0, kStreamPolicy);
+        t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16 * i, 0, POL);
       t.ks = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ksr, soff, 0, 0));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        t.v[i] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + ROW * i, 0, kStreamPolicy);
+        t.v[i] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + ROW * i, 0, POL);
       t.vs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vsr, soff, 0, 0));
     }
   }
@@ -617,7 +614,7 @@ struct MfmaWave {
 // Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split (tile n
 // starts at token (b0 + n) * 16); leaves the wave's (m, l, acc) for the rows
 // R0 .. R0 + nrows - 1 in LDS row `wave`.
-template <int QT, int CT, int D, int G, int NW>
+template <int QT, int CT, int D, int G, int NW, int POL>
 __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int R0,
                                                int nrows, const RowRanges &rr, int b0, int wb0,
                                                int wb1, int lane, int wave,
@@ -657,43 +654,47 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   st.l = 0.f;
   st.wsum = 0.f;
 
-  int my_id = 0;
-  if (lane < wb1 - wb0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
   const int last_block = (int)(p.num_blocks - 1);
   const int koff = CT == PA_BF16 ? c * Wv::ROW + 16 * g : c * Wv::ROW + 32 * g;
   const int voff = 4 * g * Wv::ROW + 8 * Wv::ELT * c;
   const int soff = 16 * g;  // scales of tokens 4g .. 4g+3
-  // Physical block of tile n of the wave (clamped: a corrupt table entry reads
-  // a wrong but existing block instead of faulting).
-  auto block_of = [&](int n) {
-    return min(max(__builtin_amdgcn_readlane(my_id, min(n - wb0, kWave - 1)), 0), last_block);
-  };
   auto eat = [&](MfmaTile<CT> &t, int n) {
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
   };
+  // Tiles in chunks of 64: the chunk's physical block ids sit one per lane.
+  for (int c0 = wb0; c0 < wb1; c0 += kWave) {
+    const int c1 = min(wb1, c0 + kWave);
+    int my_id = 0;
+    if (lane < c1 - c0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+    // Physical block of tile n (clamped: a corrupt table entry reads a wrong
+    // but existing block instead of faulting).
+    auto block_of = [&](int n) {
+      return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0), last_block);
+    };
 #if PA_MFMA_PREFETCH
-  // Two tiles in flight: tile n + 1 is requested before tile n is consumed.
-  // The look-ahead load is unconditional (a dead one reads nothing), so the
-  // wait before each consume is the same on every path.
-  MfmaTile<CT> ta, tb;
-  st.load_tile(ta, p, block_of(wb0), kvh, koff, voff, soff, wb0 < wb1);
-  for (int n = wb0; n < wb1; n += 2) {
-    st.load_tile(tb, p, block_of(n + 1), kvh, koff, voff, soff, n + 1 < wb1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead ahead of the wait
-    eat(ta, n);
-    if (n + 1 >= wb1) break;
-    st.load_tile(ta, p, block_of(n + 2), kvh, koff, voff, soff, n + 2 < wb1);
-    __builtin_amdgcn_sched_barrier(0);
-    eat(tb, n + 1);
-  }
+    // Two tiles in flight: tile n + 1 is requested before tile n is consumed.
+    // The look-ahead load is unconditional (a dead one reads nothing), so the
+    // wait before each consume is the same on every path.
+    MfmaTile<CT> ta, tb;
+    st.template load_tile<POL>(ta, p, block_of(c0), kvh, koff, voff, soff, c0 < c1);
+    for (int n = c0; n < c1; n += 2) {
+      st.template load_tile<POL>(tb, p, block_of(n + 1), kvh, koff, voff, soff, n + 1 < c1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead ahead of the wait
+      eat(ta, n);
+      if (n + 1 >= c1) break;
+      st.template load_tile<POL>(ta, p, block_of(n + 2), kvh, koff, voff, soff, n + 2 < c1);
+      __builtin_amdgcn_sched_barrier(0);
+      eat(tb, n + 1);
+    }
 #else
-  MfmaTile<CT> t;
-  for (int n = wb0; n < wb1; ++n) {
-    st.load_tile(t, p, block_of(n), kvh, koff, voff, soff);
-    eat(t, n);
-  }
+    MfmaTile<CT> t;
+    for (int n = c0; n < c1; ++n) {
+      st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
+      eat(t, n);
+    }
 #endif
+  }
   // Renormalise to the true max (every lane takes part: rescale reads other
   // lanes' factors), then sum l over the four lane groups.
   st.rescale(fmaxf(st.mtrue, st.m), g);
@@ -725,7 +726,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
 }
 
 // Per-wave pass of the VALU engine (every dtype and head_dim); same contract.
-template <int QT, int CT, int D, int G, int NW>
+template <int QT, int CT, int D, int G, int NW, int POL>
 __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int kvh, int R0,
                                                int nrows, const RowRanges &rr, int b0, int wb0,
                                                int wb1, int lane, int wave,
@@ -780,46 +781,23 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
     }
   }
 
-  // Physical block ids of this wave's blocks, one per lane (per <= 64).
-  int my_id = 0;
-  if (lane < wb1 - wb0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + wb0 + lane];
   const int last_block = (int)(p.num_blocks - 1);  // the host checks 0 < num_blocks < 2^31
-  auto block_id = [&](int n) {
-    int b = __builtin_amdgcn_readlane(my_id, n - wb0);
-    return min(max(b, 0), last_block);
-  };
   auto eat = [&](const Tile<S> &t, int n) {
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, lane, p.scale_log2);
   };
-
   const int lane_off = (lane / S::LPR) * S::ROW_BYTES + (lane % S::LPR) * 16;
   const int scale_off = (lane / S::LPR) * 4;
-  // Double-buffered stream: tile n+1 is in flight while tile n is consumed.
-  // The steady-state loop issues its loads unconditionally so that the
-  // compiler's memory-counter waits only cover the tile being consumed; the
-  // last one or two tiles are peeled.
-  Tile<S> ta, tb;
-  if constexpr (kPrefetch == 0) {
-    for (int n = wb0; n < wb1; ++n) {
-      st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
-      eat(ta, n);
-    }
-  } else if (wb0 < wb1) {
-    int n = wb0;
-    st.load_tile(ta, p, block_id(n), kvh, lane_off, scale_off);
-    for (; n + 2 < wb1; n += 2) {
-      st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
-      eat(ta, n);
-      st.load_tile(ta, p, block_id(n + 2), kvh, lane_off, scale_off);
-      eat(tb, n + 1);
-    }
-    if (n + 1 < wb1) {
-      st.load_tile(tb, p, block_id(n + 1), kvh, lane_off, scale_off);
-      eat(ta, n);
-      eat(tb, n + 1);
-    } else {
-      eat(ta, n);
+  // Tiles in chunks of 64: the chunk's physical block ids sit one per lane.
+  Tile<S> t;
+  for (int c0 = wb0; c0 < wb1; c0 += kWave) {
+    const int c1 = min(wb1, c0 + kWave);
+    int my_id = 0;
+    if (lane < c1 - c0) my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+    for (int n = c0; n < c1; ++n) {
+      const int blk = min(max(__builtin_amdgcn_readlane(my_id, n - c0), 0), last_block);
+      st.template load_tile<POL>(t, p, blk, kvh, lane_off, scale_off);
+      eat(t, n);
     }
   }
 
@@ -848,15 +826,20 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   }
 }
 
-// One work item: split j of sequence s for KV head kvh, row group hg (rows
-// hg*G .. of the Q*g rows of the KV head). The NW waves of the workgroup share
-// the split's tiles, merge their states in LDS and write the split's partials.
-// Contains one workgroup barrier.
-template <int QT, int CT, int D, int G, int NW>
+// One work item: split j of sequence s for KV head kvh and RW row groups of
+// G rows (the quad-th set of RW among the Q*g rows of the KV head). The NW
+// waves split into RW row groups of TW = NW / RW waves: the TW waves of a row
+// group divide the tiles of the split that its rows reach, and merge their
+// states in LDS; different row groups read the same tiles at about the same
+// time (with RW > 1 they are loaded through the caches, not streamed) and
+// write their own partials. Contains two workgroup barriers.
+template <int QT, int CT, int D, int G, int NW, int RW>
 __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
-                                              int kvh, int hg, int lane, int wave,
+                                              int kvh, int quad, int lane, int wave,
                                               float (&sm_m)[NW][G],
                                               float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
+  constexpr int TW = NW / RW;                        // waves per row group
+  constexpr int POL = RW > 1 ? 0 : kStreamPolicy;    // shared tiles stay cached
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
   const int L = max(0, min(len, lmax));
@@ -866,41 +849,71 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   const int t0 = base + j * p.split_tokens;  // a multiple of 16
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
-  const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;
-  const int per = (nb + NW - 1) / NW;
-  const int wb0 = min(nb, wave * per);
-  const int wb1 = min(nb, wb0 + per);
-  const int R0 = hg * G;
-  const int nrows = min(G, Q * p.group - R0);
-  const RowRanges rr = RowRanges::make(L, Q, W, p.group, R0, nrows);
-
+  const int rg = wave / TW, tp = wave % TW;  // this wave's row group and tile share
+  const int rows = Q * p.group;
+  const int R0 = (quad * RW + rg) * G;
+  const int nrows = min(G, rows - R0);       // <= 0: a padding row group (no rows)
+  // Tiles of the split the row group's rows reach: tokens [ta, tz].
+  RowRanges rr{};
+  int wb0 = 0, wb1 = 0;
+  if (nrows > 0) {
+    rr = RowRanges::make(L, Q, W, p.group, R0, nrows);
+    const int ta = max(t0, rr.ulo), tz = min(t1 - 1, rr.uhi);
+    if (tz >= ta) {
+      const int first = (ta - t0) / kBlock, count = (tz - t0) / kBlock - first + 1;
+      const int per = (count + TW - 1) / TW;
+      wb0 = first + min(count, tp * per);
+      wb1 = first + min(count, tp * per + per);
+    }
+  }
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value)
-    wave_pass_mfma<QT, CT, D, G, NW>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave, sm_m,
-                                     sm_l, sm_acc);
+    wave_pass_mfma<QT, CT, D, G, NW, POL>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+                                          sm_m, sm_l, sm_acc);
   else
-    wave_pass_valu<QT, CT, D, G, NW>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave, sm_m,
-                                     sm_l, sm_acc);
+    wave_pass_valu<QT, CT, D, G, NW, POL>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+                                          sm_m, sm_l, sm_acc);
   __syncthreads();
 
-  // Merge the waves and write the split's partials.
-  for (int idx = threadIdx.x; idx < nrows * D; idx += NW * kWave) {
-    const int h = idx / D, d = idx % D;
-    float M = sm_m[0][h];
+  // Merge the TW waves of each row group and write the split's partials: one
+  // thread per row finds the row's common max, turns sm_m into the waves'
+  // factors 2^(m_w - M) and writes (m, l); then all threads sum the rows'
+  // dims, four per thread.
+  auto rows_of = [&](int g) { return min(G, rows - (quad * RW + g) * G); };
+  if (threadIdx.x < RW * G) {
+    const int g = threadIdx.x / G, h = threadIdx.x % G;
+    if (h < rows_of(g)) {
+      const int w0 = g * TW;
+      float M = sm_m[w0][h];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float a = 0.f, lsum = 0.f;
+      for (int w = 1; w < TW; ++w) M = fmaxf(M, sm_m[w0 + w][h]);
+      float lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(sm_m[w][h] - M);
-      a = fmaf(f, sm_acc[w][h][d], a);
-      lsum = fmaf(f, sm_l[w][h], lsum);
-    }
-    const int64_t row = query_row(p, s, kvh, R0 + h) * p.max_splits + j;
-    p.part_acc[row * D + d] = a;
-    if (d == 0) {
+      for (int w = 0; w < TW; ++w) {
+        const float f = fast_exp2(sm_m[w0 + w][h] - M);
+        sm_m[w0 + w][h] = f;
+        lsum = fmaf(f, sm_l[w0 + w][h], lsum);
+      }
+      const int64_t row = query_row(p, s, kvh, (quad * RW + g) * G + h) * p.max_splits + j;
       p.part_l[row] = lsum;
       p.part_m[row] = lsum > 0.f ? M * kLn2 : -INFINITY;
     }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < RW * G * (D / 4); idx += NW * kWave) {
+    const int g = idx / (G * (D / 4));
+    const int h = idx / (D / 4) % G, d = (idx % (D / 4)) * 4;
+    if (h >= rows_of(g)) continue;
+    const int w0 = g * TW;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < TW; ++w) {
+      const float f = sm_m[w0 + w][h];
+      const f32x4 v = *(const f32x4 *)&sm_acc[w0 + w][h][d];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = fmaf(f, v[e], a[e]);
+    }
+    const int64_t row = query_row(p, s, kvh, (quad * RW + g) * G + h) * p.max_splits + j;
+    *(f32x4 *)(p.part_acc + row * D + d) = a;
   }
 }
 
@@ -923,12 +936,12 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 #define PA_OCCUPANCY_ATTR
 #endif
 
-template <int QT, int CT, int D, int G, int NW>
+template <int QT, int CT, int D, int G, int NW, int RW>
 __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_kernel(
     const DecodeParams p) {
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
+  __shared__ __align__(16) float sm_acc[NW][G][D];
 
   const int heff = p.num_kv_heads * p.head_groups;
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
@@ -947,9 +960,9 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
   const int len = p.sched[kSchedHeader + 2 * (k / heff) + 1];
   // The sequence index is clamped so that no entry can send a read out of
   // bounds; process_split ignores a split index past the sequence's end.
-  process_split<QT, CT, D, G, NW>(p, min(packed >> 16, p.num_seqs - 1), len, packed & 0xffff,
-                                  e / p.head_groups, e % p.head_groups, lane, wave, sm_m, sm_l,
-                                  sm_acc);
+  process_split<QT, CT, D, G, NW, RW>(p, min(packed >> 16, p.num_seqs - 1), len,
+                                      packed & 0xffff, e / p.head_groups, e % p.head_groups, lane,
+                                      wave, sm_m, sm_l, sm_acc);
 }
 
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
@@ -958,14 +971,12 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
 #define PA_DECODE_WAVES 4
 #endif
 
-template <int QT, int CT, int D, int G>
+template <int QT, int CT, int D, int G, int RW>
 hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;
-  // Each wave keeps its blocks' ids one per lane: at most 64 blocks per wave.
-  static_assert(PA_MAX_SPLIT_TOKENS <= kWave * kBlock * NW, "split_tokens cap vs waves");
   // One workgroup per possible item; those past the planned list exit at once.
   const int64_t max_items = (int64_t)p.num_seqs * grid_splits * p.num_kv_heads * p.head_groups;
-  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), dim3((unsigned)max_items),
+  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW, RW>), dim3((unsigned)max_items),
                      dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
@@ -987,15 +998,22 @@ hipError_t dispatch_decode(DecodeParams p, int grid_splits, hipStream_t stream) 
     constexpr int D = decltype(dtag)::value;
     constexpr int kMaxRows = (QT == PA_BF16 && MfmaEligible<CT, D>::value) ? 16 : 8;
     const int G = min(kMaxRows, pow2_at_least(rows));
-    p.head_groups = (rows + G - 1) / G;
+    // Row groups of G rows; with several, a workgroup takes up to four of
+    // them (one per wave or pair of waves) over the same tiles.
+    const int row_groups = (rows + G - 1) / G;
+    const int RW = row_groups >= 4 ? 4 : row_groups >= 2 ? 2 : 1;
+    p.head_groups = (row_groups + RW - 1) / RW;
     switch (G) {
-      case 1: return launch_decode<QT, CT, D, 1>(p, grid_splits, stream);
-      case 2: return launch_decode<QT, CT, D, 2>(p, grid_splits, stream);
-      case 4: return launch_decode<QT, CT, D, 4>(p, grid_splits, stream);
-      case 8: return launch_decode<QT, CT, D, 8>(p, grid_splits, stream);
-      default:
-        if constexpr (kMaxRows >= 16) return launch_decode<QT, CT, D, 16>(p, grid_splits, stream);
-        return hipErrorInvalidValue;
+      case 1: return launch_decode<QT, CT, D, 1, 1>(p, grid_splits, stream);
+      case 2: return launch_decode<QT, CT, D, 2, 1>(p, grid_splits, stream);
+      case 4: return launch_decode<QT, CT, D, 4, 1>(p, grid_splits, stream);
+      default: break;
+    }
+    if (G == 8 && kMaxRows == 16) return launch_decode<QT, CT, D, 8, 1>(p, grid_splits, stream);
+    switch (RW) {
+      case 1: return launch_decode<QT, CT, D, kMaxRows, 1>(p, grid_splits, stream);
+      case 2: return launch_decode<QT, CT, D, kMaxRows, 2>(p, grid_splits, stream);
+      default: return launch_decode<QT, CT, D, kMaxRows, 4>(p, grid_splits, stream);
     }
   };
   if (p.head_dim == 64) return by_rows(std::integral_constant<int, 64>{});

@@ -57,7 +57,7 @@ def test_default_split_tokens_is_valid(lib):
         for D in (64, 128):
             for dt in (F32, BF16, I8):
                 for Q, W in ((1, 0), (4, 0), (1, 4096), (16, 128)):
-                    T = lib.pa_default_split_tokens(B, Hkv, D, dt, L, Q, W)
+                    T = lib.pa_default_split_tokens(B, 4 * Hkv, Hkv, D, dt, L, Q, W)
                     assert 64 <= T <= 4096 and T % 16 == 0, (B, Hkv, L, D, dt, Q, W, T)
 
 
@@ -75,22 +75,31 @@ def test_default_split_tokens_is_valid(lib):
     (4, 2, 64, F32, 128, 64),
 ])
 def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
-    assert lib.pa_default_split_tokens(B, Hkv, D, dt, L, 1, 0) == T
+    assert lib.pa_default_split_tokens(B, 4 * Hkv, Hkv, D, dt, L, 1, 0) == T
+
+
+def test_default_split_tokens_for_prefill_chunks(lib):
+    # 8 sequences x 8 KV heads x 512 query tokens x g = 4: 32 sets of 64 rows per
+    # KV head, so even 4096-token splits leave 8*8*32*2 = 4096 items at L = 8192.
+    assert lib.pa_default_split_tokens(8, 32, 8, 128, BF16, 8192, 512, 0) == 4096
+    # One query token: no growth beyond the byte-sized 512.
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 1, 0) == 512
 
 
 def test_default_split_tokens_with_window(lib):
     # 64 seqs x 8 heads, window 4096: ranges of at most 4111 tokens, 9 splits of
     # 512 -> 4608 items, so T stays 512; a 128-token window on 8 seqs shrinks T.
-    assert lib.pa_default_split_tokens(64, 8, 128, BF16, 65536, 1, 4096) == 512
-    assert lib.pa_default_split_tokens(8, 8, 128, BF16, 65536, 1, 128) == 64
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 65536, 1, 4096) == 512
+    assert lib.pa_default_split_tokens(8, 32, 8, 128, BF16, 65536, 1, 128) == 64
 
 
 def test_default_split_tokens_rejects_unknown(lib):
-    assert lib.pa_default_split_tokens(4, 8, 96, BF16, 100, 1, 0) == 0
-    assert lib.pa_default_split_tokens(4, 8, 128, 7, 100, 1, 0) == 0
-    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 0, 0) == 0
-    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 17, 0) == 0
-    assert lib.pa_default_split_tokens(4, 8, 128, BF16, 100, 1, -1) == 0
+    assert lib.pa_default_split_tokens(4, 32, 8, 96, BF16, 100, 1, 0) == 0
+    assert lib.pa_default_split_tokens(4, 32, 8, 128, 7, 100, 1, 0) == 0
+    assert lib.pa_default_split_tokens(4, 32, 8, 128, BF16, 100, 0, 0) == 0
+    assert lib.pa_default_split_tokens(4, 32, 8, 128, BF16, 100, 4097, 0) == 0
+    assert lib.pa_default_split_tokens(4, 4, 8, 128, BF16, 100, 1, 0) == 0  # Hq < Hkv
+    assert lib.pa_default_split_tokens(4, 32, 8, 128, BF16, 100, 1, -1) == 0
 
 
 @pytest.mark.parametrize("L,Q,W,T,n", [
@@ -156,9 +165,9 @@ def test_prepare_validation(lib):
     assert prep(mb=0) == ERR_SHAPE
     assert prep(B=65536) == ERR_SHAPE
     assert prep(split=40) == ERR_SPLIT
-    assert prep(split=0, mcl=100000, mb=8000, B=4, sched=None) == ERR_NULL  # default T accepted
+    assert prep(split=0) == ERR_SPLIT   # no default here: the plan knows no query heads
     assert prep(Q=0) == ERR_SHAPE
-    assert prep(Q=17) == ERR_SHAPE
+    assert prep(Q=4097) == ERR_SHAPE
     assert prep(W=-1) == ERR_SHAPE
     assert prep(sched=None) == ERR_NULL
     assert prep(k=None) == ERR_NULL
@@ -178,7 +187,7 @@ def test_plan_validation(lib):
     assert plan(split=0) == ERR_SPLIT                  # no default without the cache
     assert plan(sched=None) == ERR_NULL
     assert plan(Q=0) == ERR_SHAPE
-    assert plan(Q=17) == ERR_SHAPE
+    assert plan(Q=4097) == ERR_SHAPE
     assert plan(W=-5) == ERR_SHAPE
     assert plan(B=0, cl=None, sched=None) == OK
 
@@ -209,7 +218,7 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, mcl=1025, S=2, mb=100) == ERR_SPLIT  # needs 3 splits
     assert _partial(lib, mcl=100000, mb=8000, W=500, S=1) == ERR_SPLIT  # 515 tokens: 2 splits
     assert _partial(lib, Q=0) == ERR_SHAPE
-    assert _partial(lib, Q=17) == ERR_SHAPE
+    assert _partial(lib, Q=4097) == ERR_SHAPE
     assert _partial(lib, W=-1) == ERR_SHAPE
     assert _partial(lib, q=None) == ERR_NULL
     assert _partial(lib, sched=None) == ERR_NULL

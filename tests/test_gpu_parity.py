@@ -448,8 +448,8 @@ def test_graph_capture_replays_match_eager():
     eager = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
                                    g.scale, max_context_len=g.max_context_len).clone()
     out = torch.empty_like(g.q)
-    T = pa().default_split_tokens(8, g.k_cache.shape[1], g.q.shape[2], g.k_cache.dtype,
-                                  g.max_context_len)
+    T = pa().default_split_tokens(8, g.q.shape[1], g.k_cache.shape[1], g.q.shape[2],
+                                  g.k_cache.dtype, g.max_context_len)
     ws = torch.empty(pa().workspace_bytes(8, g.q.shape[1], g.q.shape[2],
                                           pa().num_splits(g.max_context_len, T)),
                      dtype=torch.uint8, device="cuda")
@@ -482,7 +482,8 @@ def _sample_rows(B, Q, Hq, n, seed):
 
 
 @pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "fp8_kv",
-                                  "shared_prefix_bf16", "mtp4_llama8b_bf16", "swa4k_bf16"])
+                                  "shared_prefix_bf16", "mtp4_llama8b_bf16", "swa4k_bf16",
+                                  "prefill512_bf16"])
 def test_full_size_sampled_rows(name):
     """Full workload sizes, the launch the benchmark times (default split),
     checked on sampled (sequence, query token, head) rows; every output must
@@ -534,13 +535,22 @@ MTP_CASES = [
     ("int8_kv", 4, 50),
     ("fp8_kv", 4, 0),
     ("fp8_kv", 1, 50),
+    # prefill chunks: many row groups per KV head, handled four to a workgroup
+    ("llama8b_bf16", 32, 0),    # 128 rows: 8 row groups, 2 workgroups per (split, KV head)
+    ("llama8b_bf16", 100, 0),   # 400 rows: 25 row groups, the last set of four ragged
+    ("llama8b_bf16", 257, 0),   # 1028 rows: a partial row group
+    ("llama8b_bf16", 64, 100),
+    ("tiny_fp32", 20, 0),       # VALU engine: 80 rows in groups of 8
+    ("tiny_fp32", 9, 30),
+    ("int8_kv", 40, 0),
+    ("fp8_kv", 40, 0),
 ]
 
 
 def _mtp_batch(name, Q, W, seed, **kw):
     small = name == "tiny_fp32"  # its pool is fixed at 64 blocks
     kw.setdefault("num_seqs", 4 if small else 6)
-    kw.setdefault("ctx_range", (Q, 128 if small else 700))
+    kw.setdefault("ctx_range", (Q, 128 if small else max(700, 2 * Q)))
     return workloads.make_batch(name, seed, "cpu", query_tokens=Q, window=W, **kw)
 
 

@@ -607,7 +607,7 @@ def _dense(b, s):
     return k, v
 
 
-@pytest.mark.parametrize("Q,W", [(4, 0), (1, 37), (4, 37), (3, 16), (2, 1)])
+@pytest.mark.parametrize("Q,W", [(4, 0), (1, 37), (4, 37), (3, 16), (2, 1), (40, 0), (24, 50)])
 def test_query_ranges_match_masked_sdpa(Q, W):
     """Textbook masked attention: torch SDPA in fp64 with a boolean mask that
     lets query i (position p = L - Q + i) see t <= p and, with a window W,

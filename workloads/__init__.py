@@ -53,6 +53,9 @@ Workloads (block size 16 throughout):
   (3 draft tokens and the target token of MTP speculative decoding).
 * ``swa4k_bf16``: 64 seqs, 32 q / 8 KV heads, head_dim 128, bf16, L uniform in
   [8192, 65536], sliding window of 4096 tokens.
+* ``prefill512_bf16``: chunked prefill, 8 seqs, 32 q / 8 KV heads, head_dim 128,
+  bf16, L uniform in [2048, 8192] including a 512-token chunk whose tokens are
+  the step's query tokens (written through the KV write first).
 """
 from __future__ import annotations
 
@@ -103,6 +106,8 @@ WORKLOADS = {
         Workload("mtp4_llama8b_bf16", 64, 32, 8, 128, "bf16", "bf16", 512, 4096,
                  query_tokens=4),
         Workload("swa4k_bf16", 64, 32, 8, 128, "bf16", "bf16", 8192, 65536, window=4096),
+        Workload("prefill512_bf16", 8, 32, 8, 128, "bf16", "bf16", 2048, 8192,
+                 query_tokens=512),
     ]
 }
 
