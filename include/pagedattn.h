@@ -123,11 +123,13 @@ int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t
 /* Split size T (tokens) the library uses when a caller passes
  * split_tokens = 0 [EchoLLMServing notes, section 2: the split count follows
  * the context length, one split per 512 tokens in the notes' setting].
- * T starts at 256 KiB of K and V per (split, KV head), i.e. 262144 /
- * (2 * head_dim * element bytes): 512 tokens for a 16-bit 128-dim cache, 1024
- * for an INT8 one, capped at 4096. With items = num_seqs * num_kv_heads *
- * ceil(Q * g / 64) * pa_max_splits(max_context_len, Q, W, T) (g = num_q_heads /
- * num_kv_heads): T is halved, down to 64, while items < 1024 (small batches
+ * T starts at 256 KiB of K and V per (split, KV head) for every 8 query rows
+ * of the KV head (rows = Q * g, g = num_q_heads / num_kv_heads; at least one
+ * unit), i.e. 262144 * max(1, rows / 8) / (2 * head_dim * element bytes): 512
+ * tokens for a 16-bit 128-dim cache and up to 15 rows, 1024 with 16 rows or
+ * an INT8 cache, capped at 4096. With items = num_seqs * num_kv_heads *
+ * ceil(Q * g / 64) * pa_max_splits(max_context_len, Q, W, T): T is halved,
+ * down to 64, while items < 1024 (small batches
  * still fill the device); with more than 64 query rows per KV head it is then
  * doubled, up to 4096, while items stay >= 1024 (fewer partials to write).
  * Returns 0 for a head_dim other than 64 or 128, an unknown cache_dtype, bad

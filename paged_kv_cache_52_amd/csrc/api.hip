@@ -85,13 +85,18 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (head_dim != 64 && head_dim != 128) return 0;
   if (bad_query_shape(num_query_tokens, sliding_window)) return 0;
   if (num_kv_heads <= 0 || num_q_heads < num_kv_heads) return 0;
-  // 256 KiB of K and V codes per (split, KV head): 512 tokens of a 16-bit
-  // 128-dim cache, 1024 of an INT8 one.
+  // 256 KiB of K and V codes per (split, KV head) and 8 query rows: 512
+  // tokens of a 16-bit 128-dim cache for up to 15 rows (one query token,
+  // g <= 8), 1024 for 16 rows (g = 16, or 4 query tokens at g = 4; an item's
+  // fixed cost, its q rows and merged partials, grows with its rows), 1024
+  // tokens of an INT8 cache for up to 15 rows.
+  const int64_t rows = (int64_t)num_query_tokens * (num_q_heads / num_kv_heads);
   const int64_t kv_bytes_per_token = 2LL * head_dim * elt;
-  int32_t t = (int32_t)std::min<int64_t>(PA_MAX_SPLIT_TOKENS, (256 << 10) / kv_bytes_per_token);
+  int32_t t = (int32_t)std::min<int64_t>(
+      PA_MAX_SPLIT_TOKENS, (256 << 10) * std::max<int64_t>(1, rows / 8) / kv_bytes_per_token);
+  t = t / PA_BLOCK_SIZE * PA_BLOCK_SIZE;
   // Work items: (split, KV head, set of up to 64 query rows); a decode step
   // has one row set per KV head, a prefill chunk many.
-  const int64_t rows = (int64_t)num_query_tokens * (num_q_heads / num_kv_heads);
   const int64_t per_split = (int64_t)std::max(num_seqs, 0) * num_kv_heads * ((rows + 63) / 64);
   auto items = [&](int32_t tt) {
     return per_split * pa_max_splits(max_context_len, num_query_tokens, sliding_window, tt);

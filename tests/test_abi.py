@@ -78,6 +78,14 @@ def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
     assert lib.pa_default_split_tokens(B, 4 * Hkv, Hkv, D, dt, L, 1, 0) == T
 
 
+def test_default_split_tokens_grow_with_query_rows(lib):
+    # 16 rows per KV head (4 query tokens at g = 4, or g = 16): 512 KiB, 1024 tokens.
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 4, 0) == 1024
+    assert lib.pa_default_split_tokens(256, 64, 4, 128, BF16, 18385, 1, 0) == 1024
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 2, 0) == 512   # 8 rows
+    assert lib.pa_default_split_tokens(128, 32, 8, 128, I8, 8192, 4, 0) == 2048
+
+
 def test_default_split_tokens_for_prefill_chunks(lib):
     # 8 sequences x 8 KV heads x 512 query tokens x g = 4: 32 sets of 64 rows per
     # KV head, so even 4096-token splits leave 8*8*32*2 = 4096 items at L = 8192.
