@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_bf16")
     ap.add_argument("--split-tokens", type=int, default=0, help="0: library default")
+    ap.add_argument("--group-members", type=int, default=0,
+                    help="plan groups of sequences sharing blocks (1: off; 0: 4 for "
+                         "shared-prefix workloads, else 1)")
     ap.add_argument("--contiguous-tables", action="store_true",
                     help="blocks in logical order (contiguous-slice layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +213,7 @@ def main():
                         acc=torch.empty((B, Q, Hq, S, D), dtype=torch.float32, device=dev),
                         context_lens=b.context_lens, split_tokens=T, sliding_window=W)
     sched = torch.empty(pa.sched_bytes(B, S) // 4, dtype=torch.int32, device=dev)
+    M = args.group_members or (4 if w.groups and W == 0 else 1)
     stream = torch.cuda.current_stream(dev)
     plan = [None]
 
@@ -218,7 +222,9 @@ def main():
         plan[0] = pa.paged_decode_prepare(b.new_k, b.new_v, b.slot_mapping, b.k_cache,
                                           b.v_cache, b.context_lens, mb, b.k_scale, b.v_scale,
                                           max_context_len=b.max_context_len, split_tokens=T,
-                                          num_query_tokens=Q, sliding_window=W, sched=sched)
+                                          num_query_tokens=Q, sliding_window=W,
+                                          block_tables=b.block_tables, group_members=M,
+                                          sched=sched)
 
     def decode():
         pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
@@ -305,7 +311,7 @@ def main():
             "head_dim": D, "block_size": 16, "cache_dtype": w.cache_dtype,
             "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
-            "query_tokens": Q, "sliding_window": W,
+            "query_tokens": Q, "sliding_window": W, "group_members": M,
             "tables": "contiguous" if args.contiguous_tables else "permuted",
             "context_range": list(args.ctx_range) if args.ctx_range else
             [b.workload.ctx_lo, b.workload.ctx_hi],

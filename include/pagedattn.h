@@ -87,6 +87,7 @@ extern "C" {
 #define PA_MAX_SPLIT_TOKENS 4096
 #define PA_MAX_SEQS 65535
 #define PA_MAX_QUERY_TOKENS 4096
+#define PA_MAX_GROUP_MEMBERS 4
 
 /* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
  * NaN, largest finite 448). */
@@ -177,39 +178,55 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  * the device and writes into `sched` the list of every split of the batch,
  * max(1, ceil((L_s - base_s) / T)) per sequence (see the split range above),
  * full splits first and then the last split of each sequence, longest first.
- * The list depends only on the lengths, Q, W, T and the length bounds, so one
- * plan serves every attention layer of a step that uses the same window.
+ * The list depends only on the lengths, Q, W, T and the length bounds (and,
+ * with grouping, the tables), so one plan serves every attention layer of a
+ * step that uses the same window.
  *   context_lens       [num_seqs] int32 (device)
+ *   block_tables       [num_seqs][max_blocks_per_seq] int32 (device); read
+ *                      only with group_members > 1, may be NULL otherwise
  *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
  *   num_query_tokens   Q, 1 .. PA_MAX_QUERY_TOKENS
  *   sliding_window     W >= 0 (0: none)
  *   split_tokens       T, a positive multiple of 16 <= 4096 (the plan knows no
  *                      cache, so there is no default here: pass what the
  *                      decode call will use, e.g. pa_default_split_tokens())
+ *   group_members      1, or up to PA_MAX_GROUP_MEMBERS [ATOM article 5.1-5.2:
+ *                      blocks are reference counted and shared, e.g. a
+ *                      prompt's prefix across its samples]: within aligned
+ *                      runs of that many consecutive sequences, full splits j
+ *                      that start on the same physical block as the previous
+ *                      sequence's split j become one work item, its sequences
+ *                      one per wave over shared, cached tile reads. Results do
+ *                      not depend on it (each sequence still reads its own
+ *                      table); it costs a few table reads per split in the plan.
+ *                      Requires W = 0; a plan with groups is used only when
+ *                      Q * g <= 16 rows (MFMA engine) or 8 (VALU engine), and
+ *                      is otherwise ignored like any mismatched plan.
  *   sched              device scratch of pa_sched_bytes(num_seqs, max_splits)
  *                      bytes, max_splits >= pa_max_splits(max_context_len, Q, W, T)
  */
-int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
-                    int32_t split_tokens, int32_t *sched, hipStream_t stream);
+int paged_attn_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
+                    int32_t group_members, int32_t *sched, hipStream_t stream);
 
 /*
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
  * depend on each other, so one kernel does both (its last workgroup plans, the
  * others write). Arguments, layouts and errors are those of the two calls
  * (split_tokens is required, as for the plan); the results are identical to
- * calling them in turn. Serves the start of a decode
- * step, where the new tokens (num_seqs * Q of them with several query tokens)
- * are written and the batch's splits are listed.
+ * calling them in turn. Serves the start of a decode step, where the new tokens
+ * (num_seqs * Q of them with several query tokens) are written and the batch's
+ * splits are listed.
  */
 int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, int32_t num_seqs,
-                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         const int32_t *context_lens, const int32_t *block_tables,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
                          int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                         int32_t *sched, hipStream_t stream);
+                         int32_t group_members, int32_t *sched, hipStream_t stream);
 
 /*
  * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
@@ -271,7 +288,7 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
                       hipStream_t stream);
 
 /*
- * Whole decode step of one attention layer: paged_attn_plan and
+ * Whole decode step of one attention layer: paged_attn_plan (no grouping) and
  * paged_attn_decode_partial into the caller's workspace, then
  * paged_attn_reduce into out (dtype = q_dtype).
  * The split count is pa_max_splits(max_context_len', Q, W, T) with

@@ -140,6 +140,7 @@ class Plan:
     max_splits: int
     num_query_tokens: int = 1
     sliding_window: int = 0
+    group_members: int = 1
 
 
 @dataclasses.dataclass
@@ -201,23 +202,28 @@ def _plan_sizes(context_lens, max_blocks_per_seq, max_context_len, split_tokens,
 
 def paged_attn_plan(context_lens, max_blocks_per_seq: int, *, max_context_len=None,
                     split_tokens=None, num_query_tokens: int = 1, sliding_window: int = 0,
+                    block_tables=None, group_members: int = 1,
                     sched: Optional[torch.Tensor] = None, _cache=None) -> Plan:
     """Plan kernel: list every split of the batch (on the device, from
-    context_lens) for the split kernel. split_tokens is required."""
+    context_lens) for the split kernel. split_tokens is required. With
+    group_members > 1 (and block_tables), splits of consecutive sequences that
+    start on the same physical block become shared work items."""
     Q, W = int(num_query_tokens), int(sliding_window)
     B, mcl, T, S, sched = _plan_sizes(context_lens, max_blocks_per_seq, max_context_len,
                                       split_tokens, sched, Q, W, _cache)
-    _check(_lib.load().paged_attn_plan(_dev(context_lens, "context_lens", torch.int32), B,
-                                       max_blocks_per_seq, mcl, Q, W, T,
+    _check(_lib.load().paged_attn_plan(_dev(context_lens, "context_lens", torch.int32),
+                                       _dev(block_tables, "block_tables", torch.int32), B,
+                                       max_blocks_per_seq, mcl, Q, W, T, int(group_members),
                                        _dev(sched, "sched", torch.int32),
                                        _stream(context_lens.device)))
-    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W)
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W, int(group_members))
 
 
 def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
                          max_blocks_per_seq: int, k_scale=None, v_scale=None, *,
                          max_context_len=None, split_tokens=None, num_query_tokens: int = 1,
                          sliding_window: int = 0, num_q_heads: Optional[int] = None,
+                         block_tables=None, group_members: int = 1,
                          sched: Optional[torch.Tensor] = None) -> Plan:
     """paged_kv_write + paged_attn_plan in one launch; returns the plan.
     Without split_tokens the default is taken for num_q_heads query heads."""
@@ -238,9 +244,10 @@ def paged_decode_prepare(k, v, slot_mapping, k_cache, v_cache, context_lens,
         _dev(slot_mapping, "slot_mapping", torch.int64), T_tok, Hkv, D, _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache", k_cache.dtype), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), NB, _code(k_cache),
-        _dev(context_lens, "context_lens", torch.int32), B, max_blocks_per_seq, mcl, Q, W, T,
-        _dev(sched, "sched", torch.int32), _stream(k.device)))
-    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W)
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), B, max_blocks_per_seq, mcl, Q, W, T,
+        int(group_members), _dev(sched, "sched", torch.int32), _stream(k.device)))
+    return Plan(sched, context_lens, max_blocks_per_seq, mcl, T, S, Q, W, int(group_members))
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
@@ -280,6 +287,13 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
           (max_context_len is not None and int(max_context_len) != plan.max_context_len) or
           plan.num_query_tokens != Q or plan.sliding_window != W):
         raise PagedAttnError("plan was made for other arguments")
+    if plan.group_members > 1:
+        # Group entries put each member's rows in one wave: all Q*g rows of a
+        # KV head must fit one row group of the engine that runs.
+        mfma = q.dtype == torch.bfloat16 and D == 128 and k_cache.dtype != torch.float32
+        if Q * (Hq // Hkv) > (16 if mfma else 8):
+            raise PagedAttnError("a plan with group entries needs num_query_tokens * "
+                                 f"(Hq / Hkv) <= {16 if mfma else 8} here")
     T, S = plan.split_tokens, plan.max_splits
     if partials is None:
         partials = Partials(m=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=q.device),

@@ -29,10 +29,11 @@ SIGNATURES = {
     "paged_attn_decode_partial": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
                                                  _P, _I32, _I64, _I32, _P, _I32, _P, _I32, _I32,
                                                  _F32, _I32, _I32, _P, _P, _P, _P, _P]),
-    "paged_attn_plan": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P]),
+    "paged_attn_plan": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                       _P]),
     "paged_decode_prepare": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P,
-                                            _I64, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
-                                            _P, _P]),
+                                            _I64, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _P, _P]),
     "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _I32, _P, _I32, _P]),
     "pa_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),

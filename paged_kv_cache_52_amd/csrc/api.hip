@@ -153,17 +153,22 @@ int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *s
 }
 
 // Argument checks of the plan; fills `out` on success.
-int check_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-               int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
-               int32_t split_tokens, int32_t *sched, pa::PlanParams *out) {
+int check_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
+               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_query_tokens,
+               int32_t sliding_window, int32_t split_tokens, int32_t group_members,
+               int32_t *sched, pa::PlanParams *out) {
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
   if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (group_members < 1 || group_members > PA_MAX_GROUP_MEMBERS) return PA_ERR_SHAPE;
+  if (group_members > 1 && sliding_window > 0) return PA_ERR_SHAPE;
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
+  if (num_seqs > 0 && group_members > 1 && !block_tables) return PA_ERR_NULL;
   *out = pa::PlanParams{context_lens, sched, num_seqs,
                         clamped_bound(max_context_len, max_blocks_per_seq), split_tokens,
-                        num_query_tokens, sliding_window};
+                        num_query_tokens, sliding_window, block_tables, max_blocks_per_seq,
+                        group_members};
   return PA_OK;
 }
 
@@ -182,12 +187,14 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
   return launch_status(pa::launch_kv_write(w, stream));
 }
 
-int paged_attn_plan(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
-                    int32_t split_tokens, int32_t *sched, hipStream_t stream) {
+int paged_attn_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
+                    int32_t group_members, int32_t *sched, hipStream_t stream) {
   pa::PlanParams pl;
-  const int st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
-                            num_query_tokens, sliding_window, split_tokens, sched, &pl);
+  const int st = check_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                            max_context_len, num_query_tokens, sliding_window, split_tokens,
+                            group_members, sched, &pl);
   if (st != PA_OK || num_seqs == 0) return st;
   return launch_status(pa::launch_plan(pl, stream));
 }
@@ -196,17 +203,17 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, int32_t num_seqs,
-                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         const int32_t *context_lens, const int32_t *block_tables,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
                          int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                         int32_t *sched, hipStream_t stream) {
+                         int32_t group_members, int32_t *sched, hipStream_t stream) {
   pa::WriteParams w;
   pa::PlanParams pl;
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
                        v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK) return st;
-  st = check_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len, num_query_tokens,
-                  sliding_window, split_tokens, sched, &pl);
+  st = check_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq, max_context_len,
+                  num_query_tokens, sliding_window, split_tokens, group_members, sched, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
   return launch_status(pa::launch_prepare(w, pl, stream));
@@ -346,8 +353,9 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   float *m = (float *)base;
   float *l = (float *)(base + align256(rows * sizeof(float)));
   float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
-  int st = paged_attn_plan(context_lens, num_seqs, max_blocks_per_seq, max_context_len,
-                           num_query_tokens, sliding_window, split_tokens, sched, stream);
+  int st = paged_attn_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                           max_context_len, num_query_tokens, sliding_window, split_tokens, 1,
+                           sched, stream);
   if (st != PA_OK) return st;
   st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_query_tokens, num_q_heads, head_dim,
                                  k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks,

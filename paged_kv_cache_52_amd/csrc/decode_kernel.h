@@ -826,33 +826,43 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   }
 }
 
-// One work item: split j of sequence s for KV head kvh and RW row groups of
-// G rows (the quad-th set of RW among the Q*g rows of the KV head). The NW
-// waves split into RW row groups of TW = NW / RW waves: the TW waves of a row
-// group divide the tiles of the split that its rows reach, and merge their
-// states in LDS; different row groups read the same tiles at about the same
-// time (with RW > 1 they are loaded through the caches, not streamed) and
-// write their own partials. Contains two workgroup barriers.
+// One work item for KV head kvh: split j of sequence s for RW row groups of G
+// rows (the quad-th set of RW among the Q*g rows of the KV head), or, for a
+// group entry (group > 0), split j of the `group` sequences s, s+1, ... whose
+// splits share tiles, one row group (all Q*g <= G rows) each. The NW waves
+// split into rw row groups of tw = NW / rw waves: the tw waves of a row group
+// divide the tiles of the split that its rows reach, and merge their states
+// in LDS; different row groups read their tiles at about the same time (with
+// rw > 1 through the caches, not streamed) and write their own partials.
+// Contains two workgroup barriers.
 template <int QT, int CT, int D, int G, int NW, int RW>
 __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
-                                              int kvh, int quad, int lane, int wave,
+                                              int kvh, int quad, int group, int lane, int wave,
                                               float (&sm_m)[NW][G],
                                               float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
-  constexpr int TW = NW / RW;                        // waves per row group
-  constexpr int POL = RW > 1 ? 0 : kStreamPolicy;    // shared tiles stay cached
+  constexpr int POL = RW > 1 ? 0 : kStreamPolicy;  // shared tiles stay cached
+  const int rw = group > 0 ? NW : RW;               // row groups of this item
+  const int tw = NW / rw;                            // waves per row group
+  const int rg = wave / tw, tp = wave % tw;          // this wave's row group and tile share
+  const int Q = p.num_query_tokens, W = p.window;
+  const int rows = Q * p.group;
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
-  const int L = max(0, min(len, lmax));
-  const int Q = p.num_query_tokens, W = p.window;
+  // The row group's sequence, rows and split range.
+  auto seq_of = [&](int g) { return group > 0 ? s + g : s; };
+  auto rows_of = [&](int g) {
+    if (group > 0) return g < group ? min(G, rows) : 0;
+    return min(G, rows - (quad * RW + g) * G);
+  };
+  const int s_rg = min(seq_of(rg), p.num_seqs - 1);
+  const int L = max(0, min(group > 0 ? p.context_lens[s_rg] : len, lmax));
   const int base = split_base(L, Q, W);
-  if (j >= splits_of(L, Q, W, p.split_tokens)) return;  // never for planned items; uniform
+  const bool has_split = j < splits_of(L, Q, W, p.split_tokens);  // always, for planned items
   const int t0 = base + j * p.split_tokens;  // a multiple of 16
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
-  const int rg = wave / TW, tp = wave % TW;  // this wave's row group and tile share
-  const int rows = Q * p.group;
-  const int R0 = (quad * RW + rg) * G;
-  const int nrows = min(G, rows - R0);       // <= 0: a padding row group (no rows)
+  const int R0 = group > 0 ? 0 : (quad * RW + rg) * G;
+  const int nrows = has_split ? rows_of(rg) : 0;  // <= 0: a padding row group (no rows)
   // Tiles of the split the row group's rows reach: tokens [ta, tz].
   RowRanges rr{};
   int wb0 = 0, wb1 = 0;
@@ -861,64 +871,79 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     const int ta = max(t0, rr.ulo), tz = min(t1 - 1, rr.uhi);
     if (tz >= ta) {
       const int first = (ta - t0) / kBlock, count = (tz - t0) / kBlock - first + 1;
-      const int per = (count + TW - 1) / TW;
+      const int per = (count + tw - 1) / tw;
       wb0 = first + min(count, tp * per);
       wb1 = first + min(count, tp * per + per);
     }
   }
-  if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value)
-    wave_pass_mfma<QT, CT, D, G, NW, POL>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+  if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
+    if (group > 0)
+      wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
-  else
-    wave_pass_valu<QT, CT, D, G, NW, POL>(p, s, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+    else
+      wave_pass_mfma<QT, CT, D, G, NW, POL>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+                                            sm_m, sm_l, sm_acc);
+  } else {
+    if (group > 0)
+      wave_pass_valu<QT, CT, D, G, NW, 0>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
+    else
+      wave_pass_valu<QT, CT, D, G, NW, POL>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+                                            sm_m, sm_l, sm_acc);
+  }
   __syncthreads();
 
-  // Merge the TW waves of each row group and write the split's partials: one
+  // Merge the tw waves of each row group and write the split's partials: one
   // thread per row finds the row's common max, turns sm_m into the waves'
   // factors 2^(m_w - M) and writes (m, l); then all threads sum the rows'
-  // dims, four per thread.
-  auto rows_of = [&](int g) { return min(G, rows - (quad * RW + g) * G); };
-  if (threadIdx.x < RW * G) {
+  // dims, four per thread. A row group without the split writes nothing.
+  auto out_row = [&](int g, int h) {
+    const int sg = seq_of(g);
+    return query_row(p, sg, kvh, (group > 0 ? 0 : (quad * RW + g) * G) + h) * p.max_splits + j;
+  };
+  auto live = [&](int g) {  // rows of row group g that have this split
+    if (group == 0) return has_split ? rows_of(g) : 0;
+    if (g >= group || s + g >= p.num_seqs) return 0;
+    const int Lg = max(0, min(p.context_lens[s + g], lmax));
+    return j < splits_of(Lg, Q, W, p.split_tokens) ? rows_of(g) : 0;
+  };
+  if (threadIdx.x < rw * G) {
     const int g = threadIdx.x / G, h = threadIdx.x % G;
-    if (h < rows_of(g)) {
-      const int w0 = g * TW;
+    if (h < live(g)) {
+      const int w0 = g * tw;
       float M = sm_m[w0][h];
-#pragma unroll
-      for (int w = 1; w < TW; ++w) M = fmaxf(M, sm_m[w0 + w][h]);
+      for (int w = 1; w < tw; ++w) M = fmaxf(M, sm_m[w0 + w][h]);
       float lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < TW; ++w) {
+      for (int w = 0; w < tw; ++w) {
         const float f = fast_exp2(sm_m[w0 + w][h] - M);
         sm_m[w0 + w][h] = f;
         lsum = fmaf(f, sm_l[w0 + w][h], lsum);
       }
-      const int64_t row = query_row(p, s, kvh, (quad * RW + g) * G + h) * p.max_splits + j;
+      const int64_t row = out_row(g, h);
       p.part_l[row] = lsum;
       p.part_m[row] = lsum > 0.f ? M * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < RW * G * (D / 4); idx += NW * kWave) {
+  for (int idx = threadIdx.x; idx < rw * G * (D / 4); idx += NW * kWave) {
     const int g = idx / (G * (D / 4));
     const int h = idx / (D / 4) % G, d = (idx % (D / 4)) * 4;
-    if (h >= rows_of(g)) continue;
-    const int w0 = g * TW;
+    if (h >= live(g)) continue;
+    const int w0 = g * tw;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < TW; ++w) {
+    for (int w = 0; w < tw; ++w) {
       const float f = sm_m[w0 + w][h];
       const f32x4 v = *(const f32x4 *)&sm_acc[w0 + w][h][d];
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = fmaf(f, v[e], a[e]);
     }
-    const int64_t row = query_row(p, s, kvh, (quad * RW + g) * G + h) * p.max_splits + j;
-    *(f32x4 *)(p.part_acc + row * D + d) = a;
+    *(f32x4 *)(p.part_acc + out_row(g, h) * D + d) = a;
   }
 }
 
 // Split kernel. Work item k is split sched[kSchedHeader + 2*(k / heff)]
-// (packed sequence << 16 | split, followed by the sequence's context length)
+// (packed sequence << 16 | split, followed by the sequence's context length,
+// or minus the member count of a group entry)
 // for (KV head, row group) k % heff (heff = KV heads x row groups), from the
 // list the plan kernel wrote (full splits first, the shortest last splits at
 // the end). Workgroup k processes item k; the grid is an upper bound on the
@@ -945,9 +970,13 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
 
   const int heff = p.num_kv_heads * p.head_groups;
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  // A plan made with group entries needs every sequence's rows in one row
+  // group (Q*g <= G), and a wave per member.
+  static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
   const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
                        p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
-                       p.sched[5] == p.window;
+                       p.sched[5] == p.window &&
+                       (p.sched[6] <= 1 || p.num_query_tokens * p.group <= G);
   const int n_items = plan_ok ? p.sched[0] * heff : 0;
   const int k = blockIdx.x;
   if (k >= n_items) return;
@@ -957,12 +986,15 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int e = k % heff;
   const int packed = p.sched[kSchedHeader + 2 * (k / heff)];
-  const int len = p.sched[kSchedHeader + 2 * (k / heff) + 1];
+  const int word1 = p.sched[kSchedHeader + 2 * (k / heff) + 1];
+  // word1 is the sequence's length, or minus the member count of a group
+  // entry (made only with one row group per KV head: e / head_groups = kvh).
+  const int group = word1 < 0 ? min(-word1, NW) : 0;
   // The sequence index is clamped so that no entry can send a read out of
-  // bounds; process_split ignores a split index past the sequence's end.
-  process_split<QT, CT, D, G, NW, RW>(p, min(packed >> 16, p.num_seqs - 1), len,
-                                      packed & 0xffff, e / p.head_groups, e % p.head_groups, lane,
-                                      wave, sm_m, sm_l, sm_acc);
+  // bounds; process_split ignores a split index past a sequence's end.
+  process_split<QT, CT, D, G, NW, RW>(p, min(packed >> 16, p.num_seqs - 1), max(word1, 0),
+                                      packed & 0xffff, e / p.head_groups, e % p.head_groups,
+                                      group, lane, wave, sm_m, sm_l, sm_acc);
 }
 
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.

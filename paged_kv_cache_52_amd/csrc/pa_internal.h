@@ -38,6 +38,9 @@ struct PlanParams {
   int32_t *sched;
   int32_t num_seqs, max_len, split_tokens;
   int32_t num_query_tokens, window;
+  const int32_t *block_tables;  // read only with group_members > 1
+  int32_t max_blocks_per_seq;
+  int32_t group_members;        // 1: no grouping; 2..4: sequences per group entry
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);

@@ -7,15 +7,20 @@
 // sliding window, of the span the window reaches]. It writes
 // into the scheduling scratch:
 //   sched[0]  = number of splits of the batch
-//   sched[1..5] = split_tokens, num_seqs, clamped max length, query tokens,
-//                 window (checked by the split kernel); sched[6..7] = 0
-//   sched[4+2i], sched[5+2i] = (s << 16) | j, L_s   split i, in this order:
+//   sched[1..6] = split_tokens, num_seqs, clamped max length, query tokens,
+//                 window, group_members (0 when grouping is off), checked by
+//                 the split kernel; sched[7] = 0
+//   sched[8+2i], sched[9+2i] = (s << 16) | j, L_s   split i, in this order:
 //     1. all splits but the last of each sequence (full T-token splits),
-//        sequence by sequence;
+//        sequence by sequence; with grouping on (group_members M > 1), the
+//        full split j of up to M consecutive sequences of an aligned run of M
+//        whose split j starts on the same physical block is one entry
+//        ((s0 << 16) | j, -count), listed at its first sequence;
 //     2. the last split of each sequence, longest first (counting sort on its
 //        16-token tile count), so the shortest work runs at the very end.
 // A sequence of length 0 contributes one empty split. Lengths are clamped
-// exactly as the split kernel clamps them.
+// exactly as the split kernel clamps them. A group entry is only a hint for
+// cache sharing: the split kernel reads each member's own block table.
 #pragma once
 
 #include "pa_common.h"
@@ -27,6 +32,18 @@ constexpr int kMaxTileBuckets = PA_MAX_SPLIT_TOKENS / kBlock;  // tile counts 1.
 
 __device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
   return max(0, min(p.context_lens[s], p.max_len));
+}
+
+// Whether sequence s takes part in the group of sequence s - 1 for its full
+// split j: both splits are full and start on the same physical block.
+__device__ __forceinline__ bool joins_previous(const PlanParams &p, int s, int j) {
+  if (s <= 0 || s >= p.num_seqs) return false;
+  const int Q = p.num_query_tokens, W = p.window, T = p.split_tokens;
+  if (j >= splits_of(clamp_len(p, s), Q, W, T) - 1) return false;
+  if (j >= splits_of(clamp_len(p, s - 1), Q, W, T) - 1) return false;
+  const int jb = j * (p.split_tokens / kBlock);  // first block of split j (no window: base 0)
+  return p.block_tables[(int64_t)s * p.max_blocks_per_seq + jb] ==
+         p.block_tables[(int64_t)(s - 1) * p.max_blocks_per_seq + jb];
 }
 
 __device__ __forceinline__ int seq_splits(const PlanParams &p, int L) {
@@ -41,6 +58,18 @@ __device__ __forceinline__ int last_tiles(const PlanParams &p, int L) {
   return (rest + kBlock - 1) / kBlock;
 }
 
+// Last i with first[i] <= e, over a chunk's ascending entry offsets.
+// Sequences with no full split share their offset with the next one; the
+// search lands on the last of them, which is the one that owns entry e.
+__device__ __forceinline__ int owner_of(const int (&first)[kPlanThreads], int e) {
+  int lo = 0, hi = kPlanThreads - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 static __device__ void plan_workgroup(const PlanParams &p) {
   __shared__ int wave_sum[kPlanThreads / kWave];
   __shared__ int bucket[kMaxTileBuckets + 1];  // count, then start offset, of each tile count
@@ -50,7 +79,6 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int T = p.split_tokens;
 
   for (int i = tid; i <= kMaxTileBuckets; i += kPlanThreads) bucket[i] = 0;
   if (tid == 0) carry = 0;
@@ -85,21 +113,60 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     chunk_len[tid] = L;
     __syncthreads();
     const int base_entry = carry;
-    for (int e = tid; e < total; e += kPlanThreads) {
-      int lo = 0, hi = kPlanThreads - 1;  // last i with chunk_first[i] <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_first[mid] <= e) lo = mid; else hi = mid - 1;
+    if (p.group_members <= 1) {
+      for (int e = tid; e < total; e += kPlanThreads) {
+        const int lo = owner_of(chunk_first, e);
+        const int q = e - chunk_first[lo];
+        p.sched[kSchedHeader + 2 * (base_entry + e)] = ((base + lo) << 16) | q;
+        p.sched[kSchedHeader + 2 * (base_entry + e) + 1] = chunk_len[lo];
       }
-      // Sequences with no full split share their offset with the next one;
-      // the search lands on the last of them, which is the one that owns e.
-      const int q = e - chunk_first[lo];
-      p.sched[kSchedHeader + 2 * (base_entry + e)] = ((base + lo) << 16) | q;
-      p.sched[kSchedHeader + 2 * (base_entry + e) + 1] = chunk_len[lo];
+      __syncthreads();
+      if (tid == 0) carry += total;
+      __syncthreads();
+    } else {
+      // Grouping: an entry (s, j) whose sequence joins its predecessor inside
+      // the aligned run of M is dropped (its group's first sequence lists it);
+      // the others count how many following sequences of the run join. The
+      // kept entries are compacted with a workgroup scan per stride.
+      const int M = p.group_members;
+      for (int e0 = 0; e0 < total; e0 += kPlanThreads) {
+        const int e = e0 + tid;
+        int keep = 0, cnt = 1, word0 = 0, L_e = 0;
+        if (e < total) {
+          const int lo = owner_of(chunk_first, e);
+          const int s_e = base + lo, j = e - chunk_first[lo];
+          word0 = (s_e << 16) | j;
+          L_e = chunk_len[lo];
+          const int pos = s_e % M;
+          keep = !(pos > 0 && joins_previous(p, s_e, j));
+          if (keep)
+            while (pos + cnt < M && joins_previous(p, s_e + cnt, j)) ++cnt;
+        }
+        int incl_k = keep;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_up(incl_k, o);
+          if (lane >= o) incl_k += y;
+        }
+        __syncthreads();  // wave_sum is free again
+        if (lane == kWave - 1) wave_sum[wave] = incl_k;
+        __syncthreads();
+        int before_k = 0, total_k = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanThreads / kWave; ++w) {
+          if (w < wave) before_k += wave_sum[w];
+          total_k += wave_sum[w];
+        }
+        if (keep) {
+          const int at = carry + before_k + incl_k - 1;
+          p.sched[kSchedHeader + 2 * at] = word0;
+          p.sched[kSchedHeader + 2 * at + 1] = cnt > 1 ? -cnt : L_e;
+        }
+        __syncthreads();
+        if (tid == 0) carry += total_k;
+        __syncthreads();
+      }
     }
-    __syncthreads();
-    if (tid == 0) carry += total;
-    __syncthreads();
   }
   const int n_full = carry;
 
@@ -138,12 +205,12 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   }
   if (tid == 0) {
     p.sched[0] = n_full + p.num_seqs;
-    p.sched[1] = T;
+    p.sched[1] = p.split_tokens;
     p.sched[2] = p.num_seqs;
     p.sched[3] = p.max_len;
     p.sched[4] = p.num_query_tokens;
     p.sched[5] = p.window;
-    p.sched[6] = 0;
+    p.sched[6] = p.group_members > 1 ? p.group_members : 0;
     p.sched[7] = 0;
   }
 }

@@ -163,12 +163,13 @@ def test_kv_write_validation(lib):
 def test_prepare_validation(lib):
     def prep(**kw):
         a = dict(k=FAKE, v=FAKE, idt=BF16, slots=FAKE, T=4, Hkv=8, D=128, kc=FAKE, vc=FAKE,
-                 NB=100, cdt=BF16, cl=FAKE, B=4, mb=8, mcl=128, Q=1, W=0, split=512, sched=FAKE)
+                 NB=100, cdt=BF16, cl=FAKE, bt=None, B=4, mb=8, mcl=128, Q=1, W=0, split=512,
+                 gm=1, sched=FAKE)
         a.update(kw)
         return lib.paged_decode_prepare(a["k"], a["v"], a["idt"], a["slots"], a["T"], a["Hkv"],
                                         a["D"], a["kc"], a["vc"], None, None, a["NB"], a["cdt"],
-                                        a["cl"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
-                                        a["split"], a["sched"], None)
+                                        a["cl"], a["bt"], a["B"], a["mb"], a["mcl"], a["Q"],
+                                        a["W"], a["split"], a["gm"], a["sched"], None)
     assert prep(D=96) == ERR_SHAPE
     assert prep(mb=0) == ERR_SHAPE
     assert prep(B=65536) == ERR_SHAPE
@@ -180,15 +181,19 @@ def test_prepare_validation(lib):
     assert prep(sched=None) == ERR_NULL
     assert prep(k=None) == ERR_NULL
     assert prep(kc=FAKE_ODD) == ERR_ALIGN
+    assert prep(gm=0) == ERR_SHAPE
+    assert prep(gm=5, bt=FAKE) == ERR_SHAPE
+    assert prep(gm=2) == ERR_NULL                      # grouping reads the tables
+    assert prep(gm=2, bt=FAKE, W=64) == ERR_SHAPE      # and needs no window
     assert prep(T=0, B=0, k=None, cl=None) == OK
 
 
 def test_plan_validation(lib):
     def plan(**kw):
-        a = dict(cl=FAKE, B=4, mb=8, mcl=128, Q=1, W=0, split=512, sched=FAKE)
+        a = dict(cl=FAKE, bt=None, B=4, mb=8, mcl=128, Q=1, W=0, split=512, gm=1, sched=FAKE)
         a.update(kw)
-        return lib.paged_attn_plan(a["cl"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
-                                   a["split"], a["sched"], None)
+        return lib.paged_attn_plan(a["cl"], a["bt"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
+                                   a["split"], a["gm"], a["sched"], None)
     assert plan(mb=0) == ERR_SHAPE
     assert plan(mcl=-1) == ERR_SHAPE
     assert plan(split=8) == ERR_SPLIT
@@ -197,6 +202,10 @@ def test_plan_validation(lib):
     assert plan(Q=0) == ERR_SHAPE
     assert plan(Q=4097) == ERR_SHAPE
     assert plan(W=-5) == ERR_SHAPE
+    assert plan(gm=0) == ERR_SHAPE
+    assert plan(gm=5, bt=FAKE) == ERR_SHAPE
+    assert plan(gm=2) == ERR_NULL
+    assert plan(gm=4, bt=FAKE, W=1) == ERR_SHAPE
     assert plan(B=0, cl=None, sched=None) == OK
 
 

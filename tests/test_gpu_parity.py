@@ -674,3 +674,165 @@ def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+# ---------------------------------------------------------------------------
+# Plans with group entries: full splits j of consecutive sequences that start
+# on the same physical block (shared prefix blocks) become one work item.
+
+def _share_prefixes(b, n_blocks=None):
+    """Let every odd sequence share the leading blocks of the sequence before
+    it (all but its last block, or n_blocks), as prefix sharing does."""
+    t = b.block_tables.clone()
+    lens = b.context_lens.tolist()
+    for s in range(1, len(lens), 2):
+        n = min(-(-lens[s] // 16), -(-lens[s - 1] // 16)) - 1
+        if n_blocks is not None:
+            n = min(n, n_blocks)
+        if n > 0:
+            t[s, :n] = t[s - 1, :n]
+    b.block_tables = t
+    return b
+
+
+def _expected_group_entries(tables, lens, T, M):
+    """Full-split entries of a plan with groups of up to M, in list order: a
+    sequence joins the previous one for its full split j when both splits are
+    full and start on the same physical block, within aligned runs of M."""
+    nsp = [max(1, -(-L // T)) for L in lens]
+
+    def joins(s, j):
+        if s <= 0 or s >= len(lens) or j >= nsp[s] - 1 or j >= nsp[s - 1] - 1:
+            return False
+        return tables[s, j * T // 16] == tables[s - 1, j * T // 16]
+
+    out = []
+    for s in range(len(lens)):
+        for j in range(nsp[s] - 1):
+            pos = s % M
+            if pos > 0 and joins(s, j):
+                continue
+            cnt = 1
+            while pos + cnt < M and joins(s + cnt, j):
+                cnt += 1
+            out.append(((s << 16) | j, -cnt if cnt > 1 else lens[s]))
+    return out
+
+
+@pytest.mark.parametrize("T,M", [(64, 2), (64, 4), (512, 4), (16, 3)])
+def test_grouped_plan(T, M):
+    """Group entries cover every full split exactly once, only join
+    sequences whose split starts on the same block, and keep the list order."""
+    print(f"[case] grouped plan T={T} M={M}", flush=True)
+    b = workloads.make_batch("shared_prefix_bf16", 251, "cpu", groups=3, suffix_max=600)
+    lens = b.context_lens.clone()
+    lens[9] = 10                         # no full split inside a group
+    lens[13] = 2000                      # prefix only
+    b.context_lens = lens
+    t = b.block_tables.clone()
+    half = b.block_tables.shape[1] // 2
+    t[5, 4] = t[5, 4 + half]           # breaks sharing of the splits starting there
+    t[6, 32] = t[6, 32 + half]
+    b.block_tables = t
+    g = _to(b, "cuda")
+    mb = g.block_tables.shape[1]
+    plan = pa().paged_attn_plan(g.context_lens, mb, max_context_len=g.max_context_len,
+                                split_tokens=T, block_tables=g.block_tables, group_members=M)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    lmax = min(g.max_context_len, 16 * mb)
+    L = [min(int(x), lmax) for x in lens]
+    full = _expected_group_entries(b.block_tables.numpy(), L, T, M)
+    n = len(full) + len(L)
+    assert list(sched[:8]) == [n, T, len(L), lmax, 1, 0, M, 0]
+    got = list(zip(sched[8:8 + 2 * len(full):2].tolist(), sched[9:9 + 2 * len(full):2].tolist()))
+    assert got == full
+    assert any(w1 < 0 for _, w1 in got), "the batch should form groups"
+    # Expanded, the list covers every (sequence, split) exactly once.
+    pairs = []
+    for w0, w1 in zip(sched[8:8 + 2 * n:2].tolist(), sched[9:9 + 2 * n:2].tolist()):
+        s, j = w0 >> 16, w0 & 0xffff
+        pairs += [(s + i, j) for i in range(-w1 if w1 < 0 else 1)]
+    assert sorted(pairs) == sorted((s, j) for s in range(len(L))
+                                   for j in range(max(1, -(-L[s] // T))))
+
+
+GROUPED_CASES = [
+    ("shared_prefix_bf16", 64, 2),
+    ("shared_prefix_bf16", 64, 4),
+    ("shared_prefix_bf16", 512, 4),
+    ("llama8b_bf16", 64, 4),          # shared blocks built by the test
+    ("mtp4_llama8b_bf16", 64, 4),     # Q = 4: 16 rows per KV head
+    ("int8_kv", 64, 4),
+    ("fp8_kv", 16, 3),
+    ("tiny_fp32", 16, 4),             # VALU engine
+]
+
+
+@pytest.mark.parametrize("name,T,M", GROUPED_CASES)
+def test_grouped_decode_matches_oracle(name, T, M):
+    """Decode through a plan with group entries: each member still reads its
+    own table, so results match the oracle whatever the grouping."""
+    print(f"[case] grouped decode {name} T={T} M={M}", flush=True)
+    if name == "shared_prefix_bf16":
+        b = workloads.make_batch(name, 261, "cpu", groups=2, suffix_max=600)
+    else:
+        b = _share_prefixes(_mtp_batch(name, workloads.WORKLOADS[name].query_tokens, 0, 262))
+    g = _to(b, "cuda")
+    if b.fill_k is not None:
+        _fill_quantised(b, g)
+    ref = _oracle_decode(b)
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=T,
+                                num_query_tokens=b.query_tokens, block_tables=g.block_tables,
+                                group_members=M)
+    parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                           g.context_lens, g.scale, g.k_scale, g.v_scale,
+                                           max_context_len=g.max_context_len, plan=plan)
+    out = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+    pa().paged_attn_reduce(parts, out)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    n = int(sched[0])
+    assert (sched[9:9 + 2 * n:2] < 0).any(), "the batch should form groups"
+    _check_out(out.cpu().double().numpy(), ref, _tol(b), f"grouped {name} T={T} M={M}")
+
+
+def test_grouped_prepare_equals_write_then_plan():
+    print("[case] grouped prepare", flush=True)
+    b = workloads.make_batch("shared_prefix_bf16", 271, "cpu", groups=2, suffix_max=600)
+    g1, g2 = _to(b, "cuda"), _to(b, "cuda")
+    mb = b.block_tables.shape[1]
+    pa().paged_kv_write(g1.new_k, g1.new_v, g1.slot_mapping, g1.k_cache, g1.v_cache)
+    p1 = pa().paged_attn_plan(g1.context_lens, mb, max_context_len=b.max_context_len,
+                              split_tokens=64, block_tables=g1.block_tables, group_members=4)
+    p2 = pa().paged_decode_prepare(g2.new_k, g2.new_v, g2.slot_mapping, g2.k_cache, g2.v_cache,
+                                   g2.context_lens, mb, max_context_len=b.max_context_len,
+                                   split_tokens=64, block_tables=g2.block_tables,
+                                   group_members=4)
+    torch.cuda.synchronize()
+    assert torch.equal(g1.k_cache.view(torch.uint8), g2.k_cache.view(torch.uint8))
+    assert torch.equal(g1.v_cache.view(torch.uint8), g2.v_cache.view(torch.uint8))
+    n = int(p1.sched[0].item())
+    s1, s2 = p1.sched[:8 + 2 * n].cpu(), p2.sched[:8 + 2 * n].cpu()
+    assert torch.equal(s1[:8], s2[:8])
+    n_full = n - b.num_seqs
+    assert torch.equal(s1[8:8 + 2 * n_full], s2[8:8 + 2 * n_full])  # full splits: list order
+    e1 = sorted(zip(s1[8 + 2 * n_full::2].tolist(), s1[9 + 2 * n_full::2].tolist()))
+    e2 = sorted(zip(s2[8 + 2 * n_full::2].tolist(), s2[9 + 2 * n_full::2].tolist()))
+    assert e1 == e2
+
+
+def test_grouped_plan_needs_one_row_group():
+    """A plan with group entries is refused where a KV head's rows span
+    several row groups (Q * g > 16 on the MFMA engine)."""
+    b = workloads.make_batch("llama8b_bf16", 281, "cpu", num_seqs=4, ctx_range=(100, 300),
+                             query_tokens=8)
+    g = _to(b, "cuda")
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=64,
+                                num_query_tokens=8, block_tables=g.block_tables, group_members=2)
+    with pytest.raises(pa().PagedAttnError):
+        pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                       g.context_lens, g.scale,
+                                       max_context_len=g.max_context_len, plan=plan)
