@@ -34,18 +34,6 @@ __device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
   return max(0, min(p.context_lens[s], p.max_len));
 }
 
-// Whether sequence s takes part in the group of sequence s - 1 for its full
-// split j: both splits are full and start on the same physical block.
-__device__ __forceinline__ bool joins_previous(const PlanParams &p, int s, int j) {
-  if (s <= 0 || s >= p.num_seqs) return false;
-  const int Q = p.num_query_tokens, W = p.window, T = p.split_tokens;
-  if (j >= splits_of(clamp_len(p, s), Q, W, T) - 1) return false;
-  if (j >= splits_of(clamp_len(p, s - 1), Q, W, T) - 1) return false;
-  const int jb = j * (p.split_tokens / kBlock);  // first block of split j (no window: base 0)
-  return p.block_tables[(int64_t)s * p.max_blocks_per_seq + jb] ==
-         p.block_tables[(int64_t)(s - 1) * p.max_blocks_per_seq + jb];
-}
-
 __device__ __forceinline__ int seq_splits(const PlanParams &p, int L) {
   return splits_of(L, p.num_query_tokens, p.window, p.split_tokens);
 }
@@ -56,6 +44,32 @@ __device__ __forceinline__ int last_tiles(const PlanParams &p, int L) {
   if (span <= 0) return 1;
   const int rest = span - (seq_splits(p, L) - 1) * p.split_tokens;
   return (rest + kBlock - 1) / kBlock;
+}
+
+// Join flags of the full split j of sequence s: bit c (c < M) is set when
+// sequence s + c takes part in the group of sequence s + c - 1 for split j,
+// that is when both splits are full and start on the same physical block.
+// Lengths and table words of sequences s - 1 .. s + M - 1 are read together
+// (two rounds of loads, whatever M).
+__device__ __forceinline__ int join_bits(const PlanParams &p, int s, int j) {
+  constexpr int kMax = PA_MAX_GROUP_MEMBERS;
+  const int M = p.group_members;
+  const int jb = j * (p.split_tokens / kBlock);  // first block of split j (no window: base 0)
+  bool full[kMax + 1];
+  int blk[kMax + 1];
+#pragma unroll
+  for (int c = 0; c <= kMax; ++c) {
+    const int t = s - 1 + c;
+    full[c] = c <= M && t >= 0 && t < p.num_seqs && j < seq_splits(p, clamp_len(p, t)) - 1;
+  }
+#pragma unroll
+  for (int c = 0; c <= kMax; ++c)  // j < splits - 1 keeps jb inside the table row
+    blk[c] = full[c] ? p.block_tables[(int64_t)(s - 1 + c) * p.max_blocks_per_seq + jb] : -1;
+  int bits = 0;
+#pragma unroll
+  for (int c = 0; c < kMax; ++c)
+    if (c < M && full[c] && full[c + 1] && blk[c] == blk[c + 1]) bits |= 1 << c;
+  return bits;
 }
 
 // Last i with first[i] <= e, over a chunk's ascending entry offsets.
@@ -138,9 +152,10 @@ static __device__ void plan_workgroup(const PlanParams &p) {
           word0 = (s_e << 16) | j;
           L_e = chunk_len[lo];
           const int pos = s_e % M;
-          keep = !(pos > 0 && joins_previous(p, s_e, j));
+          const int bits = join_bits(p, s_e, j);
+          keep = !(pos > 0 && (bits & 1));
           if (keep)
-            while (pos + cnt < M && joins_previous(p, s_e + cnt, j)) ++cnt;
+            while (pos + cnt < M && ((bits >> cnt) & 1)) ++cnt;
         }
         int incl_k = keep;
 #pragma unroll
