@@ -11,7 +11,10 @@ Shapes:
 
 * q            [num_seqs][num_q_heads][head_dim], or
                [num_seqs][num_query_tokens][num_q_heads][head_dim] (several query
-               tokens per sequence: the last num_query_tokens tokens of its context)
+               tokens per sequence: the last num_query_tokens tokens of its context),
+               or, with query_start [num_seqs + 1], the packed
+               [query_start[-1]][num_q_heads][head_dim] (sequence s owns rows
+               query_start[s] .. query_start[s+1]-1, its last tokens)
 * k/v cache    [num_blocks][num_kv_heads][16][head_dim]
 * k/v scale    [num_blocks][num_kv_heads][16] float32 (INT8 / FP8 caches only)
 * block_tables [num_seqs][max_blocks_per_seq] int32
@@ -44,11 +47,11 @@ def _load():
         P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_kv_write.argtypes = [P, P, I, P, L, I, I, P, P, P, P, L, I]
         lib.oracle_kv_write.restype = I
-        lib.oracle_decode.argtypes = [P, I, I, I, I, P, P, P, P, I, I, I, P, I, P, D, P, P, P,
-                                      L, P]
+        lib.oracle_decode.argtypes = [P, I, I, I, I, P, P, P, P, P, I, I, I, P, I, P, D, P, P,
+                                      P, L, P]
         lib.oracle_decode.restype = None
-        lib.oracle_decode_split.argtypes = [P, I, I, I, I, I, P, P, P, P, I, I, I, P, I, P, D, I,
-                                            I, P, P, P]
+        lib.oracle_decode_split.argtypes = [P, I, I, I, I, I, P, P, P, P, P, I, I, I, P, I, P, D,
+                                            I, I, P, P, P]
         lib.oracle_decode_split.restype = None
         lib.oracle_merge.argtypes = [P, P, P, L, I, I, P]
         lib.oracle_merge.restype = None
@@ -134,16 +137,26 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
         raise ValueError("oracle_kv_write rejected its arguments")
 
 
-def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window):
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window,
+                   query_start=None):
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
     block_tables, context_lens = _c(block_tables, np.int32), _c(context_lens, np.int32)
-    if q.ndim == 3:
-        q = q.reshape(q.shape[0], 1, q.shape[1], q.shape[2])
-    num_seqs, nqt, num_q_heads, head_dim = q.shape
+    num_seqs = len(context_lens)
+    if query_start is not None:
+        query_start = _c(query_start, np.int32)
+        assert q.ndim == 3 and query_start.shape == (num_seqs + 1,) and query_start[0] == 0
+        assert (np.diff(query_start) >= 0).all() and query_start[-1] == q.shape[0]
+        counts = np.diff(query_start)
+    else:
+        if q.ndim == 3:
+            q = q.reshape(q.shape[0], 1, q.shape[1], q.shape[2])
+        assert q.shape[0] == num_seqs and q.shape[1] >= 1
+        counts = np.full(num_seqs, q.shape[1])
+    num_q_heads, head_dim = q.shape[-2], q.shape[-1]
     num_blocks, num_kv_heads, bs, hd = k_cache.shape
     assert bs == BLOCK_SIZE and hd == head_dim and num_q_heads % num_kv_heads == 0
-    assert nqt >= 1 and window >= 0
+    assert window >= 0
     if _code(k_cache) in (I8, FP8):
         assert k_scale is not None and v_scale is not None
     # Every block the definition will read must exist in the pool (blocks
@@ -152,37 +165,43 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
         L = int(context_lens[s])
         nb = -(-L // BLOCK_SIZE)
         assert nb <= block_tables.shape[1]
-        ids = block_tables[s, split_base(L, nqt, window) // BLOCK_SIZE:nb]
+        ids = block_tables[s, split_base(L, int(counts[s]), window) // BLOCK_SIZE:nb]
         assert (ids >= 0).all() and (ids < num_blocks).all()
-    return q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
+    return q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, query_start, counts
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None,
-           rows=None, window=0):
+           rows=None, window=0, query_start=None):
     """Decode attention by definition, in fp64.
 
-    q is [B][Hq][D] (one query token per sequence) or [B][Q][Hq][D]; window
-    is the sliding window in tokens (0: none). rows: optional (seq_ids,
-    head_ids) pair, or (seq_ids, query_token_ids, head_ids) triple, of
-    equal-length int arrays; the result is then [n_rows][head_dim]. Without
-    rows it has q's shape.
+    q is [B][Hq][D] (one query token per sequence) or [B][Q][Hq][D], or with
+    query_start ([B + 1] offsets) the packed [N][Hq][D]; window is the sliding
+    window in tokens (0: none). rows: optional (seq_ids, head_ids) pair, or
+    (seq_ids, query_token_ids, head_ids) triple, of equal-length int arrays
+    (query_token_ids count within the sequence); the result is then
+    [n_rows][head_dim]. Without rows it has q's shape.
     """
     shape = np.shape(q)
-    q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
-        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window)
-    num_seqs, nqt, num_q_heads, head_dim = q.shape
+    (q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, query_start,
+     counts) = _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                              window, query_start)
+    num_seqs = len(context_lens)
+    num_q_heads, head_dim = q.shape[-2], q.shape[-1]
+    nqt = 0 if query_start is not None else q.shape[1]
     if rows is None:
-        seq_ids = np.repeat(np.arange(num_seqs, dtype=np.int32), nqt * num_q_heads)
-        tok_ids = np.tile(np.repeat(np.arange(nqt, dtype=np.int32), num_q_heads), num_seqs)
-        head_ids = np.tile(np.arange(num_q_heads, dtype=np.int32), num_seqs * nqt)
+        seq_ids = np.repeat(np.arange(num_seqs, dtype=np.int32), counts * num_q_heads)
+        tok_ids = np.concatenate([np.repeat(np.arange(c, dtype=np.int32), num_q_heads)
+                                  for c in counts] or [np.zeros(0, np.int32)])
+        head_ids = np.tile(np.arange(num_q_heads, dtype=np.int32), int(counts.sum()))
     elif len(rows) == 2:
         seq_ids, head_ids = _c(rows[0], np.int32), _c(rows[1], np.int32)
         tok_ids = np.zeros_like(seq_ids)
     else:
         seq_ids, tok_ids, head_ids = (_c(r, np.int32) for r in rows)
     out = np.zeros((len(seq_ids), head_dim), dtype=np.float64)
-    _load().oracle_decode(_ptr(q), _code(q), num_q_heads, nqt, int(window), _ptr(k_cache),
-                          _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _code(k_cache),
+    _load().oracle_decode(_ptr(q), _code(q), num_q_heads, nqt, int(window), _ptr(query_start),
+                          _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                          _code(k_cache),
                           k_cache.shape[1], head_dim, _ptr(block_tables), block_tables.shape[1],
                           _ptr(context_lens), float(scale), _ptr(seq_ids), _ptr(tok_ids),
                           _ptr(head_ids), len(seq_ids), _ptr(out))
@@ -192,20 +211,26 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None,
 
 
 def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, split_tokens,
-                 max_splits=None, k_scale=None, v_scale=None, window=0):
+                 max_splits=None, k_scale=None, v_scale=None, window=0, query_start=None):
     """Split-K partials (m, l, acc) in fp64; acc is not divided by l. Shapes:
-    m, l [B](+[Q])[Hq][S], acc [B](+[Q])[Hq][S][D], following q."""
+    m, l [B](+[Q])[Hq][S], acc [B](+[Q])[Hq][S][D], following q ([N][Hq][S]
+    and [N][Hq][S][D] with query_start)."""
     lead = np.shape(q)[:-1]
-    q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens = _decode_common(
-        q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, window)
-    num_seqs, nqt, num_q_heads, head_dim = q.shape
+    (q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, query_start,
+     counts) = _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                              window, query_start)
+    num_seqs = len(context_lens)
+    num_q_heads, head_dim = q.shape[-2], q.shape[-1]
+    nqt = 0 if query_start is not None else q.shape[1]
     if max_splits is None:
-        max_splits = max(num_splits(int(L), split_tokens, nqt, window) for L in context_lens)
+        max_splits = max([num_splits(int(L), split_tokens, int(c), window)
+                          for L, c in zip(context_lens, counts)] or [1])
     m = np.zeros(lead + (max_splits,), dtype=np.float64)
     l = np.zeros_like(m)
     acc = np.zeros(lead + (max_splits, head_dim), dtype=np.float64)
     _load().oracle_decode_split(_ptr(q), _code(q), num_seqs, num_q_heads, nqt, int(window),
-                                _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                _ptr(query_start), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                _ptr(v_scale),
                                 _code(k_cache), k_cache.shape[1], head_dim, _ptr(block_tables),
                                 block_tables.shape[1], _ptr(context_lens), float(scale),
                                 int(split_tokens), int(max_splits), _ptr(m), _ptr(l), _ptr(acc))

@@ -22,6 +22,10 @@
  *                 kernel merges them.
  *   [Echo 3]      same notes, section 3, "KV Cache INT8 quantisation": INT8
  *                 cache with per-token scales, dequantised right after loading.
+ *   [Echo 3, chunked prefill]  same notes, section 3, "Chunked Prefill"
+ *                 scheduling: prompts run in chunks beside decode steps; a
+ *                 mixed batch runs either as two kernels or as one unified
+ *                 kernel that treats a decode as a prefill of length 1.
  *   [ATOM 3]      same article, quick start: every example runs with
  *                 --kv_cache_dtype fp8 (an FP8 KV cache).
  *   [ATOM 4.2]    "AMD ATOM Inference Engine" article, section 4.2 (decode
@@ -48,6 +52,12 @@
  *     tokens); with a sliding window of W > 0 tokens only p - W < t <= p
  *     (the W most recent positions, its own included); W = 0 means no window.
  *     A query with p < 0 attends nothing and gives a zero output;
+ *   - per-sequence query counts [Echo 3, chunked prefill: a batch mixing
+ *     prefill chunks and decodes in one call]: with query_start, sequence s
+ *     has Q_s = query_start[s+1] - query_start[s] query tokens (0 allowed),
+ *     stored as rows query_start[s] .. query_start[s+1]-1 of a packed q of
+ *     [query_start[num_seqs]][num_q_heads][head_dim]; each follows the rule
+ *     above with Q = Q_s (a decode sequence is the case Q_s = 1);
  *   - splits cover [base, L) with base = the start of the block holding the
  *     earliest attended token (0 without a window); split j holds tokens
  *     [base + j*T, min(base + (j+1)*T, L)), T = split_tokens, and there are
@@ -226,8 +236,10 @@ int oracle_kv_write(const void *k, const void *v, int in_dtype, const int64_t *s
 
 /* Everything the decode definition reads. */
 typedef struct {
-  const void *q; /* [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype */
+  const void *q; /* [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype, or
+                    [query_start[num_seqs]][num_q_heads][head_dim] with query_start */
   int q_dtype, num_q_heads, num_query_tokens;
+  const int32_t *query_start; /* NULL: num_query_tokens per sequence */
   const void *k, *v;      /* pool, [num_blocks][num_kv_heads][16][head_dim] */
   const float *k_scale, *v_scale; /* [num_blocks][num_kv_heads][16], INT8 / FP8 only */
   int cache_dtype, num_kv_heads, head_dim;
@@ -264,10 +276,23 @@ static double kv_elem(const decode_args *a, int which, int s, int kv, int t, int
   return x;
 }
 
-/* Logit z_t = scale * q[s][i][h] . k_t. */
+/* Number of query tokens of sequence s; *first = the q row (token index) of
+ * its query token 0. */
+static int seq_queries(const decode_args *a, int s, int64_t *first) {
+  if (a->query_start) {
+    *first = a->query_start[s];
+    return a->query_start[s + 1] - a->query_start[s];
+  }
+  *first = (int64_t)s * a->num_query_tokens;
+  return a->num_query_tokens;
+}
+
+/* Logit z_t = scale * q[s][i][h] . k_t (query token i of sequence s). */
 static double logit(const decode_args *a, int s, int i, int h, int t) {
   int kv = h / (a->num_q_heads / a->num_kv_heads);
-  int64_t row = ((int64_t)s * a->num_query_tokens + i) * a->num_q_heads + h;
+  int64_t first;
+  seq_queries(a, s, &first);
+  int64_t row = (first + i) * a->num_q_heads + h;
   double dot = 0.0;
   for (int d = 0; d < a->head_dim; ++d) {
     double qd = load_elem(a->q, a->q_dtype, row * a->head_dim + d);
@@ -311,23 +336,27 @@ static void weighted_sums(const decode_args *a, int s, int i, int h, int t0, int
  * token attends (query_range), with K and V gathered token by token through
  * the block table and the whole range taken at once (no splitting). Rows are
  * given as index lists so that a caller can check a sample of a large batch;
- * out is [n_rows][head_dim].
+ * out is [n_rows][head_dim]. query_start may be NULL (num_query_tokens per
+ * sequence).
  */
 void oracle_decode(const void *q, int q_dtype, int num_q_heads, int num_query_tokens,
-                   int window, const void *k_cache, const void *v_cache, const float *k_scale,
+                   int window, const int32_t *query_start, const void *k_cache,
+                   const void *v_cache, const float *k_scale,
                    const float *v_scale, int cache_dtype, int num_kv_heads, int head_dim,
                    const int32_t *block_tables, int max_blocks_per_seq,
                    const int32_t *context_lens, double scale, const int32_t *row_seq,
                    const int32_t *row_tok, const int32_t *row_head, int64_t n_rows,
                    double *out) {
-  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, k_cache, v_cache, k_scale,
-                   v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
+  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, query_start, k_cache, v_cache,
+                   k_scale, v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
                    max_blocks_per_seq, scale, window};
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
     int s = row_seq[r], i = row_tok[r], h = row_head[r];
+    int64_t first;
+    int Q = seq_queries(&a, s, &first);
     int t0, t1;
-    query_range(context_lens[s], num_query_tokens, window, i, &t0, &t1);
+    query_range(context_lens[s], Q, window, i, &t0, &t1);
     double m, l;
     double *o = out + r * head_dim;
     weighted_sums(&a, s, i, h, t0, t1, &m, &l, o);
@@ -358,38 +387,56 @@ int oracle_split_base(int context_len, int num_query_tokens, int window) {
  * for weighted_sums over the tokens of the split that query token attends.
  * Splits j >= max(1, ceil((L - base)/T)) are empty.
  * Layout: m, l [num_seqs][num_query_tokens][num_q_heads][max_splits];
- *         acc  [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim].
+ *         acc  [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim];
+ * with query_start the leading [num_seqs][num_query_tokens] is the packed
+ * [query_start[num_seqs]] of q.
  */
 void oracle_decode_split(const void *q, int q_dtype, int num_seqs, int num_q_heads,
-                         int num_query_tokens, int window, const void *k_cache,
+                         int num_query_tokens, int window, const int32_t *query_start,
+                         const void *k_cache,
                          const void *v_cache, const float *k_scale, const float *v_scale,
                          int cache_dtype, int num_kv_heads, int head_dim,
                          const int32_t *block_tables, int max_blocks_per_seq,
                          const int32_t *context_lens, double scale, int split_tokens,
                          int max_splits, double *m, double *l, double *acc) {
-  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, k_cache, v_cache, k_scale,
-                   v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
+  decode_args a = {q, q_dtype, num_q_heads, num_query_tokens, query_start, k_cache, v_cache,
+                   k_scale, v_scale, cache_dtype, num_kv_heads, head_dim, block_tables,
                    max_blocks_per_seq, scale, window};
-  int64_t rows_per_seq = (int64_t)num_query_tokens * num_q_heads;
-  int64_t jobs = (int64_t)num_seqs * rows_per_seq * max_splits;
+  /* The sequence and query token of every q row (token index). */
+  int64_t n_tok = query_start ? query_start[num_seqs] : (int64_t)num_seqs * num_query_tokens;
+  int *tok_seq = (int *)malloc(sizeof(int) * (size_t)(n_tok > 0 ? n_tok : 1));
+  int *tok_idx = (int *)malloc(sizeof(int) * (size_t)(n_tok > 0 ? n_tok : 1));
+  for (int s = 0; s < num_seqs; ++s) {
+    int64_t first;
+    int Q = seq_queries(&a, s, &first);
+    for (int i = 0; i < Q; ++i) {
+      tok_seq[first + i] = s;
+      tok_idx[first + i] = i;
+    }
+  }
+  int64_t jobs = n_tok * num_q_heads * max_splits;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < jobs; ++r) {
     int j = (int)(r % max_splits);
-    int64_t row = r / max_splits; /* (s, i, h) */
-    int s = (int)(row / rows_per_seq);
-    int i = (int)(row % rows_per_seq / num_q_heads);
+    int64_t row = r / max_splits; /* (token, h) */
+    int64_t tok = row / num_q_heads;
+    int s = tok_seq[tok], i = tok_idx[tok];
     int h = (int)(row % num_q_heads);
+    int64_t first;
+    int Q = seq_queries(&a, s, &first);
     int L = context_lens[s];
-    int base = oracle_split_base(L, num_query_tokens, window);
+    int base = oracle_split_base(L, Q, window);
     int t0 = base + j * split_tokens;
     int t1 = t0 + split_tokens < L ? t0 + split_tokens : L;
     if (j >= oracle_num_splits(L - base, split_tokens)) t1 = t0; /* empty split */
     int q0, q1; /* the query token's own range */
-    query_range(L, num_query_tokens, window, i, &q0, &q1);
+    query_range(L, Q, window, i, &q0, &q1);
     if (q0 > t0) t0 = q0;
     if (q1 < t1) t1 = q1;
     weighted_sums(&a, s, i, h, t0, t1, &m[r], &l[r], acc + r * head_dim);
   }
+  free(tok_seq);
+  free(tok_idx);
 }
 
 /*

@@ -709,3 +709,93 @@ def test_empty_splits_and_rows_in_multi_token_partials():
         assert np.all(m[s, :3, :, last] == -np.inf) and np.all(l[s, :3, :, last] == 0)
         assert np.all(acc[s, :3, :, last] == 0)
         assert np.all(l[s, 3, :, last] == 1.0)
+
+
+# ------------------------------------------------ per-sequence query counts
+#
+# [Echo 3, chunked prefill]: a batch may mix prefill chunks with decodes in one
+# call, a decode being a prefill of length 1. Read as: sequence s has its own
+# count Q_s (0 allowed) of query tokens, its last Q_s positions, packed as
+# rows query_start[s] .. query_start[s+1]-1 of q.
+
+MIXED_LENS = [40, 1, 100, 17, 70, 5, 33]
+MIXED_COUNTS = [3, 1, 0, 17, 1, 8, 33]   # L < Q_s for the sixth sequence
+
+
+def _mixed(seed, **kw):
+    kw.setdefault("lengths", MIXED_LENS)
+    kw.setdefault("query_counts", MIXED_COUNTS)
+    return _small("llama8b_bf16", seed, **kw)
+
+
+def _decode_mixed(b, **kw):
+    return _decode(b, query_start=_np(b.query_start), **kw)
+
+
+@pytest.mark.parametrize("W", [0, 20])
+def test_packed_queries_match_masked_sdpa(W):
+    """Every sequence against torch SDPA in fp64 on its own dense K/V, with the
+    causal (and window) mask of its own Q_s; rows of query tokens before the
+    sequence start are zero."""
+    b = _mixed(41, window=W)
+    qs = _np(b.query_start)
+    out = _decode_mixed(b, window=W)
+    assert out.shape == tuple(b.q.shape)
+    q = _f64(b.q)
+    Hq, Hkv = q.shape[1], b.k_cache.shape[1]
+    for s, (L, Q) in enumerate(zip(MIXED_LENS, MIXED_COUNTS)):
+        rows = out[qs[s]:qs[s + 1]]
+        assert rows.shape[0] == Q
+        if Q == 0:
+            continue
+        p = L - Q + np.arange(Q)
+        live = p >= 0
+        assert np.all(rows[~live] == 0)
+        k, v = _dense(b, s)
+        t = np.arange(L)
+        mask = t[None, :] <= p[live, None]
+        if W:
+            mask &= t[None, :] > (p[live, None] - W)
+        qq = torch.from_numpy(q[qs[s]:qs[s + 1]][live]).permute(1, 0, 2).unsqueeze(0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, k.unsqueeze(0).contiguous(), v.unsqueeze(0).contiguous(),
+            attn_mask=torch.from_numpy(mask), scale=b.scale, enable_gqa=(Hq != Hkv))
+        np.testing.assert_allclose(rows[live], ref[0].permute(1, 0, 2).numpy(), rtol=0,
+                                   atol=1e-12)
+
+
+def test_packed_queries_with_equal_counts_equal_the_batched_layout():
+    """Q_s = Q for every sequence is the [B][Q][Hq][D] layout flattened: the
+    same rows, bitwise, for decode and for the split partials."""
+    b = _small("llama8b_bf16", 43, num_seqs=5, ctx_range=(3, 120), query_tokens=3)
+    ref = _decode(b)
+    flat = _np(b.q).reshape(-1, *b.q.shape[2:])
+    qs = np.arange(0, 16, 3, dtype=np.int32)
+    args = (_np(b.k_cache), _np(b.v_cache), _np(b.block_tables), _np(b.context_lens), b.scale)
+    out = oracle.decode(flat, *args, query_start=qs)
+    assert np.array_equal(out.reshape(ref.shape), ref)
+    m, l, acc = oracle.decode_split(_np(b.q), *args, 32)
+    m2, l2, acc2 = oracle.decode_split(flat, *args, 32, query_start=qs)
+    assert np.array_equal(m2.reshape(m.shape), m) and np.array_equal(l2.reshape(l.shape), l)
+    assert np.array_equal(acc2.reshape(acc.shape), acc)
+
+
+@pytest.mark.parametrize("W", [0, 20])
+def test_split_invariance_with_packed_queries(W):
+    b = _mixed(45, window=W)
+    ref = _decode_mixed(b, window=W)
+    for T in (16, 48, 512):
+        m, l, acc = oracle.decode_split(_np(b.q), _np(b.k_cache), _np(b.v_cache),
+                                        _np(b.block_tables), _np(b.context_lens), b.scale, T,
+                                        window=W, query_start=_np(b.query_start))
+        assert m.shape[:2] == tuple(b.q.shape[:2])
+        np.testing.assert_allclose(oracle.merge(m, l, acc), ref, rtol=0, atol=1e-12)
+
+
+def test_one_query_token_per_sequence_is_plain_decode():
+    """Q_s = 1 everywhere (a decode batch in the packed layout) is the
+    one-token decode, bitwise."""
+    b = _small("tiny_fp32", 47, ctx_range=(1, 128))
+    ref = _decode(b)
+    qs = np.arange(b.num_seqs + 1, dtype=np.int32)
+    assert np.array_equal(_decode(b, query_start=qs), ref)

@@ -56,6 +56,16 @@ Workloads (block size 16 throughout):
 * ``prefill512_bf16``: chunked prefill, 8 seqs, 32 q / 8 KV heads, head_dim 128,
   bf16, L uniform in [2048, 8192] including a 512-token chunk whose tokens are
   the step's query tokens (written through the KV write first).
+* ``mixed_llama8b_bf16``: one call mixing decode and chunked prefill: the
+  8B-shaped batch's 64 decode sequences (one query token, L uniform in
+  [512, 4096]) followed by 2 sequences each carrying a 512-token prefill chunk
+  (L uniform in [2048, 8192], chunk included).
+
+Per-sequence query counts (``query_counts``, or a workload with prefill
+chunks): sequence s has Q_s query tokens, its last Q_s positions; q is packed
+as [N][Hq][D] with N = sum Q_s, sequence s owning rows query_start[s] ..
+query_start[s+1]-1 (``Batch.query_start``, [B+1] int32), and slot_mapping,
+new_k, new_v hold the same N rows.
 """
 from __future__ import annotations
 
@@ -84,6 +94,11 @@ class Workload:
     split_tokens: int = 512
     query_tokens: int = 1      # query tokens per sequence (mtp_k + 1)
     window: int = 0            # sliding window in tokens, 0 = none
+    # mixed batches: chunk_seqs more sequences with chunk_tokens query tokens
+    chunk_seqs: int = 0
+    chunk_tokens: int = 0
+    chunk_lo: int = 0
+    chunk_hi: int = 0
     # shared-prefix workloads
     groups: int = 0
     samples: int = 0
@@ -108,6 +123,8 @@ WORKLOADS = {
         Workload("swa4k_bf16", 64, 32, 8, 128, "bf16", "bf16", 8192, 65536, window=4096),
         Workload("prefill512_bf16", 8, 32, 8, 128, "bf16", "bf16", 2048, 8192,
                  query_tokens=512),
+        Workload("mixed_llama8b_bf16", 64, 32, 8, 128, "bf16", "bf16", 512, 4096,
+                 chunk_seqs=2, chunk_tokens=512, chunk_lo=2048, chunk_hi=8192),
     ]
 }
 
@@ -119,7 +136,8 @@ QUANTISED = ("int8", "fp8")  # caches filled through the quantising KV write
 @dataclasses.dataclass
 class Batch:
     workload: Workload
-    q: torch.Tensor               # [B][Hq][D], or [B][Q][Hq][D] with Q query tokens
+    q: torch.Tensor               # [B][Hq][D], or [B][Q][Hq][D] with Q query tokens, or
+                                  # [N][Hq][D] with per-sequence counts (query_start)
     k_cache: torch.Tensor         # [NB][Hkv][16][D]
     v_cache: torch.Tensor
     k_scale: Optional[torch.Tensor]  # [NB][Hkv][16] float32 (INT8 / FP8 only)
@@ -137,12 +155,13 @@ class Batch:
     fill_slots: Optional[torch.Tensor] = None
     num_blocks_shared: int = 0    # physical blocks referenced (shared counted once)
     num_blocks_logical: int = 0   # sum over seqs of ceil(L/16)
-    query_tokens: int = 1
+    query_tokens: int = 1         # Q, or with query_start the largest Q_s
     window: int = 0
+    query_start: Optional[torch.Tensor] = None  # [B+1] int32 (per-sequence counts)
 
     @property
     def num_seqs(self) -> int:
-        return self.q.shape[0]
+        return self.context_lens.shape[0]
 
 
 def _lengths(w: Workload, rng: np.random.Generator, num_seqs: int, ctx_lo: int, ctx_hi: int):
@@ -183,15 +202,16 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
                ctx_range: Optional[tuple] = None, poison: bool = False,
                contiguous_tables: bool = False, groups: Optional[int] = None,
                suffix_max: Optional[int] = None, query_tokens: Optional[int] = None,
-               window: Optional[int] = None, lengths=None) -> Batch:
+               window: Optional[int] = None, lengths=None, query_counts=None) -> Batch:
     """Draw one decode batch of workload ``name`` (a key of WORKLOADS or a
     Workload).
 
     num_seqs / ctx_range / groups / suffix_max shrink a workload for tests;
     query_tokens / window override the workload's; lengths fixes the context
-    lengths (one per sequence); contiguous_tables assigns physical blocks in
-    logical order instead of a random permutation (the "contiguous slice"
-    layout).
+    lengths (one per sequence); query_counts gives every sequence its own number
+    of query tokens (a packed q with query_start); contiguous_tables assigns
+    physical blocks in logical order instead of a random permutation (the
+    "contiguous slice" layout).
     """
     w = name if isinstance(name, Workload) else WORKLOADS[name]
     if groups is not None or suffix_max is not None:
@@ -208,12 +228,24 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         B = num_seqs or w.num_seqs
     lo, hi = ctx_range if ctx_range is not None else (w.ctx_lo, w.ctx_hi)
     L, suffix = _lengths(w, rng, B, lo, hi)
+    if w.chunk_seqs and lengths is None and query_counts is None:
+        Lc = rng.integers(w.chunk_lo, w.chunk_hi + 1, size=w.chunk_seqs).astype(np.int64)
+        L = np.concatenate([L, Lc])
+        query_counts = [Q] * B + [w.chunk_tokens] * w.chunk_seqs
+        B = len(L)
     if lengths is not None:
         L = np.asarray(lengths, dtype=np.int64)
         B = len(L)
+    varlen = query_counts is not None
+    if varlen:
+        Qs = np.asarray(query_counts, dtype=np.int64)
+        assert Qs.shape == (B,) and (Qs >= 0).all()
+        Q = int(Qs.max()) if B else 0
+    else:
+        Qs = np.full(B, Q, dtype=np.int64)
     nblk = -(-L // BLOCK_SIZE)
     max_blocks = int(nblk.max()) if B else 1
-    first_blk = reach_start(L, Q, W) // BLOCK_SIZE  # blocks before it are never read
+    first_blk = reach_start(L, Qs, W) // BLOCK_SIZE  # blocks before it are never read
     nalloc = nblk - first_blk
 
     # Physical block assignment.
@@ -255,13 +287,18 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
 
     D, Hq, Hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
     in_dt = TORCH_DTYPES[w.dtype]
-    q = _randn((B, Hq, D) if Q == 1 else (B, Q, Hq, D), gen, device, in_dt)
-    new_k = _randn((B * Q, Hkv, D), gen, device, in_dt)
-    new_v = _randn((B * Q, Hkv, D), gen, device, in_dt)
-    # Positions L-Q .. L-1 of every sequence, sequence-major (negative
-    # positions, for L < Q, get slot -1: nothing to write).
-    pos = (L[:, None] - Q + np.arange(Q)[None, :]).reshape(-1)
-    seq = np.repeat(np.arange(B), Q)
+    N = int(Qs.sum())
+    if varlen:
+        q = _randn((N, Hq, D), gen, device, in_dt)
+    else:
+        q = _randn((B, Hq, D) if Q == 1 else (B, Q, Hq, D), gen, device, in_dt)
+    new_k = _randn((N, Hkv, D), gen, device, in_dt)
+    new_v = _randn((N, Hkv, D), gen, device, in_dt)
+    # Positions L-Q_s .. L-1 of every sequence, sequence-major (negative
+    # positions, for L < Q_s, get slot -1: nothing to write).
+    seq = np.repeat(np.arange(B), Qs)
+    starts = np.concatenate([[0], np.cumsum(Qs)]).astype(np.int64)
+    pos = L[seq] - Qs[seq] + (np.arange(N) - starts[seq])
     ok = pos >= 0
     pos_c = np.maximum(pos, 0)
     slot_mapping = np.where(ok, tables[seq, pos_c // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE
@@ -277,7 +314,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         k_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         v_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         # Every attended token's K/V, to be written through the KV write.
-        fill_slots_np = np.unique(_attended_slots(tables, L, reach_start(L, Q, W)))
+        fill_slots_np = np.unique(_attended_slots(tables, L, reach_start(L, Qs, W)))
         fill_slots = torch.from_numpy(fill_slots_np).to(device)
         fill_k = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
         fill_v = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
@@ -287,7 +324,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         v_cache = _randn(cache_shape, gen, device, cdt)
         if poison:
             live = torch.zeros(num_blocks * BLOCK_SIZE, dtype=torch.bool)
-            live[torch.from_numpy(_attended_slots(tables, L, reach_start(L, Q, W)))] = True
+            live[torch.from_numpy(_attended_slots(tables, L, reach_start(L, Qs, W)))] = True
             dead = (~live).view(num_blocks, 1, BLOCK_SIZE, 1).expand(cache_shape).to(device)
             k_cache.masked_fill_(dead, float("nan"))
             v_cache.masked_fill_(dead, float("nan"))
@@ -301,7 +338,8 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         new_k=new_k, new_v=new_v, scale=1.0 / math.sqrt(D),
         max_context_len=int(L.max()) if B else 0, pad_block=pad_block,
         fill_k=fill_k, fill_v=fill_v, fill_slots=fill_slots,
-        num_blocks_shared=needed, num_blocks_logical=logical, query_tokens=Q, window=W)
+        num_blocks_shared=needed, num_blocks_logical=logical, query_tokens=Q, window=W,
+        query_start=(torch.from_numpy(starts.astype(np.int32)).to(device) if varlen else None))
 
 
 def kv_token_slots(prefix_len: int, gen_lens, shared: bool) -> int:
