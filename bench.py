@@ -10,9 +10,9 @@ Default workload: 8B-shaped bf16 decode batch (64 sequences, 32 q / 8 KV heads,
 head_dim 128, block 16, context lengths uniform in [512, 4096], random
 non-contiguous block tables over a pool of 1.1x the tokens).
 
-Prints ONE JSON line. `value` is tokens/s for the whole step (B * Q / t_step:
-one new token per sequence, Q query tokens per sequence for multi-token
-decode).
+Prints ONE JSON line. `value` is tokens/s for the whole step (query tokens /
+t_step: one new token per sequence, Q per sequence for multi-token decode and
+prefill chunks, the packed total N for a batch with per-sequence counts).
 The split kernel's roofline uses its own duration: HIP events on the launch
 stream around `steps` back-to-back launches of it after the timed region.
 Per-kernel p10/p50/p90 come from a pass with events between the kernels of
@@ -73,13 +73,23 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def query_counts(b):
+    """Query tokens of every sequence (per-sequence counts with packed queries)."""
+    import numpy as np
+    if b.query_start is not None:
+        return np.diff(b.query_start.to("cpu").numpy().astype(np.int64))
+    return np.full(b.num_seqs, b.query_tokens, dtype=np.int64)
+
+
 def algorithmic_flops(b):
     """Useful flops of the split kernel: per (query token, query head) and
     attended token, q.k and p.v are 2 * head_dim multiply-adds each."""
     import numpy as np
     L = b.context_lens.to("cpu").numpy().astype(np.int64)
-    Q, W = b.query_tokens, b.window
-    pos = L[:, None] - Q + np.arange(Q)[None, :]          # query positions
+    Qs, W = query_counts(b), b.window
+    seq = np.repeat(np.arange(len(L)), Qs)
+    first = np.concatenate([[0], np.cumsum(Qs)])[:-1]
+    pos = L[seq] - Qs[seq] + (np.arange(int(Qs.sum())) - first[seq])   # query positions
     lo = np.maximum(pos - W + 1, 0) if W > 0 else np.zeros_like(pos)
     attended = np.clip(pos + 1 - lo, 0, None)
     w = b.workload
@@ -89,16 +99,21 @@ def algorithmic_flops(b):
 def algorithmic_bytes(b):
     """Bytes the split kernel must read by definition: the K and V rows (plus
     INT8 scales) of every token some query token attends (with a sliding
-    window only the tokens it reaches), q, and the block-table entries used."""
+    window only the tokens it reaches; nothing of a sequence without query
+    tokens), q, and the block-table entries used."""
     import numpy as np
     import workloads
     L = b.context_lens.to("cpu").numpy().astype(np.int64)
-    lo = workloads.reach_start(L, b.query_tokens, b.window)
+    Qs = query_counts(b)
+    lo = workloads.reach_start(L, Qs, b.window)
+    live = Qs > 0
     w = b.workload
     per_token = workloads.kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.cache_dtype)
-    kv = int((L - lo).sum()) * per_token
+    kv = int((L - lo)[live].sum()) * per_token
     q = b.q.numel() * b.q.element_size()
-    tables = int(((L + 15) // 16 - lo // 16).sum()) * 4 + L.size * 4
+    tables = int(((L + 15) // 16 - lo // 16)[live].sum()) * 4 + L.size * 4
+    if b.query_start is not None:
+        tables += (L.size + 1) * 4
     return kv, kv + q + tables
 
 
@@ -121,24 +136,29 @@ def cpu_baseline(b, seconds):
     ks = None if b.k_scale is None else host(b.k_scale)
     vs = None if b.v_scale is None else host(b.v_scale)
     bt, cl = host(b.block_tables), host(b.context_lens)
-    B, Q, Hq = q.shape[0], b.query_tokens, q.shape[-2]
-    tok = np.repeat(np.arange(Q, dtype=np.int32), Hq)
-    h = np.tile(np.arange(Hq, dtype=np.int32), Q)
-    done, tokens, t0 = 0, 0, time.perf_counter()
+    qs = None if b.query_start is None else host(b.query_start)
+    B, Hq = b.num_seqs, q.shape[-2]
+    Qs = query_counts(b)
+    done, tokens, queries, t0 = 0, 0, 0, time.perf_counter()
     elapsed = 0.0
     # Whole sequences in batch order, wrapping around, until the time budget.
     while elapsed < seconds:
         s = done % B
+        Q = int(Qs[s])
+        tok = np.repeat(np.arange(Q, dtype=np.int32), Hq)
+        h = np.tile(np.arange(Hq, dtype=np.int32), Q)
         oracle.decode(q, kc, vc, bt, cl, b.scale, ks, vs,
-                      rows=(np.full(Q * Hq, s, np.int32), tok, h), window=b.window)
+                      rows=(np.full(Q * Hq, s, np.int32), tok, h), window=b.window,
+                      query_start=qs)
         tokens += int(cl[s])
+        queries += Q
         done += 1
         elapsed = time.perf_counter() - t0
     return {
-        "value": done * Q / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+        "value": queries / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{done} sequence decodes ({done / B:.2f} passes over the {B}-sequence "
-                  f"batch, {Q} query token(s) x {Hq} q heads, {tokens} context tokens), fp64 "
+        "sample": f"{done} sequences ({done / B:.2f} passes over the {B}-sequence batch, "
+                  f"{queries} query tokens x {Hq} q heads, {tokens} context tokens), fp64 "
                   f"block-table walk, {elapsed:.1f} s",
     }
 
@@ -201,19 +221,28 @@ def main():
         pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
                           b.v_scale)
         b.fill_k = b.fill_v = None
-    B, Hq, D = b.q.shape[0], b.q.shape[-2], b.q.shape[-1]
-    Q, W = b.query_tokens, b.window
+    B, Hq, D = b.num_seqs, b.q.shape[-2], b.q.shape[-1]
+    W = b.window
+    packed = b.query_start is not None
+    # Query tokens: per sequence, or the packed total N (per-sequence counts).
+    Q = b.q.shape[0] if packed else b.query_tokens
+    n_query = b.q.shape[0] if packed else B * Q
+    Qb = min(Q, pa.MAX_QUERY_TOKENS) if packed else Q          # per-sequence bound
+    Qd = max(1, min(pa.MAX_QUERY_TOKENS, -(-Q // B))) if packed else Q  # default-T count
     mb = b.block_tables.shape[1]
     T = args.split_tokens or pa.default_split_tokens(B, Hq, w.num_kv_heads, w.head_dim,
-                                                       b.k_cache.dtype, b.max_context_len, Q, W)
-    S = pa.max_splits(min(b.max_context_len, mb * 16), T, Q, W)
+                                                       b.k_cache.dtype, b.max_context_len, Qd, W)
+    S = pa.max_splits(min(b.max_context_len, mb * 16), T, Qb, W)
     out = torch.empty_like(b.q)
-    parts = pa.Partials(m=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=dev),
-                        l=torch.empty((B, Q, Hq, S), dtype=torch.float32, device=dev),
-                        acc=torch.empty((B, Q, Hq, S, D), dtype=torch.float32, device=dev),
-                        context_lens=b.context_lens, split_tokens=T, sliding_window=W)
-    sched = torch.empty(pa.sched_bytes(B, S) // 4, dtype=torch.int32, device=dev)
-    M = args.group_members or (4 if w.groups and W == 0 else 1)
+    lead = (n_query, Hq) if packed else (B, Q, Hq)
+    parts = pa.Partials(m=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
+                        l=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
+                        acc=torch.empty(lead + (S, D), dtype=torch.float32, device=dev),
+                        context_lens=b.context_lens, split_tokens=T, sliding_window=W,
+                        query_start=b.query_start)
+    sched = torch.empty(pa.sched_bytes(B, S, Q if packed else None, Hq // w.num_kv_heads) // 4,
+                        dtype=torch.int32, device=dev)
+    M = args.group_members or (4 if w.groups and W == 0 and not packed else 1)
     stream = torch.cuda.current_stream(dev)
     plan = [None]
 
@@ -223,6 +252,7 @@ def main():
                                           b.v_cache, b.context_lens, mb, b.k_scale, b.v_scale,
                                           max_context_len=b.max_context_len, split_tokens=T,
                                           num_query_tokens=Q, sliding_window=W,
+                                          num_q_heads=Hq, query_start=b.query_start,
                                           block_tables=b.block_tables, group_members=M,
                                           sched=sched)
 
@@ -230,7 +260,8 @@ def main():
         pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
                                      b.scale, b.k_scale, b.v_scale,
                                      max_context_len=b.max_context_len, split_tokens=T,
-                                     sliding_window=W, plan=plan[0], partials=parts)
+                                     sliding_window=W, plan=plan[0], query_start=b.query_start,
+                                     partials=parts)
 
     def reduce():
         pa.paged_attn_reduce(parts, out)
@@ -294,7 +325,7 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": B * Q / (ms_step * 1e-3),
+        "value": n_query / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -311,7 +342,8 @@ def main():
             "head_dim": D, "block_size": 16, "cache_dtype": w.cache_dtype,
             "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
-            "query_tokens": Q, "sliding_window": W, "group_members": M,
+            "query_tokens": (f"packed: {n_query} over {B} sequences" if packed else Q),
+            "sliding_window": W, "group_members": M,
             "tables": "contiguous" if args.contiguous_tables else "permuted",
             "context_range": list(args.ctx_range) if args.ctx_range else
             [b.workload.ctx_lo, b.workload.ctx_hi],
@@ -319,7 +351,7 @@ def main():
         },
         "kv_read_gbps": kv_gbps_step,
         "kv_read_frac_of_peak": kv_gbps_step / HBM_PEAK_GBPS,
-        "decode_reduce_tokens_per_s": B * Q / ((t_dec + t_red) * 1e-3),
+        "decode_reduce_tokens_per_s": n_query / ((t_dec + t_red) * 1e-3),
         "kernel_ms": {"write_and_plan": t_prep, "decode_split": t_dec, "reduce": t_red,
                       "decode_split_back_to_back": t_dec_b2b},
         "kernel_us_p10_p50_p90": {k: [round(1e3 * pct(v, q), 2) for q in (0.1, 0.5, 0.9)]

@@ -16,8 +16,11 @@
  *     a second reduce kernel, and a split count that follows the context length
  *     (split_num = context_len / chunk, chunk 256 or 512 from profiling);
  *     section 3 (KV Cache INT8): INT8 cache with per-token scales, dequantised
- *     inside the attention kernel right after loading; section 4: sliding
- *     window attention as a way to bound decode cost.
+ *     inside the attention kernel right after loading, and chunked prefill
+ *     (prompts run in chunks beside decode steps; a mixed batch runs as two
+ *     kernels or as one unified kernel that treats a decode as a prefill of
+ *     length 1); section 4: sliding window attention as a way to bound decode
+ *     cost.
  *   - "AMD ATOM Inference Engine" article, quick start (section 3): an FP8 KV
  *     cache (--kv_cache_dtype fp8); section 4.2 (decode scheduling):
  *     with MTP speculative decoding each decode step of a sequence carries
@@ -42,7 +45,12 @@
  *     q and out are [num_seqs][Q][num_q_heads][head_dim] (for Q = 1 the same
  *     memory as [num_seqs][num_q_heads][head_dim]). Q = 1 is a decode step,
  *     Q = mtp_k + 1 an MTP verification step, a larger Q a chunk of prefill
- *     over the cache.
+ *     over the cache. With packed queries (a query_start array, see
+ *     paged_attn_plan) every sequence has its own count Q_s (0 to 4096), the
+ *     same rule applies with Q = Q_s, and q, out and the partials' rows are
+ *     packed as [N][num_q_heads] with N = sum Q_s, sequence s owning rows
+ *     query_start[s] .. query_start[s+1] - 1: one call for a batch that mixes
+ *     decodes and prefill chunks.
  *   - Logits are scale * q.k; softmax uses the natural exponent over the
  *     tokens a query token attends.
  *   - Splits cover [base, L), base = 16 * floor(max(0, L - Q - W + 1) / 16)
@@ -87,6 +95,7 @@ extern "C" {
 #define PA_MAX_SPLIT_TOKENS 4096
 #define PA_MAX_SEQS 65535
 #define PA_MAX_QUERY_TOKENS 4096
+#define PA_MAX_PACKED_QUERY_TOKENS (1 << 20)
 #define PA_MAX_GROUP_MEMBERS 4
 
 /* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
@@ -143,10 +152,22 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * a small header). */
 size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits);
 
+/* The same for packed queries (query_start given): the list then holds one
+ * entry per (split, block of 64 query rows) of each sequence, at most
+ * max_splits * (num_seqs + ceil(total_query_tokens * q_heads_per_kv / 64)). */
+size_t pa_sched_bytes_packed(int32_t num_seqs, int32_t max_splits, int32_t total_query_tokens,
+                             int32_t q_heads_per_kv);
+
 /* Bytes of workspace paged_attn_decode needs: scheduling scratch plus the
  * partials (m, l, acc) of num_seqs * num_query_tokens * num_q_heads rows. */
 size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
                           int32_t head_dim, int32_t max_splits);
+
+/* The same for packed queries: partials of total_query_tokens * num_q_heads
+ * rows and the packed plan. */
+size_t pa_workspace_bytes_packed(int32_t num_seqs, int32_t total_query_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_splits);
 
 /*
  * KV write ("reshape and cache") [ATOM article 5.1; Primer 8.1]: for every
@@ -178,14 +199,31 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  * the device and writes into `sched` the list of every split of the batch,
  * max(1, ceil((L_s - base_s) / T)) per sequence (see the split range above),
  * full splits first and then the last split of each sequence, longest first.
- * The list depends only on the lengths, Q, W, T and the length bounds (and,
- * with grouping, the tables), so one plan serves every attention layer of a
- * step that uses the same window.
+ * The list depends only on the lengths, the query counts, W, T and the length
+ * bounds (and, with grouping, the tables), so one plan serves every attention
+ * layer of a step that uses the same window.
  *   context_lens       [num_seqs] int32 (device)
+ *   query_start        NULL: every sequence has num_query_tokens query tokens.
+ *                      Else packed queries [EchoLLMServing notes, section 3,
+ *                      chunked prefill: one call for a batch that mixes prefill
+ *                      chunks and decodes, a decode being a chunk of length 1]:
+ *                      [num_seqs + 1] int32 (device), 0 = query_start[0] <=
+ *                      query_start[1] <= ... <= query_start[num_seqs] =
+ *                      num_query_tokens; sequence s has Q_s = query_start[s+1]
+ *                      - query_start[s] <= PA_MAX_QUERY_TOKENS query tokens (0
+ *                      allowed), its last Q_s positions, packed as rows
+ *                      query_start[s] .. query_start[s+1] - 1. Trusted device
+ *                      data: spans are clamped into [0, num_query_tokens) so
+ *                      that nothing is read or written out of bounds, and other
+ *                      offsets give unspecified results.
  *   block_tables       [num_seqs][max_blocks_per_seq] int32 (device); read
  *                      only with group_members > 1, may be NULL otherwise
  *   max_blocks_per_seq, max_context_len   the bounds the decode call will use
- *   num_query_tokens   Q, 1 .. PA_MAX_QUERY_TOKENS
+ *   num_query_tokens   Q, 1 .. PA_MAX_QUERY_TOKENS; with query_start the total
+ *                      N, 0 .. PA_MAX_PACKED_QUERY_TOKENS
+ *   q_heads_per_kv     g = num_q_heads / num_kv_heads (1, 2, 4, 8 or 16); read
+ *                      only with query_start (a packed plan lists blocks of 64
+ *                      query rows, Q_s * g rows per sequence)
  *   sliding_window     W >= 0 (0: none)
  *   split_tokens       T, a positive multiple of 16 <= 4096 (the plan knows no
  *                      cache, so there is no default here: pass what the
@@ -199,16 +237,20 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
  *                      one per wave over shared, cached tile reads. Results do
  *                      not depend on it (each sequence still reads its own
  *                      table); it costs a few table reads per split in the plan.
- *                      Requires W = 0; a plan with groups is used only when
- *                      Q * g <= 16 rows (MFMA engine) or 8 (VALU engine), and
- *                      is otherwise ignored like any mismatched plan.
+ *                      Requires W = 0 and no query_start; a plan with groups
+ *                      is used only when Q * g <= 16 rows (MFMA engine) or 8
+ *                      (VALU engine), and is otherwise ignored like any
+ *                      mismatched plan.
  *   sched              device scratch of pa_sched_bytes(num_seqs, max_splits)
- *                      bytes, max_splits >= pa_max_splits(max_context_len, Q, W, T)
+ *                      bytes (pa_sched_bytes_packed(num_seqs, max_splits, N, g)
+ *                      with query_start), max_splits >= pa_max_splits(
+ *                      max_context_len, Q', W, T) with Q' = Q, or min(N, 4096)
  */
-int paged_attn_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
-                    int32_t max_blocks_per_seq, int32_t max_context_len,
-                    int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                    int32_t group_members, int32_t *sched, hipStream_t stream);
+int paged_attn_plan(const int32_t *context_lens, const int32_t *query_start,
+                    const int32_t *block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int32_t num_query_tokens, int32_t q_heads_per_kv,
+                    int32_t sliding_window, int32_t split_tokens, int32_t group_members,
+                    int32_t *sched, hipStream_t stream);
 
 /*
  * paged_kv_write followed by paged_attn_plan, in one launch: the two do not
@@ -216,17 +258,19 @@ int paged_attn_plan(const int32_t *context_lens, const int32_t *block_tables, in
  * others write). Arguments, layouts and errors are those of the two calls
  * (split_tokens is required, as for the plan); the results are identical to
  * calling them in turn. Serves the start of a decode step, where the new tokens
- * (num_seqs * Q of them with several query tokens) are written and the batch's
- * splits are listed.
+ * (num_seqs * Q of them with several query tokens, N with packed queries) are
+ * written and the batch's splits are listed.
  */
 int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, const int32_t *block_tables,
-                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                         int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                         int32_t group_members, int32_t *sched, hipStream_t stream);
+                         const int32_t *context_lens, const int32_t *query_start,
+                         const int32_t *block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t num_query_tokens, int32_t q_heads_per_kv,
+                         int32_t sliding_window, int32_t split_tokens, int32_t group_members,
+                         int32_t *sched, hipStream_t stream);
 
 /*
  * Split-K decode kernel [EchoLLMServing notes, section 2]: for every sequence
@@ -234,29 +278,35 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
  * (m, l, acc) of that split. The Q*g rows (query tokens x query heads) of a KV
  * head share every K/V load. Works through the split list of `sched`, which
  * paged_attn_plan must have written (on this stream, before this call) for the
- * same context_lens, num_seqs, max_blocks_per_seq, max_context_len, Q, W and
- * split_tokens; a plan for another split_tokens, num_seqs, length bound, Q or
- * W is ignored (nothing is written), other mismatches give unspecified results.
+ * same context_lens, query_start, num_seqs, max_blocks_per_seq,
+ * max_context_len, Q (or N), W and split_tokens; a plan for another
+ * split_tokens, num_seqs, length bound, query count, query layout or W is
+ * ignored (nothing is written), other mismatches give unspecified results.
  *   q                 [num_seqs][num_query_tokens][num_q_heads][head_dim] of q_dtype
- *                     (PA_F32/PA_BF16)
+ *                     (PA_F32/PA_BF16); with query_start the packed
+ *                     [num_query_tokens = N][num_q_heads][head_dim]
  *   k_cache, ...      pool as above; cache_dtype PA_F32 (q PA_F32), PA_BF16
  *                     (q PA_BF16), PA_I8 or PA_FP8 (q PA_BF16 or PA_F32;
  *                     k_scale and v_scale required). num_blocks < 2^31.
  *   block_tables      [num_seqs][max_blocks_per_seq] int32
  *   context_lens      [num_seqs] int32, each <= max_context_len
+ *   query_start       NULL, or the packed query offsets (see paged_attn_plan)
  *   max_context_len   host bound on context_lens, sizes the launch grid
  *   sliding_window    W >= 0 (0: none)
  *   scale             logit scale (commonly 1/sqrt(head_dim))
  *   split_tokens      T, a positive multiple of 16 <= 4096, or 0 for
- *                     pa_default_split_tokens()
+ *                     pa_default_split_tokens() (with Q' below for Q)
  *   max_splits        leading stride of the partials;
- *                     >= pa_max_splits(max_context_len, Q, W, T)
+ *                     >= pa_max_splits(max_context_len, Q', W, T), Q' = Q, or
+ *                     min(N, PA_MAX_QUERY_TOKENS) with query_start
  *   part_m, part_l    [num_seqs][num_query_tokens][num_q_heads][max_splits] fp32
- *   part_acc          [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim] fp32,
- *                     16-byte aligned
+ *                     ([N][num_q_heads][max_splits] with query_start)
+ *   part_acc          [num_seqs][num_query_tokens][num_q_heads][max_splits][head_dim] fp32
+ *                     ([N][num_q_heads][max_splits][head_dim]), 16-byte aligned
  *   sched             the plan (read only)
  * head_dim must be 64 or 128, num_q_heads / num_kv_heads one of 1, 2, 4, 8, 16,
- * num_query_tokens 1 .. PA_MAX_QUERY_TOKENS and num_seqs at most PA_MAX_SEQS.
+ * num_query_tokens 1 .. PA_MAX_QUERY_TOKENS (N 0 .. PA_MAX_PACKED_QUERY_TOKENS
+ * with query_start) and num_seqs at most PA_MAX_SEQS.
  */
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
@@ -264,10 +314,10 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
                               int32_t num_kv_heads, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens,
-                              int32_t max_context_len, int32_t sliding_window, float scale,
-                              int32_t split_tokens, int32_t max_splits, float *part_m,
-                              float *part_l, float *part_acc, const int32_t *sched,
-                              hipStream_t stream);
+                              const int32_t *query_start, int32_t max_context_len,
+                              int32_t sliding_window, float scale, int32_t split_tokens,
+                              int32_t max_splits, float *part_m, float *part_l,
+                              float *part_acc, const int32_t *sched, hipStream_t stream);
 
 /*
  * Reduce kernel [EchoLLMServing notes, section 2]: merge the partials of every
@@ -276,16 +326,19 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
  *   out = sum_j w_j acc_j / sum_j w_j l_j   (0 when no split holds a token),
  * written as out_dtype (PA_F32, or PA_BF16 rounded to nearest even).
  *   part_*         as written by paged_attn_decode_partial with the same
- *                  num_query_tokens, sliding_window, split_tokens (T > 0) and
- *                  max_splits
+ *                  query_start, num_query_tokens, sliding_window, split_tokens
+ *                  (T > 0) and max_splits
  *   context_lens   [num_seqs] int32 (lengths are clamped to >= 0)
+ *   query_start    NULL, or the packed query offsets (each packed row finds
+ *                  its sequence by binary search over them)
  *   out            [num_seqs][num_query_tokens][num_q_heads][head_dim]
+ *                  ([N][num_q_heads][head_dim] with query_start)
  */
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
-                      const int32_t *context_lens, int32_t num_seqs, int32_t num_query_tokens,
-                      int32_t num_q_heads, int32_t head_dim, int32_t sliding_window,
-                      int32_t split_tokens, int32_t max_splits, void *out, int32_t out_dtype,
-                      hipStream_t stream);
+                      const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
+                      int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                      int32_t sliding_window, int32_t split_tokens, int32_t max_splits,
+                      void *out, int32_t out_dtype, hipStream_t stream);
 
 /*
  * Whole decode step of one attention layer: paged_attn_plan (no grouping) and
@@ -295,16 +348,19 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
  * max_context_len' = min(max_context_len, 16 * max_blocks_per_seq) and
  * T = split_tokens (0: pa_default_split_tokens()). workspace must hold
  * pa_workspace_bytes(num_seqs, Q, num_q_heads, head_dim, that split count)
- * bytes, 256-byte aligned.
+ * bytes (pa_workspace_bytes_packed(num_seqs, N, num_q_heads, num_kv_heads,
+ * head_dim, that split count) with query_start, where Q' = min(N, 4096)
+ * stands for Q), 256-byte aligned.
  */
 int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_query_tokens,
                       int32_t num_q_heads, int32_t head_dim, const void *k_cache,
                       const void *v_cache, const float *k_scale, const float *v_scale,
                       int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
                       const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *context_lens, int32_t max_context_len,
-                      int32_t sliding_window, float scale, int32_t split_tokens, void *out,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+                      const int32_t *context_lens, const int32_t *query_start,
+                      int32_t max_context_len, int32_t sliding_window, float scale,
+                      int32_t split_tokens, void *out, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * Measurement aid (not part of the attention path): read `bytes` (a multiple

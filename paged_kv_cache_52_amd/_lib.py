@@ -23,23 +23,29 @@ SIGNATURES = {
     "pa_max_splits": (_I32, [_I32, _I32, _I32, _I32]),
     "pa_default_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_sched_bytes": (_SZ, [_I32, _I32]),
+    "pa_sched_bytes_packed": (_SZ, [_I32, _I32, _I32, _I32]),
     "pa_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_workspace_bytes_packed": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_kv_write": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P, _I64,
                                       _I32, _P]),
+    # q, q_dtype, B, Q, Hq, D, kc, vc, ks, vs, cache_dtype, NB, Hkv, tables, mb,
+    # context_lens, query_start, mcl, W, scale, T, S, m, l, acc, sched, stream
     "paged_attn_decode_partial": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
-                                                 _P, _I32, _I64, _I32, _P, _I32, _P, _I32, _I32,
-                                                 _F32, _I32, _I32, _P, _P, _P, _P, _P]),
-    "paged_attn_plan": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
-                                       _P]),
+                                                 _P, _I32, _I64, _I32, _P, _I32, _P, _P, _I32,
+                                                 _I32, _F32, _I32, _I32, _P, _P, _P, _P, _P]),
+    # context_lens, query_start, tables, B, mb, mcl, Q, g, W, T, group_members, sched, stream
+    "paged_attn_plan": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       _I32, _P, _P]),
     "paged_decode_prepare": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P,
-                                            _I64, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
-                                            _I32, _I32, _P, _P]),
-    "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _I64, _I32, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _I32, _I32, _P, _P]),
+    # m, l, acc, context_lens, query_start, B, Q, Hq, D, W, T, S, out, out_dtype, stream
+    "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _I32, _P, _I32, _P]),
     "pa_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),
     "paged_attn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
-                                         _I64, _I32, _P, _I32, _P, _I32, _I32, _F32, _I32, _P,
-                                         _P, _SZ, _P]),
+                                         _I64, _I32, _P, _I32, _P, _P, _I32, _I32, _F32, _I32,
+                                         _P, _P, _SZ, _P]),
 }
 
 _lib = None

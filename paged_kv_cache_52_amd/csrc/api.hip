@@ -29,6 +29,39 @@ bool bad_query_shape(int32_t num_query_tokens, int32_t sliding_window) {
   return num_query_tokens < 1 || num_query_tokens > PA_MAX_QUERY_TOKENS || sliding_window < 0;
 }
 
+// Query counts: Q per sequence, or (packed) the total N of all sequences.
+bool bad_queries(bool packed, int32_t num_query_tokens, int32_t sliding_window) {
+  if (!packed) return bad_query_shape(num_query_tokens, sliding_window);
+  return num_query_tokens < 0 || num_query_tokens > PA_MAX_PACKED_QUERY_TOKENS ||
+         sliding_window < 0;
+}
+
+// Largest query count of one sequence: Q, or at most min(N, PA_MAX_QUERY_TOKENS).
+int32_t query_bound(bool packed, int32_t num_query_tokens) {
+  return packed ? std::max(1, std::min(num_query_tokens, PA_MAX_QUERY_TOKENS)) : num_query_tokens;
+}
+
+// Query count the default split size is chosen for: Q, or with packed
+// queries the mean count per sequence.
+int32_t query_for_default(bool packed, int32_t num_query_tokens, int32_t num_seqs) {
+  if (!packed) return num_query_tokens;
+  const int64_t mean = ((int64_t)num_query_tokens + std::max(num_seqs, 1) - 1) /
+                       std::max(num_seqs, 1);
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(mean, PA_MAX_QUERY_TOKENS));
+}
+
+// Entries the plan lists at most: one per split of each sequence, or with
+// packed queries one per (split, block of 64 query rows) of each sequence
+// (sum over s of ceil(Q_s*g/64) <= num_seqs + ceil(N*g/64)).
+int64_t plan_capacity(int32_t num_seqs, int32_t max_splits, bool packed, int32_t num_query_tokens,
+                      int32_t g) {
+  const int64_t per_split =
+      packed ? (int64_t)num_seqs + ((int64_t)num_query_tokens * g + pa::kPackedRows - 1) /
+                                       pa::kPackedRows
+             : num_seqs;
+  return per_split * std::max(max_splits, 1);
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
 // The length bound the kernels clamp every context length to.
@@ -48,7 +81,7 @@ const char *pa_strerror(int status) {
     case PA_OK: return "success";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_DTYPE: return "unsupported dtype or dtype combination";
-    case PA_ERR_SHAPE: return "unsupported sizes (head_dim 64/128, Hq/Hkv in {1,2,4,8,16}, 1..16 query tokens, window >= 0, counts >= 0)";
+    case PA_ERR_SHAPE: return "unsupported sizes (head_dim 64/128, Hq/Hkv in {1,2,4,8,16}, 1..4096 query tokens per sequence, window >= 0, counts >= 0)";
     case PA_ERR_SPLIT: return "split_tokens must be a positive multiple of 16 up to 4096, and max_splits must cover the longest split range";
     case PA_ERR_WORKSPACE: return "workspace smaller than pa_workspace_bytes()";
     case PA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -112,7 +145,16 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits) {
   if (num_seqs < 0 || max_splits < 0) return 0;
-  return align256((pa::kSchedHeader + 2 * (size_t)num_seqs * std::max(max_splits, 1)) *
+  return align256((pa::kSchedHeader + 2 * (size_t)plan_capacity(num_seqs, max_splits, false, 0, 1)) *
+                  sizeof(int32_t));
+}
+
+size_t pa_sched_bytes_packed(int32_t num_seqs, int32_t max_splits, int32_t total_query_tokens,
+                             int32_t q_heads_per_kv) {
+  if (num_seqs < 0 || max_splits < 0 || total_query_tokens < 0 || q_heads_per_kv <= 0) return 0;
+  return align256((pa::kSchedHeader +
+                   2 * (size_t)plan_capacity(num_seqs, max_splits, true, total_query_tokens,
+                                             q_heads_per_kv)) *
                   sizeof(int32_t));
 }
 
@@ -123,6 +165,18 @@ size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t nu
   const size_t rows = (size_t)num_seqs * num_query_tokens * num_q_heads * max_splits;
   return pa_sched_bytes(num_seqs, max_splits) + 2 * align256(rows * sizeof(float)) +
          align256(rows * head_dim * sizeof(float));
+}
+
+size_t pa_workspace_bytes_packed(int32_t num_seqs, int32_t total_query_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_splits) {
+  if (num_seqs < 0 || total_query_tokens < 0 || num_q_heads < 0 || num_kv_heads <= 0 ||
+      head_dim < 0 || max_splits < 0)
+    return 0;
+  const size_t rows = (size_t)total_query_tokens * num_q_heads * max_splits;
+  return pa_sched_bytes_packed(num_seqs, max_splits, total_query_tokens,
+                               std::max(1, num_q_heads / num_kv_heads)) +
+         2 * align256(rows * sizeof(float)) + align256(rows * head_dim * sizeof(float));
 }
 
 }  // extern "C"
@@ -153,22 +207,30 @@ int check_write(const void *k, const void *v, int32_t in_dtype, const int64_t *s
 }
 
 // Argument checks of the plan; fills `out` on success.
-int check_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
-               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_query_tokens,
+int check_plan(const int32_t *context_lens, const int32_t *query_start,
+               const int32_t *block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+               int32_t max_context_len, int32_t num_query_tokens, int32_t q_heads_per_kv,
                int32_t sliding_window, int32_t split_tokens, int32_t group_members,
                int32_t *sched, pa::PlanParams *out) {
+  const bool packed = query_start != nullptr;
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
-  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (packed && !supported_group(q_heads_per_kv)) return PA_ERR_SHAPE;
   if (group_members < 1 || group_members > PA_MAX_GROUP_MEMBERS) return PA_ERR_SHAPE;
-  if (group_members > 1 && sliding_window > 0) return PA_ERR_SHAPE;
+  if (group_members > 1 && (sliding_window > 0 || packed)) return PA_ERR_SHAPE;
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   if (num_seqs > 0 && (!context_lens || !sched)) return PA_ERR_NULL;
   if (num_seqs > 0 && group_members > 1 && !block_tables) return PA_ERR_NULL;
-  *out = pa::PlanParams{context_lens, sched, num_seqs,
-                        clamped_bound(max_context_len, max_blocks_per_seq), split_tokens,
-                        num_query_tokens, sliding_window, block_tables, max_blocks_per_seq,
-                        group_members};
+  const int32_t lmax = clamped_bound(max_context_len, max_blocks_per_seq);
+  const int32_t ns = pa_max_splits(lmax, query_bound(packed, num_query_tokens), sliding_window,
+                                   split_tokens);
+  const int64_t cap = plan_capacity(num_seqs, ns, packed, num_query_tokens,
+                                    packed ? q_heads_per_kv : 1);
+  if (cap > INT_MAX / 2) return PA_ERR_SHAPE;
+  *out = pa::PlanParams{context_lens, sched, num_seqs, lmax, split_tokens, num_query_tokens,
+                        sliding_window, block_tables, max_blocks_per_seq, group_members,
+                        query_start, packed ? q_heads_per_kv : 0, (int32_t)cap};
   return PA_OK;
 }
 
@@ -187,14 +249,16 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
   return launch_status(pa::launch_kv_write(w, stream));
 }
 
-int paged_attn_plan(const int32_t *context_lens, const int32_t *block_tables, int32_t num_seqs,
-                    int32_t max_blocks_per_seq, int32_t max_context_len,
-                    int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                    int32_t group_members, int32_t *sched, hipStream_t stream) {
+int paged_attn_plan(const int32_t *context_lens, const int32_t *query_start,
+                    const int32_t *block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int32_t num_query_tokens, int32_t q_heads_per_kv,
+                    int32_t sliding_window, int32_t split_tokens, int32_t group_members,
+                    int32_t *sched, hipStream_t stream) {
   pa::PlanParams pl;
-  const int st = check_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq,
-                            max_context_len, num_query_tokens, sliding_window, split_tokens,
-                            group_members, sched, &pl);
+  const int st = check_plan(context_lens, query_start, block_tables, num_seqs,
+                            max_blocks_per_seq, max_context_len, num_query_tokens,
+                            q_heads_per_kv, sliding_window, split_tokens, group_members, sched,
+                            &pl);
   if (st != PA_OK || num_seqs == 0) return st;
   return launch_status(pa::launch_plan(pl, stream));
 }
@@ -203,17 +267,20 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, void *k_cache, void *v_cache, float *k_scale,
                          float *v_scale, int64_t num_blocks, int32_t cache_dtype,
-                         const int32_t *context_lens, const int32_t *block_tables,
-                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                         int32_t num_query_tokens, int32_t sliding_window, int32_t split_tokens,
-                         int32_t group_members, int32_t *sched, hipStream_t stream) {
+                         const int32_t *context_lens, const int32_t *query_start,
+                         const int32_t *block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t num_query_tokens, int32_t q_heads_per_kv,
+                         int32_t sliding_window, int32_t split_tokens, int32_t group_members,
+                         int32_t *sched, hipStream_t stream) {
   pa::WriteParams w;
   pa::PlanParams pl;
   int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
                        v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK) return st;
-  st = check_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq, max_context_len,
-                  num_query_tokens, sliding_window, split_tokens, group_members, sched, &pl);
+  st = check_plan(context_lens, query_start, block_tables, num_seqs, max_blocks_per_seq,
+                  max_context_len, num_query_tokens, q_heads_per_kv, sliding_window,
+                  split_tokens, group_members, sched, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
   return launch_status(pa::launch_prepare(w, pl, stream));
@@ -225,14 +292,15 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                               const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
                               int32_t num_kv_heads, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens,
-                              int32_t max_context_len, int32_t sliding_window, float scale,
-                              int32_t split_tokens, int32_t max_splits, float *part_m,
-                              float *part_l, float *part_acc, const int32_t *sched,
-                              hipStream_t stream) {
+                              const int32_t *query_start, int32_t max_context_len,
+                              int32_t sliding_window, float scale, int32_t split_tokens,
+                              int32_t max_splits, float *part_m, float *part_l,
+                              float *part_acc, const int32_t *sched, hipStream_t stream) {
+  const bool packed = query_start != nullptr;
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || num_kv_heads <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_SHAPE;
-  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0 || !supported_group(num_q_heads / num_kv_heads))
     return PA_ERR_SHAPE;
@@ -241,20 +309,32 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
                      (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
                      ((q_dtype == PA_BF16 || q_dtype == PA_F32) && quantised(cache_dtype));
   if (!dt_ok) return PA_ERR_DTYPE;
+  const int32_t qmax = query_bound(packed, num_query_tokens);
   if (split_tokens == 0)
-    split_tokens = pa_default_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           cache_dtype, max_context_len, num_query_tokens,
-                                           sliding_window);
+    split_tokens = pa_default_split_tokens(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype, max_context_len,
+        query_for_default(packed, num_query_tokens, num_seqs), sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
   // Splits of the longest range any sequence can have under the clamped bound.
-  const int32_t grid_splits =
-      pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq), num_query_tokens,
-                    sliding_window, split_tokens);
+  const int32_t grid_splits = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
+                                            qmax, sliding_window, split_tokens);
   if (max_splits < grid_splits) return PA_ERR_SPLIT;
-  if (num_seqs == 0) return PA_OK;
+  // Entries the plan can list: the grid has one workgroup per possible item.
+  const int64_t max_entries = plan_capacity(num_seqs, grid_splits, packed, num_query_tokens,
+                                            num_q_heads / num_kv_heads);
+  // Workgroups per entry: Hkv, times (uniform Q) the sets of at least 32 rows
+  // of a KV head's Q*g rows.
+  const int64_t per_entry =
+      (int64_t)num_kv_heads *
+      (packed ? 1 : ((int64_t)qmax * (num_q_heads / num_kv_heads) + 31) / 32);
+  if (max_entries * per_entry > INT_MAX) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || (packed && num_query_tokens == 0)) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !part_m || !part_l ||
       !part_acc || !sched)
     return PA_ERR_NULL;
+  if ((int64_t)num_query_tokens * num_q_heads * (packed ? 1 : num_seqs) * max_splits >
+      INT64_MAX / (head_dim * 4))
+    return PA_ERR_SHAPE;
   if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(part_acc))
     return PA_ERR_ALIGN;
@@ -282,40 +362,43 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   p.num_query_tokens = num_query_tokens;
   p.window = sliding_window;
   p.group = num_q_heads / num_kv_heads;
+  p.query_start = query_start;
   p.sched = sched;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   hipError_t e;
   if (q_dtype == PA_BF16 && cache_dtype == PA_BF16)
-    e = pa::decode_bf16_bf16(p, grid_splits, stream);
+    e = pa::decode_bf16_bf16(p, max_entries, stream);
   else if (q_dtype == PA_F32 && cache_dtype == PA_F32)
-    e = pa::decode_f32_f32(p, grid_splits, stream);
+    e = pa::decode_f32_f32(p, max_entries, stream);
   else if (q_dtype == PA_BF16 && cache_dtype == PA_I8)
-    e = pa::decode_bf16_i8(p, grid_splits, stream);
+    e = pa::decode_bf16_i8(p, max_entries, stream);
   else if (cache_dtype == PA_I8)
-    e = pa::decode_f32_i8(p, grid_splits, stream);
+    e = pa::decode_f32_i8(p, max_entries, stream);
   else if (q_dtype == PA_BF16)
-    e = pa::decode_bf16_fp8(p, grid_splits, stream);
+    e = pa::decode_bf16_fp8(p, max_entries, stream);
   else
-    e = pa::decode_f32_fp8(p, grid_splits, stream);
+    e = pa::decode_f32_fp8(p, max_entries, stream);
   return launch_status(e);
 }
 
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
-                      const int32_t *context_lens, int32_t num_seqs, int32_t num_query_tokens,
-                      int32_t num_q_heads, int32_t head_dim, int32_t sliding_window,
-                      int32_t split_tokens, int32_t max_splits, void *out, int32_t out_dtype,
-                      hipStream_t stream) {
+                      const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
+                      int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                      int32_t sliding_window, int32_t split_tokens, int32_t max_splits,
+                      void *out, int32_t out_dtype, hipStream_t stream) {
+  const bool packed = query_start != nullptr;
   if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0) return PA_ERR_SHAPE;
-  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  if ((int64_t)num_query_tokens * num_q_heads > INT_MAX) return PA_ERR_SHAPE;
   if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_DTYPE;
   if (check_split_tokens(split_tokens) != PA_OK || max_splits <= 0) return PA_ERR_SPLIT;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0 || (packed && num_query_tokens == 0)) return PA_OK;
   if (!part_m || !part_l || !part_acc || !context_lens || !out) return PA_ERR_NULL;
   pa::ReduceParams p{part_m, part_l, part_acc, context_lens, out, num_seqs, num_q_heads,
                      head_dim, split_tokens, max_splits, out_dtype, num_query_tokens,
-                     sliding_window};
+                     sliding_window, query_start};
   return launch_status(pa::launch_reduce(p, stream));
 }
 
@@ -324,47 +407,56 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       const void *v_cache, const float *k_scale, const float *v_scale,
                       int32_t cache_dtype, int64_t num_blocks, int32_t num_kv_heads,
                       const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *context_lens, int32_t max_context_len,
-                      int32_t sliding_window, float scale, int32_t split_tokens, void *out,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                      const int32_t *context_lens, const int32_t *query_start,
+                      int32_t max_context_len, int32_t sliding_window, float scale,
+                      int32_t split_tokens, void *out, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const bool packed = query_start != nullptr;
   if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
       num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0)
     return PA_ERR_SHAPE;
-  if (bad_query_shape(num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && !quantised(cache_dtype))
     return PA_ERR_DTYPE;
+  const int32_t qmax = query_bound(packed, num_query_tokens);
   if (split_tokens == 0)
-    split_tokens = pa_default_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           cache_dtype, max_context_len, num_query_tokens,
-                                           sliding_window);
+    split_tokens = pa_default_split_tokens(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype, max_context_len,
+        query_for_default(packed, num_query_tokens, num_seqs), sliding_window);
   if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
-                                   num_query_tokens, sliding_window, split_tokens);
-  const size_t need = pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim, ns);
-  if (num_seqs == 0) return PA_OK;
+  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq), qmax,
+                                   sliding_window, split_tokens);
+  const int32_t g = num_q_heads / num_kv_heads;
+  const size_t need =
+      packed ? pa_workspace_bytes_packed(num_seqs, num_query_tokens, num_q_heads, num_kv_heads,
+                                         head_dim, ns)
+             : pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim, ns);
+  if (num_seqs == 0 || (packed && num_query_tokens == 0)) return PA_OK;
   if (!workspace || !out) return PA_ERR_NULL;
   if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t rows = (size_t)num_seqs * num_query_tokens * num_q_heads * ns;
+  const size_t rows = (size_t)(packed ? 1 : num_seqs) * num_query_tokens * num_q_heads * ns;
   char *base = (char *)workspace;
   int32_t *sched = (int32_t *)base;
-  base += pa_sched_bytes(num_seqs, ns);
+  base += packed ? pa_sched_bytes_packed(num_seqs, ns, num_query_tokens, g)
+                 : pa_sched_bytes(num_seqs, ns);
   float *m = (float *)base;
   float *l = (float *)(base + align256(rows * sizeof(float)));
   float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
-  int st = paged_attn_plan(context_lens, block_tables, num_seqs, max_blocks_per_seq,
-                           max_context_len, num_query_tokens, sliding_window, split_tokens, 1,
-                           sched, stream);
+  int st = paged_attn_plan(context_lens, query_start, block_tables, num_seqs, max_blocks_per_seq,
+                           max_context_len, num_query_tokens, g, sliding_window, split_tokens,
+                           1, sched, stream);
   if (st != PA_OK) return st;
   st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_query_tokens, num_q_heads, head_dim,
                                  k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks,
                                  num_kv_heads, block_tables, max_blocks_per_seq, context_lens,
-                                 max_context_len, sliding_window, scale, split_tokens, ns, m, l,
-                                 acc, sched, stream);
+                                 query_start, max_context_len, sliding_window, scale,
+                                 split_tokens, ns, m, l, acc, sched, stream);
   if (st != PA_OK) return st;
-  return paged_attn_reduce(m, l, acc, context_lens, num_seqs, num_query_tokens, num_q_heads,
-                           head_dim, sliding_window, split_tokens, ns, out, q_dtype, stream);
+  return paged_attn_reduce(m, l, acc, context_lens, query_start, num_seqs, num_query_tokens,
+                           num_q_heads, head_dim, sliding_window, split_tokens, ns, out, q_dtype,
+                           stream);
 }
 
 int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,

@@ -3,8 +3,8 @@
 
 namespace pa {
 
-hipError_t decode_f32_fp8(const DecodeParams &p, int grid_splits, hipStream_t s) {
-  return dispatch_decode<PA_F32, PA_FP8>(p, grid_splits, s);
+hipError_t decode_f32_fp8(const DecodeParams &p, int64_t max_entries, hipStream_t s) {
+  return dispatch_decode<PA_F32, PA_FP8>(p, max_entries, s);
 }
 
 }  // namespace pa

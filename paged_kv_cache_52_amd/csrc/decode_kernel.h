@@ -43,18 +43,22 @@ struct DecodeParams {
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, max_context_len;
   int32_t split_tokens, max_splits;
-  int32_t num_query_tokens;  // Q query tokens per sequence (its last Q positions)
+  int32_t num_query_tokens;  // Q query tokens per sequence (its last Q positions), or
+                             // the packed total with query_start
   int32_t window;            // sliding window in tokens, 0 = none
   int32_t group;             // g = num_q_heads / num_kv_heads
-  int32_t head_groups;  // row groups per KV head (Q*g rows) handled by separate workgroups
+  int32_t head_groups;  // uniform Q: workgroups per (split, KV head), rw row groups each
+  int32_t rw;           // uniform Q: row groups of G rows per workgroup (1, 2 or 4)
+  const int32_t *query_start;  // [num_seqs + 1] packed query offsets, or nullptr
   float scale_log2;     // scale * log2(e)
 };
 
-// Row R (0 <= R < Q*g) of KV head kvh is query token R / g, query head
-// kvh*g + R % g; its q, out and partials row in [num_seqs][Q][Hq].
-__device__ __forceinline__ int64_t query_row(const DecodeParams &p, int s, int kvh, int R) {
+// Row R (0 <= R < Q_s*g) of KV head kvh of a sequence whose query token 0 is
+// packed row `first` is query token R / g, query head kvh*g + R % g; its q,
+// out and partials row in [tokens][Hq].
+__device__ __forceinline__ int64_t query_row(const DecodeParams &p, int first, int kvh, int R) {
   const int g = p.group;
-  return ((int64_t)s * p.num_query_tokens + R / g) * p.num_q_heads + kvh * g + R % g;
+  return ((int64_t)first + R / g) * p.num_q_heads + kvh * g + R % g;
 }
 
 // Token ranges of the rows a workgroup handles. Query token i of the sequence
@@ -64,6 +68,7 @@ __device__ __forceinline__ int64_t query_row(const DecodeParams &p, int s, int k
 struct RowRanges {
   int q0;      // position of query token 0: L - Q
   int window;  // W, 0 = none
+  int first;   // q row (token index) of query token 0
   int ulo, uhi, lo_max, hi_min;
 
   __device__ __forceinline__ int lo(int i) const {
@@ -75,10 +80,12 @@ struct RowRanges {
     return tb < lo_max || tb + kBlock - 1 > hi_min;
   }
   // Rows [R0, R0 + nrows) with g query heads per KV head.
-  __device__ __forceinline__ static RowRanges make(int L, int Q, int W, int g, int R0, int nrows) {
+  __device__ __forceinline__ static RowRanges make(int L, int Q, int W, int g, int R0, int nrows,
+                                                  int first) {
     RowRanges r;
     r.q0 = L - Q;
     r.window = W;
+    r.first = first;
     const int i0 = R0 / g, i1 = (R0 + nrows - 1) / g;
     r.ulo = r.lo(i0);
     r.uhi = r.hi(i1);
@@ -96,10 +103,12 @@ struct RowRanges {
 
 // Layout of the scheduling scratch written by the plan kernel:
 //   [0] number of splits of the batch
-//   [1] split_tokens, [2] num_seqs, [3] clamped max length, [4] query tokens,
-//   [5] window the plan was made for, [6..7] unused
-//   then two words per split, full splits first: (sequence << 16 | split) and
-//   the sequence's clamped context length.
+//   [1] split_tokens, [2] num_seqs, [3] clamped max length, [4] query tokens
+//   (per sequence, or the packed total), [5] window the plan was made for,
+//   [6] group members (0: no group entries), [7] g with packed queries, else 0
+//   then two words per entry, full splits first: (sequence << 16 | split) and
+//   the sequence's clamped context length (minus the member count for a group
+//   entry; the row block index with packed queries).
 constexpr int kSchedHeader = 8;
 
 template <int QT, int CT, int D, int G>
@@ -628,7 +637,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   const bool row_ok = c < G && c < nrows;
   const int qi = (R0 + c) / p.group;
   const int lo = row_ok ? rr.lo(qi) : rr.ulo, hi = row_ok ? rr.hi(qi) : rr.uhi;
-  const int64_t qrow = row_ok ? query_row(p, s, kvh, R0 + c) : 0;
+  const int64_t qrow = row_ok ? query_row(p, rr.first, kvh, R0 + c) : 0;
   float qs = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -748,7 +757,7 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
     const int c = lane % S::LPR;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t row = (h < nrows ? query_row(p, s, kvh, R0 + h) : 0) * D;
+      const int64_t row = (h < nrows ? query_row(p, rr.first, kvh, R0 + h) : 0) * D;
       if (h >= nrows) {
 #pragma unroll
         for (int k = 0; k < S::QW; ++k) st.qr[h][k] = 0.f;
@@ -826,48 +835,49 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   }
 }
 
-// One work item for KV head kvh: split j of sequence s for RW row groups of G
-// rows (the quad-th set of RW among the Q*g rows of the KV head), or, for a
-// group entry (group > 0), split j of the `group` sequences s, s+1, ... whose
-// splits share tiles, one row group (all Q*g <= G rows) each. The NW waves
-// split into rw row groups of tw = NW / rw waves: the tw waves of a row group
-// divide the tiles of the split that its rows reach, and merge their states
-// in LDS; different row groups read their tiles at about the same time (with
-// rw > 1 through the caches, not streamed) and write their own partials.
-// Contains two workgroup barriers.
-template <int QT, int CT, int D, int G, int NW, int RW>
+// One work item for KV head kvh: split j of sequence s for the rw row groups
+// of G rows starting at row R0 (rows R0 .. min(R_end, R0 + rw*G) - 1 of the
+// KV head's Q_s*g rows), or, for a group entry (group > 0), split j of the
+// `group` sequences s, s+1, ... whose splits share tiles, one row group (all
+// Q*g <= G rows) each, rw = NW. The NW waves split into rw row groups of
+// tw = NW / rw waves: the tw waves of a row group divide the tiles of the
+// split that its rows reach, and merge their states in LDS; different row
+// groups read their tiles at about the same time (with rw > 1 through the
+// caches, not streamed) and write their own partials. len is the sequence's
+// clamped length (not used for group entries). Contains two workgroup
+// barriers.
+template <int QT, int CT, int D, int G, int NW>
 __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int len, int j,
-                                              int kvh, int quad, int group, int lane, int wave,
-                                              float (&sm_m)[NW][G],
+                                              int kvh, int R0, int R_end, int rw, int group,
+                                              int lane, int wave, float (&sm_m)[NW][G],
                                               float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
-  constexpr int POL = RW > 1 ? 0 : kStreamPolicy;  // shared tiles stay cached
-  const int rw = group > 0 ? NW : RW;               // row groups of this item
-  const int tw = NW / rw;                            // waves per row group
-  const int rg = wave / tw, tp = wave % tw;          // this wave's row group and tile share
-  const int Q = p.num_query_tokens, W = p.window;
-  const int rows = Q * p.group;
+  const int tw = NW / rw;                     // waves per row group
+  const int rg = wave / tw, tp = wave % tw;   // this wave's row group and tile share
+  const int W = p.window;
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
   // The row group's sequence, rows and split range.
   auto seq_of = [&](int g) { return group > 0 ? s + g : s; };
-  auto rows_of = [&](int g) {
-    if (group > 0) return g < group ? min(G, rows) : 0;
-    return min(G, rows - (quad * RW + g) * G);
-  };
   const int s_rg = min(seq_of(rg), p.num_seqs - 1);
-  const int L = max(0, min(group > 0 ? p.context_lens[s_rg] : len, lmax));
+  const QuerySpan qsp = query_span(p.query_start, s_rg, p.num_query_tokens, p.num_query_tokens);
+  const int Q = qsp.count;
+  auto rows_of = [&](int g) {  // rows of row group g (<= 0: a padding row group)
+    if (group > 0) return g < group ? min(G, Q * p.group) : 0;
+    return min(G, R_end - (R0 + g * G));
+  };
+  const int L = group > 0 ? max(0, min(p.context_lens[s_rg], lmax)) : len;
   const int base = split_base(L, Q, W);
-  const bool has_split = j < splits_of(L, Q, W, p.split_tokens);  // always, for planned items
+  const bool has_split = Q > 0 && j < splits_of(L, Q, W, p.split_tokens);
   const int t0 = base + j * p.split_tokens;  // a multiple of 16
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
-  const int R0 = group > 0 ? 0 : (quad * RW + rg) * G;
-  const int nrows = has_split ? rows_of(rg) : 0;  // <= 0: a padding row group (no rows)
+  const int Rg = group > 0 ? 0 : R0 + rg * G;  // first row of this wave's row group
+  const int nrows = has_split ? rows_of(rg) : 0;
   // Tiles of the split the row group's rows reach: tokens [ta, tz].
   RowRanges rr{};
   int wb0 = 0, wb1 = 0;
   if (nrows > 0) {
-    rr = RowRanges::make(L, Q, W, p.group, R0, nrows);
+    rr = RowRanges::make(L, Q, W, p.group, Rg, nrows, qsp.first);
     const int ta = max(t0, rr.ulo), tz = min(t1 - 1, rr.uhi);
     if (tz >= ta) {
       const int first = (ta - t0) / kBlock, count = (tz - t0) / kBlock - first + 1;
@@ -876,20 +886,21 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
       wb1 = first + min(count, tp * per + per);
     }
   }
+  // Tiles that several row groups read stay cached; a lone row group streams.
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
-    if (group > 0)
-      wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+    if (rw > 1)
+      wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
     else
-      wave_pass_mfma<QT, CT, D, G, NW, POL>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
-                                            sm_m, sm_l, sm_acc);
+      wave_pass_mfma<QT, CT, D, G, NW, kStreamPolicy>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1,
+                                                      lane, wave, sm_m, sm_l, sm_acc);
   } else {
-    if (group > 0)
-      wave_pass_valu<QT, CT, D, G, NW, 0>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
+    if (rw > 1)
+      wave_pass_valu<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
     else
-      wave_pass_valu<QT, CT, D, G, NW, POL>(p, s_rg, kvh, R0, nrows, rr, b0, wb0, wb1, lane, wave,
-                                            sm_m, sm_l, sm_acc);
+      wave_pass_valu<QT, CT, D, G, NW, kStreamPolicy>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1,
+                                                      lane, wave, sm_m, sm_l, sm_acc);
   }
   __syncthreads();
 
@@ -897,9 +908,11 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   // thread per row finds the row's common max, turns sm_m into the waves'
   // factors 2^(m_w - M) and writes (m, l); then all threads sum the rows'
   // dims, four per thread. A row group without the split writes nothing.
+  // Group entries come from uniform-Q plans only: member g's rows start at
+  // packed row (s + g) * Q.
   auto out_row = [&](int g, int h) {
-    const int sg = seq_of(g);
-    return query_row(p, sg, kvh, (group > 0 ? 0 : (quad * RW + g) * G) + h) * p.max_splits + j;
+    const int first = group > 0 ? (s + g) * p.num_query_tokens : qsp.first;
+    return query_row(p, first, kvh, (group > 0 ? 0 : R0 + g * G) + h) * p.max_splits + j;
   };
   auto live = [&](int g) {  // rows of row group g that have this split
     if (group == 0) return has_split ? rows_of(g) : 0;
@@ -941,15 +954,17 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   }
 }
 
-// Split kernel. Work item k is split sched[kSchedHeader + 2*(k / heff)]
-// (packed sequence << 16 | split, followed by the sequence's context length,
-// or minus the member count of a group entry)
-// for (KV head, row group) k % heff (heff = KV heads x row groups), from the
-// list the plan kernel wrote (full splits first, the shortest last splits at
-// the end). Workgroup k processes item k; the grid is an upper bound on the
-// number of items and the workgroups past the end of the list, all at the end
-// of the grid, exit at once. A plan made for another split size, batch or
-// length bound, query-token count or window counts as an empty list.
+// Split kernel. Work item k is entry sched[kSchedHeader + 2*(k / per_entry)]
+// of the list the plan kernel wrote (full splits first, the shortest last
+// splits at the end), for KV head k % Hkv and, with a uniform query count,
+// the set (k % per_entry) / Hkv of rw row groups of the KV head's Q*g rows
+// (per_entry = Hkv * head_groups; the sets of one KV head land on the same
+// XCD when Hkv is a multiple of 8). With packed queries an entry names its
+// block of kPackedRows rows itself and per_entry = Hkv. Workgroup k processes
+// item k; the grid is an upper bound on the number of items and the
+// workgroups past the end of the list, all at the end of the grid, exit at
+// once. A plan made for another split size, batch, length bound, query count,
+// window or query layout counts as an empty list.
 // Minimum waves per SIMD the compiler must fit the split kernel's registers
 // to (0: its own choice).
 #ifndef PA_WAVES_PER_EU
@@ -961,40 +976,64 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 #define PA_OCCUPANCY_ATTR
 #endif
 
-template <int QT, int CT, int D, int G, int NW, int RW>
+template <int QT, int CT, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_kernel(
     const DecodeParams p) {
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ __align__(16) float sm_acc[NW][G][D];
 
-  const int heff = p.num_kv_heads * p.head_groups;
+  const bool packed = p.query_start != nullptr;
+  const int per_entry = packed ? p.num_kv_heads : p.num_kv_heads * p.head_groups;
   const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
-  // A plan made with group entries needs every sequence's rows in one row
-  // group (Q*g <= G), and a wave per member.
+  // A plan made with group entries needs uniform query counts, every
+  // sequence's rows in one row group (Q*g <= G), and a wave per member.
   static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
   const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
                        p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
-                       p.sched[5] == p.window &&
-                       (p.sched[6] <= 1 || p.num_query_tokens * p.group <= G);
-  const int n_items = plan_ok ? p.sched[0] * heff : 0;
+                       p.sched[5] == p.window && p.sched[7] == (packed ? p.group : 0) &&
+                       (p.sched[6] <= 1 || (!packed && p.num_query_tokens * p.group <= G));
+  const int n_items = plan_ok ? p.sched[0] * per_entry : 0;
   const int k = blockIdx.x;
   if (k >= n_items) return;
   const int lane = lane_id();
   // Wave index as a scalar, so that per-wave ranges and loop counters stay in
   // SGPRs and the tile loop runs without exec masking.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int e = k % heff;
-  const int packed = p.sched[kSchedHeader + 2 * (k / heff)];
-  const int word1 = p.sched[kSchedHeader + 2 * (k / heff) + 1];
-  // word1 is the sequence's length, or minus the member count of a group
-  // entry (made only with one row group per KV head: e / head_groups = kvh).
-  const int group = word1 < 0 ? min(-word1, NW) : 0;
+  const int e = k % per_entry;
+  const int kvh = e % p.num_kv_heads;
+  const int packed_entry = p.sched[kSchedHeader + 2 * (k / per_entry)];
+  const int word1 = p.sched[kSchedHeader + 2 * (k / per_entry) + 1];
   // The sequence index is clamped so that no entry can send a read out of
   // bounds; process_split ignores a split index past a sequence's end.
-  process_split<QT, CT, D, G, NW, RW>(p, min(packed >> 16, p.num_seqs - 1), max(word1, 0),
-                                      packed & 0xffff, e / p.head_groups, e % p.head_groups,
-                                      group, lane, wave, sm_m, sm_l, sm_acc);
+  const int s = min(packed_entry >> 16, p.num_seqs - 1);
+  const int j = packed_entry & 0xffff;
+  if (!packed) {
+    // word1 is the sequence's length, or minus the member count of a group
+    // entry (made only with one row group per KV head).
+    const int group = word1 < 0 ? min(-word1, NW) : 0;
+    const int rows = p.num_query_tokens * p.group;
+    const int R0 = (e / p.num_kv_heads) * p.rw * G;
+    process_split<QT, CT, D, G, NW>(p, s, max(word1, 0), j, kvh, R0, rows,
+                                    group > 0 ? NW : p.rw, group, lane, wave, sm_m, sm_l,
+                                    sm_acc);
+  } else {
+    // word1 is the row block: rows [rb * kPackedRows, ...) of the sequence's
+    // Q_s * g rows, in passes of up to NW row groups.
+    const int L = max(0, min(p.context_lens[s], lmax));
+    const QuerySpan qsp = query_span(p.query_start, s, p.num_query_tokens, p.num_query_tokens);
+    const int rows = qsp.count * p.group;
+    const int r0 = max(word1, 0) * kPackedRows;
+    const int r1 = min(rows, r0 + kPackedRows);
+    for (int R0 = r0; R0 < r1; R0 += NW * G) {
+      const int nr = min(NW * G, r1 - R0);
+      int rw = 1;
+      while (rw * G < nr) rw <<= 1;
+      if (R0 > r0) __syncthreads();  // the previous pass has read the LDS state
+      process_split<QT, CT, D, G, NW>(p, s, L, j, kvh, R0, r1, rw, 0, lane, wave, sm_m, sm_l,
+                                      sm_acc);
+    }
+  }
 }
 
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
@@ -1003,20 +1042,22 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
 #define PA_DECODE_WAVES 4
 #endif
 
-template <int QT, int CT, int D, int G, int RW>
-hipError_t launch_decode(const DecodeParams &p, int grid_splits, hipStream_t stream) {
+template <int QT, int CT, int D, int G>
+hipError_t launch_decode(const DecodeParams &p, int64_t max_items, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;
   // One workgroup per possible item; those past the planned list exit at once.
-  const int64_t max_items = (int64_t)p.num_seqs * grid_splits * p.num_kv_heads * p.head_groups;
-  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW, RW>), dim3((unsigned)max_items),
+  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), dim3((unsigned)max_items),
                      dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
 // Dispatch on (head_dim, rows per KV head) for one (q dtype, cache dtype)
 // pair. A KV head has Q*g query rows (query tokens x the heads of its group).
-// The MFMA engine takes up to 16 rows per workgroup, the VALU engine up to 8;
-// more rows are split into row groups handled by separate workgroups.
+// The MFMA engine takes up to 16 rows per row group, the VALU engine up to 8;
+// with a uniform query count, more rows are split into sets of up to four
+// row groups handled by separate workgroups. With packed queries the row
+// group size follows the largest possible count, min(total, PA_MAX_QUERY_TOKENS).
+// max_entries bounds the plan's list (its capacity).
 inline int pow2_at_least(int x) {
   int r = 1;
   while (r < x) r <<= 1;
@@ -1024,29 +1065,26 @@ inline int pow2_at_least(int x) {
 }
 
 template <int QT, int CT>
-hipError_t dispatch_decode(DecodeParams p, int grid_splits, hipStream_t stream) {
-  const int rows = p.num_query_tokens * p.group;
+hipError_t dispatch_decode(DecodeParams p, int64_t max_entries, hipStream_t stream) {
+  const bool packed = p.query_start != nullptr;
+  const int qmax = packed ? min(p.num_query_tokens, PA_MAX_QUERY_TOKENS) : p.num_query_tokens;
+  const int rows = max(1, qmax * p.group);
   auto by_rows = [&](auto dtag) -> hipError_t {
     constexpr int D = decltype(dtag)::value;
     constexpr int kMaxRows = (QT == PA_BF16 && MfmaEligible<CT, D>::value) ? 16 : 8;
     const int G = min(kMaxRows, pow2_at_least(rows));
-    // Row groups of G rows; with several, a workgroup takes up to four of
-    // them (one per wave or pair of waves) over the same tiles.
     const int row_groups = (rows + G - 1) / G;
-    const int RW = row_groups >= 4 ? 4 : row_groups >= 2 ? 2 : 1;
-    p.head_groups = (row_groups + RW - 1) / RW;
+    p.rw = row_groups >= 4 ? 4 : row_groups >= 2 ? 2 : 1;
+    p.head_groups = packed ? 1 : (row_groups + p.rw - 1) / p.rw;
+    const int64_t items = max_entries * p.num_kv_heads * p.head_groups;
     switch (G) {
-      case 1: return launch_decode<QT, CT, D, 1, 1>(p, grid_splits, stream);
-      case 2: return launch_decode<QT, CT, D, 2, 1>(p, grid_splits, stream);
-      case 4: return launch_decode<QT, CT, D, 4, 1>(p, grid_splits, stream);
+      case 1: return launch_decode<QT, CT, D, 1>(p, items, stream);
+      case 2: return launch_decode<QT, CT, D, 2>(p, items, stream);
+      case 4: return launch_decode<QT, CT, D, 4>(p, items, stream);
       default: break;
     }
-    if (G == 8 && kMaxRows == 16) return launch_decode<QT, CT, D, 8, 1>(p, grid_splits, stream);
-    switch (RW) {
-      case 1: return launch_decode<QT, CT, D, kMaxRows, 1>(p, grid_splits, stream);
-      case 2: return launch_decode<QT, CT, D, kMaxRows, 2>(p, grid_splits, stream);
-      default: return launch_decode<QT, CT, D, kMaxRows, 4>(p, grid_splits, stream);
-    }
+    if (G == 8 && kMaxRows == 16) return launch_decode<QT, CT, D, 8>(p, items, stream);
+    return launch_decode<QT, CT, D, kMaxRows>(p, items, stream);
   };
   if (p.head_dim == 64) return by_rows(std::integral_constant<int, 64>{});
   return by_rows(std::integral_constant<int, 128>{});

@@ -145,4 +145,42 @@ __host__ __device__ inline int max_span(int lmax, int Q, int W) {
   return lmax < cap ? lmax : cap;
 }
 
+// ---------------------------------------------------------------------------
+// Query tokens of a sequence. Every sequence has Q query tokens (rows s*Q ..
+// s*Q + Q - 1 of q), or, with per-sequence offsets qs ([num_seqs + 1]), the
+// packed rows [qs[s], qs[s+1]) of the n query tokens of the batch [EchoLLMServing
+// notes, section 3, chunked prefill: one call for a batch that mixes prefill
+// chunks and decodes]. The span is clamped into [0, n) and to at most
+// PA_MAX_QUERY_TOKENS tokens, so that no row index leaves the packed arrays
+// whatever the offsets hold.
+// ---------------------------------------------------------------------------
+struct QuerySpan {
+  int first;  // row (token index) of query token 0
+  int count;  // query tokens of the sequence
+};
+
+__device__ __forceinline__ QuerySpan query_span(const int32_t *qs, int s, int Q, int n) {
+  if (qs == nullptr) return QuerySpan{s * Q, Q};
+  const int a = min(max(qs[s], 0), n);
+  const int b = min(max(qs[s + 1], a), min(n, a + PA_MAX_QUERY_TOKENS));
+  return QuerySpan{a, b - a};
+}
+
+// Sequence owning packed query token t: the last s with qs[s] <= t (binary
+// search over nondecreasing offsets; empty sequences share their offset with
+// the next one, and the search lands on the last of them).
+__device__ __forceinline__ int seq_of_token(const int32_t *qs, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qs[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Query rows (query token x query head of a KV head's group) per work item
+// with packed queries: the plan lists one item per (split, block of this many
+// rows) of a sequence.
+constexpr int kPackedRows = 64;
+
 }  // namespace pa

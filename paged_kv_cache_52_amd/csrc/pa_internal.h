@@ -15,7 +15,8 @@ struct ReduceParams {
   const int32_t *context_lens;
   void *out;
   int32_t num_seqs, num_q_heads, head_dim, split_tokens, max_splits, out_dtype;
-  int32_t num_query_tokens, window;  // rows per sequence: num_query_tokens * num_q_heads
+  int32_t num_query_tokens, window;  // per sequence, or the packed total with query_start
+  const int32_t *query_start;        // [num_seqs + 1] packed query offsets, or nullptr
 };
 
 struct WriteParams {
@@ -37,10 +38,14 @@ struct PlanParams {
   const int32_t *context_lens;
   int32_t *sched;
   int32_t num_seqs, max_len, split_tokens;
-  int32_t num_query_tokens, window;
+  int32_t num_query_tokens;     // per sequence, or the packed total with query_start
+  int32_t window;
   const int32_t *block_tables;  // read only with group_members > 1
   int32_t max_blocks_per_seq;
   int32_t group_members;        // 1: no grouping; 2..4: sequences per group entry
+  const int32_t *query_start;   // [num_seqs + 1] packed query offsets, or nullptr
+  int32_t group;                // g = Hq / Hkv (used with query_start)
+  int32_t capacity;             // entries the scheduling scratch holds
 };
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t stream);
@@ -52,11 +57,11 @@ hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int 
                              hipStream_t stream);
 
 // One per (q dtype, cache dtype) pair; p.group = Hq / Hkv in {1, 2, 4, 8, 16}.
-hipError_t decode_bf16_bf16(const DecodeParams &p, int grid_splits, hipStream_t s);
-hipError_t decode_f32_f32(const DecodeParams &p, int grid_splits, hipStream_t s);
-hipError_t decode_bf16_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
-hipError_t decode_f32_i8(const DecodeParams &p, int grid_splits, hipStream_t s);
-hipError_t decode_bf16_fp8(const DecodeParams &p, int grid_splits, hipStream_t s);
-hipError_t decode_f32_fp8(const DecodeParams &p, int grid_splits, hipStream_t s);
+hipError_t decode_bf16_bf16(const DecodeParams &p, int64_t max_entries, hipStream_t s);
+hipError_t decode_f32_f32(const DecodeParams &p, int64_t max_entries, hipStream_t s);
+hipError_t decode_bf16_i8(const DecodeParams &p, int64_t max_entries, hipStream_t s);
+hipError_t decode_f32_i8(const DecodeParams &p, int64_t max_entries, hipStream_t s);
+hipError_t decode_bf16_fp8(const DecodeParams &p, int64_t max_entries, hipStream_t s);
+hipError_t decode_f32_fp8(const DecodeParams &p, int64_t max_entries, hipStream_t s);
 
 }  // namespace pa

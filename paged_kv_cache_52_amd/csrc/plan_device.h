@@ -6,20 +6,27 @@
 // split count derived from the context length, max(1, ceil(L/T)); with a
 // sliding window, of the span the window reaches]. It writes
 // into the scheduling scratch:
-//   sched[0]  = number of splits of the batch
-//   sched[1..6] = split_tokens, num_seqs, clamped max length, query tokens,
-//                 window, group_members (0 when grouping is off), checked by
-//                 the split kernel; sched[7] = 0
-//   sched[8+2i], sched[9+2i] = (s << 16) | j, L_s   split i, in this order:
+//   sched[0]  = number of entries of the list
+//   sched[1..7] = split_tokens, num_seqs, clamped max length, query tokens
+//                 (per sequence, or the packed total), window, group_members
+//                 (0 when grouping is off), and g = Hq/Hkv with packed
+//                 queries (0 otherwise); the split kernel checks them
+//   sched[8+2i], sched[9+2i] = entry i: (s << 16) | j, then L_s (or, with
+//     packed queries, the index of the block of kPackedRows query rows of the
+//     sequence the entry covers), in this order:
 //     1. all splits but the last of each sequence (full T-token splits),
-//        sequence by sequence; with grouping on (group_members M > 1), the
-//        full split j of up to M consecutive sequences of an aligned run of M
-//        whose split j starts on the same physical block is one entry
-//        ((s0 << 16) | j, -count), listed at its first sequence;
-//     2. the last split of each sequence, longest first (counting sort on its
-//        16-token tile count), so the shortest work runs at the very end.
-// A sequence of length 0 contributes one empty split. Lengths are clamped
-// exactly as the split kernel clamps them. A group entry is only a hint for
+//        sequence by sequence (with packed queries, every row block of a split
+//        in turn); with grouping on (group_members M > 1), the full split j
+//        of up to M consecutive sequences of an aligned run of M whose split j
+//        starts on the same physical block is one entry ((s0 << 16) | j,
+//        -count), listed at its first sequence;
+//     2. the last split of each sequence (all its row blocks), longest first
+//        (counting sort on its 16-token tile count), so the shortest work
+//        runs at the very end.
+// A sequence of length 0 contributes one empty split; with packed queries a
+// sequence without query tokens contributes nothing. Lengths are clamped
+// exactly as the split kernel clamps them, and no entry is written past the
+// capacity the caller sized the scratch for. A group entry is only a hint for
 // cache sharing: the split kernel reads each member's own block table.
 #pragma once
 
@@ -34,16 +41,44 @@ __device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
   return max(0, min(p.context_lens[s], p.max_len));
 }
 
-__device__ __forceinline__ int seq_splits(const PlanParams &p, int L) {
-  return splits_of(L, p.num_query_tokens, p.window, p.split_tokens);
+__device__ __forceinline__ int seq_splits(const PlanParams &p, int L, int Q) {
+  return splits_of(L, Q, p.window, p.split_tokens);
 }
 
 // Tiles of the last split (1 for an empty split range, which sorts last).
-__device__ __forceinline__ int last_tiles(const PlanParams &p, int L) {
-  const int span = L - split_base(L, p.num_query_tokens, p.window);
+__device__ __forceinline__ int last_tiles(const PlanParams &p, int L, int Q) {
+  const int span = L - split_base(L, Q, p.window);
   if (span <= 0) return 1;
-  const int rest = span - (seq_splits(p, L) - 1) * p.split_tokens;
+  const int rest = span - (seq_splits(p, L, Q) - 1) * p.split_tokens;
   return (rest + kBlock - 1) / kBlock;
+}
+
+// What the plan needs of sequence s: clamped length, query tokens, splits and
+// entries per split (1, or with packed queries its blocks of kPackedRows
+// query rows; 0 for a sequence without query tokens).
+struct SeqPlan {
+  int L, Q, splits, per_split;
+};
+
+__device__ __forceinline__ SeqPlan seq_plan(const PlanParams &p, int s) {
+  SeqPlan r;
+  r.L = clamp_len(p, s);
+  if (p.query_start == nullptr) {
+    r.Q = p.num_query_tokens;
+    r.per_split = 1;
+  } else {
+    r.Q = query_span(p.query_start, s, 0, p.num_query_tokens).count;
+    r.per_split = (r.Q * p.group + kPackedRows - 1) / kPackedRows;
+  }
+  r.splits = seq_splits(p, r.L, r.Q);
+  return r;
+}
+
+__device__ __forceinline__ void put_entry(const PlanParams &p, int idx, int w0, int w1) {
+  if (idx < p.capacity) {
+    p.sched[kSchedHeader + 2 * idx] = w0;
+    p.sched[kSchedHeader + 2 * idx + 1] = w1;
+  }
 }
 
 // Join flags of the full split j of sequence s: bit c (c < M) is set when
@@ -60,7 +95,8 @@ __device__ __forceinline__ int join_bits(const PlanParams &p, int s, int j) {
 #pragma unroll
   for (int c = 0; c <= kMax; ++c) {
     const int t = s - 1 + c;
-    full[c] = c <= M && t >= 0 && t < p.num_seqs && j < seq_splits(p, clamp_len(p, t)) - 1;
+    full[c] = c <= M && t >= 0 && t < p.num_seqs &&
+              j < seq_splits(p, clamp_len(p, t), p.num_query_tokens) - 1;
   }
 #pragma unroll
   for (int c = 0; c <= kMax; ++c)  // j < splits - 1 keeps jb inside the table row
@@ -90,24 +126,27 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   __shared__ int carry;
   __shared__ int chunk_first[kPlanThreads];  // first entry of each sequence of the chunk
   __shared__ int chunk_len[kPlanThreads];
+  __shared__ int chunk_per[kPlanThreads];    // entries per split of each sequence
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
+  const bool packed = p.query_start != nullptr;
 
   for (int i = tid; i <= kMaxTileBuckets; i += kPlanThreads) bucket[i] = 0;
   if (tid == 0) carry = 0;
   __syncthreads();
 
   // Pass 1: the full splits. Per chunk of kPlanThreads sequences, a
-  // workgroup-wide exclusive scan of their counts gives each sequence's first
-  // entry; all threads then write the chunk's entries together (each finds its
-  // sequence by binary search over the chunk's offsets). The last splits are
-  // histogrammed by tile count on the way.
+  // workgroup-wide exclusive scan of their entry counts gives each sequence's
+  // first entry; all threads then write the chunk's entries together (each
+  // finds its sequence by binary search over the chunk's offsets). The last
+  // splits are histogrammed by tile count on the way.
   for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
     const int s = base + tid;
     const bool valid = s < p.num_seqs;
-    const int L = valid ? clamp_len(p, s) : 0;
-    const int f = valid ? seq_splits(p, L) - 1 : 0;
+    SeqPlan sp{0, 0, 1, 0};
+    if (valid) sp = seq_plan(p, s);
+    const int f = (sp.splits - 1) * sp.per_split;
     int incl = f;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -115,7 +154,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
       if (lane >= o) incl += y;
     }
     if (lane == kWave - 1) wave_sum[wave] = incl;
-    if (valid) atomicAdd(&bucket[last_tiles(p, L)], 1);
+    if (sp.per_split > 0) atomicAdd(&bucket[last_tiles(p, sp.L, sp.Q)], sp.per_split);
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
@@ -124,24 +163,26 @@ static __device__ void plan_workgroup(const PlanParams &p) {
       total += wave_sum[w];
     }
     chunk_first[tid] = before + incl - f;  // offset inside the chunk
-    chunk_len[tid] = L;
+    chunk_len[tid] = sp.L;
+    chunk_per[tid] = max(sp.per_split, 1);
     __syncthreads();
     const int base_entry = carry;
     if (p.group_members <= 1) {
       for (int e = tid; e < total; e += kPlanThreads) {
         const int lo = owner_of(chunk_first, e);
-        const int q = e - chunk_first[lo];
-        p.sched[kSchedHeader + 2 * (base_entry + e)] = ((base + lo) << 16) | q;
-        p.sched[kSchedHeader + 2 * (base_entry + e) + 1] = chunk_len[lo];
+        const int q = e - chunk_first[lo], per = chunk_per[lo];
+        const int j = q / per, rb = q % per;  // row blocks of a split are adjacent
+        put_entry(p, base_entry + e, ((base + lo) << 16) | j, packed ? rb : chunk_len[lo]);
       }
       __syncthreads();
       if (tid == 0) carry += total;
       __syncthreads();
     } else {
-      // Grouping: an entry (s, j) whose sequence joins its predecessor inside
-      // the aligned run of M is dropped (its group's first sequence lists it);
-      // the others count how many following sequences of the run join. The
-      // kept entries are compacted with a workgroup scan per stride.
+      // Grouping (one entry per split, no packed queries): an entry (s, j)
+      // whose sequence joins its predecessor inside the aligned run of M is
+      // dropped (its group's first sequence lists it); the others count how
+      // many following sequences of the run join. The kept entries are
+      // compacted with a workgroup scan per stride.
       const int M = p.group_members;
       for (int e0 = 0; e0 < total; e0 += kPlanThreads) {
         const int e = e0 + tid;
@@ -172,11 +213,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
           if (w < wave) before_k += wave_sum[w];
           total_k += wave_sum[w];
         }
-        if (keep) {
-          const int at = carry + before_k + incl_k - 1;
-          p.sched[kSchedHeader + 2 * at] = word0;
-          p.sched[kSchedHeader + 2 * at + 1] = cnt > 1 ? -cnt : L_e;
-        }
+        if (keep) put_entry(p, carry + before_k + incl_k - 1, word0, cnt > 1 ? -cnt : L_e);
         __syncthreads();
         if (tid == 0) carry += total_k;
         __syncthreads();
@@ -187,6 +224,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
 
   // Start offset of each tile-count bucket, longest first: a reverse
   // exclusive scan over buckets kMaxTileBuckets .. 1 (one bucket per thread).
+  int n_last = 0;
   {
     const int b = kMaxTileBuckets - tid;  // tid 0 -> 256, ..., tid 255 -> 1
     const int c = bucket[b];
@@ -201,32 +239,37 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     __syncthreads();
     int before = 0;
 #pragma unroll
-    for (int w = 0; w < kPlanThreads / kWave; ++w)
+    for (int w = 0; w < kPlanThreads / kWave; ++w) {
       if (w < wave) before += wave_sum[w];
+      n_last += wave_sum[w];
+    }
     bucket[b] = n_full + before + incl - c;
   }
   __syncthreads();
 
-  // Pass 2: place each sequence's last split in its bucket (the order inside
-  // a bucket does not affect any result).
+  // Pass 2: place each sequence's last split (each of its row blocks, kept
+  // together) in its bucket (the order inside a bucket does not affect any
+  // result).
   for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
     const int s = base + tid;
     if (s < p.num_seqs) {
-      const int L = clamp_len(p, s);
-      const int pos = atomicAdd(&bucket[last_tiles(p, L)], 1);
-      p.sched[kSchedHeader + 2 * pos] = (s << 16) | (seq_splits(p, L) - 1);
-      p.sched[kSchedHeader + 2 * pos + 1] = L;
+      const SeqPlan sp = seq_plan(p, s);
+      if (sp.per_split > 0) {
+        const int pos = atomicAdd(&bucket[last_tiles(p, sp.L, sp.Q)], sp.per_split);
+        for (int rb = 0; rb < sp.per_split; ++rb)
+          put_entry(p, pos + rb, (s << 16) | (sp.splits - 1), packed ? rb : sp.L);
+      }
     }
   }
   if (tid == 0) {
-    p.sched[0] = n_full + p.num_seqs;
+    p.sched[0] = min(n_full + n_last, p.capacity);
     p.sched[1] = p.split_tokens;
     p.sched[2] = p.num_seqs;
     p.sched[3] = p.max_len;
     p.sched[4] = p.num_query_tokens;
     p.sched[5] = p.window;
     p.sched[6] = p.group_members > 1 ? p.group_members : 0;
-    p.sched[7] = 0;
+    p.sched[7] = packed ? p.group : 0;
   }
 }
 

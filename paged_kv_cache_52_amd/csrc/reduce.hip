@@ -10,14 +10,16 @@ constexpr int kReduceWaves = 4;       // waves per workgroup
 constexpr int kReduceManySplits = 32;  // from this many splits, 4 waves share one head
 
 // Every workgroup has kReduceWaves waves. WPH waves work on one row (query
-// token, query head) of a sequence: WPH = 1 gives four heads per workgroup (few splits per head),
+// token, query head): WPH = 1 gives four rows per workgroup (few splits per head),
 // WPH = 4 one head whose splits the waves divide (long contexts). Each wave
 // finds the maximum M of the split maxima (lane-parallel), then sums a
 // contiguous range of splits: lane j of a 64-split chunk turns split j's
 // (m_j, l_j) into w_j = exp(m_j - M) (0 for an empty split, so the contents of
 // its acc never matter), and the chunk's acc rows are added with those weights,
 // each lane owning head_dim / 64 output dims, four rows loaded at a time. With
-// WPH > 1 the waves' sums meet in LDS.
+// WPH > 1 the waves' sums meet in LDS. Rows are [num_seqs][Q][Hq] (grid y =
+// sequence) or, with packed queries, [N][Hq] (grid y = 1; a row's sequence is
+// found from the query offsets).
 template <int OT, int D, int WPH>
 __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const ReduceParams p) {
   constexpr int DPL = D / kWave;  // dims per lane
@@ -26,13 +28,19 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int part = wave % WPH;
-  const int rows = p.num_query_tokens * p.num_q_heads;  // (query token, head) rows per sequence
+  const bool packed = p.query_start != nullptr;
+  // (query token, head) rows per grid row: per sequence, or all packed rows.
+  const int rows = p.num_query_tokens * p.num_q_heads;
   const int hq = blockIdx.x * HPW + wave / WPH;
-  const int s = blockIdx.y;
   if (WPH == 1 && hq >= rows) return;  // no barrier below in that case
+  int s = blockIdx.y, Q = p.num_query_tokens;
+  if (packed) {
+    s = seq_of_token(p.query_start, p.num_seqs, min(hq, rows - 1) / p.num_q_heads);
+    Q = query_span(p.query_start, s, 0, p.num_query_tokens).count;
+  }
   const int L = max(0, p.context_lens[s]);
-  const int ns = min(splits_of(L, p.num_query_tokens, p.window, p.split_tokens), p.max_splits);
-  const int64_t row0 = ((int64_t)s * rows + hq) * p.max_splits;
+  const int ns = Q > 0 ? min(splits_of(L, Q, p.window, p.split_tokens), p.max_splits) : 0;
+  const int64_t row0 = ((int64_t)blockIdx.y * rows + hq) * p.max_splits;
 
   float M = -INFINITY;
   for (int j = lane; j < ns; j += kWave) {
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
     }
   };
   if constexpr (WPH == 1) {
-    const int64_t orow = ((int64_t)s * rows + hq) * D;
+    const int64_t orow = ((int64_t)blockIdx.y * rows + hq) * D;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) store(orow + lane + k * kWave, den > 0.f ? acc[k] / den : 0.f);
   } else {
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
         a += sm_acc[h * WPH + w][d];
         dn += sm_den[h * WPH + w];
       }
-      store(((int64_t)s * rows + hh) * D + d, dn > 0.f ? a / dn : 0.f);
+      store(((int64_t)blockIdx.y * rows + hh) * D + d, dn > 0.f ? a / dn : 0.f);
     }
   }
 }
@@ -119,11 +127,12 @@ template <int OT, int D>
 void launch_reduce_t(const ReduceParams &p, hipStream_t stream) {
   const dim3 block(kReduceWaves * kWave);
   const int rows = p.num_query_tokens * p.num_q_heads;
+  const int grid_y = p.query_start ? 1 : p.num_seqs;
   if (p.max_splits >= kReduceManySplits) {
-    hipLaunchKernelGGL((reduce_kernel<OT, D, kReduceWaves>), dim3(rows, p.num_seqs), block, 0,
+    hipLaunchKernelGGL((reduce_kernel<OT, D, kReduceWaves>), dim3(rows, grid_y), block, 0,
                        stream, p);
   } else {
-    const dim3 grid((rows + kReduceWaves - 1) / kReduceWaves, p.num_seqs);
+    const dim3 grid((rows + kReduceWaves - 1) / kReduceWaves, grid_y);
     hipLaunchKernelGGL((reduce_kernel<OT, D, 1>), grid, block, 0, stream, p);
   }
 }

@@ -137,6 +137,22 @@ def test_workspace_bytes(lib):
     assert lib.pa_sched_bytes(-1, 8) == 0
 
 
+def test_packed_workspace_bytes(lib):
+    """Packed queries: the plan holds max_splits * (B + ceil(N * g / 64))
+    entries, the partials N * Hq rows."""
+    # 66 sequences, N = 1088 query tokens, g = 4: 66 + 68 entries per split.
+    sched = -(-(8 + 2 * 8 * (66 + 68)) * 4 // 256) * 256
+    assert lib.pa_sched_bytes_packed(66, 8, 1088, 4) == sched
+    rows = 1088 * 32 * 8
+    expect = sched + 2 * (-(-rows * 4 // 256) * 256) + (-(-rows * 128 * 4 // 256) * 256)
+    assert lib.pa_workspace_bytes_packed(66, 1088, 32, 8, 128, 8) == expect
+    # N = B, every count 1: one entry per split and sequence, plus ceil(B*g/64).
+    assert lib.pa_sched_bytes_packed(64, 1, 64, 4) == -(-(8 + 2 * (64 + 4)) * 4 // 256) * 256
+    assert lib.pa_sched_bytes_packed(4, 8, -1, 4) == 0
+    assert lib.pa_sched_bytes_packed(4, 8, 10, 0) == 0
+    assert lib.pa_workspace_bytes_packed(4, 10, 32, 0, 128, 8) == 0
+
+
 def _write(lib, **kw):
     a = dict(k=FAKE, v=FAKE, in_dtype=BF16, slots=FAKE, T=4, Hkv=8, D=128, kc=FAKE, vc=FAKE,
              ks=None, vs=None, NB=100, cache_dtype=BF16)
@@ -163,13 +179,14 @@ def test_kv_write_validation(lib):
 def test_prepare_validation(lib):
     def prep(**kw):
         a = dict(k=FAKE, v=FAKE, idt=BF16, slots=FAKE, T=4, Hkv=8, D=128, kc=FAKE, vc=FAKE,
-                 NB=100, cdt=BF16, cl=FAKE, bt=None, B=4, mb=8, mcl=128, Q=1, W=0, split=512,
-                 gm=1, sched=FAKE)
+                 NB=100, cdt=BF16, cl=FAKE, qs=None, bt=None, B=4, mb=8, mcl=128, Q=1, g=4,
+                 W=0, split=512, gm=1, sched=FAKE)
         a.update(kw)
         return lib.paged_decode_prepare(a["k"], a["v"], a["idt"], a["slots"], a["T"], a["Hkv"],
                                         a["D"], a["kc"], a["vc"], None, None, a["NB"], a["cdt"],
-                                        a["cl"], a["bt"], a["B"], a["mb"], a["mcl"], a["Q"],
-                                        a["W"], a["split"], a["gm"], a["sched"], None)
+                                        a["cl"], a["qs"], a["bt"], a["B"], a["mb"], a["mcl"],
+                                        a["Q"], a["g"], a["W"], a["split"], a["gm"], a["sched"],
+                                        None)
     assert prep(D=96) == ERR_SHAPE
     assert prep(mb=0) == ERR_SHAPE
     assert prep(B=65536) == ERR_SHAPE
@@ -185,15 +202,21 @@ def test_prepare_validation(lib):
     assert prep(gm=5, bt=FAKE) == ERR_SHAPE
     assert prep(gm=2) == ERR_NULL                      # grouping reads the tables
     assert prep(gm=2, bt=FAKE, W=64) == ERR_SHAPE      # and needs no window
+    assert prep(gm=2, bt=FAKE, qs=FAKE, Q=8) == ERR_SHAPE  # nor packed queries
+    assert prep(qs=FAKE, Q=5000, sched=None) == ERR_NULL  # packed: Q is the total N
+    assert prep(qs=FAKE, Q=-1) == ERR_SHAPE
+    assert prep(qs=FAKE, Q=(1 << 20) + 1) == ERR_SHAPE
+    assert prep(qs=FAKE, Q=8, g=3) == ERR_SHAPE        # g must be 1, 2, 4, 8 or 16
     assert prep(T=0, B=0, k=None, cl=None) == OK
 
 
 def test_plan_validation(lib):
     def plan(**kw):
-        a = dict(cl=FAKE, bt=None, B=4, mb=8, mcl=128, Q=1, W=0, split=512, gm=1, sched=FAKE)
+        a = dict(cl=FAKE, qs=None, bt=None, B=4, mb=8, mcl=128, Q=1, g=4, W=0, split=512, gm=1,
+                 sched=FAKE)
         a.update(kw)
-        return lib.paged_attn_plan(a["cl"], a["bt"], a["B"], a["mb"], a["mcl"], a["Q"], a["W"],
-                                   a["split"], a["gm"], a["sched"], None)
+        return lib.paged_attn_plan(a["cl"], a["qs"], a["bt"], a["B"], a["mb"], a["mcl"], a["Q"],
+                                   a["g"], a["W"], a["split"], a["gm"], a["sched"], None)
     assert plan(mb=0) == ERR_SHAPE
     assert plan(mcl=-1) == ERR_SHAPE
     assert plan(split=8) == ERR_SPLIT
@@ -206,19 +229,25 @@ def test_plan_validation(lib):
     assert plan(gm=5, bt=FAKE) == ERR_SHAPE
     assert plan(gm=2) == ERR_NULL
     assert plan(gm=4, bt=FAKE, W=1) == ERR_SHAPE
+    assert plan(gm=2, bt=FAKE, qs=FAKE, Q=8) == ERR_SHAPE
+    assert plan(qs=FAKE, Q=0, sched=None) == ERR_NULL  # packed, no query tokens: valid
+    assert plan(qs=FAKE, Q=-1) == ERR_SHAPE
+    assert plan(qs=FAKE, Q=8, g=0) == ERR_SHAPE
+    assert plan(qs=FAKE, Q=8, g=32) == ERR_SHAPE
+    assert plan(Q=8, g=0, sched=None) == ERR_NULL      # g is read only with packed queries
     assert plan(B=0, cl=None, sched=None) == OK
 
 
 def _partial(lib, **kw):
     a = dict(q=FAKE, qdt=BF16, B=4, Q=1, Hq=32, D=128, kc=FAKE, vc=FAKE, ks=None, vs=None,
-             cdt=BF16, NB=100, Hkv=8, bt=FAKE, mb=8, cl=FAKE, mcl=128, W=0, scale=0.1, T=512,
-             S=1, m=FAKE, l=FAKE, acc=FAKE, sched=FAKE)
+             cdt=BF16, NB=100, Hkv=8, bt=FAKE, mb=8, cl=FAKE, qs=None, mcl=128, W=0, scale=0.1,
+             T=512, S=1, m=FAKE, l=FAKE, acc=FAKE, sched=FAKE)
     a.update(kw)
     return lib.paged_attn_decode_partial(a["q"], a["qdt"], a["B"], a["Q"], a["Hq"], a["D"],
                                          a["kc"], a["vc"], a["ks"], a["vs"], a["cdt"], a["NB"],
-                                         a["Hkv"], a["bt"], a["mb"], a["cl"], a["mcl"], a["W"],
-                                         a["scale"], a["T"], a["S"], a["m"], a["l"], a["acc"],
-                                         a["sched"], None)
+                                         a["Hkv"], a["bt"], a["mb"], a["cl"], a["qs"], a["mcl"],
+                                         a["W"], a["scale"], a["T"], a["S"], a["m"], a["l"],
+                                         a["acc"], a["sched"], None)
 
 
 def test_decode_partial_validation(lib):
@@ -246,15 +275,21 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, qdt=F32, cdt=FP8) == ERR_NULL  # fp32 q on an FP8 cache is fine
     assert _partial(lib, q=FAKE_ODD) == ERR_ALIGN
     assert _partial(lib, B=0, q=None) == OK
+    # Packed queries: Q is the total N; splits sized for min(N, 4096).
+    assert _partial(lib, qs=FAKE, Q=0, q=None) == OK   # no query tokens: nothing to do
+    assert _partial(lib, qs=FAKE, Q=-1) == ERR_SHAPE
+    assert _partial(lib, qs=FAKE, Q=5000, W=500, mcl=100000, mb=8000, S=1) == ERR_SPLIT
+    assert _partial(lib, qs=FAKE, Q=5000, q=None) == ERR_NULL
 
 
 def test_reduce_validation(lib):
     def red(**kw):
-        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, B=4, Q=1, Hq=32, D=128, W=0, T=512, S=2,
-                 out=FAKE, odt=BF16)
+        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, qs=None, B=4, Q=1, Hq=32, D=128, W=0, T=512,
+                 S=2, out=FAKE, odt=BF16)
         a.update(kw)
-        return lib.paged_attn_reduce(a["m"], a["l"], a["acc"], a["cl"], a["B"], a["Q"], a["Hq"],
-                                     a["D"], a["W"], a["T"], a["S"], a["out"], a["odt"], None)
+        return lib.paged_attn_reduce(a["m"], a["l"], a["acc"], a["cl"], a["qs"], a["B"], a["Q"],
+                                     a["Hq"], a["D"], a["W"], a["T"], a["S"], a["out"], a["odt"],
+                                     None)
     assert red(D=32) == ERR_SHAPE
     assert red(odt=I8) == ERR_DTYPE
     assert red(T=0) == ERR_SPLIT
@@ -263,12 +298,15 @@ def test_reduce_validation(lib):
     assert red(Q=0) == ERR_SHAPE
     assert red(W=-1) == ERR_SHAPE
     assert red(B=0, out=None) == OK
+    assert red(qs=FAKE, Q=0, out=None) == OK
+    assert red(qs=FAKE, Q=5000, out=None) == ERR_NULL
+    assert red(qs=FAKE, Q=(1 << 20) + 1) == ERR_SHAPE
 
 
 def test_decode_workspace_validation(lib):
     need = lib.pa_workspace_bytes(4, 1, 32, 128, lib.pa_num_splits(1000, 512))
-    args = [FAKE, BF16, 4, 1, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE, 1000,
-            0, ctypes.c_float(0.1), 512, FAKE]
+    args = [FAKE, BF16, 4, 1, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE, None,
+            1000, 0, ctypes.c_float(0.1), 512, FAKE]
     assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
     assert lib.paged_attn_decode(*args, FAKE + 16, need, None) == ERR_ALIGN  # 256-byte rule
     assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
@@ -288,6 +326,16 @@ def test_decode_workspace_with_query_tokens_and_window(lib):
     assert S == 2
     need = lib.pa_workspace_bytes(4, 4, 32, 128, S)
     args = [FAKE, BF16, 4, 4, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 8000, FAKE,
-            100000, 100, ctypes.c_float(0.1), 64, FAKE]
+            None, 100000, 100, ctypes.c_float(0.1), 64, FAKE]
+    assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
+    assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
+
+
+def test_decode_workspace_with_packed_queries(lib):
+    """Packed: workspace for N query rows and the packed plan."""
+    S = lib.pa_max_splits(1000, 8, 0, 512)   # min(N, 4096) = 8 query tokens bound
+    need = lib.pa_workspace_bytes_packed(4, 8, 32, 8, 128, S)
+    args = [FAKE, BF16, 4, 8, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE,
+            FAKE, 1000, 0, ctypes.c_float(0.1), 512, FAKE]
     assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
     assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
