@@ -975,10 +975,31 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 #else
 #define PA_OCCUPANCY_ATTR
 #endif
+// The MFMA engine on 16-bit and FP8 caches fits 128 VGPRs, i.e. four waves per
+// SIMD (16 per CU) for latency hiding; the INT8 one needs more and runs three.
+#ifndef PA_MFMA_WAVES_PER_EU
+#define PA_MFMA_WAVES_PER_EU 4
+#endif
+
+template <int QT, int CT, int D, int G, int NW>
+__device__ __forceinline__ void decode_split_body(const DecodeParams &p);
 
 template <int QT, int CT, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_kernel(
     const DecodeParams p) {
+  decode_split_body<QT, CT, D, G, NW>(p);
+}
+
+// The same kernel with the MFMA engine's occupancy bound (bf16 q, bf16 or FP8
+// cache, head_dim 128).
+template <int QT, int CT, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
+    PA_MFMA_WAVES_PER_EU))) void decode_split_kernel_mfma(const DecodeParams p) {
+  decode_split_body<QT, CT, D, G, NW>(p);
+}
+
+template <int QT, int CT, int D, int G, int NW>
+__device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ __align__(16) float sm_acc[NW][G][D];
@@ -1028,7 +1049,7 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
     for (int R0 = r0; R0 < r1; R0 += NW * G) {
       const int nr = min(NW * G, r1 - R0);
       int rw = 1;
-      while (rw * G < nr) rw <<= 1;
+      while (rw < NW && rw * G < nr) rw <<= 1;
       if (R0 > r0) __syncthreads();  // the previous pass has read the LDS state
       process_split<QT, CT, D, G, NW>(p, s, L, j, kvh, R0, r1, rw, 0, lane, wave, sm_m, sm_l,
                                       sm_acc);
@@ -1046,8 +1067,12 @@ template <int QT, int CT, int D, int G>
 hipError_t launch_decode(const DecodeParams &p, int64_t max_items, hipStream_t stream) {
   constexpr int NW = PA_DECODE_WAVES;
   // One workgroup per possible item; those past the planned list exit at once.
-  hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), dim3((unsigned)max_items),
-                     dim3(NW * kWave), 0, stream, p);
+  if constexpr (QT == PA_BF16 && (CT == PA_BF16 || CT == PA_FP8) && D == 128)
+    hipLaunchKernelGGL((decode_split_kernel_mfma<QT, CT, D, G, NW>), dim3((unsigned)max_items),
+                       dim3(NW * kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<QT, CT, D, G, NW>), dim3((unsigned)max_items),
+                       dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
