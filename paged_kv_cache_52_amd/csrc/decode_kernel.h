@@ -100,6 +100,11 @@ struct RowRanges {
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 0
 #endif
+// 1: the MFMA engine folds tiles two at a time (32 tokens per softmax step,
+// P.V on 16x16x32 instructions).
+#ifndef PA_MFMA_PAIRS
+#define PA_MFMA_PAIRS 0
+#endif
 
 // Layout of the scheduling scratch written by the plan kernel:
 //   [0] number of splits of the batch
@@ -477,11 +482,11 @@ struct MfmaWave {
     }
   }
 
-  // Fold one tile (first token tb) into the running state. With need_mask,
-  // this lane's row keeps only tokens in [lo, hi], and V rows of tokens
-  // outside the group's [ulo, uhi] are dropped by select.
-  __device__ __forceinline__ void consume(MfmaTile<CT> &t, bool need_mask, int tb, int lo,
-                                          int hi, int ulo, int uhi, int g, float scale_log2) {
+  // Logits of one tile for this lane's row (head c) and tokens 4g .. 4g+3, in
+  // log2 units: S = K q^T on the matrix cores, then the K scale (INT8 / FP8)
+  // and the softmax scale.
+  __device__ __forceinline__ void scores(const MfmaTile<CT> &t, float (&z)[4],
+                                         float scale_log2) const {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (CT == PA_BF16) {
 #pragma unroll
@@ -509,7 +514,6 @@ struct MfmaWave {
                                                     0);
       }
     }
-    float z[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (CT == PA_BF16)
@@ -519,29 +523,45 @@ struct MfmaWave {
       else
         z[r] = sc[r] * t.ks[r] * scale_log2;
     }
-    if (need_mask) {  // uniform: a tile at an edge of some row's range
+  }
+
+  // A tile at an edge of some row's range (tokens tb ..): this lane's row
+  // keeps only tokens in [lo, hi]; V rows of tokens outside the group's
+  // [ulo, uhi] are dropped by select (NaN * 0 would leak).
+  __device__ __forceinline__ static void mask(MfmaTile<CT> &t, float (&z)[4], int tb, int lo,
+                                              int hi, int ulo, int uhi, int g) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tb + 4 * g + r;
-        z[r] = (tok >= lo && tok <= hi) ? z[r] : -INFINITY;
-        // NaN * 0 would leak: tokens no row attends are removed by select.
-        const bool used = tok >= ulo && tok <= uhi;
-        if constexpr (CT == PA_BF16) {
-          if (!used) t.v[r] = u32x4{0u, 0u, 0u, 0u};
-        } else {
-          if (!used) t.vs[r] = 0.f;
-          if constexpr (CT == PA_FP8) {  // a NaN code must not meet a zero weight
-            if (!used) t.v[r] = u32x2{0u, 0u};
-          }
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tb + 4 * g + r;
+      z[r] = (tok >= lo && tok <= hi) ? z[r] : -INFINITY;
+      const bool used = tok >= ulo && tok <= uhi;
+      if constexpr (CT == PA_BF16) {
+        if (!used) t.v[r] = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        if (!used) t.vs[r] = 0.f;
+        if constexpr (CT == PA_FP8) {  // a NaN code must not meet a zero weight
+          if (!used) t.v[r] = u32x2{0u, 0u};
         }
       }
     }
-    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  }
+
+  // Running max of head c over a step's logits (bm: this lane's maximum):
+  // the maximum over the four lane groups, and a rescale when it passes the
+  // reference by more than the slack.
+  __device__ __forceinline__ void update_max(float bm, int g) {
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     mtrue = fmaxf(mtrue, bm);
     const bool grow = bm > m + kRescaleSlack;
     if (__any(grow)) rescale(grow ? bm : m, g);
+  }
+
+  // Softmax weights of one tile's logits, added to l (and, INT8, wsum); for
+  // INT8 / FP8 the V scale is folded in. P = hi + lo as bf16 pairs (tokens
+  // (0, 1) and (2, 3) of the lane's four).
+  __device__ __forceinline__ void weights(const MfmaTile<CT> &t, const float (&z)[4],
+                                          uint32_t (&hi)[2], uint32_t (&lo)[2]) {
     float pz[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
@@ -551,15 +571,16 @@ struct MfmaWave {
       for (int r = 0; r < 4; ++r) pz[r] *= t.vs[r];
       if constexpr (CT == PA_I8) wsum += (pz[0] + pz[1]) + (pz[2] + pz[3]);
     }
-    // P (INT8: the V-scaled weights) = hi + lo, both bf16.
-    const uint32_t h01 = pack_bf16(pz[0], pz[1]), h23 = pack_bf16(pz[2], pz[3]);
-    const uint32_t l01 = pack_bf16(pz[0] - bf16_lo(h01), pz[1] - bf16_hi(h01));
-    const uint32_t l23 = pack_bf16(pz[2] - bf16_lo(h23), pz[3] - bf16_hi(h23));
-    const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
-    const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
-    // FP8: V bytes of rows (0, 1) and (2, 3) interleaved per column pair, so
-    // that one conversion yields a column's bf16 pair of two rows.
-    [[maybe_unused]] uint32_t x01[4], x23[4];
+    hi[0] = pack_bf16(pz[0], pz[1]);
+    hi[1] = pack_bf16(pz[2], pz[3]);
+    lo[0] = pack_bf16(pz[0] - bf16_lo(hi[0]), pz[1] - bf16_hi(hi[0]));
+    lo[1] = pack_bf16(pz[2] - bf16_lo(hi[1]), pz[3] - bf16_hi(hi[1]));
+  }
+
+  // FP8: V bytes of rows (0, 1) and (2, 3) interleaved per column pair, so
+  // that one conversion yields a column's bf16 pair of two rows.
+  __device__ __forceinline__ static void fp8_rows(const MfmaTile<CT> &t, uint32_t (&x01)[4],
+                                                  uint32_t (&x23)[4]) {
     if constexpr (CT == PA_FP8) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
@@ -569,38 +590,113 @@ struct MfmaWave {
         x23[2 * w + 1] = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], 0x07030602u);
       }
     }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      uint32_t b01, b23;
-      if constexpr (CT == PA_FP8) {
-        // column jj = byte jj % 4 of word jj / 4; x*[jj / 2] holds columns
-        // 2(jj/2) and 2(jj/2) + 1 in its low and high halves.
-        if (jj & 1) {
-          b01 = fp8pair_to_bf16<true>(x01[jj >> 1]);
-          b23 = fp8pair_to_bf16<true>(x23[jj >> 1]);
-        } else {
-          b01 = fp8pair_to_bf16<false>(x01[jj >> 1]);
-          b23 = fp8pair_to_bf16<false>(x23[jj >> 1]);
-        }
-      } else if constexpr (CT == PA_BF16) {
-        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-        b01 = __builtin_amdgcn_perm(t.v[1][jj >> 1], t.v[0][jj >> 1], sel);
-        b23 = __builtin_amdgcn_perm(t.v[3][jj >> 1], t.v[2][jj >> 1], sel);
-      } else {
-        const int w = jj >> 2;  // dims 8c + jj live in byte jj % 4 of word jj / 4
-        const uint32_t v0 = t.v[0][w] ^ 0x80808080u, v1 = t.v[1][w] ^ 0x80808080u;
-        const uint32_t v2 = t.v[2][w] ^ 0x80808080u, v3 = t.v[3][w] ^ 0x80808080u;
-        switch (jj & 3) {
-          case 0: b01 = u8col_to_bf16<0>(v0, v1); b23 = u8col_to_bf16<0>(v2, v3); break;
-          case 1: b01 = u8col_to_bf16<1>(v0, v1); b23 = u8col_to_bf16<1>(v2, v3); break;
-          case 2: b01 = u8col_to_bf16<2>(v0, v1); b23 = u8col_to_bf16<2>(v2, v3); break;
-          default: b01 = u8col_to_bf16<3>(v0, v1); b23 = u8col_to_bf16<3>(v2, v3); break;
-        }
-      }
-      const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{b01, b23});
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[jj], 0, 0, 0);
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[jj], 0, 0, 0);
+  }
+
+  // B operand of output column block JJ from one tile: element JJ (dim
+  // 8c + JJ) of V rows (0, 1) and (2, 3) of the lane's four, as bf16 pairs.
+  template <int JJ>
+  __device__ __forceinline__ static void v_cols(const MfmaTile<CT> &t, const uint32_t (&x01)[4],
+                                                const uint32_t (&x23)[4], uint32_t &b01,
+                                                uint32_t &b23) {
+    if constexpr (CT == PA_FP8) {
+      // column JJ = byte JJ % 4 of word JJ / 4; x*[JJ / 2] holds columns
+      // 2(JJ/2) and 2(JJ/2) + 1 in its low and high halves.
+      b01 = fp8pair_to_bf16<(JJ & 1) != 0>(x01[JJ >> 1]);
+      b23 = fp8pair_to_bf16<(JJ & 1) != 0>(x23[JJ >> 1]);
+    } else if constexpr (CT == PA_BF16) {
+      constexpr uint32_t sel = (JJ & 1) ? 0x07060302u : 0x05040100u;
+      b01 = __builtin_amdgcn_perm(t.v[1][JJ >> 1], t.v[0][JJ >> 1], sel);
+      b23 = __builtin_amdgcn_perm(t.v[3][JJ >> 1], t.v[2][JJ >> 1], sel);
+    } else {
+      constexpr int w = JJ >> 2;  // dims 8c + JJ live in byte JJ % 4 of word JJ / 4
+      const uint32_t v0 = t.v[0][w] ^ 0x80808080u, v1 = t.v[1][w] ^ 0x80808080u;
+      const uint32_t v2 = t.v[2][w] ^ 0x80808080u, v3 = t.v[3][w] ^ 0x80808080u;
+      b01 = u8col_to_bf16<JJ & 3>(v0, v1);
+      b23 = u8col_to_bf16<JJ & 3>(v2, v3);
     }
+  }
+
+  // O column block JJ += P . V over one tile (16 tokens, 16x16x16 MFMAs).
+  template <int JJ>
+  __device__ __forceinline__ void pv16(const MfmaTile<CT> &t, const uint32_t (&x01)[4],
+                                       const uint32_t (&x23)[4], s16x4 phi, s16x4 plo) {
+    uint32_t b01, b23;
+    v_cols<JJ>(t, x01, x23, b01, b23);
+    const s16x4 bv = __builtin_bit_cast(s16x4, u32x2{b01, b23});
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[JJ], 0, 0, 0);
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[JJ], 0, 0, 0);
+  }
+
+  // O column block JJ += P . V over two tiles (32 tokens, 16x16x32 MFMAs).
+  template <int JJ>
+  __device__ __forceinline__ void pv32(const MfmaTile<CT> &t0, const MfmaTile<CT> &t1,
+                                       const uint32_t (&x01a)[4], const uint32_t (&x23a)[4],
+                                       const uint32_t (&x01b)[4], const uint32_t (&x23b)[4],
+                                       bf16x8 phi, bf16x8 plo) {
+    uint32_t b0, b1, b2, b3;
+    v_cols<JJ>(t0, x01a, x23a, b0, b1);
+    v_cols<JJ>(t1, x01b, x23b, b2, b3);
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{b0, b1, b2, b3});
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, acc[JJ], 0, 0, 0);
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, bv, acc[JJ], 0, 0, 0);
+  }
+
+  // Fold one tile (first token tb) into the running state; need_mask: the
+  // tile is at an edge of some row's range.
+  __device__ __forceinline__ void consume(MfmaTile<CT> &t, bool need_mask, int tb, int lo,
+                                          int hi, int ulo, int uhi, int g, float scale_log2) {
+    float z[4];
+    scores(t, z, scale_log2);
+    if (need_mask) mask(t, z, tb, lo, hi, ulo, uhi, g);  // uniform
+    update_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), g);
+    uint32_t h[2], lw[2];
+    weights(t, z, h, lw);
+    const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h[0], h[1]});
+    const s16x4 plo = __builtin_bit_cast(s16x4, u32x2{lw[0], lw[1]});
+    [[maybe_unused]] uint32_t x01[4], x23[4];
+    fp8_rows(t, x01, x23);
+    pv16<0>(t, x01, x23, phi, plo);
+    pv16<1>(t, x01, x23, phi, plo);
+    pv16<2>(t, x01, x23, phi, plo);
+    pv16<3>(t, x01, x23, phi, plo);
+    pv16<4>(t, x01, x23, phi, plo);
+    pv16<5>(t, x01, x23, phi, plo);
+    pv16<6>(t, x01, x23, phi, plo);
+    pv16<7>(t, x01, x23, phi, plo);
+  }
+
+  // Fold two consecutive tiles (first tokens tb and tb + 16) as one 32-token
+  // step: one max update for both, and P.V on 16x16x32 instructions whose k
+  // index runs over the lane's four tokens of the first tile, then its four of
+  // the second (the B operand takes the V rows in the same order), so P and V
+  // still never move between lanes.
+  __device__ __forceinline__ void consume2(MfmaTile<CT> &t0, MfmaTile<CT> &t1, bool mask0,
+                                           bool mask1, int tb, int lo, int hi, int ulo, int uhi,
+                                           int g, float scale_log2) {
+    float z0[4], z1[4];
+    scores(t0, z0, scale_log2);
+    scores(t1, z1, scale_log2);
+    if (mask0) mask(t0, z0, tb, lo, hi, ulo, uhi, g);  // uniform
+    if (mask1) mask(t1, z1, tb + kBlock, lo, hi, ulo, uhi, g);
+    update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
+                     fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
+               g);
+    uint32_t h0[2], l0[2], h1[2], l1[2];
+    weights(t0, z0, h0, l0);
+    weights(t1, z1, h1, l1);
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+    [[maybe_unused]] uint32_t x01a[4], x23a[4], x01b[4], x23b[4];
+    fp8_rows(t0, x01a, x23a);
+    fp8_rows(t1, x01b, x23b);
+    pv32<0>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<1>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<2>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<3>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<4>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<5>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<6>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
+    pv32<7>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
   }
 
   // Move the reference max of head c to mnew (per lane) and rescale l (and
@@ -697,11 +793,29 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
       eat(tb, n + 1);
     }
 #else
+#if PA_MFMA_PAIRS
+    // Two tiles per step (32 tokens), a trailing odd tile on its own.
+    int n = c0;
+    for (; n + 1 < c1; n += 2) {
+      MfmaTile<CT> ta, tb;
+      st.template load_tile<POL>(ta, p, block_of(n), kvh, koff, voff, soff);
+      st.template load_tile<POL>(tb, p, block_of(n + 1), kvh, koff, voff, soff);
+      const int tk = (b0 + n) * kBlock;
+      st.consume2(ta, tb, rr.needs_mask(tk), rr.needs_mask(tk + kBlock), tk, lo, hi, rr.ulo,
+                  rr.uhi, g, p.scale_log2);
+    }
+    if (n < c1) {
+      MfmaTile<CT> t;
+      st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
+      eat(t, n);
+    }
+#else
     MfmaTile<CT> t;
     for (int n = c0; n < c1; ++n) {
       st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
       eat(t, n);
     }
+#endif
 #endif
   }
   // Renormalise to the true max (every lane takes part: rescale reads other
