@@ -100,6 +100,11 @@ struct RowRanges {
 #ifndef PA_MFMA_PREFETCH
 #define PA_MFMA_PREFETCH 0
 #endif
+// 1: workgroups of four 16-row groups of one sequence (bf16 cache) load each
+// K/V tile once into LDS and read their operands from there.
+#ifndef PA_MFMA_STAGE
+#define PA_MFMA_STAGE 1
+#endif
 // 1: the MFMA engine folds tiles two at a time (32 tokens per softmax step,
 // P.V on 16x16x32 instructions).
 #ifndef PA_MFMA_PAIRS
@@ -716,15 +721,31 @@ struct MfmaWave {
   }
 };
 
+// LDS staging of the MFMA engine (bf16 cache): a 16-token K or V tile is 16
+// rows of 256 bytes, stored 272 bytes apart so that the lanes' 16-byte
+// operand reads of one row fall in different banks; two tiles (K and V) per
+// buffer, two buffers.
+constexpr int kStageRow = 272;
+constexpr int kStageTile = kBlock * kStageRow;   // one K or V tile
+constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
+
 // Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split (tile n
 // starts at token (b0 + n) * 16); leaves the wave's (m, l, acc) for the rows
 // R0 .. R0 + nrows - 1 in LDS row `wave`.
-template <int QT, int CT, int D, int G, int NW, int POL>
+// STAGED (bf16 cache, every wave of the workgroup on the same sequence and
+// split, one row group per wave): the workgroup walks the union [sb0, sb1) of
+// its waves' tiles together; each tile is loaded from memory once, by all
+// 256 threads, into an LDS buffer (aliasing sm_acc, which is written only
+// after the walk), and every wave reads its K and V operands from there, for
+// the tiles of its own range. One barrier per tile; the next tile's loads are
+// issued right after it, so they fly while the current tile is consumed.
+template <int QT, int CT, int D, int G, int NW, int POL, bool STAGED = false>
 __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int R0,
                                                int nrows, const RowRanges &rr, int b0, int wb0,
                                                int wb1, int lane, int wave,
                                                float (&sm_m)[NW][G], float (&sm_l)[NW][G],
-                                               float (&sm_acc)[NW][G][D]) {
+                                               float (&sm_acc)[NW][G][D], int sb0 = 0,
+                                               int sb1 = 0) {
   using Wv = MfmaWave<CT, G>;
   Wv st;
   const int c = lane % 16, g = lane / 16;
@@ -767,6 +788,53 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
   };
+  if constexpr (STAGED) {
+    static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
+    char *stage = reinterpret_cast<char *>(&sm_acc[0][0][0]);
+    const int tid = threadIdx.x;  // NW * 64 = 256 threads, 16 bytes of a tile each
+    const int srow = tid / 16, scol = (tid % 16) * 16;
+    constexpr int TB = kBlock * 256;  // bytes of a bf16 K or V tile in memory
+    for (int c0 = sb0; c0 < sb1; c0 += kWave) {
+      const int c1 = min(sb1, c0 + kWave);
+      int my_id = 0;
+      if (lane < c1 - c0)
+        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+      auto block_of = [&](int n) {
+        return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0),
+                   last_block);
+      };
+      u32x4 kr, vr;
+      auto fetch = [&](int n) {
+        const int64_t tile = (int64_t)block_of(n) * p.num_kv_heads + kvh;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char *)p.k_cache + tile * TB, TB);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char *)p.v_cache + tile * TB, TB);
+        kr = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, 0, 0);
+        vr = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, 0, 0);
+      };
+      fetch(c0);
+      for (int n = c0; n < c1; ++n) {
+        char *buf = stage + (n & 1) * 2 * kStageTile;
+        *reinterpret_cast<u32x4 *>(buf + srow * kStageRow + scol) = kr;
+        *reinterpret_cast<u32x4 *>(buf + kStageTile + srow * kStageRow + scol) = vr;
+        // The buffer is complete, and every wave has finished with the other
+        // one (read two tiles ago).
+        __syncthreads();
+        if (n + 1 < c1) fetch(n + 1);
+        if (n >= wb0 && n < wb1) {
+          MfmaTile<CT> t;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            t.k[i] = *reinterpret_cast<const u32x4 *>(buf + c * kStageRow + 64 * i + 16 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            t.v[i] = *reinterpret_cast<const u32x4 *>(buf + kStageTile +
+                                                      (4 * g + i) * kStageRow + 16 * c);
+          eat(t, n);
+        }
+      }
+    }
+    __syncthreads();  // the staging space is sm_acc: every wave is done with it
+  } else
   // Tiles in chunks of 64: the chunk's physical block ids sit one per lane.
   for (int c0 = wb0; c0 < wb1; c0 += kWave) {
     const int c1 = min(wb1, c0 + kWave);
@@ -1001,8 +1069,26 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     }
   }
   // Tiles that several row groups read stay cached; a lone row group streams.
+  // Four row groups of one sequence (bf16, 16 rows each: prefill chunks)
+  // share each tile through LDS.
+  constexpr bool kStageable = PA_MFMA_STAGE && QT == PA_BF16 && CT == PA_BF16 && D == 128 &&
+                              G == 16 && NW == 4;
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
-    if (rw > 1)
+    if (kStageable && rw == NW && group == 0) {
+      // The workgroup's tiles: those any of its rows reach.
+      int sb0 = 0, sb1 = 0;
+      const int all = min(R_end - R0, rw * G);
+      if (has_split && all > 0) {
+        const RowRanges ru = RowRanges::make(L, Q, W, p.group, R0, all, qsp.first);
+        const int ta = max(t0, ru.ulo), tz = min(t1 - 1, ru.uhi);
+        if (tz >= ta) {
+          sb0 = (ta - t0) / kBlock;
+          sb1 = (tz - t0) / kBlock + 1;
+        }
+      }
+      wave_pass_mfma<QT, CT, D, G, NW, 0, kStageable>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1,
+                                                      lane, wave, sm_m, sm_l, sm_acc, sb0, sb1);
+    } else if (rw > 1)
       wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
     else
