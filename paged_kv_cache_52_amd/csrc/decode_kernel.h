@@ -722,10 +722,15 @@ struct MfmaWave {
 };
 
 // LDS staging of the MFMA engine (bf16 cache): a 16-token K or V tile is 16
-// rows of 256 bytes, stored 272 bytes apart so that the lanes' 16-byte
-// operand reads of one row fall in different banks; two tiles (K and V) per
-// buffer, two buffers.
-constexpr int kStageRow = 272;
+// rows of 256 bytes, stored PA_STAGE_ROW bytes apart to spread the lanes'
+// 16-byte operand reads over the banks; two tiles (K and V) per buffer, two
+// buffers. Measured on the prefill chunk batch: rows 256 bytes apart spend
+// 50% of the busy cycles in bank conflicts, 272 bytes 22%, 288 bytes 12%
+// (and 288 is the fastest of 272 .. 384).
+#ifndef PA_STAGE_ROW
+#define PA_STAGE_ROW 288
+#endif
+constexpr int kStageRow = PA_STAGE_ROW;
 constexpr int kStageTile = kBlock * kStageRow;   // one K or V tile
 constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
 
