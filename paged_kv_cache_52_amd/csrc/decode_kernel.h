@@ -105,6 +105,11 @@ struct RowRanges {
 #ifndef PA_MFMA_STAGE
 #define PA_MFMA_STAGE 1
 #endif
+// 1: staged tiles go two at a time, P.V on 16x16x32 instructions fed by LDS
+// transpose reads.
+#ifndef PA_STAGE_PAIRS
+#define PA_STAGE_PAIRS 1
+#endif
 // 1: the MFMA engine folds tiles two at a time (32 tokens per softmax step,
 // P.V on 16x16x32 instructions).
 #ifndef PA_MFMA_PAIRS
@@ -442,6 +447,31 @@ __device__ __forceinline__ uint32_t u8col_to_bf16(uint32_t w0, uint32_t w1) {
   return pack_bf16(ubyte_f32<K>(w0), ubyte_f32<K>(w1));
 }
 
+// LDS staging of the MFMA engine (bf16 cache): a 16-token K or V tile is 16
+// rows of 256 bytes, stored PA_STAGE_ROW bytes apart to spread the lanes'
+// 16-byte operand reads over the banks; two tiles (K and V) per buffer, two
+// buffers. Measured on the prefill chunk batch: rows 256 bytes apart spend
+// 50% of the busy cycles in bank conflicts, 272 bytes 22%, 288 bytes 12%
+// (and 288 is the fastest of 272 .. 384).
+#ifndef PA_STAGE_ROW
+#define PA_STAGE_ROW 288
+#endif
+constexpr int kStageRow = PA_STAGE_ROW;
+constexpr int kStageTile = kBlock * kStageRow;   // one K or V tile
+constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 4a + e receives element e of the 8-byte rows addressed by lanes a,
+// a + 4, a + 8 and a + 12 (measured lane layout on gfx950).
+__device__ __forceinline__ s16x4 lds_read_tr16(const char *ptr) {
+#if __HIP_DEVICE_COMPILE__
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(char *)ptr);
+#else
+  return s16x4{0, 0, 0, 0};
+#endif
+}
+
 template <int CT, int G>
 struct MfmaWave {
   static constexpr int ELT = DtypeBytes<CT>::value;
@@ -704,6 +734,101 @@ struct MfmaWave {
     pv32<7>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
   }
 
+  // Staged tiles (bf16 K/V rows in LDS, PA_STAGE_ROW bytes apart).
+  // Logits of the tile whose K rows start at kb.
+  __device__ __forceinline__ void scores_lds(const char *kb, float (&z)[4], float scale_log2,
+                                             int c, int g) const {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 k = *reinterpret_cast<const u32x4 *>(kb + c * PA_STAGE_ROW + 64 * i + 16 * g);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                  __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
+  }
+
+  // B operand of output column block JJ (dims 16JJ .. 16JJ + 15) from the V
+  // tile at vb: this lane's column (dim 16JJ + c), tokens 4g .. 4g + 3. Lane
+  // (c, g) addresses 4 dims of token 4g + c / 4, so that the transpose read
+  // hands every lane its column.
+  template <int JJ>
+  __device__ __forceinline__ static s16x4 v_tr(const char *vb, int c, int g) {
+    return lds_read_tr16(vb + (4 * g + (c >> 2)) * PA_STAGE_ROW + (16 * JJ + 4 * (c & 3)) * 2);
+  }
+
+  template <int JJ>
+  __device__ __forceinline__ void pv32_lds(const char *v0, const char *v1, int c, int g,
+                                           bf16x8 phi, bf16x8 plo) {
+    const s16x4 a = v_tr<JJ>(v0, c, g), b = v_tr<JJ>(v1, c, g);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, acc[JJ], 0, 0, 0);
+    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, bv, acc[JJ], 0, 0, 0);
+  }
+
+  // Fold the staged tile pair (K0, V0) and (K1, V1), first tokens tb and
+  // tb + 16, as one 32-token step. in0 / in1: the tile is in this wave's range
+  // (else its logits are -inf); m0 / m1: it is at an edge of some row's range.
+  // O column block JJ holds dims 16JJ .. 16JJ + 15 here (lane c: dim 16JJ + c).
+  // V rows no row of the workgroup attends are zero in LDS, so a zero weight
+  // never meets a NaN.
+  __device__ __forceinline__ void consume_pair_lds(const char *k0, const char *v0,
+                                                   const char *k1, const char *v1, bool in0,
+                                                   bool in1, bool m0, bool m1, int tb, int lo,
+                                                   int hi, int c, int g, float scale_log2) {
+    float z0[4], z1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z0[r] = z1[r] = -INFINITY;
+    if (in0) {
+      scores_lds(k0, z0, scale_log2, c, g);
+      if (m0) mask_z(z0, tb, lo, hi, g);
+    }
+    if (in1) {
+      scores_lds(k1, z1, scale_log2, c, g);
+      if (m1) mask_z(z1, tb + kBlock, lo, hi, g);
+    }
+    update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
+                     fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
+               g);
+    uint32_t h0[2], l0[2], h1[2], l1[2];
+    weights_plain(z0, h0, l0);
+    weights_plain(z1, h1, l1);
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+    pv32_lds<0>(v0, v1, c, g, phi, plo);
+    pv32_lds<1>(v0, v1, c, g, phi, plo);
+    pv32_lds<2>(v0, v1, c, g, phi, plo);
+    pv32_lds<3>(v0, v1, c, g, phi, plo);
+    pv32_lds<4>(v0, v1, c, g, phi, plo);
+    pv32_lds<5>(v0, v1, c, g, phi, plo);
+    pv32_lds<6>(v0, v1, c, g, phi, plo);
+    pv32_lds<7>(v0, v1, c, g, phi, plo);
+  }
+
+  // Tokens of this lane's row outside [lo, hi] get -inf (tile at tb).
+  __device__ __forceinline__ static void mask_z(float (&z)[4], int tb, int lo, int hi, int g) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tb + 4 * g + r;
+      z[r] = (tok >= lo && tok <= hi) ? z[r] : -INFINITY;
+    }
+  }
+
+  // weights() without cache scales (bf16 cache).
+  __device__ __forceinline__ void weights_plain(const float (&z)[4], uint32_t (&hi)[2],
+                                                uint32_t (&lo)[2]) {
+    float pz[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
+    l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+    hi[0] = pack_bf16(pz[0], pz[1]);
+    hi[1] = pack_bf16(pz[2], pz[3]);
+    lo[0] = pack_bf16(pz[0] - bf16_lo(hi[0]), pz[1] - bf16_hi(hi[0]));
+    lo[1] = pack_bf16(pz[2] - bf16_lo(hi[1]), pz[3] - bf16_hi(hi[1]));
+  }
+
   // Move the reference max of head c to mnew (per lane) and rescale l (and
   // wsum) and the O rows (heads 4g + r get the factor computed in lane 4g + r).
   // All lanes of the wave must call it together.
@@ -721,18 +846,6 @@ struct MfmaWave {
   }
 };
 
-// LDS staging of the MFMA engine (bf16 cache): a 16-token K or V tile is 16
-// rows of 256 bytes, stored PA_STAGE_ROW bytes apart to spread the lanes'
-// 16-byte operand reads over the banks; two tiles (K and V) per buffer, two
-// buffers. Measured on the prefill chunk batch: rows 256 bytes apart spend
-// 50% of the busy cycles in bank conflicts, 272 bytes 22%, 288 bytes 12%
-// (and 288 is the fastest of 272 .. 384).
-#ifndef PA_STAGE_ROW
-#define PA_STAGE_ROW 288
-#endif
-constexpr int kStageRow = PA_STAGE_ROW;
-constexpr int kStageTile = kBlock * kStageRow;   // one K or V tile
-constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
 
 // Per-wave pass of the MFMA engine over tiles [wb0, wb1) of the split (tile n
 // starts at token (b0 + n) * 16); leaves the wave's (m, l, acc) for the rows
@@ -740,17 +853,22 @@ constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
 // STAGED (bf16 cache, every wave of the workgroup on the same sequence and
 // split, one row group per wave): the workgroup walks the union [sb0, sb1) of
 // its waves' tiles together; each tile is loaded from memory once, by all
-// 256 threads, into an LDS buffer (aliasing sm_acc, which is written only
-// after the walk), and every wave reads its K and V operands from there, for
-// the tiles of its own range. One barrier per tile; the next tile's loads are
-// issued right after it, so they fly while the current tile is consumed.
+// 256 threads, into LDS (aliasing sm_acc, which is written only after the
+// walk), and every wave reads its K and V operands from there, for the tiles
+// of its own range. With PA_STAGE_PAIRS the tiles go two at a time: V rows of
+// tokens outside the workgroup's [ulo_wg, uhi_wg] are stored as zeros, and
+// P.V runs on 16x16x32 instructions with V read by LDS transpose reads; the
+// next pair's loads fly (in registers) while the current pair is consumed,
+// two barriers per pair. Without it, one tile per step in two LDS buffers,
+// one barrier per tile.
 template <int QT, int CT, int D, int G, int NW, int POL, bool STAGED = false>
 __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int R0,
                                                int nrows, const RowRanges &rr, int b0, int wb0,
                                                int wb1, int lane, int wave,
                                                float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D], int sb0 = 0,
-                                               int sb1 = 0) {
+                                               int sb1 = 0, int ulo_wg = 0, int uhi_wg = -1) {
+  constexpr bool PAIRED = STAGED && PA_STAGE_PAIRS;
   using Wv = MfmaWave<CT, G>;
   Wv st;
   const int c = lane % 16, g = lane / 16;
@@ -793,7 +911,57 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
   };
-  if constexpr (STAGED) {
+  if constexpr (PAIRED) {
+    static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
+    char *stage = reinterpret_cast<char *>(&sm_acc[0][0][0]);
+    char *const K0 = stage, *const V0 = stage + kStageTile;
+    char *const K1 = stage + 2 * kStageTile, *const V1 = stage + 3 * kStageTile;
+    const int tid = threadIdx.x;  // NW * 64 = 256 threads, 16 bytes of a tile each
+    const int srow = tid / 16, scol = (tid % 16) * 16;
+    constexpr int TB = kBlock * 256;  // bytes of a bf16 K or V tile in memory
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int c0 = sb0; c0 < sb1; c0 += kWave) {
+      const int c1 = min(sb1, c0 + kWave);
+      int my_id = 0;
+      if (lane < c1 - c0)
+        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+      auto block_of = [&](int n) {
+        return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0),
+                   last_block);
+      };
+      u32x4 kr0 = zero, vr0 = zero, kr1 = zero, vr1 = zero;
+      auto fetch = [&](int n, u32x4 &kr, u32x4 &vr) {
+        const int64_t tile = (int64_t)block_of(n) * p.num_kv_heads + kvh;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char *)p.k_cache + tile * TB, TB);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char *)p.v_cache + tile * TB, TB);
+        kr = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, 0, 0);
+        vr = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, 0, 0);
+      };
+      fetch(c0, kr0, vr0);
+      if (c0 + 1 < c1) fetch(c0 + 1, kr1, vr1);
+      for (int n = c0; n < c1; n += 2) {
+        // Rows of tokens no row of the workgroup attends (and a missing
+        // second tile) are stored as zeros.
+        const int tok0 = (b0 + n) * kBlock + srow, tok1 = tok0 + kBlock;
+        const bool ok0 = tok0 >= ulo_wg && tok0 <= uhi_wg;
+        const bool ok1 = n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg;
+        *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = ok0 ? kr0 : zero;
+        *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = ok0 ? vr0 : zero;
+        *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = ok1 ? kr1 : zero;
+        *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = ok1 ? vr1 : zero;
+        __syncthreads();  // the pair is in LDS
+        if (n + 2 < c1) fetch(n + 2, kr0, vr0);
+        if (n + 3 < c1) fetch(n + 3, kr1, vr1);
+        const bool in0 = n >= wb0 && n < wb1, in1 = n + 1 < c1 && n + 1 >= wb0 && n + 1 < wb1;
+        if (in0 || in1) {
+          const int tb = (b0 + n) * kBlock;
+          st.consume_pair_lds(K0, V0, K1, V1, in0, in1, rr.needs_mask(tb),
+                              rr.needs_mask(tb + kBlock), tb, lo, hi, c, g, p.scale_log2);
+        }
+        __syncthreads();  // every wave is done with the pair
+      }
+    }
+  } else if constexpr (STAGED) {
     static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
     char *stage = reinterpret_cast<char *>(&sm_acc[0][0][0]);
     const int tid = threadIdx.x;  // NW * 64 = 256 threads, 16 bytes of a tile each
@@ -916,7 +1084,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int h = 4 * g + r;
     if (h < G) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sm_acc[wave][h][8 * c + jj] = st.acc[jj][r];
+      for (int jj = 0; jj < 8; ++jj) sm_acc[wave][h][PAIRED ? 16 * jj + c : 8 * c + jj] = st.acc[jj][r];
     }
   }
 }
@@ -1081,18 +1249,20 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
     if (kStageable && rw == NW && group == 0) {
       // The workgroup's tiles: those any of its rows reach.
-      int sb0 = 0, sb1 = 0;
+      int sb0 = 0, sb1 = 0, ulo = 0, uhi = -1;
       const int all = min(R_end - R0, rw * G);
       if (has_split && all > 0) {
         const RowRanges ru = RowRanges::make(L, Q, W, p.group, R0, all, qsp.first);
-        const int ta = max(t0, ru.ulo), tz = min(t1 - 1, ru.uhi);
-        if (tz >= ta) {
-          sb0 = (ta - t0) / kBlock;
-          sb1 = (tz - t0) / kBlock + 1;
+        ulo = max(t0, ru.ulo);
+        uhi = min(t1 - 1, ru.uhi);
+        if (uhi >= ulo) {
+          sb0 = (ulo - t0) / kBlock;
+          sb1 = (uhi - t0) / kBlock + 1;
         }
       }
       wave_pass_mfma<QT, CT, D, G, NW, 0, kStageable>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1,
-                                                      lane, wave, sm_m, sm_l, sm_acc, sb0, sb1);
+                                                      lane, wave, sm_m, sm_l, sm_acc, sb0, sb1,
+                                                      ulo, uhi);
     } else if (rw > 1)
       wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
