@@ -331,6 +331,43 @@ def test_quantised_decode_matches_oracle(name, qdt, D):
         _check_out(out32, ref, TOL_BF16, f"{name}/{T}")
 
 
+# Per-sequence V magnitudes (a factor on the V rows of even blocks, another on
+# odd blocks): INT8 V scales from about 2^-18 to 2^3, alone and mixed within
+# one sequence, so that weights p * vscale span a wide range.
+V_SCALE_FACTORS = [(1.0, 1.0), (16.0, 16.0), (2.0 ** -8, 2.0 ** -8), (1.0, 64.0),
+                   (1.0, 2.0 ** -10), (2.0 ** -12, 2.0 ** -12), (2.0 ** 8, 1.0)]
+
+
+@pytest.mark.parametrize("T", [16, 512])
+def test_int8_v_scale_range(T):
+    """INT8 decode with V rows scaled by powers of two over a wide range: the
+    error bound scales with the sequence's largest factor (the result is
+    linear in V)."""
+    print(f"[case] int8 V scale range T={T}", flush=True)
+    n = len(V_SCALE_FACTORS)
+    b = workloads.make_batch("int8_kv", 113, "cpu", num_seqs=n, ctx_range=(200, 1500),
+                             poison=True)
+    owner = {}
+    for s in range(n):
+        nblk = -(-int(b.context_lens[s]) // 16)
+        for j, blk in enumerate(b.block_tables[s, :nblk].tolist()):
+            owner[blk] = (s, j)
+    f = np.ones(len(b.fill_slots))
+    for i, slot in enumerate(b.fill_slots.tolist()):
+        s, j = owner[slot // 16]
+        f[i] = V_SCALE_FACTORS[s][j % 2]
+    b.fill_v = (b.fill_v.double() * torch.from_numpy(f)[:, None, None]).to(b.fill_v.dtype)
+    g = _to(b, "cuda")
+    _fill_quantised(b, g)
+    vs = _np(b.v_scale)
+    assert (vs[vs > 0] > 0.5).any() and (vs[vs > 0] < 2.0 ** -14).any()
+    ref = _oracle_decode(b)
+    out32, _ = _gpu_fp32_out(g, T)
+    for s in range(n):
+        tol = TOL_BF16 * max(V_SCALE_FACTORS[s])
+        _check_out(out32[s], ref[s], tol, f"seq {s} factors {V_SCALE_FACTORS[s]}")
+
+
 def test_identity_and_permuted_tables_agree():
     print("[case] identity vs permuted", flush=True)
     for contiguous in (True, False):
