@@ -178,6 +178,27 @@ __device__ __forceinline__ int seq_of_token(const int32_t *qs, int num_seqs, int
   return lo;
 }
 
+// seq_of_token for a whole wave that asks about one token t (t the same in
+// every lane): a 64-ary search. Each round, lane j probes the pivot lo + j *
+// step of the remaining range [lo, hi) (one load per lane, all in flight at
+// once), and the highest lane whose pivot is <= t narrows the range to its
+// step: ceil(log64(num_seqs)) dependent loads instead of log2(num_seqs). Same
+// result as seq_of_token: the largest s in [0, num_seqs) with qs[s] <= t, else
+// 0; for offsets that are not nondecreasing, some s in [0, num_seqs).
+__device__ __forceinline__ int seq_of_token_wave(const int32_t *qs, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;
+  const int lane = __lane_id();
+  while (hi - lo > 1) {  // uniform: lo and hi come from the ballot
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const unsigned long long le = __ballot(idx < hi && qs[idx] <= t);
+    const int j = le ? 63 - __clzll(le) : 0;
+    lo += j * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
 // Query rows (query token x query head of a KV head's group) per work item
 // with packed queries: the plan lists one item per (split, block of this many
 // rows) of a sequence.

@@ -264,6 +264,51 @@ def test_reduce_alone_against_oracle_merge():
     _check_out(out.cpu().double().numpy(), ref, 1e-5, "reduce")
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_reduce_many_rows_against_oracle_merge(packed):
+    """Batches of 16384 rows or more (each reduce wave then merges four rows):
+    the reduce on synthetic partials equals the oracle's merge. Some splits
+    inside a row's split count are empty; entries past it hold large finite
+    values that must not be used."""
+    print(f"[case] reduce many rows packed={packed}", flush=True)
+    rng = np.random.default_rng(321)
+    Hq, D, T = 32, 128, 512
+    B = 300 if packed else 600
+    lens = rng.integers(0, 3000, size=B).astype(np.int32)
+    lens[:3] = [0, 1, 512]
+    S = max(oracle.num_splits(int(L), T) for L in lens)
+    if packed:
+        counts = rng.integers(0, 5, size=B)
+        counts[:2] = [0, 3]
+        qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        N = int(qs[-1])
+        lead = (N, Hq)
+        tok_seq = np.repeat(np.arange(B), counts)
+        ns = np.array([oracle.num_splits(int(lens[s]), T, int(counts[s])) for s in tok_seq])
+        ns_rows = np.repeat(ns, Hq)
+    else:
+        lead = (B, 1, Hq)
+        ns_rows = np.repeat([oracle.num_splits(int(L), T) for L in lens], Hq)
+    assert ns_rows.size >= 16384
+    m = rng.normal(0.0, 2.0, lead + (S,))
+    l = rng.uniform(1.0, 100.0, lead + (S,))
+    acc = rng.normal(0.0, 1.0, lead + (S, D)) * l[..., None]
+    empty = rng.random(lead + (S,)) < 0.2
+    m[empty], l[empty], acc[empty] = -np.inf, 0.0, 0.0
+    past = (np.arange(S)[None, :] >= ns_rows[:, None]).reshape(lead + (S,))
+    ref = oracle.merge(np.where(past, -np.inf, m), np.where(past, 0.0, l),
+                       np.where(past[..., None], 0.0, acc))
+    m_g, l_g, acc_g = np.where(past, 50.0, m), np.where(past, 1e3, l), np.where(past[..., None], 1e6, acc)
+    cuda = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    parts = pa().Partials(m=cuda(m_g), l=cuda(l_g), acc=cuda(acc_g),
+                          context_lens=torch.from_numpy(lens).cuda(), split_tokens=T,
+                          query_start=torch.from_numpy(qs).cuda() if packed else None)
+    out = torch.empty(((N,) if packed else (B,)) + (Hq, D), dtype=torch.float32, device="cuda")
+    pa().paged_attn_reduce(parts, out)
+    torch.cuda.synchronize()
+    _check_out(out.cpu().double().numpy(), ref.reshape(out.shape), 1e-5, "reduce many rows")
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama8b_bf16"])
 def test_poisoned_slots_do_not_leak(name):
     """NaN in every unattended slot, the pad block and past-the-end table
