@@ -9,7 +9,8 @@ namespace pa {
 constexpr int kReduceWaves = 4;       // waves per workgroup
 constexpr int kReduceManySplits = 32;  // from this many splits, 4 waves share one head
 constexpr int kReduceU = 4;            // splits whose acc rows are loaded together
-constexpr int kReduceRowsForFour = 16384;  // from this many rows, each wave reduces four
+constexpr int kReduceRowsForFour = 16384;  // from this many rows (and at most kReduceU
+                                           // splits), each wave reduces four
 
 __device__ __forceinline__ float lane_value(float x, int j) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
@@ -220,8 +221,10 @@ void launch_reduce_t(const ReduceParams &p, hipStream_t stream) {
   const int grid_y = p.query_start ? 1 : p.num_seqs;
   if (p.max_splits >= kReduceManySplits) {
     hipLaunchKernelGGL((reduce_kernel<OT, D>), dim3(rows, grid_y), block, 0, stream, p);
-  } else if ((int64_t)rows * grid_y >= kReduceRowsForFour) {
-    // Many rows: four per wave, fewer and fuller workgroups.
+  } else if ((int64_t)rows * grid_y >= kReduceRowsForFour && p.max_splits <= kReduceU) {
+    // Many rows whose splits are all loaded up front: four per wave, fewer
+    // and fuller workgroups (with more splits the rows' remaining loads would
+    // run one row after another).
     const dim3 grid((rows + 4 * kReduceWaves - 1) / (4 * kReduceWaves), grid_y);
     hipLaunchKernelGGL((reduce_rows_kernel<OT, D, 4>), grid, block, 0, stream, p);
   } else {
