@@ -84,23 +84,33 @@ __device__ __forceinline__ void put_entry(const PlanParams &p, int idx, int w0, 
 // Join flags of the full split j of sequence s: bit c (c < M) is set when
 // sequence s + c takes part in the group of sequence s + c - 1 for split j,
 // that is when both splits are full and start on the same physical block.
-// Lengths and table words of sequences s - 1 .. s + M - 1 are read together
-// (two rounds of loads, whatever M).
-__device__ __forceinline__ int join_bits(const PlanParams &p, int s, int j) {
+// Lengths of sequences s - 1 .. s + M - 1 come from the chunk's lengths in LDS
+// (sequences base .. base + kPlanThreads - 1) or, past the chunk, from global
+// memory; their table words at block jb are loaded in the same round (a word
+// of a sequence whose split j is not full is read but not used).
+__device__ __forceinline__ int join_bits(const PlanParams &p, int s, int j, int base,
+                                         const int (&chunk_len)[kPlanThreads]) {
   constexpr int kMax = PA_MAX_GROUP_MEMBERS;
   const int M = p.group_members;
   const int jb = j * (p.split_tokens / kBlock);  // first block of split j (no window: base 0)
-  bool full[kMax + 1];
-  int blk[kMax + 1];
+  int len[kMax + 1], blk[kMax + 1];
 #pragma unroll
   for (int c = 0; c <= kMax; ++c) {
     const int t = s - 1 + c;
-    full[c] = c <= M && t >= 0 && t < p.num_seqs &&
-              j < seq_splits(p, clamp_len(p, t), p.num_query_tokens) - 1;
+    const bool seq = c <= M && t >= 0 && t < p.num_seqs;
+    len[c] = 0;
+    blk[c] = -1;
+    if (seq) {
+      len[c] = t >= base && t < base + kPlanThreads ? chunk_len[t - base] : clamp_len(p, t);
+      if (jb < p.max_blocks_per_seq)
+        blk[c] = p.block_tables[(int64_t)t * p.max_blocks_per_seq + jb];
+    }
   }
+  bool full[kMax + 1];
 #pragma unroll
-  for (int c = 0; c <= kMax; ++c)  // j < splits - 1 keeps jb inside the table row
-    blk[c] = full[c] ? p.block_tables[(int64_t)(s - 1 + c) * p.max_blocks_per_seq + jb] : -1;
+  for (int c = 0; c <= kMax; ++c)
+    full[c] = c <= M && s - 1 + c >= 0 && s - 1 + c < p.num_seqs &&
+              j < seq_splits(p, len[c], p.num_query_tokens) - 1;
   int bits = 0;
 #pragma unroll
   for (int c = 0; c < kMax; ++c)
@@ -193,7 +203,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
           word0 = (s_e << 16) | j;
           L_e = chunk_len[lo];
           const int pos = s_e % M;
-          const int bits = join_bits(p, s_e, j);
+          const int bits = join_bits(p, s_e, j, base, chunk_len);
           keep = !(pos > 0 && (bits & 1));
           if (keep)
             while (pos + cnt < M && ((bits >> cnt) & 1)) ++cnt;
