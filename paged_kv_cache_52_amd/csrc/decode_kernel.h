@@ -112,6 +112,12 @@ struct RowRanges {
 #endif
 // 1: the MFMA engine folds tiles two at a time (32 tokens per softmax step,
 // P.V on 16x16x32 instructions).
+// 1: group entries (members sharing blocks, 16 rows each) stage the first
+// member's tiles through LDS; each member takes the tiles it shares.
+#ifndef PA_STAGE_GROUPS
+#define PA_STAGE_GROUPS 1
+#endif
+
 #ifndef PA_MFMA_PAIRS
 #define PA_MFMA_PAIRS 0
 #endif
@@ -867,8 +873,12 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
                                                int wb1, int lane, int wave,
                                                float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D], int sb0 = 0,
-                                               int sb1 = 0, int ulo_wg = 0, int uhi_wg = -1) {
+                                               int sb1 = 0, int ulo_wg = 0, int uhi_wg = -1,
+                                               int s_own = -1) {
   constexpr bool PAIRED = STAGED && PA_STAGE_PAIRS;
+  // Group entry (s_own >= 0, uniform): the workgroup stages sequence s's
+  // blocks and this wave's rows belong to sequence s_own.
+  const bool grouped = PAIRED && s_own >= 0;
   using Wv = MfmaWave<CT, G>;
   Wv st;
   const int c = lane % 16, g = lane / 16;
@@ -922,12 +932,24 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int c0 = sb0; c0 < sb1; c0 += kWave) {
       const int c1 = min(sb1, c0 + kWave);
-      int my_id = 0;
-      if (lane < c1 - c0)
+      int my_id = 0, own_id = 0;
+      if (lane < c1 - c0) {
         my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+        if (grouped) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + c0 + lane];
+      }
       auto block_of = [&](int n) {
         return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0),
                    last_block);
+      };
+      // Group entry: this wave takes staged tile n only when it is its own
+      // block too and lies wholly inside its rows' tokens and the staged
+      // (unzeroed) tokens; the other tiles of its range follow the loop.
+      auto takes = [&](int n) {
+        if (!grouped) return true;
+        const int tb = (b0 + n) * kBlock;
+        return __builtin_amdgcn_readlane(own_id, n - c0) ==
+                   __builtin_amdgcn_readlane(my_id, n - c0) &&
+               tb >= max(rr.ulo, ulo_wg) && tb + kBlock - 1 <= min(rr.uhi, uhi_wg);
       };
       u32x4 kr0 = zero, vr0 = zero, kr1 = zero, vr1 = zero;
       auto fetch = [&](int n, u32x4 &kr, u32x4 &vr) {
@@ -952,13 +974,53 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         __syncthreads();  // the pair is in LDS
         if (n + 2 < c1) fetch(n + 2, kr0, vr0);
         if (n + 3 < c1) fetch(n + 3, kr1, vr1);
-        const bool in0 = n >= wb0 && n < wb1, in1 = n + 1 < c1 && n + 1 >= wb0 && n + 1 < wb1;
+        const bool in0 = n >= wb0 && n < wb1 && takes(n);
+        const bool in1 = n + 1 < c1 && n + 1 >= wb0 && n + 1 < wb1 && takes(n + 1);
         if (in0 || in1) {
           const int tb = (b0 + n) * kBlock;
           st.consume_pair_lds(K0, V0, K1, V1, in0, in1, rr.needs_mask(tb),
                               rr.needs_mask(tb + kBlock), tb, lo, hi, c, g, p.scale_log2);
         }
         __syncthreads();  // every wave is done with the pair
+      }
+    }
+    if (grouped) {
+      // O's columns leave the staged loop in the transpose-read order (block
+      // jj = dims 16jj .. 16jj+15, lane c: dim 16jj + c); the unstaged tiles
+      // below add in the register order (lane c: dims 8c .. 8c+7). Reorder
+      // through this wave's own LDS slot (the staging space is free now).
+      float *slot = &sm_acc[wave][0][0];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) slot[(4 * g + r) * D + 16 * jj + c] = st.acc[jj][r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) st.acc[jj][r] = slot[(4 * g + r) * D + 8 * c + jj];
+      // The tiles of this wave's range it did not take from LDS, from its own
+      // blocks (same test as takes()).
+      for (int c0 = wb0; c0 < wb1; c0 += kWave) {
+        const int c1 = min(wb1, c0 + kWave);
+        int mine = 0, staged_id = -1;
+        if (lane < c1 - c0) {
+          mine = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + c0 + lane];
+          if (c0 + lane >= sb0 && c0 + lane < sb1)
+            staged_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+        }
+        for (int n = c0; n < c1; ++n) {
+          const int tb = (b0 + n) * kBlock;
+          const int id = __builtin_amdgcn_readlane(mine, n - c0);
+          const bool took = n >= sb0 && n < sb1 &&
+                            id == __builtin_amdgcn_readlane(staged_id, n - c0) &&
+                            tb >= max(rr.ulo, ulo_wg) && tb + kBlock - 1 <= min(rr.uhi, uhi_wg);
+          if (!took) {
+            MfmaTile<CT> t;
+            st.template load_tile<0>(t, p, min(max(id, 0), last_block), kvh, koff, voff, soff);
+            eat(t, n);
+          }
+        }
       }
     }
   } else if constexpr (STAGED) {
@@ -1084,7 +1146,8 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int h = 4 * g + r;
     if (h < G) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sm_acc[wave][h][PAIRED ? 16 * jj + c : 8 * c + jj] = st.acc[jj][r];
+      for (int jj = 0; jj < 8; ++jj)
+        sm_acc[wave][h][PAIRED && !grouped ? 16 * jj + c : 8 * c + jj] = st.acc[jj][r];
     }
   }
 }
@@ -1247,11 +1310,20 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   constexpr bool kStageable = PA_MFMA_STAGE && QT == PA_BF16 && CT == PA_BF16 && D == 128 &&
                               G == 16 && NW == 4;
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
-    if (kStageable && rw == NW && group == 0) {
-      // The workgroup's tiles: those any of its rows reach.
+    if (kStageable && rw == NW && (group == 0 || PA_STAGE_GROUPS)) {
+      // The workgroup's tiles: those any of its rows reach; for a group
+      // entry, the blocks of the split the group's first sequence holds (each
+      // member takes those it shares).
       int sb0 = 0, sb1 = 0, ulo = 0, uhi = -1;
       const int all = min(R_end - R0, rw * G);
-      if (has_split && all > 0) {
+      if (group > 0) {
+        const int t1s = min(t0 + p.split_tokens, max(0, min(p.context_lens[s], lmax)));
+        if (t1s > t0) {
+          sb1 = (t1s - t0 + kBlock - 1) / kBlock;
+          ulo = t0;
+          uhi = t1s - 1;
+        }
+      } else if (has_split && all > 0) {
         const RowRanges ru = RowRanges::make(L, Q, W, p.group, R0, all, qsp.first);
         ulo = max(t0, ru.ulo);
         uhi = min(t1 - 1, ru.uhi);
@@ -1260,9 +1332,9 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
           sb1 = (uhi - t0) / kBlock + 1;
         }
       }
-      wave_pass_mfma<QT, CT, D, G, NW, 0, kStageable>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1,
-                                                      lane, wave, sm_m, sm_l, sm_acc, sb0, sb1,
-                                                      ulo, uhi);
+      wave_pass_mfma<QT, CT, D, G, NW, 0, kStageable>(
+          p, group > 0 ? s : s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave, sm_m, sm_l,
+          sm_acc, sb0, sb1, ulo, uhi, group > 0 ? s_rg : -1);
     } else if (rw > 1)
       wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);

@@ -781,6 +781,30 @@ def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
 # Plans with group entries: full splits j of consecutive sequences that start
 # on the same physical block (shared prefix blocks) become one work item.
 
+@pytest.mark.parametrize("T,M", [(64, 4), (512, 3)])
+def test_grouped_shared_prefix_with_poison(T, M):
+    """Group entries of 16-row members (their shared tiles staged once per
+    workgroup) with NaN in every slot no query token attends."""
+    print(f"[case] grouped shared prefix poison T={T} M={M}", flush=True)
+    b = workloads.make_batch("shared_prefix_bf16", 263, "cpu", groups=2, suffix_max=600,
+                             poison=True)
+    g = _to(b, "cuda")
+    ref = _oracle_decode(b)
+    assert np.isfinite(ref).all()
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=T,
+                                block_tables=g.block_tables, group_members=M)
+    parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                           g.context_lens, g.scale,
+                                           max_context_len=g.max_context_len, plan=plan)
+    out = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+    pa().paged_attn_reduce(parts, out)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    assert (sched[9:9 + 2 * int(sched[0]):2] < 0).any(), "the batch should form groups"
+    _check_out(out.cpu().double().numpy(), ref, _tol(b), f"grouped poison T={T} M={M}")
+
+
 def _share_prefixes(b, n_blocks=None):
     """Let every odd sequence share the leading blocks of the sequence before
     it (all but its last block, or n_blocks), as prefix sharing does."""
