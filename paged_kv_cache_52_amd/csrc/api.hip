@@ -71,6 +71,7 @@ int32_t clamped_bound(int32_t max_context_len, int32_t max_blocks_per_seq) {
 
 constexpr int32_t kMinDefaultSplit = 64;  // smallest split the default picks
 constexpr int64_t kMinWorkItems = 1024;   // (split, KV head) items the default aims for
+constexpr int64_t kGrowWorkItems = 3072;  // items a decode step keeps when its splits grow
 
 }  // namespace
 
@@ -140,6 +141,12 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
   while (t > kMinDefaultSplit && items(t) < kMinWorkItems) t /= 2;
   if (rows > 64)
     while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kMinWorkItems) t *= 2;
+  // A decode step with at most 8 rows per KV head: longer splits while at
+  // least kGrowWorkItems items remain (fewer items and partials, each a longer
+  // stream). Counted at the longest context, so a batch of many short
+  // sequences stays where the bytes put it.
+  if (rows <= 8)
+    while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kGrowWorkItems) t *= 2;
   return t;
 }
 

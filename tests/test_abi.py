@@ -63,13 +63,13 @@ def test_default_split_tokens_is_valid(lib):
 
 @pytest.mark.parametrize("B,Hkv,D,dt,L,T", [
     (64, 8, 128, BF16, 4096, 512),      # 8B-shaped bf16 batch: one split per 512 tokens
-    (8, 8, 128, BF16, 131072, 512),     # long contexts: ceil(L / 512) splits
-    (128, 8, 128, I8, 8192, 1024),      # INT8: the same 256 KiB per split is 1024 tokens
-    (256, 4, 128, BF16, 18385, 512),    # shared-prefix batch
+    (8, 8, 128, BF16, 131072, 2048),    # long contexts: 512, doubled while 3072 items remain
+    (128, 8, 128, I8, 8192, 2048),      # INT8: 256 KiB per split is 1024 tokens, doubled once
+    (256, 4, 128, BF16, 18385, 4096),   # 256 sequences at g = 4: 5120 items even at 4096
     (64, 8, 64, F32, 4096, 512),        # 64-dim fp32: 512 B per token, like bf16 x 128
-    (64, 8, 128, F32, 4096, 256),
+    (64, 8, 128, F32, 4096, 512),       # 256, doubled once (4096 items at 512)
     (64, 8, 64, I8, 4096, 2048),
-    (128, 8, 128, FP8, 8192, 1024),     # FP8: same bytes per token as INT8
+    (128, 8, 128, FP8, 8192, 2048),     # FP8: same bytes per token as INT8
     (1, 8, 128, BF16, 4096, 64),        # 8 heads x 64 splits = 512 items < 1024: floor 64
     (2, 8, 128, BF16, 8192, 128),       # 16 heads x 64 splits = 1024 items
     (4, 2, 64, F32, 128, 64),
