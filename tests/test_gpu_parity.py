@@ -423,6 +423,99 @@ def test_identity_and_permuted_tables_agree():
         _check_out(out32, _oracle_decode(b), TOL_BF16, f"contiguous={contiguous}")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp32", "int8", "fp8"])
+def test_pool_beyond_4gib(cache):
+    """A pool whose K and V arrays are each larger than 4 GiB (8 KV heads,
+    head_dim 128): the sequences' blocks sit mostly past the 4 GiB byte offset
+    of their array, so the write and the split kernel address them with 64-bit
+    offsets. Every sequence is written through the KV write on both sides; the
+    oracle holds only the used blocks, renumbered 0.., which gives the same
+    result (attention does not depend on where a block sits in the pool).
+    Written tiles are compared bytewise, outputs against the oracle."""
+    print(f"[case] pool beyond 4 GiB, {cache} cache", flush=True)
+    Hq, Hkv, D = 32, 8, 128
+    t_dt, np_dt, elt = {"bf16": (torch.bfloat16, np.uint16, 2),
+                        "fp32": (torch.float32, np.float32, 4),
+                        "int8": (torch.int8, np.int8, 1),
+                        "fp8": (torch.float8_e4m3fn, np.uint8, 1)}[cache]
+    quant = cache in ("int8", "fp8")
+    q_dt = torch.float32 if cache == "fp32" else torch.bfloat16
+    block_bytes = Hkv * 16 * D * elt
+    NB = (1 << 32) // block_bytes + 4096          # > 4 GiB per array
+    lens = np.array([1, 200, 517, 1000, 2049], np.int32)
+    need = [(int(L) + 15) // 16 for L in lens]
+    rng = np.random.default_rng(41)
+    # Mostly from the top of the pool, a few from the bottom.
+    ids = np.concatenate([NB - 1 - rng.permutation(2048)[:sum(need) - 6],
+                          rng.permutation(64)[:6]]).astype(np.int64)
+    rng.shuffle(ids)
+    mb = max(need)
+    tables = np.zeros((len(lens), mb), np.int32)
+    ctables = np.zeros_like(tables)
+    slots, cslots, used = [], [], []
+    k = 0
+    for s, L in enumerate(lens):
+        for i in range(need[s]):
+            tables[s, i], ctables[s, i] = ids[k], k
+            used.append(ids[k])
+            k += 1
+        t = np.arange(L)
+        slots.append(tables[s, t // 16].astype(np.int64) * 16 + t % 16)
+        cslots.append(ctables[s, t // 16].astype(np.int64) * 16 + t % 16)
+    slots, cslots = np.concatenate(slots), np.concatenate(cslots)
+    used = torch.from_numpy(np.array(used, np.int64))
+    N = len(slots)
+    kx = torch.from_numpy(rng.normal(size=(N, Hkv, D)).astype(np.float32)).to(q_dt)
+    vx = torch.from_numpy(rng.normal(size=(N, Hkv, D)).astype(np.float32)).to(q_dt)
+    q = torch.from_numpy(rng.normal(size=(len(lens), Hq, D)).astype(np.float32)).to(q_dt)
+    scale = 1.0 / np.sqrt(D)
+
+    # Oracle side: the used blocks only.
+    nb = len(used)
+    kc = np.zeros((nb, Hkv, 16, D), np_dt)
+    vc = np.zeros_like(kc)
+    ks = vs = None
+    if quant:
+        ks = np.zeros((nb, Hkv, 16), np.float32)
+        vs = np.zeros_like(ks)
+    oracle.kv_write(_np(kx), _np(vx), cslots, kc, vc, ks, vs)
+
+    # Library side: the whole pool; the used blocks start at zero.
+    gk = torch.empty((NB, Hkv, 16, D), dtype=t_dt, device="cuda")
+    gv = torch.empty_like(gk)
+    gks = gvs = None
+    try:
+        gk.view(torch.uint8)[used.cuda()] = 0
+        gv.view(torch.uint8)[used.cuda()] = 0
+        if quant:
+            gks = torch.zeros((NB, Hkv, 16), dtype=torch.float32, device="cuda")
+            gvs = torch.zeros_like(gks)
+        pa().paged_kv_write(kx.cuda(), vx.cuda(), torch.from_numpy(slots).cuda(), gk, gv, gks,
+                            gvs)
+        torch.cuda.synchronize()
+        ub = used.cuda()
+        assert np.array_equal(_np(gk[ub]).view(np.uint8), kc.view(np.uint8))
+        assert np.array_equal(_np(gv[ub]).view(np.uint8), vc.view(np.uint8))
+        if quant:
+            assert np.array_equal(_np(gks[ub]).view(np.uint32), ks.view(np.uint32))
+            assert np.array_equal(_np(gvs[ub]).view(np.uint32), vs.view(np.uint32))
+        ref = oracle.decode(_np(q), kc, vc, ctables, lens, scale, ks, vs)
+        tol = TOL_F32 if cache == "fp32" else TOL_BF16
+        gq, gt = q.cuda(), torch.from_numpy(tables).cuda()
+        gl = torch.from_numpy(lens).cuda()
+        for T in (64, None):
+            parts = pa().paged_attn_decode_partial(gq, gk, gv, gt, gl, scale, gks, gvs,
+                                                   max_context_len=int(lens.max()),
+                                                   split_tokens=T)
+            out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+            pa().paged_attn_reduce(parts, out)
+            torch.cuda.synchronize()
+            _check_out(out.cpu().double().numpy(), ref, tol, f"{cache}/T={T}")
+    finally:
+        del gk, gv, gks, gvs
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T", [16, 512])
 def test_plan_lists_every_split_once(T):
     """The plan kernel's work list holds each (sequence, split) exactly once:
@@ -1142,3 +1235,4 @@ def test_packed_batch_without_query_tokens():
                                  query_start=g.query_start)
     torch.cuda.synchronize()
     assert out.shape == (0, b.q.shape[1], b.q.shape[2])
+
