@@ -97,6 +97,7 @@ extern "C" {
 #define PA_MAX_QUERY_TOKENS 4096
 #define PA_MAX_PACKED_QUERY_TOKENS (1 << 20)
 #define PA_MAX_GROUP_MEMBERS 4
+#define PA_MAX_SPLITS 65536  /* splits per sequence: the plan stores the split index in 16 bits */
 
 /* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
  * NaN, largest finite 448). */
@@ -108,7 +109,8 @@ enum {
   PA_ERR_NULL = -1,      /* a required pointer is NULL */
   PA_ERR_DTYPE = -2,     /* unsupported dtype or dtype combination */
   PA_ERR_SHAPE = -3,     /* unsupported sizes (head_dim, head counts, ...) */
-  PA_ERR_SPLIT = -4,     /* bad split_tokens, or max_splits below what is needed */
+  PA_ERR_SPLIT = -4,     /* bad split_tokens, max_splits below what is needed, or more than
+                            PA_MAX_SPLITS splits for the longest possible sequence */
   PA_ERR_WORKSPACE = -5, /* workspace smaller than pa_workspace_bytes() */
   PA_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned */
   PA_ERR_LAUNCH = -7     /* the kernel launch failed */

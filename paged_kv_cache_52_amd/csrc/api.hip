@@ -232,6 +232,7 @@ int check_plan(const int32_t *context_lens, const int32_t *query_start,
   const int32_t lmax = clamped_bound(max_context_len, max_blocks_per_seq);
   const int32_t ns = pa_max_splits(lmax, query_bound(packed, num_query_tokens), sliding_window,
                                    split_tokens);
+  if (ns > PA_MAX_SPLITS) return PA_ERR_SPLIT;
   const int64_t cap = plan_capacity(num_seqs, ns, packed, num_query_tokens,
                                     packed ? q_heads_per_kv : 1);
   if (cap > INT_MAX / 2) return PA_ERR_SHAPE;
@@ -325,7 +326,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   // Splits of the longest range any sequence can have under the clamped bound.
   const int32_t grid_splits = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
                                             qmax, sliding_window, split_tokens);
-  if (max_splits < grid_splits) return PA_ERR_SPLIT;
+  if (max_splits < grid_splits || grid_splits > PA_MAX_SPLITS) return PA_ERR_SPLIT;
   // Entries the plan can list: the grid has one workgroup per possible item.
   const int64_t max_entries = plan_capacity(num_seqs, grid_splits, packed, num_query_tokens,
                                             num_q_heads / num_kv_heads);

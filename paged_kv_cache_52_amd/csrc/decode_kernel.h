@@ -1474,7 +1474,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
   const int word1 = p.sched[kSchedHeader + 2 * (k / per_entry) + 1];
   // The sequence index is clamped so that no entry can send a read out of
   // bounds; process_split ignores a split index past a sequence's end.
-  const int s = min(packed_entry >> 16, p.num_seqs - 1);
+  const int s = min((int)((uint32_t)packed_entry >> 16), p.num_seqs - 1);
   const int j = packed_entry & 0xffff;
   if (!packed) {
     // word1 is the sequence's length, or minus the member count of a group

@@ -74,6 +74,13 @@ __device__ __forceinline__ SeqPlan seq_plan(const PlanParams &p, int s) {
   return r;
 }
 
+// First word of an entry: sequence s (< 65536) in the high 16 bits, split j
+// (< 65536) in the low 16, packed as unsigned (the word is negative for
+// s >= 32768; readers shift it as unsigned).
+__device__ __forceinline__ int entry_word(int s, int j) {
+  return (int)(((uint32_t)s << 16) | (uint32_t)j);
+}
+
 __device__ __forceinline__ void put_entry(const PlanParams &p, int idx, int w0, int w1) {
   if (idx < p.capacity) {
     p.sched[kSchedHeader + 2 * idx] = w0;
@@ -182,7 +189,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
         const int lo = owner_of(chunk_first, e);
         const int q = e - chunk_first[lo], per = chunk_per[lo];
         const int j = q / per, rb = q % per;  // row blocks of a split are adjacent
-        put_entry(p, base_entry + e, ((base + lo) << 16) | j, packed ? rb : chunk_len[lo]);
+        put_entry(p, base_entry + e, entry_word(base + lo, j), packed ? rb : chunk_len[lo]);
       }
       __syncthreads();
       if (tid == 0) carry += total;
@@ -200,7 +207,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
         if (e < total) {
           const int lo = owner_of(chunk_first, e);
           const int s_e = base + lo, j = e - chunk_first[lo];
-          word0 = (s_e << 16) | j;
+          word0 = entry_word(s_e, j);
           L_e = chunk_len[lo];
           const int pos = s_e % M;
           const int bits = join_bits(p, s_e, j, base, chunk_len);
@@ -267,7 +274,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
       if (sp.per_split > 0) {
         const int pos = atomicAdd(&bucket[last_tiles(p, sp.L, sp.Q)], sp.per_split);
         for (int rb = 0; rb < sp.per_split; ++rb)
-          put_entry(p, pos + rb, (s << 16) | (sp.splits - 1), packed ? rb : sp.L);
+          put_entry(p, pos + rb, entry_word(s, sp.splits - 1), packed ? rb : sp.L);
       }
     }
   }

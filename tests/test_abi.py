@@ -220,6 +220,9 @@ def test_plan_validation(lib):
     assert plan(mb=0) == ERR_SHAPE
     assert plan(mcl=-1) == ERR_SHAPE
     assert plan(split=8) == ERR_SPLIT
+    # More than PA_MAX_SPLITS (65536) splits for the longest sequence: the
+    # split index would not fit the plan's 16 bits.
+    assert plan(mcl=16 * 65536 + 16, mb=65537, split=16) == ERR_SPLIT
     assert plan(split=0) == ERR_SPLIT                  # no default without the cache
     assert plan(sched=None) == ERR_NULL
     assert plan(Q=0) == ERR_SHAPE
@@ -261,6 +264,7 @@ def test_decode_partial_validation(lib):
     assert _partial(lib, qdt=I8, cdt=I8) == ERR_DTYPE
     assert _partial(lib, T=24) == ERR_SPLIT
     assert _partial(lib, T=8192) == ERR_SPLIT
+    assert _partial(lib, mcl=16 * 65536 + 16, mb=65537, T=16, S=65537) == ERR_SPLIT
     assert _partial(lib, mcl=1025, S=2, mb=100) == ERR_SPLIT  # needs 3 splits
     assert _partial(lib, mcl=100000, mb=8000, W=500, S=1) == ERR_SPLIT  # 515 tokens: 2 splits
     assert _partial(lib, Q=0) == ERR_SHAPE

@@ -516,6 +516,35 @@ def test_pool_beyond_4gib(cache):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_sequence_indices_past_32767(dtype, D):
+    """40,000 short sequences: the plan's first entry word holds the sequence
+    in its high 16 bits, so the words of sequences from 32,768 on are negative
+    as int32 and must be read as unsigned. Every sequence is listed, and the
+    decode (new tokens written first) matches the oracle, MFMA and VALU
+    engines, one and several splits per sequence."""
+    print(f"[case] 40000 sequences {dtype} D={D}", flush=True)
+    w = workloads.Workload("many_short_sequences", 40000, 8, 2, D, dtype, dtype, 1, 40)
+    b = workloads.make_batch(w, 281, "cpu")
+    g = _to(b, "cuda")
+    _write_new_tokens(b, g)
+    ref = _oracle_decode(b)
+    plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                max_context_len=g.max_context_len, split_tokens=16)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy().astype(np.int64) & 0xffffffff
+    n = int(sched[0])
+    seqs = sched[8:8 + 2 * n:2] >> 16
+    splits = sched[8:8 + 2 * n:2] & 0xffff
+    lens = _np(b.context_lens).astype(np.int64)
+    assert n == int(np.maximum(1, -(-lens // 16)).sum())
+    assert np.array_equal(np.bincount(seqs, minlength=40000), np.maximum(1, -(-lens // 16)))
+    assert splits.max() < 3
+    for T in (16, None):
+        out32, _ = _gpu_fp32_out(g, T)
+        _check_out(out32, ref, _tol(b), f"40000 sequences T={T}")
+
+
 @pytest.mark.parametrize("T", [16, 512])
 def test_plan_lists_every_split_once(T):
     """The plan kernel's work list holds each (sequence, split) exactly once:
@@ -534,7 +563,7 @@ def test_plan_lists_every_split_once(T):
     n = sum(nsplit)
     assert list(sched[:8]) == [n, T, len(lens), min(g.max_context_len, 16 * b.block_tables.shape[1]),
                                1, 0, 0, 0]
-    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
+    entries = [((int(e) & 0xffffffff) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
     assert list(sched[9:9 + 2 * n:2]) == [lens[s] for s, _ in entries]
     assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
     n_full = n - len(lens)
@@ -850,7 +879,7 @@ def test_plan_with_query_ranges(Q, W, T):
     nsplit = [oracle.num_splits(L, T, Q, W) for L in lens]
     n = sum(nsplit)
     assert list(sched[:8]) == [n, T, len(lens), g.max_context_len, Q, W, 0, 0]
-    entries = [(int(e) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
+    entries = [((int(e) & 0xffffffff) >> 16, int(e) & 0xffff) for e in sched[8:8 + 2 * n:2]]
     assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
 
 
@@ -969,7 +998,7 @@ def test_grouped_plan(T, M):
     # Expanded, the list covers every (sequence, split) exactly once.
     pairs = []
     for w0, w1 in zip(sched[8:8 + 2 * n:2].tolist(), sched[9:9 + 2 * n:2].tolist()):
-        s, j = w0 >> 16, w0 & 0xffff
+        s, j = (w0 & 0xffffffff) >> 16, w0 & 0xffff
         pairs += [(s + i, j) for i in range(-w1 if w1 < 0 else 1)]
     assert sorted(pairs) == sorted((s, j) for s in range(len(L))
                                    for j in range(max(1, -(-L[s] // T))))
@@ -1174,7 +1203,7 @@ def test_packed_plan_lists_every_row_block_once(T, W):
     assert sorted(got[len(full):]) == last
 
     def tiles(w0):
-        s = w0 >> 16
+        s = (w0 & 0xffffffff) >> 16
         base = oracle.split_base(lens[s], counts[s], W)
         rest = lens[s] - base - (nsp[s] - 1) * T
         return max(1, -(-rest // 16)) if lens[s] - base > 0 else 1
