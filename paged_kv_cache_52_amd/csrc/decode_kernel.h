@@ -1273,7 +1273,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   const int rg = wave / tw, tp = wave % tw;   // this wave's row group and tile share
   const int W = p.window;
   // Context length, clamped so that no read leaves the table or the pool.
-  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  const int lmax = (int)min((int64_t)p.max_context_len, (int64_t)p.max_blocks_per_seq * kBlock);
   // The row group's sequence, rows and split range.
   auto seq_of = [&](int g) { return group > 0 ? s + g : s; };
   const int s_rg = min(seq_of(rg), p.num_seqs - 1);
@@ -1453,7 +1453,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
 
   const bool packed = p.query_start != nullptr;
   const int per_entry = packed ? p.num_kv_heads : p.num_kv_heads * p.head_groups;
-  const int lmax = min(p.max_context_len, p.max_blocks_per_seq * kBlock);
+  const int lmax = (int)min((int64_t)p.max_context_len, (int64_t)p.max_blocks_per_seq * kBlock);
   // A plan made with group entries needs uniform query counts, every
   // sequence's rows in one row group (Q*g <= G), and a wave per member.
   static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
