@@ -110,14 +110,13 @@ struct RowRanges {
 #ifndef PA_STAGE_PAIRS
 #define PA_STAGE_PAIRS 1
 #endif
-// 1: the MFMA engine folds tiles two at a time (32 tokens per softmax step,
-// P.V on 16x16x32 instructions).
 // 1: group entries (members sharing blocks, 16 rows each) stage the first
 // member's tiles through LDS; each member takes the tiles it shares.
 #ifndef PA_STAGE_GROUPS
 #define PA_STAGE_GROUPS 1
 #endif
-
+// 1: the unstaged MFMA engine folds tiles two at a time (32 tokens per softmax
+// step, P.V on 16x16x32 instructions).
 #ifndef PA_MFMA_PAIRS
 #define PA_MFMA_PAIRS 0
 #endif
@@ -127,7 +126,8 @@ struct RowRanges {
 //   [1] split_tokens, [2] num_seqs, [3] clamped max length, [4] query tokens
 //   (per sequence, or the packed total), [5] window the plan was made for,
 //   [6] group members (0: no group entries), [7] g with packed queries, else 0
-//   then two words per entry, full splits first: (sequence << 16 | split) and
+//   then two words per entry, full splits first: (sequence << 16 | split),
+//   read as unsigned (negative as int32 from sequence 32768 on), and
 //   the sequence's clamped context length (minus the member count for a group
 //   entry; the row block index with packed queries).
 constexpr int kSchedHeader = 8;
