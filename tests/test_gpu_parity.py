@@ -737,6 +737,28 @@ def test_full_size_sampled_rows(name):
                     f"{name}/bf16-out")
 
 
+def test_long_contexts_with_thousands_of_splits():
+    """The long-context batch at its full size (8 sequences up to 128k tokens)
+    with 16-token splits: up to 8,192 splits per sequence, so the split index
+    uses 13 of its 16 plan bits and the reduce merges thousands of partials per
+    row. Sampled rows against the oracle."""
+    print("[case] long contexts, 16-token splits", flush=True)
+    g = workloads.make_batch("long_bf16", 3, "cuda")
+    b = workloads.Batch(**{f: getattr(g, f) for f in g.__dataclass_fields__})
+    for f in g.__dataclass_fields__:
+        v = getattr(g, f)
+        if isinstance(v, torch.Tensor):
+            setattr(b, f, v.cpu())
+    out32, parts = _gpu_fp32_out(g, 16)
+    assert parts.max_splits >= 4096
+    B, Hq = g.q.shape[0], g.q.shape[-2]
+    seqs, toks, heads = _sample_rows(B, 1, Hq, 16, 9)
+    ref = _oracle_decode(b, rows=(seqs, toks, heads))
+    D = g.q.shape[-1]
+    flat = seqs.astype(np.int64) * Hq + heads
+    _check_out(out32.reshape(-1, D)[flat], ref, TOL_BF16, "long contexts T=16")
+
+
 # ------------------------------------------------ several query tokens, windows
 
 MTP_CASES = [
