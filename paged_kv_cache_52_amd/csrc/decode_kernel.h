@@ -787,6 +787,10 @@ struct MfmaWave {
     float z0[4], z1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) z0[r] = z1[r] = -INFINITY;
+    // The matrix-core blocks (logits, then P.V) run at a raised wave priority
+    // and the softmax between them at the normal one, so that a SIMD's waves
+    // tend to alternate between the two phases instead of bunching up in one.
+    __builtin_amdgcn_s_setprio(1);
     if (in0) {
       scores_lds(k0, z0, scale_log2, c, g);
       if (m0) mask_z(z0, tb, lo, hi, g);
@@ -795,6 +799,7 @@ struct MfmaWave {
       scores_lds(k1, z1, scale_log2, c, g);
       if (m1) mask_z(z1, tb + kBlock, lo, hi, g);
     }
+    __builtin_amdgcn_s_setprio(0);
     update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
                      fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
                g);
@@ -803,6 +808,7 @@ struct MfmaWave {
     weights_plain(z1, h1, l1);
     const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
     const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+    __builtin_amdgcn_s_setprio(1);
     pv32_lds<0>(v0, v1, c, g, phi, plo);
     pv32_lds<1>(v0, v1, c, g, phi, plo);
     pv32_lds<2>(v0, v1, c, g, phi, plo);
@@ -811,6 +817,7 @@ struct MfmaWave {
     pv32_lds<5>(v0, v1, c, g, phi, plo);
     pv32_lds<6>(v0, v1, c, g, phi, plo);
     pv32_lds<7>(v0, v1, c, g, phi, plo);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Tokens of this lane's row outside [lo, hi] get -inf (tile at tb).
