@@ -95,11 +95,6 @@ struct RowRanges {
   }
 };
 
-// Software pipeline of the MFMA engine: 1 keeps the next tile's loads in
-// flight while the current tile is consumed.
-#ifndef PA_MFMA_PREFETCH
-#define PA_MFMA_PREFETCH 0
-#endif
 // 1: workgroups of four 16-row groups of one sequence (bf16 cache) load each
 // K/V tile once into LDS and read their operands from there.
 #ifndef PA_MFMA_STAGE
@@ -1087,22 +1082,6 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     auto block_of = [&](int n) {
       return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0), last_block);
     };
-#if PA_MFMA_PREFETCH
-    // Two tiles in flight: tile n + 1 is requested before tile n is consumed.
-    // The look-ahead load is unconditional (a dead one reads nothing), so the
-    // wait before each consume is the same on every path.
-    MfmaTile<CT> ta, tb;
-    st.template load_tile<POL>(ta, p, block_of(c0), kvh, koff, voff, soff, c0 < c1);
-    for (int n = c0; n < c1; n += 2) {
-      st.template load_tile<POL>(tb, p, block_of(n + 1), kvh, koff, voff, soff, n + 1 < c1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead ahead of the wait
-      eat(ta, n);
-      if (n + 1 >= c1) break;
-      st.template load_tile<POL>(ta, p, block_of(n + 2), kvh, koff, voff, soff, n + 2 < c1);
-      __builtin_amdgcn_sched_barrier(0);
-      eat(tb, n + 1);
-    }
-#else
 #if PA_MFMA_PAIRS
     // Two tiles per step (32 tokens), a trailing odd tile on its own.
     int n = c0;
@@ -1125,7 +1104,6 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
       st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
       eat(t, n);
     }
-#endif
 #endif
   }
   // Renormalise to the true max (every lane takes part: rescale reads other
