@@ -15,17 +15,27 @@ t_step: one new token per sequence, Q per sequence for multi-token decode and
 prefill chunks, the packed total N for a batch with per-sequence counts).
 The split kernel's roofline uses its own duration: HIP events on the launch
 stream around `steps` back-to-back launches of it after the timed region.
+Its bytes are the unique K/V bytes the launch must read (a block shared by
+several sequences counts once) plus q, out and the table entries used; the
+logical bytes (every sequence's tokens counted in full) are a side figure.
 Per-kernel p10/p50/p90 come from a pass with events between the kernels of
 each step. The line also carries the practical HBM read ceiling measured by
 the library's read probe on the same device.
 """
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
 import sys
 import time
+
+# The CPU baseline's OpenMP threads are bound close together, one per core.
+# OpenMP reads this when its runtime starts, which torch's import does, so it
+# is set before anything is imported.
+os.environ.setdefault("OMP_PROC_BIND", "close")
+os.environ.setdefault("OMP_PLACES", "cores")
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -97,10 +107,13 @@ def algorithmic_flops(b):
 
 
 def algorithmic_bytes(b):
-    """Bytes the split kernel must read by definition: the K and V rows (plus
-    INT8 scales) of every token some query token attends (with a sliding
-    window only the tokens it reaches; nothing of a sequence without query
-    tokens), q, and the block-table entries used."""
+    """Bytes one decode step must move by definition: the K and V rows (plus
+    INT8 / FP8 scales) of every token some query token attends (with a
+    sliding window only the tokens it reaches; nothing of a sequence without
+    query tokens), q, out, the block-table entries used and the lengths.
+    Returns (unique, logical): unique counts each pool slot once however many
+    sequences attend it (shared prefix blocks), logical counts every
+    sequence's tokens in full. The two differ only when tables share blocks."""
     import numpy as np
     import workloads
     L = b.context_lens.to("cpu").numpy().astype(np.int64)
@@ -109,17 +122,58 @@ def algorithmic_bytes(b):
     live = Qs > 0
     w = b.workload
     per_token = workloads.kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.cache_dtype)
-    kv = int((L - lo)[live].sum()) * per_token
-    q = b.q.numel() * b.q.element_size()
-    tables = int(((L + 15) // 16 - lo // 16)[live].sum()) * 4 + L.size * 4
+    kv_logical = int((L - lo)[live].sum()) * per_token
+    tables = b.block_tables.to("cpu").numpy()[live]
+    slots = workloads.attended_slots(tables, L[live], lo[live])
+    kv_unique = int(np.unique(slots).size) * per_token
+    qo = 2 * b.q.numel() * b.q.element_size()  # out has q's shape and dtype
+    meta = int(((L + 15) // 16 - lo // 16)[live].sum()) * 4 + L.size * 4
     if b.query_start is not None:
-        tables += (L.size + 1) * 4
-    return kv, kv + q + tables
+        meta += (L.size + 1) * 4
+    return kv_unique + qo + meta, kv_logical + qo + meta, kv_unique, kv_logical
+
+
+def fragmentation(b):
+    """Internal fragmentation of the batch's K/V memory [LLM Primer ch. 8,
+    8.1]: the fraction of reserved token slots that hold no token. `paged`:
+    the distinct 16-token blocks the tables reference for the tokens they
+    hold (shared blocks once) against those tokens; `max_length_slots`: every
+    sequence reserving a contiguous slot of the batch's longest context, with
+    its whole context stored privately."""
+    import numpy as np
+    import workloads
+    L = b.context_lens.to("cpu").numpy().astype(np.int64)
+    lo = workloads.reach_start(L, query_counts(b), b.window) // 16 * 16
+    tables = b.block_tables.to("cpu").numpy()
+    slots = np.unique(workloads.attended_slots(tables, L, lo))
+    blocks = np.unique(slots // 16)
+    paged = 1.0 - slots.size / (16.0 * max(blocks.size, 1))
+    maxlen = 1.0 - float(L.sum()) / max(1, L.size * int(L.max(initial=0)))
+    return {"paged": paged, "max_length_slots": maxlen,
+            "paged_figure_of_the_primer": 0.04}
+
+
+def host_description():
+    """CPU model, NUMA nodes and usable cores of the machine the CPU baseline
+    runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nodes = len(glob.glob("/sys/devices/system/node/node[0-9]*")) or 1
+    return {"cpu_model": model, "numa_nodes": nodes, "usable_cpus": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(b, seconds):
     """Time the oracle on a bounded sample of the same batch: whole sequences
-    (all heads) in order until about `seconds` of CPU time have passed."""
+    (all heads) in order until about `seconds` of CPU time have passed. Its
+    OpenMP threads are bound close, one per core; on a machine with several
+    NUMA nodes a pool over 1 GiB is spread over all of them first."""
     import numpy as np
     import torch
     import oracle
@@ -135,6 +189,14 @@ def cpu_baseline(b, seconds):
     q, kc, vc = host(b.q), host(b.k_cache), host(b.v_cache)
     ks = None if b.k_scale is None else host(b.k_scale)
     vs = None if b.v_scale is None else host(b.v_scale)
+    hw = host_description()
+    pool = kc.nbytes + vc.nbytes
+    policy = "first touch (one NUMA node)" if hw["numa_nodes"] == 1 else \
+        f"first touch (pool {pool / 2**30:.2f} GiB, not over 1 GiB)"
+    if hw["numa_nodes"] > 1 and pool > 2**30:
+        errs = [oracle.interleave(a, hw["numa_nodes"]) for a in (kc, vc) if a is not None]
+        policy = (f"interleaved over {hw['numa_nodes']} nodes" if not any(errs) else
+                  f"interleave failed (errno {max(errs)}), first touch")
     bt, cl = host(b.block_tables), host(b.context_lens)
     qs = None if b.query_start is None else host(b.query_start)
     B, Hq = b.num_seqs, q.shape[-2]
@@ -160,6 +222,8 @@ def cpu_baseline(b, seconds):
         "sample": f"{done} sequences ({done / B:.2f} passes over the {B}-sequence batch, "
                   f"{queries} query tokens x {Hq} q heads, {tokens} context tokens), fp64 "
                   f"block-table walk, {elapsed:.1f} s",
+        "host": dict(hw, omp_threads=oracle.num_threads(), omp_proc_bind=oracle.proc_bind(),
+                     omp_places=os.environ.get("OMP_PLACES", ""), numa_policy=policy),
     }
 
 
@@ -200,6 +264,73 @@ def hbm_probe(pa, torch, dev, stream, mib, reps=10):
     return (mib << 20) / (ms * 1e-3) / 1e9
 
 
+class Step:
+    """One decode step of one attention layer, exactly as the benchmark times
+    it: paged_decode_prepare (the step's new tokens written into the pool and
+    the split plan made, one launch), paged_attn_decode_partial (the split
+    kernel, through that plan) and paged_attn_reduce into `out` (q's dtype).
+    split_tokens 0 takes the library default; group_members 0 takes 4 (group
+    entries over shared blocks) for shared-prefix batches without a window or
+    packed queries, else 1. The parity tests run this same object."""
+
+    def __init__(self, pa, b, split_tokens=0, group_members=0):
+        import torch
+        w = b.workload
+        dev = b.q.device
+        self.pa, self.b = pa, b
+        B, Hq, D = b.num_seqs, b.q.shape[-2], b.q.shape[-1]
+        W = b.window
+        self.packed = packed = b.query_start is not None
+        # Query tokens: per sequence, or the packed total N (per-sequence counts).
+        Q = b.q.shape[0] if packed else b.query_tokens
+        self.num_query_tokens = Q
+        self.n_query = b.q.shape[0] if packed else B * Q
+        Qb = min(Q, pa.MAX_QUERY_TOKENS) if packed else Q          # per-sequence bound
+        Qd = max(1, min(pa.MAX_QUERY_TOKENS, -(-Q // B))) if packed else Q  # default-T count
+        self.mb = mb = b.block_tables.shape[1]
+        self.T = T = split_tokens or pa.default_split_tokens(
+            B, Hq, w.num_kv_heads, w.head_dim, b.k_cache.dtype, b.max_context_len, Qd, W)
+        self.S = S = pa.max_splits(min(b.max_context_len, mb * 16), T, Qb, W)
+        self.out = torch.empty_like(b.q)
+        lead = (self.n_query, Hq) if packed else (B, Q, Hq)
+        self.parts = pa.Partials(
+            m=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
+            l=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
+            acc=torch.empty(lead + (S, D), dtype=torch.float32, device=dev),
+            context_lens=b.context_lens, split_tokens=T, sliding_window=W,
+            query_start=b.query_start)
+        self.sched = torch.empty(pa.sched_bytes(B, S, Q if packed else None,
+                                                Hq // w.num_kv_heads) // 4,
+                                 dtype=torch.int32, device=dev)
+        self.M = group_members or (4 if w.groups and W == 0 and not packed else 1)
+        self.plan = None
+
+    def prepare(self):
+        b = self.b
+        self.plan = self.pa.paged_decode_prepare(
+            b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, b.context_lens, self.mb,
+            b.k_scale, b.v_scale, max_context_len=b.max_context_len, split_tokens=self.T,
+            num_query_tokens=self.num_query_tokens, sliding_window=b.window,
+            num_q_heads=b.q.shape[-2], query_start=b.query_start, block_tables=b.block_tables,
+            group_members=self.M, sched=self.sched)
+
+    def decode(self):
+        b = self.b
+        self.pa.paged_attn_decode_partial(
+            b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale, b.k_scale,
+            b.v_scale, max_context_len=b.max_context_len, split_tokens=self.T,
+            sliding_window=b.window, plan=self.plan, query_start=b.query_start,
+            partials=self.parts)
+
+    def reduce(self, out=None):
+        self.pa.paged_attn_reduce(self.parts, self.out if out is None else out)
+
+    def __call__(self):
+        self.prepare()
+        self.decode()
+        self.reduce()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -221,56 +352,14 @@ def main():
         pa.paged_kv_write(b.fill_k, b.fill_v, b.fill_slots, b.k_cache, b.v_cache, b.k_scale,
                           b.v_scale)
         b.fill_k = b.fill_v = None
+    st = Step(pa, b, args.split_tokens, args.group_members)
     B, Hq, D = b.num_seqs, b.q.shape[-2], b.q.shape[-1]
-    W = b.window
-    packed = b.query_start is not None
-    # Query tokens: per sequence, or the packed total N (per-sequence counts).
-    Q = b.q.shape[0] if packed else b.query_tokens
-    n_query = b.q.shape[0] if packed else B * Q
-    Qb = min(Q, pa.MAX_QUERY_TOKENS) if packed else Q          # per-sequence bound
-    Qd = max(1, min(pa.MAX_QUERY_TOKENS, -(-Q // B))) if packed else Q  # default-T count
-    mb = b.block_tables.shape[1]
-    T = args.split_tokens or pa.default_split_tokens(B, Hq, w.num_kv_heads, w.head_dim,
-                                                       b.k_cache.dtype, b.max_context_len, Qd, W)
-    S = pa.max_splits(min(b.max_context_len, mb * 16), T, Qb, W)
-    out = torch.empty_like(b.q)
-    lead = (n_query, Hq) if packed else (B, Q, Hq)
-    parts = pa.Partials(m=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
-                        l=torch.empty(lead + (S,), dtype=torch.float32, device=dev),
-                        acc=torch.empty(lead + (S, D), dtype=torch.float32, device=dev),
-                        context_lens=b.context_lens, split_tokens=T, sliding_window=W,
-                        query_start=b.query_start)
-    sched = torch.empty(pa.sched_bytes(B, S, Q if packed else None, Hq // w.num_kv_heads) // 4,
-                        dtype=torch.int32, device=dev)
-    M = args.group_members or (4 if w.groups and W == 0 and not packed else 1)
+    W, T, S, M = b.window, st.T, st.S, st.M
+    packed, n_query = st.packed, st.n_query
     stream = torch.cuda.current_stream(dev)
-    plan = [None]
-
-    def prepare():
-        # KV write of the step's new tokens and the split plan, one launch.
-        plan[0] = pa.paged_decode_prepare(b.new_k, b.new_v, b.slot_mapping, b.k_cache,
-                                          b.v_cache, b.context_lens, mb, b.k_scale, b.v_scale,
-                                          max_context_len=b.max_context_len, split_tokens=T,
-                                          num_query_tokens=Q, sliding_window=W,
-                                          num_q_heads=Hq, query_start=b.query_start,
-                                          block_tables=b.block_tables, group_members=M,
-                                          sched=sched)
-
-    def decode():
-        pa.paged_attn_decode_partial(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
-                                     b.scale, b.k_scale, b.v_scale,
-                                     max_context_len=b.max_context_len, split_tokens=T,
-                                     sliding_window=W, plan=plan[0], query_start=b.query_start,
-                                     partials=parts)
-
-    def reduce():
-        pa.paged_attn_reduce(parts, out)
-
-    def step():
-        prepare(); decode(); reduce()
 
     for _ in range(args.warmup):
-        step()
+        st()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` whole steps.
@@ -279,7 +368,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        st()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -288,9 +377,9 @@ def main():
     # Per-kernel durations: identical launches with events between them.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
-        e[0].record(stream); prepare()
-        e[1].record(stream); decode()
-        e[2].record(stream); reduce()
+        e[0].record(stream); st.prepare()
+        e[1].record(stream); st.decode()
+        e[2].record(stream); st.reduce()
         e[3].record(stream)
     torch.cuda.synchronize()
     per = {k: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
@@ -304,24 +393,25 @@ def main():
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record(stream)
     for _ in range(args.steps):
-        decode()
+        st.decode()
     d1.record(stream)
     torch.cuda.synchronize()
     t_dec_b2b = d0.elapsed_time(d1) / args.steps
 
-    kv_bytes, alg_bytes = algorithmic_bytes(b)
+    alg_bytes, logical_bytes, kv_unique, kv_logical = algorithmic_bytes(b)
     alg_flops = algorithmic_flops(b)
     dec_gbps = alg_bytes / (t_dec_b2b * 1e-3) / 1e9
     dec_tflops = alg_flops / (t_dec_b2b * 1e-3) / 1e12
     # The kernel's bound: matrix cores once its arithmetic intensity passes
     # the ridge point of the two peaks (dense bf16 MFMA / HBM).
     mfma_bound = alg_flops / alg_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
+    kv_gbps_step = kv_unique / (ms_step * 1e-3) / 1e9
     counters = load_counters(w.name)
     traffic = None
     if counters is not None:
         traffic = counters["fetch_bytes_per_launch"] + counters["write_bytes_per_launch"]
     probe_gbps = hbm_probe(pa, torch, dev, stream, args.probe_mib) if args.probe_mib else None
+    shared = kv_unique != kv_logical
 
     line = {
         "metric": METRIC,
@@ -342,7 +432,8 @@ def main():
             "head_dim": D, "block_size": 16, "cache_dtype": w.cache_dtype,
             "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "split_tokens": T, "max_splits": S, "pool_blocks": int(b.k_cache.shape[0]),
-            "query_tokens": (f"packed: {n_query} over {B} sequences" if packed else Q),
+            "query_tokens": (f"packed: {n_query} over {B} sequences" if packed else
+                             st.num_query_tokens),
             "sliding_window": W, "group_members": M,
             "tables": "contiguous" if args.contiguous_tables else "permuted",
             "context_range": list(args.ctx_range) if args.ctx_range else
@@ -370,8 +461,17 @@ def main():
             "read_probe_gbps": probe_gbps,
             "frac_of_read_probe": dec_gbps / probe_gbps if probe_gbps else None,
         }),
+        "fragmentation": fragmentation(b),
         "wall_s_timed": wall,
     }
+    if shared:
+        # Blocks shared by several sequences: the roofline counts them once;
+        # the logical figure counts every sequence's tokens in full (it can
+        # pass the HBM peak, since a shared block is read once for several).
+        line["roofline"]["bytes_basis"] = "unique"
+        line["roofline"]["algorithmic_bytes_logical"] = logical_bytes
+        line["roofline"]["logical_gbps"] = logical_bytes / (t_dec_b2b * 1e-3) / 1e9
+        line["kv_read_gbps_logical"] = kv_logical / (ms_step * 1e-3) / 1e9
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

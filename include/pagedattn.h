@@ -333,7 +333,11 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
  *   part_*         as written by paged_attn_decode_partial with the same
  *                  query_start, num_query_tokens, sliding_window, split_tokens
  *                  (T > 0) and max_splits
- *   context_lens   [num_seqs] int32 (lengths are clamped to >= 0)
+ *   context_lens   [num_seqs] int32; each length is clamped to
+ *                  [0, min(max_context_len, 16 * max_blocks_per_seq)] exactly
+ *                  as the split kernel clamps it, so the reduce merges the
+ *                  splits that call wrote and no others
+ *   max_blocks_per_seq, max_context_len   the bounds given to the decode call
  *   query_start    NULL, or the packed query offsets (each packed row finds
  *                  its sequence by binary search over them)
  *   out            [num_seqs][num_query_tokens][num_q_heads][head_dim]
@@ -342,6 +346,7 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
                       const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
                       int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                      int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t sliding_window, int32_t split_tokens, int32_t max_splits,
                       void *out, int32_t out_dtype, hipStream_t stream);
 

@@ -65,6 +65,10 @@ def _load():
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
+        lib.oracle_proc_bind.argtypes = []
+        lib.oracle_proc_bind.restype = I
+        lib.oracle_interleave.argtypes = [P, ctypes.c_size_t, I]
+        lib.oracle_interleave.restype = I
         _lib = lib
     return _lib
 
@@ -107,6 +111,17 @@ def e4m3_encode(x: float) -> int:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def proc_bind() -> str:
+    """Thread binding of the oracle's OpenMP loops (omp_get_proc_bind)."""
+    v = int(_load().oracle_proc_bind())
+    return {0: "false", 1: "true", 2: "primary", 3: "close", 4: "spread"}.get(v, str(v))
+
+
+def interleave(a: np.ndarray, nodes: int) -> int:
+    """Spread the pages of array a over NUMA nodes 0 .. nodes-1 (0 or an errno)."""
+    return int(_load().oracle_interleave(_ptr(a), a.nbytes, int(nodes)))
 
 
 def split_base(context_len: int, num_query_tokens: int = 1, window: int = 0) -> int:

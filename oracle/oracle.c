@@ -76,11 +76,15 @@
  * -ffp-contract=off and without -ffast-math (the INT8 quantiser relies on IEEE
  * fp32 division and the default round-to-nearest-even mode).
  */
+#define _GNU_SOURCE /* syscall() for the NUMA placement helper at the end */
+#include <errno.h>
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <sys/syscall.h>
+#include <unistd.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3 };
 enum { OR_BLOCK = 16 };
@@ -470,3 +474,27 @@ void oracle_merge(const double *m, const double *l, const double *acc, int64_t n
 
 /* Threads the OpenMP loops above use (reported with the CPU baseline). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Thread binding of the OpenMP loops, as omp_get_proc_bind() reports it
+ * (0 false, 1 true, 2 primary, 3 close, 4 spread); reported with the CPU
+ * baseline. */
+int oracle_proc_bind(void) { return (int)omp_get_proc_bind(); }
+
+/* Spread the pages of [addr, addr + bytes) round robin over NUMA nodes
+ * 0 .. nodes - 1 (the memory policy `numactl --interleave` gives a whole
+ * process), moving pages that are already placed, so that the CPU baseline's
+ * threads read a large pool from every node's memory rather than from the
+ * node that first touched it. Returns 0, or the errno of the mbind call. */
+int oracle_interleave(void *addr, size_t bytes, int nodes) {
+  enum { MPOL_INTERLEAVE_ = 3, MPOL_MF_MOVE_ = 1 << 1 };
+  unsigned long mask[16] = {0};
+  if (nodes < 1 || nodes > (int)(8 * sizeof mask)) return EINVAL;
+  for (int n = 0; n < nodes; ++n) mask[n / (8 * sizeof(unsigned long))] |= 1UL << (n % (8 * sizeof(unsigned long)));
+  const uintptr_t page = (uintptr_t)sysconf(_SC_PAGESIZE);
+  const uintptr_t a0 = (uintptr_t)addr & ~(page - 1);
+  const uintptr_t a1 = ((uintptr_t)addr + bytes + page - 1) & ~(page - 1);
+  if (syscall(SYS_mbind, (void *)a0, (unsigned long)(a1 - a0), MPOL_INTERLEAVE_, mask,
+              (unsigned long)(8 * sizeof mask), MPOL_MF_MOVE_) != 0)
+    return errno;
+  return 0;
+}

@@ -35,6 +35,7 @@ from . import _lib
 
 BLOCK_SIZE = 16
 MAX_QUERY_TOKENS = 4096
+_INT32_MAX = 2**31 - 1
 PA_F32, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3
 _DTYPE_CODES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
                 torch.float8_e4m3fn: PA_FP8}
@@ -174,6 +175,11 @@ class Partials:
     split_tokens: int
     sliding_window: int = 0
     query_start: Optional[torch.Tensor] = None  # [B+1] int32 with packed queries
+    # Bounds of the decode call that wrote the partials: the reduce clamps each
+    # context length to min(max_context_len, 16 * max_blocks_per_seq) as the
+    # split kernel did (None: no bound beyond the int32 range).
+    max_context_len: Optional[int] = None
+    max_blocks_per_seq: Optional[int] = None
 
     @property
     def max_splits(self) -> int:
@@ -368,6 +374,7 @@ def paged_attn_decode_partial(q, k_cache, v_cache, block_tables, context_lens, s
                                  "[N][Hq][max_splits](...) with packed queries")
         partials.context_lens, partials.split_tokens = context_lens, T
         partials.sliding_window, partials.query_start = W, query_start
+    partials.max_context_len, partials.max_blocks_per_seq = plan.max_context_len, mb
     args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                         query_start)
     _check(lib.paged_attn_decode_partial(
@@ -392,11 +399,14 @@ def paged_attn_reduce(partials: Partials, out: torch.Tensor) -> torch.Tensor:
         B, Q, Hq, S = partials.m.shape
         if out.shape not in ((B, Q, Hq, D),) + (((B, Hq, D),) if Q == 1 else ()):
             raise PagedAttnError("out must be [B][Hq][D] or [B][Q][Hq][D]")
+    mcl = _INT32_MAX if partials.max_context_len is None else int(partials.max_context_len)
+    mb = (_INT32_MAX // BLOCK_SIZE if partials.max_blocks_per_seq is None
+          else int(partials.max_blocks_per_seq))
     _check(lib.paged_attn_reduce(
         _dev(partials.m, "m", torch.float32), _dev(partials.l, "l", torch.float32),
         _dev(partials.acc, "acc", torch.float32),
         _dev(partials.context_lens, "context_lens", torch.int32),
-        _dev(partials.query_start, "query_start", torch.int32), B, Q, Hq, D,
+        _dev(partials.query_start, "query_start", torch.int32), B, Q, Hq, D, mb, mcl,
         partials.sliding_window, partials.split_tokens, S, _dev(out, "out"), _code(out),
         _stream(out.device)))
     return out

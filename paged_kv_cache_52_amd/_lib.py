@@ -39,9 +39,10 @@ SIGNATURES = {
     "paged_decode_prepare": (ctypes.c_int, [_P, _P, _I32, _P, _I64, _I32, _I32, _P, _P, _P, _P,
                                             _I64, _I32, _P, _P, _P, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _I32, _I32, _P, _P]),
-    # m, l, acc, context_lens, query_start, B, Q, Hq, D, W, T, S, out, out_dtype, stream
+    # m, l, acc, context_lens, query_start, B, Q, Hq, D, mb, mcl, W, T, S, out, out_dtype,
+    # stream
     "paged_attn_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
-                                         _I32, _P, _I32, _P]),
+                                         _I32, _I32, _I32, _P, _I32, _P]),
     "pa_hbm_read_probe": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),
     "paged_attn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
                                          _I64, _I32, _P, _I32, _P, _P, _I32, _I32, _F32, _I32,

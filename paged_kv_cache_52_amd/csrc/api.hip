@@ -399,10 +399,13 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
 int paged_attn_reduce(const float *part_m, const float *part_l, const float *part_acc,
                       const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
                       int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                      int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t sliding_window, int32_t split_tokens, int32_t max_splits,
                       void *out, int32_t out_dtype, hipStream_t stream) {
   const bool packed = query_start != nullptr;
-  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0) return PA_ERR_SHAPE;
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PA_ERR_SHAPE;
   if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
   if ((int64_t)num_query_tokens * num_q_heads > INT_MAX) return PA_ERR_SHAPE;
@@ -412,7 +415,8 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
   if (!part_m || !part_l || !part_acc || !context_lens || !out) return PA_ERR_NULL;
   pa::ReduceParams p{part_m, part_l, part_acc, context_lens, out, num_seqs, num_q_heads,
                      head_dim, split_tokens, max_splits, out_dtype, num_query_tokens,
-                     sliding_window, query_start};
+                     sliding_window, query_start,
+                     clamped_bound(max_context_len, max_blocks_per_seq)};
   return launch_status(pa::launch_reduce(p, stream));
 }
 
@@ -469,8 +473,8 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                                  split_tokens, ns, m, l, acc, sched, stream);
   if (st != PA_OK) return st;
   return paged_attn_reduce(m, l, acc, context_lens, query_start, num_seqs, num_query_tokens,
-                           num_q_heads, head_dim, sliding_window, split_tokens, ns, out, q_dtype,
-                           stream);
+                           num_q_heads, head_dim, max_blocks_per_seq, max_context_len,
+                           sliding_window, split_tokens, ns, out, q_dtype, stream);
 }
 
 int pa_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t sink_words,

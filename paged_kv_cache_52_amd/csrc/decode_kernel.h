@@ -95,27 +95,6 @@ struct RowRanges {
   }
 };
 
-// 1: workgroups of four 16-row groups of one sequence (bf16 cache) load each
-// K/V tile once into LDS and read their operands from there.
-#ifndef PA_MFMA_STAGE
-#define PA_MFMA_STAGE 1
-#endif
-// 1: staged tiles go two at a time, P.V on 16x16x32 instructions fed by LDS
-// transpose reads.
-#ifndef PA_STAGE_PAIRS
-#define PA_STAGE_PAIRS 1
-#endif
-// 1: group entries (members sharing blocks, 16 rows each) stage the first
-// member's tiles through LDS; each member takes the tiles it shares.
-#ifndef PA_STAGE_GROUPS
-#define PA_STAGE_GROUPS 1
-#endif
-// 1: the unstaged MFMA engine folds tiles two at a time (32 tokens per softmax
-// step, P.V on 16x16x32 instructions).
-#ifndef PA_MFMA_PAIRS
-#define PA_MFMA_PAIRS 0
-#endif
-
 // Layout of the scheduling scratch written by the plan kernel:
 //   [0] number of splits of the batch
 //   [1] split_tokens, [2] num_seqs, [3] clamped max length, [4] query tokens
@@ -449,15 +428,12 @@ __device__ __forceinline__ uint32_t u8col_to_bf16(uint32_t w0, uint32_t w1) {
 }
 
 // LDS staging of the MFMA engine (bf16 cache): a 16-token K or V tile is 16
-// rows of 256 bytes, stored PA_STAGE_ROW bytes apart to spread the lanes'
+// rows of 256 bytes, stored kStageRow bytes apart to spread the lanes'
 // 16-byte operand reads over the banks; two tiles (K and V) per buffer, two
 // buffers. Measured on the prefill chunk batch: rows 256 bytes apart spend
 // 50% of the busy cycles in bank conflicts, 272 bytes 22%, 288 bytes 12%
 // (and 288 is the fastest of 272 .. 384).
-#ifndef PA_STAGE_ROW
-#define PA_STAGE_ROW 288
-#endif
-constexpr int kStageRow = PA_STAGE_ROW;
+constexpr int kStageRow = 288;
 constexpr int kStageTile = kBlock * kStageRow;   // one K or V tile
 constexpr int kStageBytes = 4 * kStageTile;      // 2 buffers x (K, V)
 
@@ -663,20 +639,6 @@ struct MfmaWave {
     acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[JJ], 0, 0, 0);
   }
 
-  // O column block JJ += P . V over two tiles (32 tokens, 16x16x32 MFMAs).
-  template <int JJ>
-  __device__ __forceinline__ void pv32(const MfmaTile<CT> &t0, const MfmaTile<CT> &t1,
-                                       const uint32_t (&x01a)[4], const uint32_t (&x23a)[4],
-                                       const uint32_t (&x01b)[4], const uint32_t (&x23b)[4],
-                                       bf16x8 phi, bf16x8 plo) {
-    uint32_t b0, b1, b2, b3;
-    v_cols<JJ>(t0, x01a, x23a, b0, b1);
-    v_cols<JJ>(t1, x01b, x23b, b2, b3);
-    const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{b0, b1, b2, b3});
-    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, acc[JJ], 0, 0, 0);
-    acc[JJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, bv, acc[JJ], 0, 0, 0);
-  }
-
   // Fold one tile (first token tb) into the running state; need_mask: the
   // tile is at an edge of some row's range.
   __device__ __forceinline__ void consume(MfmaTile<CT> &t, bool need_mask, int tb, int lo,
@@ -701,48 +663,14 @@ struct MfmaWave {
     pv16<7>(t, x01, x23, phi, plo);
   }
 
-  // Fold two consecutive tiles (first tokens tb and tb + 16) as one 32-token
-  // step: one max update for both, and P.V on 16x16x32 instructions whose k
-  // index runs over the lane's four tokens of the first tile, then its four of
-  // the second (the B operand takes the V rows in the same order), so P and V
-  // still never move between lanes.
-  __device__ __forceinline__ void consume2(MfmaTile<CT> &t0, MfmaTile<CT> &t1, bool mask0,
-                                           bool mask1, int tb, int lo, int hi, int ulo, int uhi,
-                                           int g, float scale_log2) {
-    float z0[4], z1[4];
-    scores(t0, z0, scale_log2);
-    scores(t1, z1, scale_log2);
-    if (mask0) mask(t0, z0, tb, lo, hi, ulo, uhi, g);  // uniform
-    if (mask1) mask(t1, z1, tb + kBlock, lo, hi, ulo, uhi, g);
-    update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
-                     fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
-               g);
-    uint32_t h0[2], l0[2], h1[2], l1[2];
-    weights(t0, z0, h0, l0);
-    weights(t1, z1, h1, l1);
-    const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
-    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
-    [[maybe_unused]] uint32_t x01a[4], x23a[4], x01b[4], x23b[4];
-    fp8_rows(t0, x01a, x23a);
-    fp8_rows(t1, x01b, x23b);
-    pv32<0>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<1>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<2>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<3>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<4>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<5>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<6>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-    pv32<7>(t0, t1, x01a, x23a, x01b, x23b, phi, plo);
-  }
-
-  // Staged tiles (bf16 K/V rows in LDS, PA_STAGE_ROW bytes apart).
+  // Staged tiles (bf16 K/V rows in LDS, kStageRow bytes apart).
   // Logits of the tile whose K rows start at kb.
   __device__ __forceinline__ void scores_lds(const char *kb, float (&z)[4], float scale_log2,
                                              int c, int g) const {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 k = *reinterpret_cast<const u32x4 *>(kb + c * PA_STAGE_ROW + 64 * i + 16 * g);
+      const u32x4 k = *reinterpret_cast<const u32x4 *>(kb + c * kStageRow + 64 * i + 16 * g);
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
                                                   __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0, 0);
     }
@@ -756,7 +684,7 @@ struct MfmaWave {
   // hands every lane its column.
   template <int JJ>
   __device__ __forceinline__ static s16x4 v_tr(const char *vb, int c, int g) {
-    return lds_read_tr16(vb + (4 * g + (c >> 2)) * PA_STAGE_ROW + (16 * JJ + 4 * (c & 3)) * 2);
+    return lds_read_tr16(vb + (4 * g + (c >> 2)) * kStageRow + (16 * JJ + 4 * (c & 3)) * 2);
   }
 
   template <int JJ>
@@ -863,12 +791,10 @@ struct MfmaWave {
 // its waves' tiles together; each tile is loaded from memory once, by all
 // 256 threads, into LDS (aliasing sm_acc, which is written only after the
 // walk), and every wave reads its K and V operands from there, for the tiles
-// of its own range. With PA_STAGE_PAIRS the tiles go two at a time: V rows of
-// tokens outside the workgroup's [ulo_wg, uhi_wg] are stored as zeros, and
-// P.V runs on 16x16x32 instructions with V read by LDS transpose reads; the
-// next pair's loads fly (in registers) while the current pair is consumed,
-// two barriers per pair. Without it, one tile per step in two LDS buffers,
-// one barrier per tile.
+// of its own range. The tiles go two at a time: V rows of tokens outside the
+// workgroup's [ulo_wg, uhi_wg] are stored as zeros, and P.V runs on 16x16x32
+// instructions with V read by LDS transpose reads; the next pair's loads fly
+// (in registers) while the current pair is consumed, two barriers per pair.
 template <int QT, int CT, int D, int G, int NW, int POL, bool STAGED = false>
 __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int kvh, int R0,
                                                int nrows, const RowRanges &rr, int b0, int wb0,
@@ -877,10 +803,9 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
                                                float (&sm_acc)[NW][G][D], int sb0 = 0,
                                                int sb1 = 0, int ulo_wg = 0, int uhi_wg = -1,
                                                int s_own = -1) {
-  constexpr bool PAIRED = STAGED && PA_STAGE_PAIRS;
   // Group entry (s_own >= 0, uniform): the workgroup stages sequence s's
   // blocks and this wave's rows belong to sequence s_own.
-  const bool grouped = PAIRED && s_own >= 0;
+  const bool grouped = STAGED && s_own >= 0;
   using Wv = MfmaWave<CT, G>;
   Wv st;
   const int c = lane % 16, g = lane / 16;
@@ -923,7 +848,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
   };
-  if constexpr (PAIRED) {
+  if constexpr (STAGED) {
     static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
     char *stage = reinterpret_cast<char *>(&sm_acc[0][0][0]);
     char *const K0 = stage, *const V0 = stage + kStageTile;
@@ -1025,52 +950,6 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         }
       }
     }
-  } else if constexpr (STAGED) {
-    static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
-    char *stage = reinterpret_cast<char *>(&sm_acc[0][0][0]);
-    const int tid = threadIdx.x;  // NW * 64 = 256 threads, 16 bytes of a tile each
-    const int srow = tid / 16, scol = (tid % 16) * 16;
-    constexpr int TB = kBlock * 256;  // bytes of a bf16 K or V tile in memory
-    for (int c0 = sb0; c0 < sb1; c0 += kWave) {
-      const int c1 = min(sb1, c0 + kWave);
-      int my_id = 0;
-      if (lane < c1 - c0)
-        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
-      auto block_of = [&](int n) {
-        return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0),
-                   last_block);
-      };
-      u32x4 kr, vr;
-      auto fetch = [&](int n) {
-        const int64_t tile = (int64_t)block_of(n) * p.num_kv_heads + kvh;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char *)p.k_cache + tile * TB, TB);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char *)p.v_cache + tile * TB, TB);
-        kr = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, 0, 0);
-        vr = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, 0, 0);
-      };
-      fetch(c0);
-      for (int n = c0; n < c1; ++n) {
-        char *buf = stage + (n & 1) * 2 * kStageTile;
-        *reinterpret_cast<u32x4 *>(buf + srow * kStageRow + scol) = kr;
-        *reinterpret_cast<u32x4 *>(buf + kStageTile + srow * kStageRow + scol) = vr;
-        // The buffer is complete, and every wave has finished with the other
-        // one (read two tiles ago).
-        __syncthreads();
-        if (n + 1 < c1) fetch(n + 1);
-        if (n >= wb0 && n < wb1) {
-          MfmaTile<CT> t;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            t.k[i] = *reinterpret_cast<const u32x4 *>(buf + c * kStageRow + 64 * i + 16 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            t.v[i] = *reinterpret_cast<const u32x4 *>(buf + kStageTile +
-                                                      (4 * g + i) * kStageRow + 16 * c);
-          eat(t, n);
-        }
-      }
-    }
-    __syncthreads();  // the staging space is sm_acc: every wave is done with it
   } else
   // Tiles in chunks of 64: the chunk's physical block ids sit one per lane.
   for (int c0 = wb0; c0 < wb1; c0 += kWave) {
@@ -1082,29 +961,11 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     auto block_of = [&](int n) {
       return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0), last_block);
     };
-#if PA_MFMA_PAIRS
-    // Two tiles per step (32 tokens), a trailing odd tile on its own.
-    int n = c0;
-    for (; n + 1 < c1; n += 2) {
-      MfmaTile<CT> ta, tb;
-      st.template load_tile<POL>(ta, p, block_of(n), kvh, koff, voff, soff);
-      st.template load_tile<POL>(tb, p, block_of(n + 1), kvh, koff, voff, soff);
-      const int tk = (b0 + n) * kBlock;
-      st.consume2(ta, tb, rr.needs_mask(tk), rr.needs_mask(tk + kBlock), tk, lo, hi, rr.ulo,
-                  rr.uhi, g, p.scale_log2);
-    }
-    if (n < c1) {
-      MfmaTile<CT> t;
-      st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
-      eat(t, n);
-    }
-#else
     MfmaTile<CT> t;
     for (int n = c0; n < c1; ++n) {
       st.template load_tile<POL>(t, p, block_of(n), kvh, koff, voff, soff);
       eat(t, n);
     }
-#endif
   }
   // Renormalise to the true max (every lane takes part: rescale reads other
   // lanes' factors), then sum l over the four lane groups.
@@ -1132,7 +993,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     if (h < G) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        sm_acc[wave][h][PAIRED && !grouped ? 16 * jj + c : 8 * c + jj] = st.acc[jj][r];
+        sm_acc[wave][h][STAGED && !grouped ? 16 * jj + c : 8 * c + jj] = st.acc[jj][r];
     }
   }
 }
@@ -1292,10 +1153,10 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   // Tiles that several row groups read stay cached; a lone row group streams.
   // Four row groups of one sequence (bf16, 16 rows each: prefill chunks)
   // share each tile through LDS.
-  constexpr bool kStageable = PA_MFMA_STAGE && QT == PA_BF16 && CT == PA_BF16 && D == 128 &&
+  constexpr bool kStageable = QT == PA_BF16 && CT == PA_BF16 && D == 128 &&
                               G == 16 && NW == 4;
   if constexpr (QT == PA_BF16 && MfmaEligible<CT, D>::value) {
-    if (kStageable && rw == NW && (group == 0 || PA_STAGE_GROUPS)) {
+    if (kStageable && rw == NW) {
       // The workgroup's tiles: those any of its rows reach; for a group
       // entry, the blocks of the split the group's first sequence holds (each
       // member takes those it shares).
@@ -1397,27 +1258,15 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 // workgroups past the end of the list, all at the end of the grid, exit at
 // once. A plan made for another split size, batch, length bound, query count,
 // window or query layout counts as an empty list.
-// Minimum waves per SIMD the compiler must fit the split kernel's registers
-// to (0: its own choice).
-#ifndef PA_WAVES_PER_EU
-#define PA_WAVES_PER_EU 0
-#endif
-#if PA_WAVES_PER_EU > 0
-#define PA_OCCUPANCY_ATTR __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
-#else
-#define PA_OCCUPANCY_ATTR
-#endif
 // The MFMA engine on 16-bit and FP8 caches fits 128 VGPRs, i.e. four waves per
 // SIMD (16 per CU) for latency hiding; the INT8 one needs more and runs three.
-#ifndef PA_MFMA_WAVES_PER_EU
-#define PA_MFMA_WAVES_PER_EU 4
-#endif
+constexpr int kMfmaWavesPerEu = 4;
 
 template <int QT, int CT, int D, int G, int NW>
 __device__ __forceinline__ void decode_split_body(const DecodeParams &p);
 
 template <int QT, int CT, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_kernel(
+__global__ __launch_bounds__(NW * kWave) void decode_split_kernel(
     const DecodeParams p) {
   decode_split_body<QT, CT, D, G, NW>(p);
 }
@@ -1426,7 +1275,7 @@ __global__ __launch_bounds__(NW * kWave) PA_OCCUPANCY_ATTR void decode_split_ker
 // cache, head_dim 128).
 template <int QT, int CT, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
-    PA_MFMA_WAVES_PER_EU))) void decode_split_kernel_mfma(const DecodeParams p) {
+    kMfmaWavesPerEu))) void decode_split_kernel_mfma(const DecodeParams p) {
   decode_split_body<QT, CT, D, G, NW>(p);
 }
 
@@ -1491,13 +1340,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
 
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
 // Waves per workgroup (they share one split).
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
+constexpr int kDecodeWaves = 4;
 
 template <int QT, int CT, int D, int G>
 hipError_t launch_decode(const DecodeParams &p, int64_t max_items, hipStream_t stream) {
-  constexpr int NW = PA_DECODE_WAVES;
+  constexpr int NW = kDecodeWaves;
   // One workgroup per possible item; those past the planned list exit at once.
   if constexpr (QT == PA_BF16 && (CT == PA_BF16 || CT == PA_FP8) && D == 128)
     hipLaunchKernelGGL((decode_split_kernel_mfma<QT, CT, D, G, NW>), dim3((unsigned)max_items),

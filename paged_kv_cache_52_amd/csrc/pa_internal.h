@@ -17,6 +17,7 @@ struct ReduceParams {
   int32_t num_seqs, num_q_heads, head_dim, split_tokens, max_splits, out_dtype;
   int32_t num_query_tokens, window;  // per sequence, or the packed total with query_start
   const int32_t *query_start;        // [num_seqs + 1] packed query offsets, or nullptr
+  int32_t len_bound;  // context lengths are clamped to [0, len_bound], as in the split kernel
 };
 
 struct WriteParams {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_rows_kernel(const 
   for (int r = 0; r < R; ++r) {
     const int Q = p.query_start ? query_span(p.query_start, seq[r], 0, p.num_query_tokens).count
                                 : p.num_query_tokens;
-    const int L = max(0, p.context_lens[seq[r]]);
+    const int L = min(max(0, p.context_lens[seq[r]]), p.len_bound);
     const int ns = Q > 0 ? min(splits_of(L, Q, p.window, p.split_tokens), S) : 0;
     const bool live = lane < ns && l0[r] > 0.f;
     const float M = group_max<kWave>(live ? m0[r] : -INFINITY);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
     s = seq_of_token_wave(p.query_start, p.num_seqs, hq / p.num_q_heads);
     Q = query_span(p.query_start, s, 0, p.num_query_tokens).count;
   }
-  const int L = max(0, p.context_lens[s]);
+  const int L = min(max(0, p.context_lens[s]), p.len_bound);
   const int ns = Q > 0 ? min(splits_of(L, Q, p.window, p.split_tokens), p.max_splits) : 0;
 
   float M = -INFINITY;

@@ -291,12 +291,12 @@ def test_decode_partial_validation(lib):
 
 def test_reduce_validation(lib):
     def red(**kw):
-        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, qs=None, B=4, Q=1, Hq=32, D=128, W=0, T=512,
-                 S=2, out=FAKE, odt=BF16)
+        a = dict(m=FAKE, l=FAKE, acc=FAKE, cl=FAKE, qs=None, B=4, Q=1, Hq=32, D=128, mb=64,
+                 mcl=1000, W=0, T=512, S=2, out=FAKE, odt=BF16)
         a.update(kw)
         return lib.paged_attn_reduce(a["m"], a["l"], a["acc"], a["cl"], a["qs"], a["B"], a["Q"],
-                                     a["Hq"], a["D"], a["W"], a["T"], a["S"], a["out"], a["odt"],
-                                     None)
+                                     a["Hq"], a["D"], a["mb"], a["mcl"], a["W"], a["T"], a["S"],
+                                     a["out"], a["odt"], None)
     assert red(D=32) == ERR_SHAPE
     assert red(odt=I8) == ERR_DTYPE
     assert red(T=0) == ERR_SPLIT
@@ -304,6 +304,8 @@ def test_reduce_validation(lib):
     assert red(out=None) == ERR_NULL
     assert red(Q=0) == ERR_SHAPE
     assert red(W=-1) == ERR_SHAPE
+    assert red(mb=0) == ERR_SHAPE
+    assert red(mcl=-1) == ERR_SHAPE
     assert red(B=0, out=None) == OK
     assert red(qs=FAKE, Q=0, out=None) == OK
     assert red(qs=FAKE, Q=5000, out=None) == ERR_NULL

@@ -323,6 +323,34 @@ def test_poisoned_slots_do_not_leak(name):
         _check_out(out32, ref, _tol(b), f"poison/{T}")
 
 
+def test_reduce_clamps_lengths_like_the_split_kernel():
+    """Lengths past 16 * max_blocks_per_seq are clamped by the split kernel;
+    the reduce clamps them the same way, so it merges exactly the splits the
+    kernel wrote even when the partials have room for more (here filled with
+    stale values that would spoil the result if merged)."""
+    print("[case] reduce length clamp", flush=True)
+    b = workloads.make_batch("llama8b_bf16", 291, "cpu", lengths=[128, 128, 64])
+    assert b.block_tables.shape[1] == 8
+    g = _to(b, "cuda")
+    g.context_lens = torch.tensor([300, 129, 64], dtype=torch.int32, device="cuda")
+    ref = _oracle_decode(b)  # the lengths the clamp leaves: 128, 128, 64
+    B, Hq, D = g.q.shape
+    S = 40  # 16-token splits: the clamped bound needs 8, the raw lengths up to 19
+    parts = pa().Partials(
+        m=torch.full((B, 1, Hq, S), 50.0, device="cuda"),
+        l=torch.ones((B, 1, Hq, S), device="cuda"),
+        acc=torch.full((B, 1, Hq, S, D), 1e3, device="cuda"),
+        context_lens=g.context_lens, split_tokens=16)
+    pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
+                                   g.scale, max_context_len=300, split_tokens=16,
+                                   partials=parts)
+    out = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+    pa().paged_attn_reduce(parts, out)
+    torch.cuda.synchronize()
+    assert parts.max_context_len == 300 and parts.max_blocks_per_seq == 8
+    _check_out(out.cpu().double().numpy(), ref, TOL_BF16, "clamped lengths")
+
+
 def test_edge_lengths():
     """L = 0, 1, block and split boundaries in one ragged batch."""
     print("[case] edge lengths", flush=True)
@@ -690,51 +718,109 @@ def _sample_rows(B, Q, Hq, n, seed):
     return seqs, toks, heads
 
 
-@pytest.mark.parametrize("name", ["llama8b_bf16", "long_bf16", "int8_kv", "fp8_kv",
-                                  "shared_prefix_bf16", "mtp4_llama8b_bf16", "swa4k_bf16",
-                                  "prefill512_bf16", "mixed_llama8b_bf16"])
-def test_full_size_sampled_rows(name):
-    """Full workload sizes, the launch the benchmark times (default split),
-    checked on sampled (sequence, query token, head) rows; every output must
-    be finite. The oracle reads only its own copy of the inputs and its own
-    writes."""
-    print(f"[case] full-size {name}", flush=True)
-    g = workloads.make_batch(name, 1, "cuda")
+def _cpu_copy(g):
     b = workloads.Batch(**{f: getattr(g, f) for f in g.__dataclass_fields__})
     for f in g.__dataclass_fields__:
         v = getattr(g, f)
         if isinstance(v, torch.Tensor):
             setattr(b, f, v.cpu())
-    if g.fill_k is not None:
-        _fill_quantised(b, g)
-    _write_new_tokens(b, g)
-    out = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
-                                 g.scale, k_scale=g.k_scale, v_scale=g.v_scale,
-                                 max_context_len=g.max_context_len, sliding_window=g.window,
-                                 query_start=g.query_start)
-    out32, _ = _gpu_fp32_out(g)
-    assert torch.isfinite(out).all()
+    return b
+
+
+# Full sizes, every row compared with the oracle; the two batches with
+# 512-token prefill chunks (whose rows cost the oracle minutes) compare whole
+# sequences plus 256 sampled rows.
+FULL_ALL_ROWS = ["llama8b_bf16", "long_bf16", "int8_kv", "fp8_kv", "shared_prefix_bf16",
+                 "mtp4_llama8b_bf16", "swa4k_bf16"]
+FULL_SAMPLED = ["prefill512_bf16", "mixed_llama8b_bf16"]
+
+
+def _full_rows(g, whole_seqs, n_sampled, seed):
+    """(sequence, query token, head) rows: every row of the given sequences,
+    plus n_sampled random rows; and their flat indices into out."""
     Hq = g.q.shape[-2]
     if g.query_start is None:
         B, Q = g.q.shape[0], g.query_tokens
-        seqs, toks, heads = _sample_rows(B, Q, Hq, 24, 7)
-        flat = (seqs.astype(np.int64) * Q + toks) * Hq + heads
+        first = np.arange(B + 1, dtype=np.int64) * Q
     else:
-        # Packed rows: sample tokens (with the first and the last), map to (s, i).
-        qs = _np(g.query_start)
-        N = int(qs[-1])
-        rng = np.random.default_rng(7)
-        tok = rng.integers(0, N, size=24)
-        tok[0], tok[1] = 0, N - 1
-        seqs = (np.searchsorted(qs, tok, side="right") - 1).astype(np.int32)
-        toks = (tok - qs[seqs]).astype(np.int32)
-        heads = rng.integers(0, Hq, size=24).astype(np.int32)
-        flat = tok * Hq + heads
-    ref = _oracle_decode(b, rows=(seqs, toks, heads))
+        first = _np(g.query_start).astype(np.int64)
+        B = len(first) - 1
+    N = int(first[-1])
+    rng = np.random.default_rng(seed)
+    tok = [np.arange(first[s], first[s + 1]) for s in whole_seqs]
+    tok = np.concatenate(tok + [rng.integers(0, N, size=n_sampled)])
+    tok = np.repeat(tok, Hq)
+    heads = np.tile(np.arange(Hq), len(tok) // Hq)
+    heads[len(heads) - n_sampled * Hq:] = rng.integers(0, Hq, size=n_sampled * Hq)
+    seqs = np.searchsorted(first, tok, side="right") - 1
+    return ((seqs.astype(np.int32), (tok - first[seqs]).astype(np.int32),
+             heads.astype(np.int32)), tok * Hq + heads)
+
+
+@pytest.mark.parametrize("name", FULL_ALL_ROWS + FULL_SAMPLED)
+def test_full_size_as_benchmarked(name):
+    """Each workload at its full size and seed, run by bench.py's own Step
+    object (the launches the benchmark times: fused write + plan with its
+    default split and grouping, the split kernel, the reduce into q's dtype).
+    The fused write is compared byte for byte with the oracle's, then the
+    output row by row: bf16 (as benchmarked) and fp32 (the same partials
+    reduced again). The one-call paged_attn_decode is checked on the same rows.
+    The oracle reads only its own copy of the inputs and its own writes."""
+    import bench
+    print(f"[case] full-size {name} as benchmarked", flush=True)
+    g = workloads.make_batch(name, 1, "cuda")
+    b = _cpu_copy(g)
+    if g.fill_k is not None:
+        _fill_quantised(b, g)
+    kc, vc = _np(b.k_cache).copy(), _np(b.v_cache).copy()
+    ks = vs = None
+    if b.k_scale is not None:
+        ks, vs = _np(b.k_scale).copy(), _np(b.v_scale).copy()
+    oracle.kv_write(_np(b.new_k), _np(b.new_v), _np(b.slot_mapping), kc, vc, ks, vs)
+    b.k_cache, b.v_cache = _from_np(kc, b.k_cache.dtype), _from_np(vc, b.v_cache.dtype)
+    if ks is not None:
+        b.k_scale, b.v_scale = torch.from_numpy(ks), torch.from_numpy(vs)
+    step = bench.Step(pa(), g)
+    step()
+    out32 = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+    step.reduce(out32)
+    torch.cuda.synchronize()
+    if name == "shared_prefix_bf16":
+        assert step.M == 4 and (step.plan.sched[9:9 + 2 * int(step.plan.sched[0]):2] < 0).any()
+    assert np.array_equal(_np(g.k_cache).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(_np(g.v_cache).view(np.uint8), vc.view(np.uint8))
+    if ks is not None:
+        assert np.array_equal(_np(g.k_scale).view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(_np(g.v_scale).view(np.uint32), vs.view(np.uint32))
+    one_call = pa().paged_attn_decode(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                      g.context_lens, g.scale, k_scale=g.k_scale,
+                                      v_scale=g.v_scale, max_context_len=g.max_context_len,
+                                      sliding_window=g.window, query_start=g.query_start)
+    torch.cuda.synchronize()
     D = g.q.shape[-1]
-    _check_out(out32.reshape(-1, D)[flat], ref, TOL_BF16, f"{name}/fp32-out")
-    _check_bf16_out(out.reshape(-1, D)[torch.from_numpy(flat).long()].cpu(), ref,
-                    f"{name}/bf16-out")
+    out32 = out32.cpu().double().numpy().reshape(-1, D)
+    out_bf = step.out.cpu().reshape(-1, D)
+    one_call = one_call.cpu().reshape(-1, D)
+    assert np.isfinite(out32).all() and torch.isfinite(out_bf).all()
+    if name in FULL_ALL_ROWS:
+        ref = _oracle_decode(b).reshape(-1, D)
+        sel = slice(None)
+    else:
+        # The shortest prefill chunk's sequence (and, mixed, the first decode).
+        lens = _np(g.context_lens).astype(np.int64)
+        if g.query_start is None:
+            whole = [int(np.argmin(lens))]
+        else:
+            counts = np.diff(_np(g.query_start).astype(np.int64))
+            chunk = np.flatnonzero(counts > 1)
+            whole = [int(chunk[np.argmin(lens[chunk])]), 0]
+        rows, flat = _full_rows(g, whole, 256, 7)
+        ref = _oracle_decode(b, rows=rows)
+        sel = torch.from_numpy(flat).long()
+        out32 = out32[flat]
+    _check_out(out32, ref, TOL_BF16, f"{name}/fp32-out")
+    _check_bf16_out(out_bf[sel], ref, f"{name}/bf16-out as benchmarked")
+    _check_bf16_out(one_call[sel], ref, f"{name}/bf16-out one call")
 
 
 def test_long_contexts_with_thousands_of_splits():
@@ -925,7 +1011,7 @@ def test_hbm_read_probe_reads_every_word_once(nbytes, blocks):
 # Plans with group entries: full splits j of consecutive sequences that start
 # on the same physical block (shared prefix blocks) become one work item.
 
-@pytest.mark.parametrize("T,M", [(64, 4), (512, 3)])
+@pytest.mark.parametrize("T,M", [(64, 4), (512, 3), (1024, 4), (2048, 4)])
 def test_grouped_shared_prefix_with_poison(T, M):
     """Group entries of 16-row members (their shared tiles staged once per
     workgroup) with NaN in every slot no query token attends."""
@@ -1030,6 +1116,8 @@ GROUPED_CASES = [
     ("shared_prefix_bf16", 64, 2),
     ("shared_prefix_bf16", 64, 4),
     ("shared_prefix_bf16", 512, 4),
+    ("shared_prefix_bf16", 1024, 4),  # the benchmark's split and grouping
+    ("shared_prefix_bf16", 2048, 4),  # 128 tiles: the staged walk takes two chunks of 64
     ("llama8b_bf16", 64, 4),          # shared blocks built by the test
     ("mtp4_llama8b_bf16", 64, 4),     # Q = 4: 16 rows per KV head
     ("int8_kv", 64, 4),

@@ -181,7 +181,7 @@ def reach_start(L, query_tokens: int = 1, window: int = 0):
     return np.maximum(L - query_tokens - window + 1, 0)
 
 
-def _attended_slots(tables: np.ndarray, L: np.ndarray, lo: Optional[np.ndarray] = None):
+def attended_slots(tables: np.ndarray, L: np.ndarray, lo: Optional[np.ndarray] = None):
     """Physical slot of every (sequence, lo <= position < L) pair, sequence-major."""
     if len(L) == 0:
         return np.zeros(0, np.int64)
@@ -314,7 +314,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         k_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         v_scale = torch.full(cache_shape[:3], fill, dtype=torch.float32, device=device)
         # Every attended token's K/V, to be written through the KV write.
-        fill_slots_np = np.unique(_attended_slots(tables, L, reach_start(L, Qs, W)))
+        fill_slots_np = np.unique(attended_slots(tables, L, reach_start(L, Qs, W)))
         fill_slots = torch.from_numpy(fill_slots_np).to(device)
         fill_k = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
         fill_v = _randn((len(fill_slots_np), Hkv, D), gen, device, in_dt)
@@ -324,7 +324,7 @@ def make_batch(name, seed: int, device="cpu", *, num_seqs: Optional[int] = None,
         v_cache = _randn(cache_shape, gen, device, cdt)
         if poison:
             live = torch.zeros(num_blocks * BLOCK_SIZE, dtype=torch.bool)
-            live[torch.from_numpy(_attended_slots(tables, L, reach_start(L, Qs, W)))] = True
+            live[torch.from_numpy(attended_slots(tables, L, reach_start(L, Qs, W)))] = True
             dead = (~live).view(num_blocks, 1, BLOCK_SIZE, 1).expand(cache_shape).to(device)
             k_cache.masked_fill_(dead, float("nan"))
             v_cache.masked_fill_(dead, float("nan"))
