@@ -28,14 +28,11 @@ import hashlib
 import json
 import math
 import os
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
-
-# The CPU baseline's OpenMP threads are bound close together, one per core.
-# OpenMP reads this when its runtime starts, which torch's import does, so it
-# is set before anything is imported.
-os.environ.setdefault("OMP_PROC_BIND", "close")
-os.environ.setdefault("OMP_PLACES", "cores")
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -70,6 +67,7 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -169,14 +167,18 @@ def host_description():
     return {"cpu_model": model, "numa_nodes": nodes, "usable_cpus": len(os.sched_getaffinity(0))}
 
 
+# Binding of the CPU baseline's OpenMP threads: one per core, close together.
+CPU_BASELINE_ENV = {"OMP_PROC_BIND": "close", "OMP_PLACES": "cores"}
+
+
 def cpu_baseline(b, seconds):
     """Time the oracle on a bounded sample of the same batch: whole sequences
-    (all heads) in order until about `seconds` of CPU time have passed. Its
-    OpenMP threads are bound close, one per core; on a machine with several
-    NUMA nodes a pool over 1 GiB is spread over all of them first."""
+    (all heads) in order until about `seconds` of CPU time have passed. It
+    runs in a child process started with CPU_BASELINE_ENV (OpenMP binds the
+    thread that starts its runtime, so the binding stays out of this GPU
+    process), on the batch's host copies handed over as .npy files."""
     import numpy as np
     import torch
-    import oracle
 
     def host(t):
         t = t.detach().cpu().contiguous()
@@ -186,37 +188,70 @@ def cpu_baseline(b, seconds):
             return t.view(torch.uint8).numpy()
         return t.numpy()
 
-    q, kc, vc = host(b.q), host(b.k_cache), host(b.v_cache)
-    ks = None if b.k_scale is None else host(b.k_scale)
-    vs = None if b.v_scale is None else host(b.v_scale)
-    hw = host_description()
+    arrays = {"q": b.q, "k_cache": b.k_cache, "v_cache": b.v_cache, "k_scale": b.k_scale,
+              "v_scale": b.v_scale, "block_tables": b.block_tables,
+              "context_lens": b.context_lens, "query_start": b.query_start}
+    arrays = {k: host(v) for k, v in arrays.items() if v is not None}
+    need = sum(a.nbytes for a in arrays.values())
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") and \
+        shutil.disk_usage("/dev/shm").free > 2 * need else None
+    d = tempfile.mkdtemp(prefix="pa_cpu_baseline_", dir=shm)
+    try:
+        for k, a in arrays.items():
+            np.save(os.path.join(d, k + ".npy"), a)
+        del arrays
+        with open(os.path.join(d, "meta.json"), "w") as f:
+            json.dump({"scale": b.scale, "window": b.window, "query_tokens": b.query_tokens,
+                       "seconds": seconds}, f)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", d],
+                           env=dict(os.environ, **CPU_BASELINE_ENV), capture_output=True,
+                           text=True, timeout=600 + 2 * seconds)
+        if r.returncode != 0:
+            raise RuntimeError(f"CPU baseline failed ({r.returncode}): {r.stderr[-2000:]}")
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def cpu_baseline_child(d):
+    """The CPU baseline's own process: the oracle over whole sequences of the
+    batch in `d`. On a machine with several NUMA nodes a pool over 1 GiB is
+    first spread over all of them."""
+    import numpy as np
+    hw = host_description()  # before OpenMP starts and binds this thread
+    import oracle
+    with open(os.path.join(d, "meta.json")) as f:
+        meta = json.load(f)
+    arr = {os.path.basename(p)[:-4]: np.load(p) for p in glob.glob(os.path.join(d, "*.npy"))}
+    q, kc, vc = arr["q"], arr["k_cache"], arr["v_cache"]
+    ks, vs, qs = arr.get("k_scale"), arr.get("v_scale"), arr.get("query_start")
+    bt, cl = arr["block_tables"], arr["context_lens"]
     pool = kc.nbytes + vc.nbytes
     policy = "first touch (one NUMA node)" if hw["numa_nodes"] == 1 else \
         f"first touch (pool {pool / 2**30:.2f} GiB, not over 1 GiB)"
     if hw["numa_nodes"] > 1 and pool > 2**30:
-        errs = [oracle.interleave(a, hw["numa_nodes"]) for a in (kc, vc) if a is not None]
+        errs = [oracle.interleave(a, hw["numa_nodes"]) for a in (kc, vc)]
         policy = (f"interleaved over {hw['numa_nodes']} nodes" if not any(errs) else
                   f"interleave failed (errno {max(errs)}), first touch")
-    bt, cl = host(b.block_tables), host(b.context_lens)
-    qs = None if b.query_start is None else host(b.query_start)
-    B, Hq = b.num_seqs, q.shape[-2]
-    Qs = query_counts(b)
+    B, Hq = len(cl), q.shape[-2]
+    Qs = np.diff(qs.astype(np.int64)) if qs is not None else \
+        np.full(B, meta["query_tokens"], dtype=np.int64)
     done, tokens, queries, t0 = 0, 0, 0, time.perf_counter()
     elapsed = 0.0
     # Whole sequences in batch order, wrapping around, until the time budget.
-    while elapsed < seconds:
+    while elapsed < meta["seconds"]:
         s = done % B
         Q = int(Qs[s])
         tok = np.repeat(np.arange(Q, dtype=np.int32), Hq)
         h = np.tile(np.arange(Hq, dtype=np.int32), Q)
-        oracle.decode(q, kc, vc, bt, cl, b.scale, ks, vs,
-                      rows=(np.full(Q * Hq, s, np.int32), tok, h), window=b.window,
+        oracle.decode(q, kc, vc, bt, cl, meta["scale"], ks, vs,
+                      rows=(np.full(Q * Hq, s, np.int32), tok, h), window=meta["window"],
                       query_start=qs)
         tokens += int(cl[s])
         queries += Q
         done += 1
         elapsed = time.perf_counter() - t0
-    return {
+    print(json.dumps({
         "value": queries / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{done} sequences ({done / B:.2f} passes over the {B}-sequence batch, "
@@ -224,7 +259,7 @@ def cpu_baseline(b, seconds):
                   f"block-table walk, {elapsed:.1f} s",
         "host": dict(hw, omp_threads=oracle.num_threads(), omp_proc_bind=oracle.proc_bind(),
                      omp_places=os.environ.get("OMP_PLACES", ""), numa_policy=policy),
-    }
+    }), flush=True)
 
 
 def load_counters(workload):
@@ -333,6 +368,9 @@ class Step:
 
 def main():
     args = parse()
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_baseline_child)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path runs on a single MI355X and "
               "this build has no multi-GPU leg (run with --gpus 1).", file=sys.stderr)

@@ -116,7 +116,9 @@ enum {
   PA_ERR_LAUNCH = -7     /* the kernel launch failed */
 };
 
-/* Human-readable text for a status code (static storage). */
+/* Human-readable text for a status code (static storage). An auxiliary call
+ * of this library's error convention; the pages define no interface, so it
+ * follows no passage of theirs. */
 const char *pa_strerror(int status);
 
 /* Number of splits for a context of length context_len:
@@ -126,7 +128,8 @@ int32_t pa_num_splits(int32_t context_len, int32_t split_tokens);
 
 /* Splits of the longest split range a sequence of length <= max_context_len
  * can have with num_query_tokens query tokens and the given window: the
- * max_splits the partials need. Without a window this is
+ * max_splits the partials need [EchoLLMServing notes, section 2, FlashDecoding
+ * split heuristic; section 4 for the window]. Without a window this is
  * pa_num_splits(max_context_len, split_tokens); with one the range is at
  * most min(max_context_len, Q + W + 14) tokens. 0 for bad arguments. */
 int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t sliding_window,
@@ -154,7 +157,8 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
                                 int32_t num_query_tokens, int32_t sliding_window);
 
 /* Bytes of the plan paged_attn_plan writes (an int32 list of every split plus
- * a small header). */
+ * a small header) [EchoLLMServing notes, section 2: one program per split of
+ * every sequence, the split count following the context length]. */
 size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits);
 
 /* The same for packed queries (query_start given): the list then holds one
@@ -163,8 +167,12 @@ size_t pa_sched_bytes(int32_t num_seqs, int32_t max_splits);
 size_t pa_sched_bytes_packed(int32_t num_seqs, int32_t max_splits, int32_t total_query_tokens,
                              int32_t q_heads_per_kv);
 
-/* Bytes of workspace paged_attn_decode needs: scheduling scratch plus the
- * partials (m, l, acc) of num_seqs * num_query_tokens * num_q_heads rows. */
+/* Bytes of workspace paged_attn_decode needs [EchoLLMServing notes, section 2,
+ * FlashDecoding: every split leaves temporaries (m, l, acc) for the reduce
+ * kernel, and their size grows with the split count, which is why the split
+ * count follows the context length]: scheduling scratch plus the partials
+ * (m, l, acc) of num_seqs * num_query_tokens * num_q_heads rows of max_splits
+ * splits each (fp32; acc has head_dim values per split). */
 size_t pa_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
                           int32_t head_dim, int32_t max_splits);
 
@@ -351,9 +359,14 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
                       void *out, int32_t out_dtype, hipStream_t stream);
 
 /*
- * Whole decode step of one attention layer: paged_attn_plan (no grouping) and
+ * Whole decode step of one attention layer [EchoLLMServing notes, section 2,
+ * FlashDecoding: the context is cut into splits whose count follows its
+ * length, one program per split leaves (m, l, acc), a second reduce kernel
+ * merges them; LLM Primer ch. 8, section 8.1: K and V are gathered through
+ * the block table]: paged_attn_plan (no grouping) and
  * paged_attn_decode_partial into the caller's workspace, then
- * paged_attn_reduce into out (dtype = q_dtype).
+ * paged_attn_reduce into out (dtype = q_dtype). The partials live in the
+ * workspace only for the length of the call.
  * The split count is pa_max_splits(max_context_len', Q, W, T) with
  * max_context_len' = min(max_context_len, 16 * max_blocks_per_seq) and
  * T = split_tokens (0: pa_default_split_tokens()). workspace must hold

@@ -30,7 +30,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIB names another build of oracle.c (the sanitizer build of
+# tests/sanitize_host.py); by default the in-tree build.
+_LIB_PATH = os.environ.get("PA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 BLOCK_SIZE = 16

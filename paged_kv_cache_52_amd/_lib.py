@@ -8,7 +8,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpagedattn.so")
+# PAGEDATTN_LIB names another build of the same library (the sanitizer build
+# of tests/sanitize_host.py); by default the in-tree build.
+LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(PKG, "libpagedattn.so")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
