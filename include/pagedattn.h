@@ -77,7 +77,9 @@
  *     clamped to [0, min(max_context_len, 16 * max_blocks_per_seq)], block ids
  *     to [0, num_blocks), and slots outside the pool are skipped, so bad data
  *     gives unspecified results, not memory faults.
- *   - Thread safety: the library keeps no mutable global state.
+ *   - Thread safety: the library keeps no mutable global state, except the
+ *     per-device address table of paged_attn_decode_noalloc's fixed scratch
+ *     (guarded by a mutex; see that call).
  */
 #ifndef PAGEDATTN_H_
 #define PAGEDATTN_H_
@@ -98,6 +100,8 @@ extern "C" {
 #define PA_MAX_PACKED_QUERY_TOKENS (1 << 20)
 #define PA_MAX_GROUP_MEMBERS 4
 #define PA_MAX_SPLITS 65536  /* splits per sequence: the plan stores the split index in 16 bits */
+/* Fixed device scratch of paged_attn_decode_noalloc, per GPU. */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Element types. PA_FP8 is OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF
  * NaN, largest finite 448). */
@@ -113,7 +117,10 @@ enum {
                             PA_MAX_SPLITS splits for the longest possible sequence */
   PA_ERR_WORKSPACE = -5, /* workspace smaller than pa_workspace_bytes() */
   PA_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned */
-  PA_ERR_LAUNCH = -7     /* the kernel launch failed */
+  PA_ERR_LAUNCH = -7,    /* the kernel launch failed (paged_attn_decode_noalloc: or its
+                            device's fixed scratch could not be set up) */
+  PA_ERR_SCRATCH = -8    /* paged_attn_decode_noalloc: the call needs more than
+                            PA_NOALLOC_SCRATCH_BYTES of workspace */
 };
 
 /* Human-readable text for a status code (static storage). An auxiliary call
@@ -384,6 +391,38 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       int32_t max_context_len, int32_t sliding_window, float scale,
                       int32_t split_tokens, void *out, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, and harnesses that forbid hipMalloc. Same arguments (minus workspace
+ * and workspace_bytes), results and errors as paged_attn_decode, the same
+ * kernels; the plan and the partials go to a fixed scratch array of
+ * PA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it is
+ * called for, from that GPU's first call until the process ends.
+ *   - The call allocates nothing: no hipMalloc, hipFree or allocating library
+ *     routine. Its first call for a GPU looks up that GPU's copy of the array
+ *     (hipGetSymbolAddress, with that GPU current), which loads it; make that
+ *     first call outside a graph capture.
+ *   - A call whose plan and partials need more than PA_NOALLOC_SCRATCH_BYTES
+ *     (pa_workspace_bytes for its sizes) returns PA_ERR_SCRATCH before anything
+ *     is enqueued; a GPU whose scratch cannot be set up gives PA_ERR_LAUNCH.
+ *   - The GPU is the one `stream` belongs to. Every call on a GPU shares its
+ *     array, and the array keeps the last call's contents: nothing in it has
+ *     to start cleared (the plan kernel writes every word the split kernel
+ *     reads, the split kernel every partial the reduce reads). Calls that
+ *     overlap on one GPU (different streams, or host threads without an
+ *     order between their streams) race on the array: order them.
+ */
+int paged_attn_decode_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs,
+                              int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                              const void *k_cache, const void *v_cache, const float *k_scale,
+                              const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
+                              int32_t num_kv_heads, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              const int32_t *query_start, int32_t max_context_len,
+                              int32_t sliding_window, float scale, int32_t split_tokens,
+                              void *out, hipStream_t stream);
 
 /*
  * Measurement aid (not part of the attention path): read `bytes` (a multiple

@@ -445,6 +445,30 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                              k_scale=None, v_scale=None, *, max_context_len=None,
+                              split_tokens=None, sliding_window: int = 0,
+                              query_start=None) -> torch.Tensor:
+    """paged_attn_decode with no workspace: the library's fixed per-GPU
+    scratch holds the plan and partials (calls on one GPU must not overlap).
+    out (q's shape and dtype) is required; nothing is allocated. A call that
+    needs more than NOALLOC_SCRATCH_BYTES raises."""
+    lib = _lib.load()
+    B, Q, Hq, D = _q_shape(q, query_start, context_lens)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedAttnError("out must match q's shape and dtype")
+    args = _decode_args(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                        query_start)
+    _check(lib.paged_attn_decode_noalloc(*args, _max_len(context_lens, max_context_len),
+                                         int(sliding_window), float(scale),
+                                         int(split_tokens or 0), _dev(out, "out"),
+                                         _stream(q.device)))
+    return out
+
+
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
     """Read all of `buf` once (measurement aid: practical HBM read bandwidth)."""
     if buf.numel() * buf.element_size() % 16:
@@ -458,5 +482,5 @@ __all__ = [
     "BLOCK_SIZE", "MAX_QUERY_TOKENS", "PagedAttnError", "Plan", "Partials", "num_splits",
     "max_splits", "default_split_tokens", "sched_bytes", "workspace_bytes", "paged_kv_write",
     "paged_attn_plan", "paged_decode_prepare", "paged_attn_decode_partial", "paged_attn_reduce",
-    "paged_attn_decode", "hbm_read_probe",
+    "paged_attn_decode", "paged_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "hbm_read_probe",
 ]

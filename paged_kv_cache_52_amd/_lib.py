@@ -49,6 +49,9 @@ SIGNATURES = {
     "paged_attn_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
                                          _I64, _I32, _P, _I32, _P, _P, _I32, _I32, _F32, _I32,
                                          _P, _P, _SZ, _P]),
+    "paged_attn_decode_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                                 _P, _I32, _I64, _I32, _P, _I32, _P, _P, _I32,
+                                                 _I32, _F32, _I32, _P, _P]),
 }
 
 _lib = None

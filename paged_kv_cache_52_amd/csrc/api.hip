@@ -87,7 +87,8 @@ const char *pa_strerror(int status) {
     case PA_ERR_SPLIT: return "split_tokens must be a positive multiple of 16 up to 4096, and max_splits must cover the longest split range";
     case PA_ERR_WORKSPACE: return "workspace smaller than pa_workspace_bytes()";
     case PA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_LAUNCH: return "kernel launch failed (or the device's fixed scratch could not be set up)";
+    case PA_ERR_SCRATCH: return "the call needs more than the library's fixed scratch (PA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -420,6 +421,54 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
   return launch_status(pa::launch_reduce(p, stream));
 }
 
+}  // extern "C"
+
+namespace pa {
+
+int decode_workspace_need(const void *q, int32_t q_dtype, int32_t num_seqs,
+                          int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                          const void *k_cache, const void *v_cache, const float *k_scale,
+                          const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
+                          int32_t num_kv_heads, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          const int32_t *query_start, int32_t max_context_len,
+                          int32_t sliding_window, int32_t split_tokens, const void *out,
+                          size_t *need) {
+  *need = 0;
+  const bool packed = query_start != nullptr;
+  if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !supported_group(num_q_heads / num_kv_heads) || num_blocks <= 0 || num_blocks > INT_MAX)
+    return PA_ERR_SHAPE;
+  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
+  const bool dt_ok = (q_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
+                     (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
+                     ((q_dtype == PA_BF16 || q_dtype == PA_F32) && quantised(cache_dtype));
+  if (!dt_ok) return PA_ERR_DTYPE;
+  const int32_t qmax = query_bound(packed, num_query_tokens);
+  if (split_tokens == 0)
+    split_tokens = pa_default_split_tokens(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype, max_context_len,
+        query_for_default(packed, num_query_tokens, num_seqs), sliding_window);
+  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
+  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq), qmax,
+                                   sliding_window, split_tokens);
+  if (ns > PA_MAX_SPLITS) return PA_ERR_SPLIT;
+  if (num_seqs == 0 || (packed && num_query_tokens == 0)) return PA_OK;
+  if (!q || !out || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return PA_ERR_ALIGN;
+  *need = packed ? pa_workspace_bytes_packed(num_seqs, num_query_tokens, num_q_heads,
+                                             num_kv_heads, head_dim, ns)
+                 : pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim, ns);
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
 int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_query_tokens,
                       int32_t num_q_heads, int32_t head_dim, const void *k_cache,
                       const void *v_cache, const float *k_scale, const float *v_scale,
@@ -429,31 +478,25 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       int32_t max_context_len, int32_t sliding_window, float scale,
                       int32_t split_tokens, void *out, void *workspace, size_t workspace_bytes,
                       hipStream_t stream) {
+  size_t need;
+  int st = pa::decode_workspace_need(q, q_dtype, num_seqs, num_query_tokens, num_q_heads,
+                                     head_dim, k_cache, v_cache, k_scale, v_scale, cache_dtype,
+                                     num_blocks, num_kv_heads, block_tables, max_blocks_per_seq,
+                                     context_lens, query_start, max_context_len, sliding_window,
+                                     split_tokens, out, &need);
+  if (st != PA_OK || need == 0) return st;
+  if (!workspace) return PA_ERR_NULL;
+  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   const bool packed = query_start != nullptr;
-  if (max_context_len < 0 || num_seqs < 0 || num_seqs > PA_MAX_SEQS || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0)
-    return PA_ERR_SHAPE;
-  if (bad_queries(packed, num_query_tokens, sliding_window)) return PA_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128) return PA_ERR_SHAPE;
-  if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && !quantised(cache_dtype))
-    return PA_ERR_DTYPE;
-  const int32_t qmax = query_bound(packed, num_query_tokens);
   if (split_tokens == 0)
     split_tokens = pa_default_split_tokens(
         num_seqs, num_q_heads, num_kv_heads, head_dim, cache_dtype, max_context_len,
         query_for_default(packed, num_query_tokens, num_seqs), sliding_window);
-  if (check_split_tokens(split_tokens) != PA_OK) return PA_ERR_SPLIT;
-  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq), qmax,
-                                   sliding_window, split_tokens);
+  const int32_t ns = pa_max_splits(clamped_bound(max_context_len, max_blocks_per_seq),
+                                   query_bound(packed, num_query_tokens), sliding_window,
+                                   split_tokens);
   const int32_t g = num_q_heads / num_kv_heads;
-  const size_t need =
-      packed ? pa_workspace_bytes_packed(num_seqs, num_query_tokens, num_q_heads, num_kv_heads,
-                                         head_dim, ns)
-             : pa_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, head_dim, ns);
-  if (num_seqs == 0 || (packed && num_query_tokens == 0)) return PA_OK;
-  if (!workspace || !out) return PA_ERR_NULL;
-  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_ALIGN;
-  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   const size_t rows = (size_t)(packed ? 1 : num_seqs) * num_query_tokens * num_q_heads * ns;
   char *base = (char *)workspace;
   int32_t *sched = (int32_t *)base;
@@ -462,9 +505,9 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t num_seqs, int32_t 
   float *m = (float *)base;
   float *l = (float *)(base + align256(rows * sizeof(float)));
   float *acc = (float *)(base + 2 * align256(rows * sizeof(float)));
-  int st = paged_attn_plan(context_lens, query_start, block_tables, num_seqs, max_blocks_per_seq,
-                           max_context_len, num_query_tokens, g, sliding_window, split_tokens,
-                           1, sched, stream);
+  st = paged_attn_plan(context_lens, query_start, block_tables, num_seqs, max_blocks_per_seq,
+                       max_context_len, num_query_tokens, g, sliding_window, split_tokens, 1,
+                       sched, stream);
   if (st != PA_OK) return st;
   st = paged_attn_decode_partial(q, q_dtype, num_seqs, num_query_tokens, num_q_heads, head_dim,
                                  k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks,

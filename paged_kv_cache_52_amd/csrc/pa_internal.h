@@ -57,6 +57,19 @@ hipError_t launch_kv_write(const WriteParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int blocks,
                              hipStream_t stream);
 
+// paged_attn_decode's argument checks (every one made before it enqueues
+// anything) and the workspace it needs: *need = 0 when the call has nothing to
+// do. split_tokens 0 means the default.
+int decode_workspace_need(const void *q, int32_t q_dtype, int32_t num_seqs,
+                          int32_t num_query_tokens, int32_t num_q_heads, int32_t head_dim,
+                          const void *k_cache, const void *v_cache, const float *k_scale,
+                          const float *v_scale, int32_t cache_dtype, int64_t num_blocks,
+                          int32_t num_kv_heads, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          const int32_t *query_start, int32_t max_context_len,
+                          int32_t sliding_window, int32_t split_tokens, const void *out,
+                          size_t *need);
+
 // One per (q dtype, cache dtype) pair; p.group = Hq / Hkv in {1, 2, 4, 8, 16}.
 hipError_t decode_bf16_bf16(const DecodeParams &p, int64_t max_entries, hipStream_t s);
 hipError_t decode_f32_f32(const DecodeParams &p, int64_t max_entries, hipStream_t s);

@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_SPLIT, ERR_WS, ERR_ALIGN, ERR_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+ERR_SCRATCH = -8
 F32, BF16, I8, FP8 = 0, 1, 2, 3
 FAKE = 0x10000       # non-null, 16-byte aligned, never dereferenced
 FAKE_ODD = 0x10008   # non-null, not 16-byte aligned
@@ -39,7 +40,8 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_strerror(lib):
-    for code in (OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_SPLIT, ERR_WS, ERR_ALIGN, ERR_LAUNCH):
+    for code in (OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_SPLIT, ERR_WS, ERR_ALIGN, ERR_LAUNCH,
+                 ERR_SCRATCH):
         assert lib.pa_strerror(code)
     assert lib.pa_strerror(12345) == b"unknown status"
 
@@ -319,6 +321,32 @@ def test_decode_workspace_validation(lib):
     assert lib.paged_attn_decode(*args, FAKE, need - 1, None) == ERR_WS
     assert lib.paged_attn_decode(*args, FAKE + 16, need, None) == ERR_ALIGN  # 256-byte rule
     assert lib.paged_attn_decode(*args, None, need, None) == ERR_NULL
+
+
+def test_decode_noalloc_host_checks(lib):
+    """The allocation-free decode rejects bad arguments, and calls needing more
+    than its fixed scratch, on the host: these return before any device is
+    touched (this runs without a GPU)."""
+    args = [FAKE, BF16, 4, 1, 32, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 64, FAKE, None,
+            1000, 0, ctypes.c_float(0.1), 512]
+    assert lib.paged_attn_decode_noalloc(*args, None, None) == ERR_NULL    # out
+    bad = list(args); bad[5] = 96
+    assert lib.paged_attn_decode_noalloc(*bad, FAKE, None) == ERR_SHAPE     # head_dim
+    bad = list(args); bad[1] = F32
+    assert lib.paged_attn_decode_noalloc(*bad, FAKE, None) == ERR_DTYPE     # fp32 q, bf16 cache
+    bad = list(args); bad[20] = 24
+    assert lib.paged_attn_decode_noalloc(*bad, FAKE, None) == ERR_SPLIT
+    bad = list(args); bad[2] = 0
+    assert lib.paged_attn_decode_noalloc(*bad, None, None) == OK            # nothing to do
+    # 1 sequence, 8 query heads, up to 1,000,000 tokens in 16-token splits:
+    # 62,500 splits of 8 rows of partials, about 260 MB > 64 MiB.
+    big = [FAKE, BF16, 1, 1, 8, 128, FAKE, FAKE, None, None, BF16, 100, 8, FAKE, 70000, FAKE,
+           None, 1000000, 0, ctypes.c_float(0.1), 16]
+    need = lib.pa_workspace_bytes(1, 1, 8, 128, lib.pa_max_splits(1000000, 1, 0, 16))
+    assert need > (64 << 20)
+    assert lib.paged_attn_decode_noalloc(*big, FAKE, None) == ERR_SCRATCH
+    # The same call with a caller workspace is only short of workspace.
+    assert lib.paged_attn_decode(*big, FAKE, FAKE, 64 << 20, None) == ERR_WS
 
 
 def test_read_probe_validation(lib):
