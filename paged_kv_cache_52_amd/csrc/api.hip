@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "pa_internal.h"
 #include "pagedattn.h"
@@ -75,6 +76,42 @@ constexpr int64_t kGrowWorkItems = 2048;  // items a decode step keeps when its 
 constexpr int64_t kGrowMaxBytes = 1 << 20;  // K/V bytes per (split, KV head) growth stops at
 
 }  // namespace
+
+namespace pa {
+
+int compute_units(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices];  // a device property, looked up once
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    (void)hipGetLastError();
+    if (hipGetDevice(&dev) != hipSuccess) (void)hipGetLastError();
+  }
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int v = known[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                     hipSuccess) {
+    (void)hipGetLastError();
+    n = 0;
+  }
+  n = std::max(n, 1);
+  if (dev >= 0 && dev < kMaxDevices) known[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int resident_per_cu(const void *kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  return std::max(n, 1);
+}
+
+}  // namespace pa
 
 extern "C" {
 

@@ -21,6 +21,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "pa_common.h"
@@ -39,6 +40,8 @@ struct DecodeParams {
   float *part_l;
   float *part_acc;
   const int32_t *sched;  // work list from the plan kernel (see kSchedHeader)
+  int32_t num_bins;      // bins the first items are dealt over (one per compute unit)
+  int32_t bin_wgs;       // workgroups per bin resident at launch
   int64_t num_blocks;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks_per_seq, max_context_len;
@@ -105,6 +108,9 @@ struct RowRanges {
 //   the sequence's clamped context length (minus the member count for a group
 //   entry; the row block index with packed queries).
 constexpr int kSchedHeader = 8;
+// Largest number of bins the split kernel deals its first items over (one
+// bin per compute unit).
+constexpr int kMaxBins = 1024;
 
 template <int QT, int CT, int D, int G>
 struct DecodeShape {
@@ -1247,17 +1253,6 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   }
 }
 
-// Split kernel. Work item k is entry sched[kSchedHeader + 2*(k / per_entry)]
-// of the list the plan kernel wrote (full splits first, the shortest last
-// splits at the end), for KV head k % Hkv and, with a uniform query count,
-// the set (k % per_entry) / Hkv of rw row groups of the KV head's Q*g rows
-// (per_entry = Hkv * head_groups; the sets of one KV head land on the same
-// XCD when Hkv is a multiple of 8). With packed queries an entry names its
-// block of kPackedRows rows itself and per_entry = Hkv. Workgroup k processes
-// item k; the grid is an upper bound on the number of items and the
-// workgroups past the end of the list, all at the end of the grid, exit at
-// once. A plan made for another split size, batch, length bound, query count,
-// window or query layout counts as an empty list.
 // The MFMA engine on 16-bit and FP8 caches fits 128 VGPRs, i.e. four waves per
 // SIMD (16 per CU) for latency hiding; the INT8 one needs more and runs three.
 constexpr int kMfmaWavesPerEu = 4;
@@ -1279,25 +1274,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
   decode_split_body<QT, CT, D, G, NW>(p);
 }
 
+// Work item k of the list (k < the list's item count): split j of sequence s
+// for KV head kvh (and, uniform Q, its row set), or a group entry. Contains
+// workgroup barriers; every thread of the workgroup calls it with the same k.
 template <int QT, int CT, int D, int G, int NW>
-__device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ __align__(16) float sm_acc[NW][G][D];
-
+__device__ __forceinline__ void decode_item(const DecodeParams &p, int k, int per_entry,
+                                            float (&sm_m)[NW][G], float (&sm_l)[NW][G],
+                                            float (&sm_acc)[NW][G][D]) {
   const bool packed = p.query_start != nullptr;
-  const int per_entry = packed ? p.num_kv_heads : p.num_kv_heads * p.head_groups;
   const int lmax = (int)min((int64_t)p.max_context_len, (int64_t)p.max_blocks_per_seq * kBlock);
-  // A plan made with group entries needs uniform query counts, every
-  // sequence's rows in one row group (Q*g <= G), and a wave per member.
-  static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
-  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
-                       p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
-                       p.sched[5] == p.window && p.sched[7] == (packed ? p.group : 0) &&
-                       (p.sched[6] <= 1 || (!packed && p.num_query_tokens * p.group <= G));
-  const int n_items = plan_ok ? p.sched[0] * per_entry : 0;
-  const int k = blockIdx.x;
-  if (k >= n_items) return;
   const int lane = lane_id();
   // Wave index as a scalar, so that per-wave ranges and loop counters stay in
   // SGPRs and the tile loop runs without exec masking.
@@ -1338,15 +1323,98 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
   }
 }
 
+// Items are dealt over num_bins bins in snake order (round r of num_bins
+// consecutive items goes to bins 0, 1, ... for even r and back for odd r), so
+// that, with the plan's list running from the longest items to the shortest,
+// every bin gets about the same number of bytes. Item i of bin b:
+__device__ __forceinline__ int64_t bin_item(int b, int i, int nb) {
+  return (int64_t)i * nb + ((i & 1) ? nb - 1 - b : b);
+}
+
+
+// Split kernel. Work item k is entry sched[kSchedHeader + 2*(k / per_entry)]
+// of the list the plan kernel wrote, for KV head k % Hkv and (uniform Q) the
+// set (k % per_entry) / Hkv of rw row groups of the KV head's Q*g rows
+// (per_entry = Hkv * head_groups); with packed queries an entry names its
+// block of kPackedRows rows itself and per_entry = Hkv. A plan made for
+// another split size, batch, length bound, query count, window or query
+// layout counts as an empty list.
+//
+// Which workgroup runs which item. The grid has a workgroup per possible
+// item. The first num_bins * bin_wgs of them are resident at launch, and the
+// dispatcher places workgroups w, w + num_bins, ... on one compute unit (one
+// bin per compute unit). Those take the first num_bins * bin_wgs items of the
+// list dealt over the bins in snake order (workgroup w: item
+// bin_item(w % num_bins, w / num_bins)), so that, with the list running from
+// the longest items to the shortest, every compute unit starts with about
+// the same bytes: they read at about the same rate when all are busy, and a
+// unit dealt the longest items would otherwise set the kernel's length. Each
+// later workgroup w, started when a slot frees up, takes item w (as does
+// every workgroup of a plan with group entries). Every item has exactly one
+// workgroup whatever the placement, which only decides the balance;
+// workgroups past the list exit at once.
+template <int QT, int CT, int D, int G, int NW>
+__device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ __align__(16) float sm_acc[NW][G][D];
+
+  const bool packed = p.query_start != nullptr;
+  const int per_entry = packed ? p.num_kv_heads : p.num_kv_heads * p.head_groups;
+  const int lmax = (int)min((int64_t)p.max_context_len, (int64_t)p.max_blocks_per_seq * kBlock);
+  // A plan made with group entries needs uniform query counts, every
+  // sequence's rows in one row group (Q*g <= G), and a wave per member.
+  static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
+  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
+                       p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
+                       p.sched[5] == p.window && p.sched[7] == (packed ? p.group : 0) &&
+                       (p.sched[6] <= 1 || (!packed && p.num_query_tokens * p.group <= G));
+  const int n_items = plan_ok ? p.sched[0] * per_entry : 0;
+  const int w = blockIdx.x;
+  const int nb = p.num_bins;
+  // Group entries keep the list order: the entries of the groups that share
+  // one prompt's blocks follow each other and run side by side.
+  const bool dealt = p.sched[6] <= 1 && w < nb * p.bin_wgs;
+  const int64_t k = dealt ? bin_item(w % nb, w / nb, nb) : (int64_t)w;
+  if (k >= n_items) return;
+  decode_item<QT, CT, D, G, NW>(p, (int)k, per_entry, sm_m, sm_l, sm_acc);
+}
+
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
 // Waves per workgroup (they share one split).
 constexpr int kDecodeWaves = 4;
 
+// Compute units of the device `stream` runs on (cached per device: a fixed
+// property).
+int compute_units(hipStream_t stream);
+
+// Resident workgroups per compute unit of a kernel (its registers and LDS
+// decide; cached per kernel by the caller).
+int resident_per_cu(const void *kernel, int threads);
+
 template <int QT, int CT, int D, int G>
-hipError_t launch_decode(const DecodeParams &p, int64_t max_items, hipStream_t stream) {
+hipError_t launch_decode(DecodeParams p, int64_t max_items, hipStream_t stream) {
   constexpr int NW = kDecodeWaves;
-  // One workgroup per possible item; those past the planned list exit at once.
-  if constexpr (QT == PA_BF16 && (CT == PA_BF16 || CT == PA_FP8) && D == 128)
+  constexpr bool kMfmaBound = QT == PA_BF16 && (CT == PA_BF16 || CT == PA_FP8) && D == 128;
+  const void *kernel;
+  if constexpr (kMfmaBound)
+    kernel = reinterpret_cast<const void *>(&decode_split_kernel_mfma<QT, CT, D, G, NW>);
+  else
+    kernel = reinterpret_cast<const void *>(&decode_split_kernel<QT, CT, D, G, NW>);
+  // A bin per compute unit (at most one per possible item) and as many
+  // workgroups per bin as fit on a compute unit at once (so that the dealt
+  // workgroups are those resident at launch); a workgroup per possible item.
+  static std::atomic<int> known{0};  // a property of the kernel: computed once
+  int per_cu = known.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    per_cu = resident_per_cu(kernel, NW * kWave);
+    known.store(per_cu, std::memory_order_relaxed);
+  }
+  const int64_t nb = std::min<int64_t>({compute_units(stream), kMaxBins, max_items});
+  const int64_t w = std::max<int64_t>(1, std::min<int64_t>(per_cu, max_items / nb));
+  p.num_bins = (int32_t)nb;
+  p.bin_wgs = (int32_t)w;
+  if constexpr (kMfmaBound)
     hipLaunchKernelGGL((decode_split_kernel_mfma<QT, CT, D, G, NW>), dim3((unsigned)max_items),
                        dim3(NW * kWave), 0, stream, p);
   else
