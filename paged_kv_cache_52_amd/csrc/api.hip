@@ -74,6 +74,7 @@ constexpr int32_t kMinDefaultSplit = 64;  // smallest split the default picks
 constexpr int64_t kMinWorkItems = 1024;   // (split, KV head) items the default aims for
 constexpr int64_t kGrowWorkItems = 2048;  // items a decode step keeps when its splits grow
 constexpr int64_t kGrowMaxBytes = 1 << 20;  // K/V bytes per (split, KV head) growth stops at
+constexpr int32_t kGrowStep = 256;          // tokens a decode step's split grows by
 
 }  // namespace
 
@@ -181,16 +182,16 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (rows > 64)
     while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kMinWorkItems) t *= 2;
   // A decode step with at most 8 rows per KV head: longer splits (fewer
-  // items and partials, each a longer stream) while at least kGrowWorkItems
-  // items remain and a split's K/V stays within kGrowMaxBytes per KV head.
-  // Items are counted at the longest context, so a batch of many short
-  // sequences stays where the bytes put it; the byte cap keeps a few very
-  // long sequences (whose item count the longest context overstates) at
-  // enough items.
+  // items and partials, each a longer stream), kGrowStep tokens at a time,
+  // while at least kGrowWorkItems items remain and a split's K/V stays within
+  // kGrowMaxBytes per KV head. Items are counted at the longest context, so a
+  // batch of many short sequences stays where the bytes put it; the byte cap
+  // keeps a few very long sequences (whose item count the longest context
+  // overstates) at enough items.
   if (rows <= 8)
-    while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kGrowWorkItems &&
-           2 * t * kv_bytes_per_token <= kGrowMaxBytes)
-      t *= 2;
+    while (t + kGrowStep <= PA_MAX_SPLIT_TOKENS && items(t + kGrowStep) >= kGrowWorkItems &&
+           (t + kGrowStep) * kv_bytes_per_token <= kGrowMaxBytes)
+      t += kGrowStep;
   return t;
 }
 
