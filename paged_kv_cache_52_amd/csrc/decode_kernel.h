@@ -564,12 +564,13 @@ struct MfmaWave {
     }
   }
 
-  // Running max of head c over a step's logits (bm: this lane's maximum):
-  // the maximum over the four lane groups, and a rescale when it passes the
-  // reference by more than the slack.
-  __device__ __forceinline__ void update_max(float bm, int g) {
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+  // Running max of head c over a step's logits (bm: this lane's maximum, of
+  // logits that still need the factor `scale` > 0): the maximum over the four
+  // lane groups, and a rescale when it passes the reference by more than the
+  // slack.
+  __device__ __forceinline__ void update_max(float bm, int g, float scale = 1.f) {
+    bm = xor_max<16>(bm);
+    bm = xor_max<32>(bm) * scale;
     mtrue = fmaxf(mtrue, bm);
     const bool grow = bm > m + kRescaleSlack;
     if (__any(grow)) rescale(grow ? bm : m, g);
@@ -670,18 +671,28 @@ struct MfmaWave {
   }
 
   // Staged tiles (bf16 K/V rows in LDS, kStageRow bytes apart).
-  // Logits of the tile whose K rows start at kb.
-  __device__ __forceinline__ void scores_lds(const char *kb, float (&z)[4], float scale_log2,
-                                             int c, int g) const {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  // Raw q.k sums of the two staged tiles whose K rows start at k0 and k1.
+  __device__ __forceinline__ void scores2_lds(const char *k0, const char *k1, float (&z0)[4],
+                                              float (&z1)[4], int c, int g) const {
+    u32x4 a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 k = *reinterpret_cast<const u32x4 *>(kb + c * kStageRow + 64 * i + 16 * g);
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                  __builtin_bit_cast(bf16x8, qB[i]), sc, 0, 0, 0);
+      a[i] = *reinterpret_cast<const u32x4 *>(k0 + c * kStageRow + 64 * i + 16 * g);
+      b[i] = *reinterpret_cast<const u32x4 *>(k1 + c * kStageRow + 64 * i + 16 * g);
+    }
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                  __builtin_bit_cast(bf16x8, qB[i]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b[i]),
+                                                  __builtin_bit_cast(bf16x8, qB[i]), s1, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = sc[r] * scale_log2;
+    for (int r = 0; r < 4; ++r) {
+      z0[r] = s0[r];
+      z1[r] = s1[r];
+    }
   }
 
   // B operand of output column block JJ (dims 16JJ .. 16JJ + 15) from the V
@@ -714,27 +725,32 @@ struct MfmaWave {
                                                    bool in1, bool m0, bool m1, int tb, int lo,
                                                    int hi, int c, int g, float scale_log2) {
     float z0[4], z1[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z0[r] = z1[r] = -INFINITY;
     // The matrix-core blocks (logits, then P.V) run at a raised wave priority
     // and the softmax between them at the normal one, so that a SIMD's waves
     // tend to alternate between the two phases instead of bunching up in one.
+    // Both tiles' logits are computed (two independent MFMA chains); a tile
+    // outside this wave's range then gets -inf by select, so whatever its
+    // LDS rows hold never reaches a weight. The logits stay raw q.k sums (q
+    // carries the scale's sign, so scale_log2 > 0 here): the maximum is taken
+    // on them and scaled once, and each weight is exp2(fma(sum, scale, -m)).
     __builtin_amdgcn_s_setprio(1);
-    if (in0) {
-      scores_lds(k0, z0, scale_log2, c, g);
+    scores2_lds(k0, k1, z0, z1, c, g);
+    __builtin_amdgcn_s_setprio(0);
+    if (!(in0 && in1) || m0 || m1) {  // uniform
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z0[r] = in0 ? z0[r] : -INFINITY;
+        z1[r] = in1 ? z1[r] : -INFINITY;
+      }
       if (m0) mask_z(z0, tb, lo, hi, g);
-    }
-    if (in1) {
-      scores_lds(k1, z1, scale_log2, c, g);
       if (m1) mask_z(z1, tb + kBlock, lo, hi, g);
     }
-    __builtin_amdgcn_s_setprio(0);
     update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
                      fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
-               g);
+               g, scale_log2);
     uint32_t h0[2], l0[2], h1[2], l1[2];
-    weights_plain(z0, h0, l0);
-    weights_plain(z1, h1, l1);
+    weights_plain(z0, h0, l0, scale_log2);
+    weights_plain(z1, h1, l1, scale_log2);
     const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
     const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
     __builtin_amdgcn_s_setprio(1);
@@ -758,12 +774,13 @@ struct MfmaWave {
     }
   }
 
-  // weights() without cache scales (bf16 cache).
+  // weights() without cache scales (bf16 cache), from raw sums z: exp2(z *
+  // scale - m) with one rounding.
   __device__ __forceinline__ void weights_plain(const float (&z)[4], uint32_t (&hi)[2],
-                                                uint32_t (&lo)[2]) {
+                                                uint32_t (&lo)[2], float scale) {
     float pz[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(z[r] - m);
+    for (int r = 0; r < 4; ++r) pz[r] = fast_exp2(fmaf(z[r], scale, -m));
     l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
     hi[0] = pack_bf16(pz[0], pz[1]);
     hi[1] = pack_bf16(pz[2], pz[3]);
@@ -822,12 +839,21 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   const int lo = row_ok ? rr.lo(qi) : rr.ulo, hi = row_ok ? rr.hi(qi) : rr.uhi;
   const int64_t qrow = row_ok ? query_row(p, rr.first, kvh, R0 + c) : 0;
   float qs = 0.f;
+  // Staged walks: the scale's sign goes into q (exact for bf16) and every
+  // tile of the walk uses |scale| > 0 (a zero scale becomes the smallest
+  // normal float, which leaves every weight at exactly 1).
+  const uint32_t qsign = STAGED && p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sl2 = STAGED ? fmaxf(fabsf(p.scale_log2), 1.17549435e-38f) : p.scale_log2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     st.qB[i] = u32x4{0u, 0u, 0u, 0u};
     if (row_ok) {
       const int dim0 = CT == PA_BF16 ? 32 * i + 8 * g : 32 * g + 8 * i;
       st.qB[i] = *(const u32x4 *)((const uint16_t *)p.q + qrow * D + dim0);
+      if constexpr (STAGED) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) st.qB[i][w] ^= qsign;
+      }
     }
     if constexpr (CT == PA_I8) {
 #pragma unroll
@@ -835,8 +861,8 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     }
   }
   if constexpr (CT == PA_I8) {
-    qs += __shfl_xor(qs, 16);
-    qs += __shfl_xor(qs, 32);
+    qs = xor_sum<16>(qs);
+    qs = xor_sum<32>(qs);
   }
   st.qbias = 128.f * qs;
 #pragma unroll
@@ -852,7 +878,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   const int soff = 16 * g;  // scales of tokens 4g .. 4g+3
   auto eat = [&](MfmaTile<CT> &t, int n) {
     const int tb = (b0 + n) * kBlock;
-    st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, p.scale_log2);
+    st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, sl2);
   };
   if constexpr (STAGED) {
     static_assert(CT == PA_BF16 && sizeof(float) * NW * G * D >= kStageBytes, "staging space");
@@ -897,13 +923,21 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
       for (int n = c0; n < c1; n += 2) {
         // Rows of tokens no row of the workgroup attends (and a missing
         // second tile) are stored as zeros.
-        const int tok0 = (b0 + n) * kBlock + srow, tok1 = tok0 + kBlock;
-        const bool ok0 = tok0 >= ulo_wg && tok0 <= uhi_wg;
-        const bool ok1 = n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg;
-        *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = ok0 ? kr0 : zero;
-        *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = ok0 ? vr0 : zero;
-        *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = ok1 ? kr1 : zero;
-        *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = ok1 ? vr1 : zero;
+        const int tp = (b0 + n) * kBlock;  // first token of the pair
+        if (n + 1 < c1 && tp >= ulo_wg && tp + 2 * kBlock - 1 <= uhi_wg) {  // uniform
+          *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
+          *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
+          *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
+          *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
+        } else {
+          const int tok0 = tp + srow, tok1 = tok0 + kBlock;
+          const bool ok0 = tok0 >= ulo_wg && tok0 <= uhi_wg;
+          const bool ok1 = n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg;
+          *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = ok0 ? kr0 : zero;
+          *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = ok0 ? vr0 : zero;
+          *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = ok1 ? kr1 : zero;
+          *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = ok1 ? vr1 : zero;
+        }
         __syncthreads();  // the pair is in LDS
         if (n + 2 < c1) fetch(n + 2, kr0, vr0);
         if (n + 3 < c1) fetch(n + 3, kr1, vr1);
@@ -912,7 +946,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         if (in0 || in1) {
           const int tb = (b0 + n) * kBlock;
           st.consume_pair_lds(K0, V0, K1, V1, in0, in1, rr.needs_mask(tb),
-                              rr.needs_mask(tb + kBlock), tb, lo, hi, c, g, p.scale_log2);
+                              rr.needs_mask(tb + kBlock), tb, lo, hi, c, g, sl2);
         }
         __syncthreads();  // every wave is done with the pair
       }
@@ -976,12 +1010,10 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   // Renormalise to the true max (every lane takes part: rescale reads other
   // lanes' factors), then sum l over the four lane groups.
   st.rescale(fmaxf(st.mtrue, st.m), g);
-  float lt = st.l + __shfl_xor(st.l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = xor_sum<32>(xor_sum<16>(st.l));
   if constexpr (CT == PA_I8) {
     // Remove the code bias from O: row 4g + r loses 128 * (its head's wsum).
-    float wt = st.wsum + __shfl_xor(st.wsum, 16);
-    wt += __shfl_xor(wt, 32);
+    const float wt = xor_sum<32>(xor_sum<16>(st.wsum));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float bias = 128.f * __shfl(wt, 4 * g + r);

@@ -58,6 +58,40 @@ constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
+// Values of lane l and lane l ^ K (K = 16 or 32) as (the one whose bit K is
+// clear, the one whose bit K is set), the same pair in both lanes: gfx950's
+// v_permlane16_swap / v_permlane32_swap of x with itself, one VALU op instead
+// of an LDS permute.
+struct LanePair {
+  float lo, hi;
+};
+template <int K>
+__device__ __forceinline__ LanePair lane_pair(float x) {
+  static_assert(K == 16 || K == 32, "row pairs of 16 or halves of 32 lanes");
+  const uint32_t u = __float_as_uint(x);
+#if __HIP_DEVICE_COMPILE__
+  if constexpr (K == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+  }
+#else
+  return {__uint_as_float(u), __uint_as_float(u)};
+#endif
+}
+template <int K>
+__device__ __forceinline__ float xor_sum(float x) {
+  const LanePair p = lane_pair<K>(x);
+  return p.lo + p.hi;
+}
+template <int K>
+__device__ __forceinline__ float xor_max(float x) {
+  const LanePair p = lane_pair<K>(x);
+  return fmaxf(p.lo, p.hi);
+}
+
 // Sum over each aligned group of N consecutive lanes; every lane of the group
 // receives the same (bitwise) result because each step adds commutative pairs.
 template <int N>
@@ -66,8 +100,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
   if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = xor_sum<16>(x);
+  if constexpr (N >= 64) x = xor_sum<32>(x);
   return x;
 }
 
@@ -77,8 +111,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  if constexpr (N >= 32) x = xor_max<16>(x);
+  if constexpr (N >= 64) x = xor_max<32>(x);
   return x;
 }
 
