@@ -262,15 +262,33 @@ def cpu_baseline_child(d):
     }), flush=True)
 
 
-def load_counters(workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs on this
-    workload, if they were taken on the current kernel sources."""
+def run_tag(args):
+    """Suffix naming a run's departures from the workload's defaults (it
+    selects the committed counter file that belongs to the run)."""
+    tag = ""
+    if args.split_tokens:
+        tag += f"_T{args.split_tokens}"
+    if args.group_members:
+        tag += f"_M{args.group_members}"
+    if args.contiguous_tables:
+        tag += "_contiguous"
+    if args.seed != 1:
+        tag += f"_seed{args.seed}"
+    if args.ctx_range:
+        tag += f"_ctx{args.ctx_range[0]}-{args.ctx_range[1]}"
+    return tag
+
+
+def load_counters(workload, tag, launch):
+    """HBM bytes per launch from committed rocprofv3 counter runs of this
+    workload and launch configuration, if they were taken on the current
+    kernel sources."""
     try:
-        with open(os.path.join(PROFILES, f"decode_{workload}_counters.json")) as f:
+        with open(os.path.join(PROFILES, f"decode_{workload}{tag}_counters.json")) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("launch") != launch:
         return None
     return c
 
@@ -468,7 +486,9 @@ def main():
     # the ridge point of the two peaks (dense bf16 MFMA / HBM).
     mfma_bound = alg_flops / alg_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     kv_gbps_step = kv_unique / (ms_step * 1e-3) / 1e9
-    counters = load_counters(w.name)
+    launch = {"split_tokens": T, "group_members": M,
+              "tables": "contiguous" if args.contiguous_tables else "permuted"}
+    counters = load_counters(w.name, run_tag(args), launch)
     traffic = None
     if counters is not None:
         traffic = counters["fetch_bytes_per_launch"] + counters["write_bytes_per_launch"]
