@@ -397,7 +397,9 @@ template <>
 struct MfmaTile<PA_I8> {
   u32x4 k[2];  // K codes: token c, dims 32g .. 32g+31
   u32x2 v[4];  // V codes: rows 4g + i, dims 8c .. 8c+7
-  f32x4 ks;    // K scales of tokens 4g .. 4g+3
+  float ks1;   // K scale of token 4g + c % 4 (as loaded)
+  float vs1;   // V scale of token 4g + c % 4
+  f32x4 ks;    // K scales of tokens 4g .. 4g+3 (handed out from ks1 within the quad)
   f32x4 vs;    // V scales of tokens 4g .. 4g+3
 };
 template <>
@@ -492,11 +494,11 @@ struct MfmaWave {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16 * i, 0, POL);
-      t.ks = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ksr, soff, 0, 0));
+      t.ks1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, soff, 0, 0));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         t.v[i] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + ROW * i, 0, POL);
-      t.vs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vsr, soff, 0, 0));
+      t.vs1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, soff, 0, 0));
     }
   }
 
@@ -650,6 +652,12 @@ struct MfmaWave {
   // tile is at an edge of some row's range.
   __device__ __forceinline__ void consume(MfmaTile<CT> &t, bool need_mask, int tb, int lo,
                                           int hi, int ulo, int uhi, int g, float scale_log2) {
+    if constexpr (Quantised<CT>::value) {
+      // Each lane loaded the scales of one token of its quad's four (4g + c % 4);
+      // every lane takes all four from its quad.
+      t.ks = f32x4{dpp<0x00>(t.ks1), dpp<0x55>(t.ks1), dpp<0xAA>(t.ks1), dpp<0xFF>(t.ks1)};
+      t.vs = f32x4{dpp<0x00>(t.vs1), dpp<0x55>(t.vs1), dpp<0xAA>(t.vs1), dpp<0xFF>(t.vs1)};
+    }
     float z[4];
     scores(t, z, scale_log2);
     if (need_mask) mask(t, z, tb, lo, hi, ulo, uhi, g);  // uniform
@@ -875,7 +883,8 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   const int last_block = (int)(p.num_blocks - 1);
   const int koff = CT == PA_BF16 ? c * Wv::ROW + 16 * g : c * Wv::ROW + 32 * g;
   const int voff = 4 * g * Wv::ROW + 8 * Wv::ELT * c;
-  const int soff = 16 * g;  // scales of tokens 4g .. 4g+3
+  // Scales: this lane reads token 4g + c % 4's (its quad shares them out).
+  const int soff = CT == PA_BF16 ? 0 : 4 * (4 * g + c % 4);
   auto eat = [&](MfmaTile<CT> &t, int n) {
     const int tb = (b0 + n) * kBlock;
     st.consume(t, rr.needs_mask(tb), tb, lo, hi, rr.ulo, rr.uhi, g, sl2);
