@@ -181,14 +181,17 @@ int32_t pa_default_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
   while (t > kMinDefaultSplit && items(t) < kMinWorkItems) t /= 2;
   if (rows > 64)
     while (t < PA_MAX_SPLIT_TOKENS && items(2 * t) >= kMinWorkItems) t *= 2;
-  // A decode step with at most 8 rows per KV head: longer splits (fewer
-  // items and partials, each a longer stream), kGrowStep tokens at a time,
+  // A decode step with at most 8 rows per KV head, or at most 16 rows of
+  // several query tokens (4 draft + target tokens at g = 4): longer splits
+  // (fewer items and partials, each a longer stream), kGrowStep tokens at a time,
   // while at least kGrowWorkItems items remain and a split's K/V stays within
   // kGrowMaxBytes per KV head. Items are counted at the longest context, so a
   // batch of many short sequences stays where the bytes put it; the byte cap
   // keeps a few very long sequences (whose item count the longest context
-  // overstates) at enough items.
-  if (rows <= 8)
+  // overstates) at enough items. One query token with 16 rows (g = 16) keeps
+  // its size: it is the shape of shared-prefix batches, whose group entries
+  // (one per shared full split) get longer with it.
+  if (rows <= 8 || (rows <= 16 && num_query_tokens >= 2))
     while (t + kGrowStep <= PA_MAX_SPLIT_TOKENS && items(t + kGrowStep) >= kGrowWorkItems &&
            (t + kGrowStep) * kv_bytes_per_token <= kGrowMaxBytes)
       t += kGrowStep;

@@ -85,11 +85,13 @@ def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
 
 
 def test_default_split_tokens_grow_with_query_rows(lib):
-    # 16 rows per KV head (4 query tokens at g = 4, or g = 16): 512 KiB, 1024 tokens.
-    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 4, 0) == 1024
+    # 16 rows per KV head (4 query tokens at g = 4, or g = 16): 512 KiB, 1024 tokens;
+    # several query tokens then grow like a one-token step (4 splits of 1280 =
+    # 2048 items), one query token at g = 16 stays.
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 4, 0) == 1280
     assert lib.pa_default_split_tokens(256, 64, 4, 128, BF16, 18385, 1, 0) == 1024
     assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 2, 0) == 1280  # 8 rows
-    assert lib.pa_default_split_tokens(128, 32, 8, 128, I8, 8192, 4, 0) == 2048
+    assert lib.pa_default_split_tokens(128, 32, 8, 128, I8, 8192, 4, 0) == 4096  # 1 MiB cap
 
 
 def test_default_split_tokens_for_prefill_chunks(lib):
