@@ -453,6 +453,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char *ptr) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(char *)ptr);
 #else
+  (void)ptr;
   return s16x4{0, 0, 0, 0};
 #endif
 }
@@ -1260,7 +1261,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     const int Lg = max(0, min(p.context_lens[s + g], lmax));
     return j < splits_of(Lg, Q, W, p.split_tokens) ? rows_of(g) : 0;
   };
-  if (threadIdx.x < rw * G) {
+  if ((int)threadIdx.x < rw * G) {
     const int g = threadIdx.x / G, h = threadIdx.x % G;
     if (h < live(g)) {
       const int w0 = g * tw;

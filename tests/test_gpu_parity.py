@@ -1112,6 +1112,51 @@ def test_grouped_plan(T, M):
                                    for j in range(max(1, -(-L[s] // T))))
 
 
+SCALE_CASES = [0.0, -0.0884, 3.0]
+
+
+@pytest.mark.parametrize("scale", SCALE_CASES)
+@pytest.mark.parametrize("kind", ["decode", "staged", "packed", "grouped"])
+def test_softmax_scale_zero_negative_and_large(kind, scale):
+    """The logit scale is any float: zero gives the mean of V over the tokens
+    a row attends, a negative scale reverses the logits, a large one makes the
+    weights peaked (and the running max move often). The LDS-staged walks
+    (many query rows per KV head, packed prefill chunks, group entries) fold
+    the scale's sign into q and take |scale| (a zero scale as the smallest
+    normal float); the streaming decode keeps the scale as given. Every form
+    is compared with the oracle at the same scale."""
+    print(f"[case] scale {scale} {kind}", flush=True)
+    if kind == "decode":
+        b = _mtp_batch("llama8b_bf16", 1, 0, 281)
+    elif kind == "staged":
+        b = _mtp_batch("llama8b_bf16", 100, 0, 282)  # 400 rows per KV head
+    elif kind == "packed":
+        b = _packed_batch("llama8b_bf16", [300, 700, 90], [1, 40, 17], 0, 283)
+    else:
+        b = workloads.make_batch("shared_prefix_bf16", 284, "cpu", groups=2, suffix_max=600)
+    b.scale = scale
+    g = _to(b, "cuda")
+    ref = _oracle_decode(b)
+    assert np.isfinite(ref).all()
+    if kind != "grouped":
+        out, _ = _gpu_fp32_out(g, 64)
+    else:
+        plan = pa().paged_attn_plan(g.context_lens, g.block_tables.shape[1],
+                                    max_context_len=g.max_context_len, split_tokens=1024,
+                                    num_query_tokens=b.query_tokens,
+                                    block_tables=g.block_tables, group_members=4)
+        parts = pa().paged_attn_decode_partial(g.q, g.k_cache, g.v_cache, g.block_tables,
+                                               g.context_lens, g.scale,
+                                               max_context_len=g.max_context_len, plan=plan)
+        o = torch.empty(g.q.shape, dtype=torch.float32, device="cuda")
+        pa().paged_attn_reduce(parts, o)
+        torch.cuda.synchronize()
+        sched = plan.sched.cpu().numpy()
+        assert (sched[9:9 + 2 * int(sched[0]):2] < 0).any(), "the batch should form groups"
+        out = o.cpu().double().numpy()
+    _check_out(out.reshape(ref.shape), ref, _tol(b), f"scale {scale} {kind}")
+
+
 GROUPED_CASES = [
     ("shared_prefix_bf16", 64, 2),
     ("shared_prefix_bf16", 64, 4),
