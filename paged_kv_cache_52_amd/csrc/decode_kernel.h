@@ -572,9 +572,9 @@ struct MfmaWave {
   // lane groups, and a rescale when it passes the reference by more than the
   // slack.
   __device__ __forceinline__ void update_max(float bm, int g, float scale = 1.f) {
-    bm = xor_max<16>(bm);
-    bm = xor_max<32>(bm) * scale;
-    mtrue = fmaxf(mtrue, bm);
+    bm = xor_max_raw<16>(bm);
+    bm = xor_max_raw<32>(bm) * scale;
+    mtrue = max_raw(mtrue, bm);
     const bool grow = bm > m + kRescaleSlack;
     if (__any(grow)) rescale(grow ? bm : m, g);
   }
@@ -662,7 +662,7 @@ struct MfmaWave {
     float z[4];
     scores(t, z, scale_log2);
     if (need_mask) mask(t, z, tb, lo, hi, ulo, uhi, g);  // uniform
-    update_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), g);
+    update_max(max3_raw(z[0], z[1], max_raw(z[2], z[3])), g);
     uint32_t h[2], lw[2];
     weights(t, z, h, lw);
     const s16x4 phi = __builtin_bit_cast(s16x4, u32x2{h[0], h[1]});
@@ -754,8 +754,8 @@ struct MfmaWave {
       if (m0) mask_z(z0, tb, lo, hi, g);
       if (m1) mask_z(z1, tb + kBlock, lo, hi, g);
     }
-    update_max(fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
-                     fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3]))),
+    update_max(max3_raw(max3_raw(z0[0], z0[1], z0[2]), max3_raw(z0[3], z1[0], z1[1]),
+                        max_raw(z1[2], z1[3])),
                g, scale_log2);
     uint32_t h0[2], l0[2], h1[2], l1[2];
     weights_plain(z0, h0, l0, scale_log2);
@@ -934,19 +934,23 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         // Rows of tokens no row of the workgroup attends (and a missing
         // second tile) are stored as zeros.
         const int tp = (b0 + n) * kBlock;  // first token of the pair
-        if (n + 1 < c1 && tp >= ulo_wg && tp + 2 * kBlock - 1 <= uhi_wg) {  // uniform
-          *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
-          *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
-          *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
-          *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
-        } else {
+        // The loaded rows are stored as they are; at the workgroup's range
+        // edges the rows outside it are then overwritten with zeros (a
+        // thread's two LDS stores land in order).
+        *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
+        *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
+        *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
+        *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
+        if (!(n + 1 < c1 && tp >= ulo_wg && tp + 2 * kBlock - 1 <= uhi_wg)) {  // uniform
           const int tok0 = tp + srow, tok1 = tok0 + kBlock;
-          const bool ok0 = tok0 >= ulo_wg && tok0 <= uhi_wg;
-          const bool ok1 = n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg;
-          *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = ok0 ? kr0 : zero;
-          *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = ok0 ? vr0 : zero;
-          *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = ok1 ? kr1 : zero;
-          *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = ok1 ? vr1 : zero;
+          if (!(tok0 >= ulo_wg && tok0 <= uhi_wg)) {
+            *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = zero;
+            *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = zero;
+          }
+          if (!(n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg)) {
+            *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = zero;
+            *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = zero;
+          }
         }
         __syncthreads();  // the pair is in LDS
         if (n + 2 < c1) fetch(n + 2, kr0, vr0);

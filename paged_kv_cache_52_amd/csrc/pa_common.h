@@ -92,6 +92,35 @@ __device__ __forceinline__ float xor_max(float x) {
   return fmaxf(p.lo, p.hi);
 }
 
+// Maximum of two or three floats as one v_max / v_max3. fmaxf must quiet a
+// signalling NaN operand, so the compiler puts a canonicalising max in front
+// of every operand it cannot prove canonical (matrix-core results, lane
+// swaps); these skip that and return the largest non-NaN operand, as fmaxf
+// does for every input but a signalling NaN.
+__device__ __forceinline__ float max_raw(float a, float b) {
+#if __HIP_DEVICE_COMPILE__
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+#else
+  return fmaxf(a, b);
+#endif
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+#if __HIP_DEVICE_COMPILE__
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(fmaxf(a, b), c);
+#endif
+}
+template <int K>
+__device__ __forceinline__ float xor_max_raw(float x) {
+  const LanePair p = lane_pair<K>(x);
+  return max_raw(p.lo, p.hi);
+}
+
 // Sum over each aligned group of N consecutive lanes; every lane of the group
 // receives the same (bitwise) result because each step adds commutative pairs.
 template <int N>
