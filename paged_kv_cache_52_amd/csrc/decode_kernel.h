@@ -901,48 +901,52 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int c0 = sb0; c0 < sb1; c0 += kWave) {
       const int c1 = min(sb1, c0 + kWave);
+      // Lane i describes tile c0 + i of the chunk: its byte offset in the
+      // pools and, as bits of wave-wide masks, whether this wave takes it,
+      // whether its rows need no mask on it and whether it lies wholly inside
+      // the workgroup's staged tokens. Each pair step then tests two bits.
+      const int nl = c0 + lane;
+      const bool lane_ok = nl < c1;
       int my_id = 0, own_id = 0;
-      if (lane < c1 - c0) {
-        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
-        if (grouped) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + c0 + lane];
+      if (lane_ok) {
+        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + nl];
+        if (grouped) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + nl];
       }
-      auto block_of = [&](int n) {
-        return min(max(__builtin_amdgcn_readlane(my_id, min(n - c0, kWave - 1)), 0),
-                   last_block);
-      };
+      const int tbl = (b0 + nl) * kBlock;
       // Group entry: this wave takes staged tile n only when it is its own
       // block too and lies wholly inside its rows' tokens and the staged
       // (unzeroed) tokens; the other tiles of its range follow the loop.
-      auto takes = [&](int n) {
-        if (!grouped) return true;
-        const int tb = (b0 + n) * kBlock;
-        return __builtin_amdgcn_readlane(own_id, n - c0) ==
-                   __builtin_amdgcn_readlane(my_id, n - c0) &&
-               tb >= max(rr.ulo, ulo_wg) && tb + kBlock - 1 <= min(rr.uhi, uhi_wg);
-      };
+      const bool took_l = lane_ok && nl >= wb0 && nl < wb1 &&
+                          (!grouped || (own_id == my_id && tbl >= max(rr.ulo, ulo_wg) &&
+                                        tbl + kBlock - 1 <= min(rr.uhi, uhi_wg)));
+      const uint64_t took = __ballot(took_l);
+      const uint64_t plain = __ballot(!rr.needs_mask(tbl));
+      const uint64_t whole = __ballot(lane_ok && tbl >= ulo_wg && tbl + kBlock - 1 <= uhi_wg);
+      // Physical block (clamped: a corrupt table entry reads a wrong but
+      // existing block instead of faulting) as a byte offset into the pools.
+      const uint64_t off_l =
+          ((uint64_t)min(max(my_id, 0), last_block) * p.num_kv_heads + kvh) * (uint64_t)TB;
+      const uint32_t off_lo = (uint32_t)off_l, off_hi = (uint32_t)(off_l >> 32);
       u32x4 kr0 = zero, vr0 = zero, kr1 = zero, vr1 = zero;
-      auto fetch = [&](int n, u32x4 &kr, u32x4 &vr) {
-        const int64_t tile = (int64_t)block_of(n) * p.num_kv_heads + kvh;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char *)p.k_cache + tile * TB, TB);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char *)p.v_cache + tile * TB, TB);
-        kr = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, 0, 0);
-        vr = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, 0, 0);
+      auto fetch = [&](int i, u32x4 &kr, u32x4 &vr) {  // tile c0 + i
+        const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi, i) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane(off_lo, i);
+        kr = *reinterpret_cast<const u32x4 *>((const char *)p.k_cache + off + tid * 16);
+        vr = *reinterpret_cast<const u32x4 *>((const char *)p.v_cache + off + tid * 16);
       };
-      fetch(c0, kr0, vr0);
-      if (c0 + 1 < c1) fetch(c0 + 1, kr1, vr1);
+      fetch(0, kr0, vr0);
+      if (c0 + 1 < c1) fetch(1, kr1, vr1);
       for (int n = c0; n < c1; n += 2) {
-        // Rows of tokens no row of the workgroup attends (and a missing
-        // second tile) are stored as zeros.
-        const int tp = (b0 + n) * kBlock;  // first token of the pair
+        const int i = n - c0;
         // The loaded rows are stored as they are; at the workgroup's range
-        // edges the rows outside it are then overwritten with zeros (a
-        // thread's two LDS stores land in order).
+        // edges the rows outside it (and a missing second tile) are then
+        // overwritten with zeros (a thread's two LDS stores land in order).
         *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
         *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
         *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
         *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
-        if (!(n + 1 < c1 && tp >= ulo_wg && tp + 2 * kBlock - 1 <= uhi_wg)) {  // uniform
-          const int tok0 = tp + srow, tok1 = tok0 + kBlock;
+        if (((whole >> i) & 3u) != 3u) {  // uniform
+          const int tok0 = (b0 + n) * kBlock + srow, tok1 = tok0 + kBlock;
           if (!(tok0 >= ulo_wg && tok0 <= uhi_wg)) {
             *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = zero;
             *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = zero;
@@ -953,14 +957,13 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
           }
         }
         __syncthreads();  // the pair is in LDS
-        if (n + 2 < c1) fetch(n + 2, kr0, vr0);
-        if (n + 3 < c1) fetch(n + 3, kr1, vr1);
-        const bool in0 = n >= wb0 && n < wb1 && takes(n);
-        const bool in1 = n + 1 < c1 && n + 1 >= wb0 && n + 1 < wb1 && takes(n + 1);
-        if (in0 || in1) {
-          const int tb = (b0 + n) * kBlock;
-          st.consume_pair_lds(K0, V0, K1, V1, in0, in1, rr.needs_mask(tb),
-                              rr.needs_mask(tb + kBlock), tb, lo, hi, c, g, sl2);
+        if (n + 2 < c1) fetch(i + 2, kr0, vr0);
+        if (n + 3 < c1) fetch(i + 3, kr1, vr1);
+        const uint32_t tk = (uint32_t)(took >> i) & 3u;
+        if (tk != 0u) {  // uniform
+          const uint32_t pl = (uint32_t)(plain >> i);
+          st.consume_pair_lds(K0, V0, K1, V1, tk & 1u, tk >> 1, !(pl & 1u), !(pl & 2u),
+                              (b0 + n) * kBlock, lo, hi, c, g, sl2);
         }
         __syncthreads();  // every wave is done with the pair
       }
@@ -981,26 +984,26 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) st.acc[jj][r] = slot[(4 * g + r) * D + 8 * c + jj];
       // The tiles of this wave's range it did not take from LDS, from its own
-      // blocks (same test as takes()).
+      // blocks (same test as in the staged loop, one lane per tile; the wave
+      // then visits only the tiles it did not take).
       for (int c0 = wb0; c0 < wb1; c0 += kWave) {
-        const int c1 = min(wb1, c0 + kWave);
+        const int nl = c0 + lane;
+        const bool lane_ok = nl < min(wb1, c0 + kWave);
         int mine = 0, staged_id = -1;
-        if (lane < c1 - c0) {
-          mine = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + c0 + lane];
-          if (c0 + lane >= sb0 && c0 + lane < sb1)
-            staged_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + c0 + lane];
+        if (lane_ok) {
+          mine = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + nl];
+          if (nl >= sb0 && nl < sb1)
+            staged_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + nl];
         }
-        for (int n = c0; n < c1; ++n) {
-          const int tb = (b0 + n) * kBlock;
-          const int id = __builtin_amdgcn_readlane(mine, n - c0);
-          const bool took = n >= sb0 && n < sb1 &&
-                            id == __builtin_amdgcn_readlane(staged_id, n - c0) &&
-                            tb >= max(rr.ulo, ulo_wg) && tb + kBlock - 1 <= min(rr.uhi, uhi_wg);
-          if (!took) {
-            MfmaTile<CT> t;
-            st.template load_tile<0>(t, p, min(max(id, 0), last_block), kvh, koff, voff, soff);
-            eat(t, n);
-          }
+        const int tbl = (b0 + nl) * kBlock;
+        const bool took_l = nl >= sb0 && nl < sb1 && mine == staged_id &&
+                            tbl >= max(rr.ulo, ulo_wg) && tbl + kBlock - 1 <= min(rr.uhi, uhi_wg);
+        for (uint64_t rest = __ballot(lane_ok && !took_l); rest != 0; rest &= rest - 1) {
+          const int i = __builtin_ctzll(rest);
+          MfmaTile<CT> t;
+          st.template load_tile<0>(t, p, min(max(__builtin_amdgcn_readlane(mine, i), 0), last_block),
+                                   kvh, koff, voff, soff);
+          eat(t, c0 + i);
         }
       }
     }

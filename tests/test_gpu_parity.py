@@ -456,9 +456,11 @@ def test_pool_beyond_4gib(cache):
     """A pool whose K and V arrays are each larger than 4 GiB (8 KV heads,
     head_dim 128): the sequences' blocks sit mostly past the 4 GiB byte offset
     of their array, so the write and the split kernel address them with 64-bit
-    offsets. Every sequence is written through the KV write on both sides; the
-    oracle holds only the used blocks, renumbered 0.., which gives the same
-    result (attention does not depend on where a block sits in the pool).
+    offsets (the bf16 pool also with 32 query tokens per sequence, which the
+    split kernel stages through LDS). Every sequence is written through the KV
+    write on both sides; the oracle holds only the used blocks, renumbered
+    0.., which gives the same result (attention does not depend on where a
+    block sits in the pool).
     Written tiles are compared bytewise, outputs against the oracle."""
     print(f"[case] pool beyond 4 GiB, {cache} cache", flush=True)
     Hq, Hkv, D = 32, 8, 128
@@ -539,6 +541,20 @@ def test_pool_beyond_4gib(cache):
             pa().paged_attn_reduce(parts, out)
             torch.cuda.synchronize()
             _check_out(out.cpu().double().numpy(), ref, tol, f"{cache}/T={T}")
+        if cache == "bf16":
+            # 32 query tokens per sequence (128 rows per KV head): the workgroup
+            # stages each tile through LDS and addresses it past 4 GiB as well.
+            q4 = torch.from_numpy(rng.normal(size=(len(lens), 32, Hq, D)).astype(np.float32))
+            q4 = q4.to(q_dt)
+            ref4 = oracle.decode(_np(q4), kc, vc, ctables, lens, scale)
+            for T in (256, None):
+                parts = pa().paged_attn_decode_partial(q4.cuda(), gk, gv, gt, gl, scale,
+                                                       max_context_len=int(lens.max()),
+                                                       split_tokens=T)
+                out = torch.empty(q4.shape, dtype=torch.float32, device="cuda")
+                pa().paged_attn_reduce(parts, out)
+                torch.cuda.synchronize()
+                _check_out(out.cpu().double().numpy(), ref4, tol, f"staged/T={T}")
     finally:
         del gk, gv, gks, gvs
         torch.cuda.empty_cache()
