@@ -1268,8 +1268,13 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     const int Lg = max(0, min(p.context_lens[s + g], lmax));
     return j < splits_of(Lg, Q, W, p.split_tokens) ? rows_of(g) : 0;
   };
+  // The row threads also leave each row's partials index in sm_row (-1: the
+  // row has no split here), so that the dims loop below needs no table reads
+  // or divisions of its own.
+  __shared__ int64_t sm_row[NW][G];
   if ((int)threadIdx.x < rw * G) {
     const int g = threadIdx.x / G, h = threadIdx.x % G;
+    int64_t row = -1;
     if (h < live(g)) {
       const int w0 = g * tw;
       float M = sm_m[w0][h];
@@ -1280,16 +1285,18 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
         sm_m[w0 + w][h] = f;
         lsum = fmaf(f, sm_l[w0 + w][h], lsum);
       }
-      const int64_t row = out_row(g, h);
+      row = out_row(g, h);
       p.part_l[row] = lsum;
       p.part_m[row] = lsum > 0.f ? M * kLn2 : -INFINITY;
     }
+    sm_row[g][h] = row;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < rw * G * (D / 4); idx += NW * kWave) {
     const int g = idx / (G * (D / 4));
     const int h = idx / (D / 4) % G, d = (idx % (D / 4)) * 4;
-    if (h >= live(g)) continue;
+    const int64_t row = sm_row[g][h];
+    if (row < 0) continue;
     const int w0 = g * tw;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < tw; ++w) {
@@ -1298,7 +1305,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = fmaf(f, v[e], a[e]);
     }
-    *(f32x4 *)(p.part_acc + out_row(g, h) * D + d) = a;
+    *(f32x4 *)(p.part_acc + row * D + d) = a;
   }
 }
 
