@@ -729,6 +729,7 @@ struct MfmaWave {
   // O column block JJ holds dims 16JJ .. 16JJ + 15 here (lane c: dim 16JJ + c).
   // V rows no row of the workgroup attends are zero in LDS, so a zero weight
   // never meets a NaN.
+  template <int PRIO = 0>
   __device__ __forceinline__ void consume_pair_lds(const char *k0, const char *v0,
                                                    const char *k1, const char *v1, bool in0,
                                                    bool in1, bool m0, bool m1, int tb, int lo,
@@ -742,9 +743,9 @@ struct MfmaWave {
     // LDS rows hold never reaches a weight. The logits stay raw q.k sums (q
     // carries the scale's sign, so scale_log2 > 0 here): the maximum is taken
     // on them and scaled once, and each weight is exp2(fma(sum, scale, -m)).
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(PRIO + 1);
     scores2_lds(k0, k1, z0, z1, c, g);
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(PRIO);
     if (!(in0 && in1) || m0 || m1) {  // uniform
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -762,7 +763,7 @@ struct MfmaWave {
     weights_plain(z1, h1, l1, scale_log2);
     const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
     const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(PRIO + 1);
     pv32_lds<0>(v0, v1, c, g, phi, plo);
     pv32_lds<1>(v0, v1, c, g, phi, plo);
     pv32_lds<2>(v0, v1, c, g, phi, plo);
@@ -771,7 +772,7 @@ struct MfmaWave {
     pv32_lds<5>(v0, v1, c, g, phi, plo);
     pv32_lds<6>(v0, v1, c, g, phi, plo);
     pv32_lds<7>(v0, v1, c, g, phi, plo);
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(PRIO);
   }
 
   // Tokens of this lane's row outside [lo, hi] get -inf (tile at tb).
@@ -899,75 +900,89 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
     const int srow = tid / 16, scol = (tid % 16) * 16;
     constexpr int TB = kBlock * 256;  // bytes of a bf16 K or V tile in memory
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int c0 = sb0; c0 < sb1; c0 += kWave) {
-      const int c1 = min(sb1, c0 + kWave);
-      // Lane i describes tile c0 + i of the chunk: its byte offset in the
-      // pools and, as bits of wave-wide masks, whether this wave takes it,
-      // whether its rows need no mask on it and whether it lies wholly inside
-      // the workgroup's staged tokens. Each pair step then tests two bits.
-      const int nl = c0 + lane;
-      const bool lane_ok = nl < c1;
-      int my_id = 0, own_id = 0;
-      if (lane_ok) {
-        my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + nl];
-        if (grouped) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + nl];
-      }
-      const int tbl = (b0 + nl) * kBlock;
-      // Group entry: this wave takes staged tile n only when it is its own
-      // block too and lies wholly inside its rows' tokens and the staged
-      // (unzeroed) tokens; the other tiles of its range follow the loop.
-      const bool took_l = lane_ok && nl >= wb0 && nl < wb1 &&
-                          (!grouped || (own_id == my_id && tbl >= max(rr.ulo, ulo_wg) &&
-                                        tbl + kBlock - 1 <= min(rr.uhi, uhi_wg)));
-      const uint64_t took = __ballot(took_l);
-      const uint64_t plain = __ballot(!rr.needs_mask(tbl));
-      const uint64_t whole = __ballot(lane_ok && tbl >= ulo_wg && tbl + kBlock - 1 <= uhi_wg);
-      // Physical block (clamped: a corrupt table entry reads a wrong but
-      // existing block instead of faulting) as a byte offset into the pools.
-      const uint64_t off_l =
-          ((uint64_t)min(max(my_id, 0), last_block) * p.num_kv_heads + kvh) * (uint64_t)TB;
-      const uint32_t off_lo = (uint32_t)off_l, off_hi = (uint32_t)(off_l >> 32);
-      u32x4 kr0 = zero, vr0 = zero, kr1 = zero, vr1 = zero;
-      auto fetch = [&](int i, u32x4 &kr, u32x4 &vr) {  // tile c0 + i
-        const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi, i) << 32) |
-                             (uint32_t)__builtin_amdgcn_readlane(off_lo, i);
-        kr = *reinterpret_cast<const u32x4 *>((const char *)p.k_cache + off + tid * 16);
-        vr = *reinterpret_cast<const u32x4 *>((const char *)p.v_cache + off + tid * 16);
-      };
-      fetch(0, kr0, vr0);
-      if (c0 + 1 < c1) fetch(1, kr1, vr1);
-      for (int n = c0; n < c1; n += 2) {
-        const int i = n - c0;
-        // The loaded rows are stored as they are; at the workgroup's range
-        // edges the rows outside it (and a missing second tile) are then
-        // overwritten with zeros (a thread's two LDS stores land in order).
-        *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
-        *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
-        *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
-        *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
-        if (((whole >> i) & 3u) != 3u) {  // uniform
-          const int tok0 = (b0 + n) * kBlock + srow, tok1 = tok0 + kBlock;
-          if (!(tok0 >= ulo_wg && tok0 <= uhi_wg)) {
-            *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = zero;
-            *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = zero;
-          }
-          if (!(n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg)) {
-            *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = zero;
-            *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = zero;
-          }
+    // The walk, instantiated twice: a group entry's walk holds a raised wave
+    // priority throughout (2, and 3 around its matrix-core blocks). Its items
+    // are the launch's longest and share the SIMDs with plain decode items;
+    // favouring them shortens the launch. Other staged walks use 0 and 1.
+    auto walk = [&](auto prio) {
+      constexpr int PRIO = decltype(prio)::value;
+      constexpr bool kGroup = PRIO > 0;  // walk<2> runs group entries only
+      __builtin_amdgcn_s_setprio(PRIO);
+      for (int c0 = sb0; c0 < sb1; c0 += kWave) {
+        const int c1 = min(sb1, c0 + kWave);
+        // Lane i describes tile c0 + i of the chunk: its byte offset in the
+        // pools and, as bits of wave-wide masks, whether this wave takes it,
+        // whether its rows need no mask on it and whether it lies wholly inside
+        // the workgroup's staged tokens. Each pair step then tests two bits.
+        const int nl = c0 + lane;
+        const bool lane_ok = nl < c1;
+        int my_id = 0, own_id = 0;
+        if (lane_ok) {
+          my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + nl];
+          if (kGroup) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + nl];
         }
-        __syncthreads();  // the pair is in LDS
-        if (n + 2 < c1) fetch(i + 2, kr0, vr0);
-        if (n + 3 < c1) fetch(i + 3, kr1, vr1);
-        const uint32_t tk = (uint32_t)(took >> i) & 3u;
-        if (tk != 0u) {  // uniform
-          const uint32_t pl = (uint32_t)(plain >> i);
-          st.consume_pair_lds(K0, V0, K1, V1, tk & 1u, tk >> 1, !(pl & 1u), !(pl & 2u),
-                              (b0 + n) * kBlock, lo, hi, c, g, sl2);
+        const int tbl = (b0 + nl) * kBlock;
+        // Group entry: this wave takes staged tile n only when it is its own
+        // block too and lies wholly inside its rows' tokens and the staged
+        // (unzeroed) tokens; the other tiles of its range follow the loop.
+        const bool took_l = lane_ok && nl >= wb0 && nl < wb1 &&
+                            (!kGroup || (own_id == my_id && tbl >= max(rr.ulo, ulo_wg) &&
+                                          tbl + kBlock - 1 <= min(rr.uhi, uhi_wg)));
+        const uint64_t took = __ballot(took_l);
+        const uint64_t plain = __ballot(!rr.needs_mask(tbl));
+        const uint64_t whole = __ballot(lane_ok && tbl >= ulo_wg && tbl + kBlock - 1 <= uhi_wg);
+        // Physical block (clamped: a corrupt table entry reads a wrong but
+        // existing block instead of faulting) as a byte offset into the pools.
+        const uint64_t off_l =
+            ((uint64_t)min(max(my_id, 0), last_block) * p.num_kv_heads + kvh) * (uint64_t)TB;
+        const uint32_t off_lo = (uint32_t)off_l, off_hi = (uint32_t)(off_l >> 32);
+        u32x4 kr0 = zero, vr0 = zero, kr1 = zero, vr1 = zero;
+        auto fetch = [&](int i, u32x4 &kr, u32x4 &vr) {  // tile c0 + i
+          const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(off_hi, i) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane(off_lo, i);
+          kr = *reinterpret_cast<const u32x4 *>((const char *)p.k_cache + off + tid * 16);
+          vr = *reinterpret_cast<const u32x4 *>((const char *)p.v_cache + off + tid * 16);
+        };
+        fetch(0, kr0, vr0);
+        if (c0 + 1 < c1) fetch(1, kr1, vr1);
+        for (int n = c0; n < c1; n += 2) {
+          const int i = n - c0;
+          // The loaded rows are stored as they are; at the workgroup's range
+          // edges the rows outside it (and a missing second tile) are then
+          // overwritten with zeros (a thread's two LDS stores land in order).
+          *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = kr0;
+          *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = vr0;
+          *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = kr1;
+          *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = vr1;
+          if (((whole >> i) & 3u) != 3u) {  // uniform
+            const int tok0 = (b0 + n) * kBlock + srow, tok1 = tok0 + kBlock;
+            if (!(tok0 >= ulo_wg && tok0 <= uhi_wg)) {
+              *reinterpret_cast<u32x4 *>(K0 + srow * kStageRow + scol) = zero;
+              *reinterpret_cast<u32x4 *>(V0 + srow * kStageRow + scol) = zero;
+            }
+            if (!(n + 1 < c1 && tok1 >= ulo_wg && tok1 <= uhi_wg)) {
+              *reinterpret_cast<u32x4 *>(K1 + srow * kStageRow + scol) = zero;
+              *reinterpret_cast<u32x4 *>(V1 + srow * kStageRow + scol) = zero;
+            }
+          }
+          __syncthreads();  // the pair is in LDS
+          if (n + 2 < c1) fetch(i + 2, kr0, vr0);
+          if (n + 3 < c1) fetch(i + 3, kr1, vr1);
+          const uint32_t tk = (uint32_t)(took >> i) & 3u;
+          if (tk != 0u) {  // uniform
+            const uint32_t pl = (uint32_t)(plain >> i);
+            st.template consume_pair_lds<PRIO>(K0, V0, K1, V1, tk & 1u, tk >> 1, !(pl & 1u),
+                                               !(pl & 2u), (b0 + n) * kBlock, lo, hi, c, g, sl2);
+          }
+          __syncthreads();  // every wave is done with the pair
         }
-        __syncthreads();  // every wave is done with the pair
       }
-    }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    if (grouped)
+      walk(std::integral_constant<int, 2>{});
+    else
+      walk(std::integral_constant<int, 0>{});
     if (grouped) {
       // O's columns leave the staged loop in the transpose-read order (block
       // jj = dims 16jj .. 16jj+15, lane c: dim 16jj + c); the unstaged tiles
