@@ -91,33 +91,34 @@ __device__ __forceinline__ void put_entry(const PlanParams &p, int idx, int w0, 
 // Join flags of the full split j of sequence s: bit c (c < M) is set when
 // sequence s + c takes part in the group of sequence s + c - 1 for split j,
 // that is when both splits are full and start on the same physical block.
-// Lengths of sequences s - 1 .. s + M - 1 come from the chunk's lengths in LDS
-// (sequences base .. base + kPlanThreads - 1) or, past the chunk, from global
-// memory; their table words at block jb are loaded in the same round (a word
-// of a sequence whose split j is not full is read but not used).
+// Split counts of sequences s - 1 .. s + M - 1 come from the chunk's counts in
+// LDS (sequences base .. base + kPlanThreads - 1) or, past the chunk, from
+// their lengths in global memory; their table words at block jb are loaded in
+// the same round (a word of a sequence whose split j is not full is read but
+// not used).
 __device__ __forceinline__ int join_bits(const PlanParams &p, int s, int j, int base,
-                                         const int (&chunk_len)[kPlanThreads]) {
+                                         const int (&chunk_splits)[kPlanThreads]) {
   constexpr int kMax = PA_MAX_GROUP_MEMBERS;
   const int M = p.group_members;
   const int jb = j * (p.split_tokens / kBlock);  // first block of split j (no window: base 0)
-  int len[kMax + 1], blk[kMax + 1];
+  int nsp[kMax + 1], blk[kMax + 1];
 #pragma unroll
   for (int c = 0; c <= kMax; ++c) {
     const int t = s - 1 + c;
     const bool seq = c <= M && t >= 0 && t < p.num_seqs;
-    len[c] = 0;
+    nsp[c] = 0;
     blk[c] = -1;
     if (seq) {
-      len[c] = t >= base && t < base + kPlanThreads ? chunk_len[t - base] : clamp_len(p, t);
+      nsp[c] = t >= base && t < base + kPlanThreads
+                   ? chunk_splits[t - base]
+                   : seq_splits(p, clamp_len(p, t), p.num_query_tokens);
       if (jb < p.max_blocks_per_seq)
         blk[c] = p.block_tables[(int64_t)t * p.max_blocks_per_seq + jb];
     }
   }
   bool full[kMax + 1];
 #pragma unroll
-  for (int c = 0; c <= kMax; ++c)
-    full[c] = c <= M && s - 1 + c >= 0 && s - 1 + c < p.num_seqs &&
-              j < seq_splits(p, len[c], p.num_query_tokens) - 1;
+  for (int c = 0; c <= kMax; ++c) full[c] = j < nsp[c] - 1;
   int bits = 0;
 #pragma unroll
   for (int c = 0; c < kMax; ++c)
@@ -144,6 +145,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   __shared__ int chunk_first[kPlanThreads];  // first entry of each sequence of the chunk
   __shared__ int chunk_len[kPlanThreads];
   __shared__ int chunk_per[kPlanThreads];    // entries per split of each sequence
+  __shared__ int chunk_splits[kPlanThreads]; // splits of each sequence
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
@@ -182,6 +184,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     chunk_first[tid] = before + incl - f;  // offset inside the chunk
     chunk_len[tid] = sp.L;
     chunk_per[tid] = max(sp.per_split, 1);
+    chunk_splits[tid] = sp.splits;
     __syncthreads();
     const int base_entry = carry;
     if (p.group_members <= 1) {
@@ -210,7 +213,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
           word0 = entry_word(s_e, j);
           L_e = chunk_len[lo];
           const int pos = s_e % M;
-          const int bits = join_bits(p, s_e, j, base, chunk_len);
+          const int bits = join_bits(p, s_e, j, base, chunk_splits);
           keep = !(pos > 0 && (bits & 1));
           if (keep)
             while (pos + cnt < M && ((bits >> cnt) & 1)) ++cnt;
