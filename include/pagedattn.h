@@ -80,6 +80,13 @@
  *   - Thread safety: the library keeps no mutable global state, except the
  *     per-device address table of paged_attn_decode_noalloc's fixed scratch
  *     (guarded by a mutex; see that call).
+ *   - Launch trace (a debugging aid): PAGEDATTN_TRACE in the environment, read
+ *     once per process, is a level. At 1 every entry point and kernel launch
+ *     prints one line of its parameters and grid to stderr. At 2 the plan
+ *     calls (paged_attn_plan, paged_decode_prepare and the calls built on
+ *     them) also synchronise `stream` and copy the plan back to print its
+ *     list, so level 2 breaks the no-synchronisation rule above and cannot
+ *     run under graph capture. Unset or 0: no output and no effect.
  */
 #ifndef PAGEDATTN_H_
 #define PAGEDATTN_H_

@@ -2,6 +2,9 @@
 // The operations and their conventions are documented in include/pagedattn.h.
 #include <limits.h>
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
@@ -101,6 +104,74 @@ int compute_units(hipStream_t stream) {
   n = std::max(n, 1);
   if (dev >= 0 && dev < kMaxDevices) known[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+int trace_level() {
+  static const int level = [] {
+    const char *e = getenv("PAGEDATTN_TRACE");
+    return e ? atoi(e) : 0;
+  }();
+  return level;
+}
+
+void trace(const char *fmt, ...) {
+  if (trace_level() <= 0) return;
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[pagedattn] %s\n", line);
+}
+
+const char *dtype_name(int dtype) {
+  switch (dtype) {
+    case PA_F32: return "f32";
+    case PA_BF16: return "bf16";
+    case PA_I8: return "int8";
+    case PA_FP8: return "fp8";
+    default: return "?";
+  }
+}
+
+// Trace level 2: wait for the plan just launched on `stream` and print its
+// list (header, group entries, the first entries). Reads through fixed stack
+// buffers: nothing is allocated.
+void trace_plan(const int32_t *sched, int64_t capacity, hipStream_t stream) {
+  if (trace_level() < 2) return;
+  int32_t head[kSchedHeader];
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(head, sched, sizeof head, hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    trace("plan: could not be read back");
+    return;
+  }
+  const int64_t n = std::min<int64_t>(head[0], capacity);
+  constexpr int kChunk = 1024;
+  int32_t buf[2 * kChunk];
+  int64_t groups = 0;
+  char first[256] = "";
+  int used = 0;
+  for (int64_t i0 = 0; i0 < n; i0 += kChunk) {
+    const int64_t cnt = std::min<int64_t>(kChunk, n - i0);
+    if (hipMemcpy(buf, sched + kSchedHeader + 2 * i0, (size_t)cnt * 2 * sizeof(int32_t),
+                  hipMemcpyDeviceToHost) != hipSuccess) {
+      (void)hipGetLastError();
+      trace("plan: could not be read back");
+      return;
+    }
+    for (int64_t i = 0; i < cnt; ++i) {
+      if (buf[2 * i + 1] < 0 && head[6] > 1) ++groups;
+      if (i0 + i < 6 && used < (int)sizeof first - 48)
+        used += snprintf(first + used, sizeof first - used, " (s %u, j %u, %d)",
+                         (uint32_t)buf[2 * i] >> 16, (uint32_t)buf[2 * i] & 0xffffu,
+                         buf[2 * i + 1]);
+    }
+  }
+  trace("plan: %lld entries (%lld group entries of up to %d sequences), split %d tokens, %d "
+        "sequences, length bound %d, %d query tokens, window %d; first:%s",
+        (long long)n, (long long)groups, head[6], head[1], head[2], head[3], head[4], head[5],
+        first);
 }
 
 int resident_per_cu(const void *kernel, int threads) {
@@ -302,6 +373,9 @@ int paged_kv_write(const void *k, const void *v, int32_t in_dtype, const int64_t
   const int st = check_write(k, v, in_dtype, slot_mapping, num_tokens, num_kv_heads, head_dim,
                              k_cache, v_cache, k_scale, v_scale, num_blocks, cache_dtype, &w);
   if (st != PA_OK || num_tokens == 0) return st;
+  pa::trace("paged_kv_write: %lld tokens x %d KV heads x %d dims, %s into a %s cache of %lld "
+            "blocks", (long long)num_tokens, num_kv_heads, head_dim, pa::dtype_name(in_dtype),
+            pa::dtype_name(cache_dtype), (long long)num_blocks);
   return launch_status(pa::launch_kv_write(w, stream));
 }
 
@@ -316,7 +390,14 @@ int paged_attn_plan(const int32_t *context_lens, const int32_t *query_start,
                             q_heads_per_kv, sliding_window, split_tokens, group_members, sched,
                             &pl);
   if (st != PA_OK || num_seqs == 0) return st;
-  return launch_status(pa::launch_plan(pl, stream));
+  pa::trace("paged_attn_plan: %d sequences, length bound %d, %d query tokens%s (g %d), "
+            "window %d, split %d tokens, group members %d, capacity %lld entries", num_seqs,
+            max_context_len, num_query_tokens, query_start ? " packed" : " each",
+            query_start ? q_heads_per_kv : 0, sliding_window, split_tokens, group_members,
+            (long long)pl.capacity);
+  const int ls = launch_status(pa::launch_plan(pl, stream));
+  if (ls == PA_OK) pa::trace_plan(sched, pl.capacity, stream);
+  return ls;
 }
 
 int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
@@ -339,7 +420,14 @@ int paged_decode_prepare(const void *k, const void *v, int32_t in_dtype,
                   split_tokens, group_members, sched, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return num_tokens == 0 ? PA_OK : launch_status(pa::launch_kv_write(w, stream));
-  return launch_status(pa::launch_prepare(w, pl, stream));
+  pa::trace("paged_decode_prepare: %lld new tokens (%s into %s), %d sequences, length bound %d, "
+            "%d query tokens%s (g %d), window %d, split %d tokens, group members %d",
+            (long long)num_tokens, pa::dtype_name(in_dtype), pa::dtype_name(cache_dtype),
+            num_seqs, max_context_len, num_query_tokens, query_start ? " packed" : " each",
+            query_start ? q_heads_per_kv : 0, sliding_window, split_tokens, group_members);
+  const int ls = launch_status(pa::launch_prepare(w, pl, stream));
+  if (ls == PA_OK) pa::trace_plan(sched, pl.capacity, stream);
+  return ls;
 }
 
 int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
@@ -421,6 +509,13 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   p.query_start = query_start;
   p.sched = sched;
   p.scale_log2 = scale * 1.4426950408889634f;
+  pa::trace("paged_attn_decode_partial: q %s, cache %s, %d sequences x %d query tokens%s, %d/%d "
+            "heads, D %d, window %d, split %d tokens, %d partial slots per row (%d needed), %lld "
+            "possible entries x %lld items each", pa::dtype_name(q_dtype),
+            pa::dtype_name(cache_dtype), num_seqs, num_query_tokens,
+            packed ? " (packed total)" : "", num_q_heads, num_kv_heads, head_dim,
+            sliding_window, split_tokens, max_splits, grid_splits, (long long)max_entries,
+            (long long)per_entry);
 
   hipError_t e;
   if (q_dtype == PA_BF16 && cache_dtype == PA_BF16)
@@ -459,6 +554,9 @@ int paged_attn_reduce(const float *part_m, const float *part_l, const float *par
                      head_dim, split_tokens, max_splits, out_dtype, num_query_tokens,
                      sliding_window, query_start,
                      clamped_bound(max_context_len, max_blocks_per_seq)};
+  pa::trace("paged_attn_reduce: %d sequences x %d query tokens%s x %d heads, D %d, %d partial "
+            "slots per row, out %s", num_seqs, num_query_tokens, packed ? " (packed total)" : "",
+            num_q_heads, head_dim, max_splits, pa::dtype_name(out_dtype));
   return launch_status(pa::launch_reduce(p, stream));
 }
 

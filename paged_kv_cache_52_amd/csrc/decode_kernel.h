@@ -1463,6 +1463,14 @@ int compute_units(hipStream_t stream);
 // decide; cached per kernel by the caller).
 int resident_per_cu(const void *kernel, int threads);
 
+// Launch tracing: PAGEDATTN_TRACE in the environment (read once per process)
+// is the level. At 1 every entry point and kernel launch prints one line of
+// its parameters and grid to stderr; at 2 a plan is also waited for and its
+// list printed. 0 or unset: silent.
+int trace_level();
+void trace(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+const char *dtype_name(int dtype);
+
 template <int QT, int CT, int D, int G>
 hipError_t launch_decode(DecodeParams p, int64_t max_items, hipStream_t stream) {
   constexpr int NW = kDecodeWaves;
@@ -1485,6 +1493,12 @@ hipError_t launch_decode(DecodeParams p, int64_t max_items, hipStream_t stream) 
   const int64_t w = std::max<int64_t>(1, std::min<int64_t>(per_cu, max_items / nb));
   p.num_bins = (int32_t)nb;
   p.bin_wgs = (int32_t)w;
+  if (trace_level() > 0)
+    trace("split kernel: %s engine, q %s, cache %s, D %d, %d rows per row group; %lld "
+          "workgroups of %d waves (one per possible item), %lld bins x %lld dealt, %d resident "
+          "per CU",
+          MfmaEligible<CT, D>::value && QT == PA_BF16 ? "MFMA" : "VALU", dtype_name(QT),
+          dtype_name(CT), D, G, (long long)max_items, NW, (long long)nb, (long long)w, per_cu);
   if constexpr (kMfmaBound)
     hipLaunchKernelGGL((decode_split_kernel_mfma<QT, CT, D, G, NW>), dim3((unsigned)max_items),
                        dim3(NW * kWave), 0, stream, p);
