@@ -162,7 +162,7 @@ int32_t pa_max_splits(int32_t max_context_len, int32_t num_query_tokens, int32_t
  * still fill the device); with more than 64 query rows per KV head it is then
  * doubled, up to 4096, while items stay >= 1024 (fewer partials to write);
  * with at most 8 query rows per KV head, or at most 16 with several query
- * tokens (a decode step, multi-token included) it then grows by 256 tokens at
+ * tokens (a decode step, multi-token included) it then grows by 64 tokens at
  * a time, up to 4096, while items stay >= 2048 and
  * T * 2 * head_dim * element bytes (the K/V codes of a split and KV head)
  * stays <= 1 MiB.

@@ -77,7 +77,7 @@ constexpr int32_t kMinDefaultSplit = 64;  // smallest split the default picks
 constexpr int64_t kMinWorkItems = 1024;   // (split, KV head) items the default aims for
 constexpr int64_t kGrowWorkItems = 2048;  // items a decode step keeps when its splits grow
 constexpr int64_t kGrowMaxBytes = 1 << 20;  // K/V bytes per (split, KV head) growth stops at
-constexpr int32_t kGrowStep = 256;          // tokens a decode step's split grows by
+constexpr int32_t kGrowStep = 64;           // tokens a decode step's split grows by
 
 }  // namespace
 

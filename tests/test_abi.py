@@ -64,15 +64,15 @@ def test_default_split_tokens_is_valid(lib):
 
 
 @pytest.mark.parametrize("B,Hkv,D,dt,L,T", [
-    # Byte-sized (256 KiB of K/V per split and KV head), then grown by 256
+    # Byte-sized (256 KiB of K/V per split and KV head), then grown by 64
     # tokens while 2048 items remain and a split's K/V stays within 1 MiB per
     # KV head.
-    (64, 8, 128, BF16, 4096, 1280),     # 8B-shaped bf16 batch: 4 splits of 1280 = 2048 items,
-                                        # 3 of 1536 would leave 1536
+    (64, 8, 128, BF16, 4096, 1344),     # 8B-shaped bf16 batch: 4 splits of 1344 = 2048 items,
+                                        # 3 of 1408 would leave 1536
     (8, 8, 128, BF16, 131072, 2048),    # long contexts: 4096 would be 2 MiB per split
     (128, 8, 128, I8, 8192, 4096),      # INT8: 1024, doubled twice (1 MiB of codes at 4096)
     (256, 4, 128, BF16, 18385, 2048),   # 256 sequences at g = 4: stops at 1 MiB
-    (64, 8, 64, F32, 4096, 1280),       # 64-dim fp32: 512 B per token, like bf16 x 128
+    (64, 8, 64, F32, 4096, 1344),       # 64-dim fp32: 512 B per token, like bf16 x 128
     (64, 8, 128, F32, 4096, 1024),      # 256, grown to 1024 (1 MiB per split)
     (64, 8, 64, I8, 4096, 2048),        # 512 items at 4096: stops at 2048
     (128, 8, 128, FP8, 8192, 4096),     # FP8: same bytes per token as INT8
@@ -86,11 +86,11 @@ def test_default_split_tokens_values(lib, B, Hkv, D, dt, L, T):
 
 def test_default_split_tokens_grow_with_query_rows(lib):
     # 16 rows per KV head (4 query tokens at g = 4, or g = 16): 512 KiB, 1024 tokens;
-    # several query tokens then grow like a one-token step (4 splits of 1280 =
+    # several query tokens then grow like a one-token step (4 splits of 1344 =
     # 2048 items), one query token at g = 16 stays.
-    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 4, 0) == 1280
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 4, 0) == 1344
     assert lib.pa_default_split_tokens(256, 64, 4, 128, BF16, 18385, 1, 0) == 1024
-    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 2, 0) == 1280  # 8 rows
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 2, 0) == 1344  # 8 rows
     assert lib.pa_default_split_tokens(128, 32, 8, 128, I8, 8192, 4, 0) == 4096  # 1 MiB cap
 
 
@@ -98,15 +98,15 @@ def test_default_split_tokens_for_prefill_chunks(lib):
     # 8 sequences x 8 KV heads x 512 query tokens x g = 4: 32 sets of 64 rows per
     # KV head, so even 4096-token splits leave 8*8*32*2 = 4096 items at L = 8192.
     assert lib.pa_default_split_tokens(8, 32, 8, 128, BF16, 8192, 512, 0) == 4096
-    # One query token: the decode growth only (512 grown to 1280).
-    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 1, 0) == 1280
+    # One query token: the decode growth only (512 grown to 1344).
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 4096, 1, 0) == 1344
 
 
 def test_default_split_tokens_with_window(lib):
     # 64 seqs x 8 heads, window 4096: ranges of at most 4111 tokens, 4 splits of
-    # 1280 -> 2048 items, 3 of 1536 -> 1536, so T grows to 1280 only; a
+    # 1344 -> 2048 items, 3 of 1408 -> 1536, so T grows to 1344 only; a
     # 128-token window on 8 seqs shrinks T.
-    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 65536, 1, 4096) == 1280
+    assert lib.pa_default_split_tokens(64, 32, 8, 128, BF16, 65536, 1, 4096) == 1344
     assert lib.pa_default_split_tokens(8, 32, 8, 128, BF16, 65536, 1, 128) == 64
 
 
