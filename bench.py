@@ -25,6 +25,7 @@ the library's read probe on the same device.
 import argparse
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -71,13 +72,22 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source without its comments and blank space."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the library's sources (code only: comments and blank space do
+    not count), which keys the stored counters to the code they were taken
+    from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_52_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "pagedattn.h"), "rb").read())
+    paths = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h"))]
+    for path in paths + [os.path.join(ROOT, "include", "pagedattn.h")]:
+        h.update(_code_only(open(path, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

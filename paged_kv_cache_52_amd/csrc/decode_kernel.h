@@ -735,9 +735,10 @@ struct MfmaWave {
                                                    bool in1, bool m0, bool m1, int tb, int lo,
                                                    int hi, int c, int g, float scale_log2) {
     float z0[4], z1[4];
-    // The matrix-core blocks (logits, then P.V) run at a raised wave priority
-    // and the softmax between them at the normal one, so that a SIMD's waves
-    // tend to alternate between the two phases instead of bunching up in one.
+    // The matrix-core blocks (logits, then P.V) run one wave-priority level
+    // above the walk's own (PRIO) and the softmax between them at PRIO, so
+    // that a SIMD's waves tend to alternate between the two phases instead of
+    // bunching up in one.
     // Both tiles' logits are computed (two independent MFMA chains); a tile
     // outside this wave's range then gets -inf by select, so whatever its
     // LDS rows hold never reaches a weight. The logits stay raw q.k sums (q
@@ -932,7 +933,9 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         const uint64_t plain = __ballot(!rr.needs_mask(tbl));
         const uint64_t whole = __ballot(lane_ok && tbl >= ulo_wg && tbl + kBlock - 1 <= uhi_wg);
         // Physical block (clamped: a corrupt table entry reads a wrong but
-        // existing block instead of faulting) as a byte offset into the pools.
+        // existing block instead of faulting) as a byte offset into the pools;
+        // with the clamp every fetch below stays inside the pool, so it is a
+        // plain load rather than one through a tile-sized buffer descriptor.
         const uint64_t off_l =
             ((uint64_t)min(max(my_id, 0), last_block) * p.num_kv_heads + kvh) * (uint64_t)TB;
         const uint32_t off_lo = (uint32_t)off_l, off_hi = (uint32_t)(off_l >> 32);
