@@ -23,3 +23,14 @@ def test_more_than_one_gpu_is_refused():
 def test_multi_rank_launch_is_refused():
     r = _run(["--gpus", "1"], {"WORLD_SIZE": "2"})
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments():
+    """Stored counters are keyed by the sources' code: a comment or blank-space
+    edit keeps the key, a code edit changes it."""
+    import bench
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* plain */\n}\n"
+    b = "int f(int x) {\n  // doubles its argument\n  return 2 * x;\n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
