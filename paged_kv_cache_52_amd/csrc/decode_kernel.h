@@ -367,11 +367,13 @@ struct DecodeWave {
 //     into the B operand;
 //   - O: heads 4g .. 4g+3, dims 8c + jj.
 // P is split into bf16 hi + lo parts (two MFMAs) so that the softmax weights
-// keep ~16 significant bits. The running max is shared by the four lane groups
-// of a head (two cross-row max steps per tile) and is only moved when a tile's
-// max exceeds it by more than kRescaleSlack (exp2 arguments stay <= that
-// slack); the true max is tracked on the side and the state is renormalised
-// to it once, at the end of the split.
+// keep ~16 significant bits. The reference max is shared by the four lane
+// groups of a head and is only moved when a tile's max exceeds it by more than
+// kRescaleSlack (exp2 arguments stay <= that slack). Each lane tests its own
+// tokens against it, so the cross-row max steps run only when some lane's
+// logits pass the limit; the true max is tracked per lane on the side, and
+// at the end of the split the head's true max (across its four lanes) is the
+// one the state is renormalised to.
 //
 // INT8 codes x are fed as u = x + 128 (x ^ 0x80 per byte), which bf16 holds
 // exactly, and the bias is removed algebraically: q.x = q.u - 128 sum(q) per
@@ -466,7 +468,8 @@ struct MfmaWave {
   u32x4 qB[4];   // q operand: head c (zero beyond the group), the K operand's dims
   f32x4 acc[8];  // O: heads 4g + r, dims 8c + jj
   float m;       // reference max (log2 units) of head c
-  float mtrue;   // true running max of head c
+  float mlim;    // m + kRescaleSlack: logits above it move m
+  float mtrue;   // true running max of head c over this lane's tokens
   float l;       // sum of exp2(z - m) over this lane's tokens of head c
   float wsum;    // INT8: sum of exp2(z - m) * vscale over this lane's tokens
   float qbias;   // INT8: 128 * sum_d q[c][d]
@@ -568,15 +571,18 @@ struct MfmaWave {
   }
 
   // Running max of head c over a step's logits (bm: this lane's maximum, of
-  // logits that still need the factor `scale` > 0): the maximum over the four
-  // lane groups, and a rescale when it passes the reference by more than the
-  // slack.
+  // logits that still need the factor `scale` > 0). The lane's true max takes
+  // it as it is; only when some lane passes the reference by more than the
+  // slack does the wave form each head's maximum over its four lane groups
+  // (scaling commutes with the maximum, as rounding is monotonic) and rescale
+  // the heads that passed.
   __device__ __forceinline__ void update_max(float bm, int g, float scale = 1.f) {
-    bm = xor_max_raw<16>(bm);
-    bm = xor_max_raw<32>(bm) * scale;
+    bm *= scale;
     mtrue = max_raw(mtrue, bm);
-    const bool grow = bm > m + kRescaleSlack;
-    if (__any(grow)) rescale(grow ? bm : m, g);
+    if (__any(bm > mlim)) {  // uniform
+      bm = xor_max_raw<32>(xor_max_raw<16>(bm));
+      rescale(bm > mlim ? bm : m, g);
+    }
   }
 
   // Softmax weights of one tile's logits, added to l (and, INT8, wsum); for
@@ -807,6 +813,7 @@ struct MfmaWave {
     l *= alpha;
     wsum *= alpha;
     m = mnew;
+    mlim = mnew + kRescaleSlack;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float ar = __shfl(alpha, 4 * g + r);
@@ -879,6 +886,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) st.acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = kNegBig;
+  st.mlim = kNegBig + kRescaleSlack;
   st.mtrue = kNegBig;
   st.l = 0.f;
   st.wsum = 0.f;
@@ -1042,9 +1050,10 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
       eat(t, n);
     }
   }
-  // Renormalise to the true max (every lane takes part: rescale reads other
-  // lanes' factors), then sum l over the four lane groups.
-  st.rescale(fmaxf(st.mtrue, st.m), g);
+  // Renormalise to the head's true max, the largest of its four lanes' (every
+  // lane takes part: rescale reads other lanes' factors), then sum l over the
+  // four lane groups.
+  st.rescale(fmaxf(xor_max_raw<32>(xor_max_raw<16>(st.mtrue)), st.m), g);
   const float lt = xor_sum<32>(xor_sum<16>(st.l));
   if constexpr (CT == PA_I8) {
     // Remove the code bias from O: row 4g + r loses 128 * (its head's wsum).
