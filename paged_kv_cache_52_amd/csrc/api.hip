@@ -506,6 +506,9 @@ int paged_attn_decode_partial(const void *q, int32_t q_dtype, int32_t num_seqs,
   p.num_query_tokens = num_query_tokens;
   p.window = sliding_window;
   p.group = num_q_heads / num_kv_heads;
+  p.group_shift = __builtin_ctz((unsigned)p.group);
+  p.fd_split = pa::FastDiv::make((uint32_t)split_tokens);
+  p.fd_kv_heads = pa::FastDiv::make((uint32_t)num_kv_heads);
   p.query_start = query_start;
   p.sched = sched;
   p.scale_log2 = scale * 1.4426950408889634f;

@@ -50,10 +50,16 @@ struct DecodeParams {
                              // the packed total with query_start
   int32_t window;            // sliding window in tokens, 0 = none
   int32_t group;             // g = num_q_heads / num_kv_heads
+  int32_t group_shift;       // log2(g) (g is a power of two)
   int32_t head_groups;  // uniform Q: workgroups per (split, KV head), rw row groups each
   int32_t rw;           // uniform Q: row groups of G rows per workgroup (1, 2 or 4)
   const int32_t *query_start;  // [num_seqs + 1] packed query offsets, or nullptr
   float scale_log2;     // scale * log2(e)
+  // The divisors of a work item's set-up (split_tokens, num_kv_heads, items
+  // per plan entry, num_bins) as multiply-and-shift constants: at launch every
+  // resident wave runs that set-up at once on its compute unit's scalar unit,
+  // before its first tile can be requested.
+  FastDiv fd_split, fd_kv_heads, fd_entry, fd_bins;
 };
 
 // Row R (0 <= R < Q_s*g) of KV head kvh of a sequence whose query token 0 is
@@ -61,7 +67,7 @@ struct DecodeParams {
 // out and partials row in [tokens][Hq].
 __device__ __forceinline__ int64_t query_row(const DecodeParams &p, int first, int kvh, int R) {
   const int g = p.group;
-  return ((int64_t)first + R / g) * p.num_q_heads + kvh * g + R % g;
+  return ((int64_t)first + (R >> p.group_shift)) * p.num_q_heads + kvh * g + (R & (g - 1));
 }
 
 // Token ranges of the rows a workgroup handles. Query token i of the sequence
@@ -82,14 +88,14 @@ struct RowRanges {
   __device__ __forceinline__ bool needs_mask(int tb) const {
     return tb < lo_max || tb + kBlock - 1 > hi_min;
   }
-  // Rows [R0, R0 + nrows) with g query heads per KV head.
-  __device__ __forceinline__ static RowRanges make(int L, int Q, int W, int g, int R0, int nrows,
+  // Rows [R0, R0 + nrows) with 2^gs query heads per KV head.
+  __device__ __forceinline__ static RowRanges make(int L, int Q, int W, int gs, int R0, int nrows,
                                                   int first) {
     RowRanges r;
     r.q0 = L - Q;
     r.window = W;
     r.first = first;
-    const int i0 = R0 / g, i1 = (R0 + nrows - 1) / g;
+    const int i0 = R0 >> gs, i1 = (R0 + nrows - 1) >> gs;
     r.ulo = r.lo(i0);
     r.uhi = r.hi(i1);
     r.lo_max = r.lo(i1);
@@ -853,7 +859,7 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
   // This lane's S row: row R0 + c (padding rows beyond nrows keep zero q and
   // the group's token range).
   const bool row_ok = c < G && c < nrows;
-  const int qi = (R0 + c) / p.group;
+  const int qi = (R0 + c) >> p.group_shift;
   const int lo = row_ok ? rr.lo(qi) : rr.ulo, hi = row_ok ? rr.hi(qi) : rr.uhi;
   const int64_t qrow = row_ok ? query_row(p, rr.first, kvh, R0 + c) : 0;
   float qs = 0.f;
@@ -1094,7 +1100,7 @@ __device__ __forceinline__ void wave_pass_valu(const DecodeParams &p, int s, int
   int lo[G], hi[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int qi = (R0 + h) / p.group;
+    const int qi = (R0 + h) >> p.group_shift;
     lo[h] = h < nrows ? rr.lo(qi) : rr.ulo;
     hi[h] = h < nrows ? rr.hi(qi) : rr.uhi;
   }
@@ -1197,8 +1203,10 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
                                               int kvh, int R0, int R_end, int rw, int group,
                                               int lane, int wave, float (&sm_m)[NW][G],
                                               float (&sm_l)[NW][G], float (&sm_acc)[NW][G][D]) {
-  const int tw = NW / rw;                     // waves per row group
-  const int rg = wave / tw, tp = wave % tw;   // this wave's row group and tile share
+  // rw and NW are powers of two: tw = NW / rw waves per row group.
+  const int tws = __builtin_ctz(NW) - __builtin_ctz(rw);
+  const int tw = 1 << tws;
+  const int rg = wave >> tws, tp = wave & (tw - 1);  // this wave's row group and tile share
   const int W = p.window;
   // Context length, clamped so that no read leaves the table or the pool.
   const int lmax = (int)min((int64_t)p.max_context_len, (int64_t)p.max_blocks_per_seq * kBlock);
@@ -1213,7 +1221,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   };
   const int L = group > 0 ? max(0, min(p.context_lens[s_rg], lmax)) : len;
   const int base = split_base(L, Q, W);
-  const bool has_split = Q > 0 && j < splits_of(L, Q, W, p.split_tokens);
+  const bool has_split = Q > 0 && j < splits_of(L, Q, W, p.fd_split);
   const int t0 = base + j * p.split_tokens;  // a multiple of 16
   const int t1 = min(t0 + p.split_tokens, L);
   const int b0 = t0 / kBlock;
@@ -1223,11 +1231,11 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
   RowRanges rr{};
   int wb0 = 0, wb1 = 0;
   if (nrows > 0) {
-    rr = RowRanges::make(L, Q, W, p.group, Rg, nrows, qsp.first);
+    rr = RowRanges::make(L, Q, W, p.group_shift, Rg, nrows, qsp.first);
     const int ta = max(t0, rr.ulo), tz = min(t1 - 1, rr.uhi);
     if (tz >= ta) {
       const int first = (ta - t0) / kBlock, count = (tz - t0) / kBlock - first + 1;
-      const int per = (count + tw - 1) / tw;
+      const int per = (count + tw - 1) >> tws;
       wb0 = first + min(count, tp * per);
       wb1 = first + min(count, tp * per + per);
     }
@@ -1252,7 +1260,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
           uhi = t1s - 1;
         }
       } else if (has_split && all > 0) {
-        const RowRanges ru = RowRanges::make(L, Q, W, p.group, R0, all, qsp.first);
+        const RowRanges ru = RowRanges::make(L, Q, W, p.group_shift, R0, all, qsp.first);
         ulo = max(t0, ru.ulo);
         uhi = min(t1 - 1, ru.uhi);
         if (uhi >= ulo) {
@@ -1293,7 +1301,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     if (group == 0) return has_split ? rows_of(g) : 0;
     if (g >= group || s + g >= p.num_seqs) return 0;
     const int Lg = max(0, min(p.context_lens[s + g], lmax));
-    return j < splits_of(Lg, Q, W, p.split_tokens) ? rows_of(g) : 0;
+    return j < splits_of(Lg, Q, W, p.fd_split) ? rows_of(g) : 0;
   };
   // The row threads also leave each row's partials index in sm_row (-1: the
   // row has no split here), so that the dims loop below needs no table reads
@@ -1361,7 +1369,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
 // for KV head kvh (and, uniform Q, its row set), or a group entry. Contains
 // workgroup barriers; every thread of the workgroup calls it with the same k.
 template <int QT, int CT, int D, int G, int NW>
-__device__ __forceinline__ void decode_item(const DecodeParams &p, int k, int per_entry,
+__device__ __forceinline__ void decode_item(const DecodeParams &p, int k,
                                             float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                             float (&sm_acc)[NW][G][D]) {
   const bool packed = p.query_start != nullptr;
@@ -1370,10 +1378,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int k, int pe
   // Wave index as a scalar, so that per-wave ranges and loop counters stay in
   // SGPRs and the tile loop runs without exec masking.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int e = k % per_entry;
-  const int kvh = e % p.num_kv_heads;
-  const int packed_entry = p.sched[kSchedHeader + 2 * (k / per_entry)];
-  const int word1 = p.sched[kSchedHeader + 2 * (k / per_entry) + 1];
+  // k = entry * per_entry + e, e = set * Hkv + kvh (per_entry items per entry).
+  const int ent = p.fd_entry.div(k);
+  const int e = k - ent * (int)p.fd_entry.d;
+  const int kvh = p.fd_kv_heads.mod(e);
+  const int packed_entry = p.sched[kSchedHeader + 2 * ent];
+  const int word1 = p.sched[kSchedHeader + 2 * ent + 1];
   // The sequence index is clamped so that no entry can send a read out of
   // bounds; process_split ignores a split index past a sequence's end.
   const int s = min((int)((uint32_t)packed_entry >> 16), p.num_seqs - 1);
@@ -1383,7 +1393,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams &p, int k, int pe
     // entry (made only with one row group per KV head).
     const int group = word1 < 0 ? min(-word1, NW) : 0;
     const int rows = p.num_query_tokens * p.group;
-    const int R0 = (e / p.num_kv_heads) * p.rw * G;
+    const int R0 = p.fd_kv_heads.div(e) * p.rw * G;
     process_split<QT, CT, D, G, NW>(p, s, max(word1, 0), j, kvh, R0, rows,
                                     group > 0 ? NW : p.rw, group, lane, wave, sm_m, sm_l,
                                     sm_acc);
@@ -1448,19 +1458,24 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams &p) {
   // A plan made with group entries needs uniform query counts, every
   // sequence's rows in one row group (Q*g <= G), and a wave per member.
   static_assert(NW >= PA_MAX_GROUP_MEMBERS, "a group entry takes one wave per member");
-  const bool plan_ok = p.sched[1] == p.split_tokens && p.sched[2] == p.num_seqs &&
-                       p.sched[3] == lmax && p.sched[4] == p.num_query_tokens &&
-                       p.sched[5] == p.window && p.sched[7] == (packed ? p.group : 0) &&
-                       (p.sched[6] <= 1 || (!packed && p.num_query_tokens * p.group <= G));
-  const int n_items = plan_ok ? p.sched[0] * per_entry : 0;
+  // The header's words are read together and compared without short
+  // circuits, so that no read waits for the one before it.
+  int hd[kSchedHeader];
+#pragma unroll
+  for (int i = 0; i < kSchedHeader; ++i) hd[i] = p.sched[i];
+  const bool plan_ok = (hd[1] == p.split_tokens) & (hd[2] == p.num_seqs) & (hd[3] == lmax) &
+                       (hd[4] == p.num_query_tokens) & (hd[5] == p.window) &
+                       (hd[7] == (packed ? p.group : 0)) &
+                       ((hd[6] <= 1) | (!packed & (p.num_query_tokens * p.group <= G)));
+  const int n_items = plan_ok ? hd[0] * per_entry : 0;
   const int w = blockIdx.x;
   const int nb = p.num_bins;
   // Group entries keep the list order: the entries of the groups that share
   // one prompt's blocks follow each other and run side by side.
-  const bool dealt = p.sched[6] <= 1 && w < nb * p.bin_wgs;
-  const int64_t k = dealt ? bin_item(w % nb, w / nb, nb) : (int64_t)w;
+  const bool dealt = hd[6] <= 1 && w < nb * p.bin_wgs;
+  const int64_t k = dealt ? bin_item(p.fd_bins.mod(w), p.fd_bins.div(w), nb) : (int64_t)w;
   if (k >= n_items) return;
-  decode_item<QT, CT, D, G, NW>(p, (int)k, per_entry, sm_m, sm_l, sm_acc);
+  decode_item<QT, CT, D, G, NW>(p, (int)k, sm_m, sm_l, sm_acc);
 }
 
 // Launch helper instantiated per (q dtype, cache dtype) in the decode_*.hip units.
@@ -1505,6 +1520,9 @@ hipError_t launch_decode(DecodeParams p, int64_t max_items, hipStream_t stream) 
   const int64_t w = std::max<int64_t>(1, std::min<int64_t>(per_cu, max_items / nb));
   p.num_bins = (int32_t)nb;
   p.bin_wgs = (int32_t)w;
+  p.fd_bins = FastDiv::make((uint32_t)nb);
+  p.fd_entry = FastDiv::make((uint32_t)(p.query_start != nullptr ? p.num_kv_heads
+                                                                  : p.num_kv_heads * p.head_groups));
   if (trace_level() > 0)
     trace("split kernel: %s engine, q %s, cache %s, D %d, %d rows per row group; %lld "
           "workgroups of %d waves (one per possible item), %lld bins x %lld dealt, %d resident "

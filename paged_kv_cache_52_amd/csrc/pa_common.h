@@ -175,6 +175,26 @@ constexpr int kStreamPolicy = 2;
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf, 1 for 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Division by a divisor fixed for a launch, as a multiply and a shift instead
+// of the long integer-division sequence (Granlund and Montgomery, "Division
+// by invariant integers using multiplication", PLDI 1994, theorem 4.2 with
+// N = 31): for 1 <= d < 2^31, l = ceil(log2 d) and m = ceil(2^(31+l) / d),
+// which fits 32 bits, floor(n / d) = floor(n * m / 2^(31+l)) for every
+// 0 <= n < 2^31. Built on the host, read by the kernels as launch arguments.
+struct FastDiv {
+  uint32_t d, m, s;  // divisor, multiplier, shift 31 + l
+  static FastDiv make(uint32_t d) {
+    uint32_t l = 0;
+    while (l < 31 && (1u << l) < d) ++l;
+    const uint64_t num = 1ull << (31 + l);
+    return FastDiv{d, (uint32_t)((num + d - 1) / d), 31 + l};
+  }
+  __host__ __device__ __forceinline__ int div(int n) const {  // 0 <= n < 2^31
+    return (int)(((uint64_t)(uint32_t)n * m) >> s);
+  }
+  __host__ __device__ __forceinline__ int mod(int n) const { return n - div(n) * (int)d; }
+};
+
 // ---------------------------------------------------------------------------
 // Split geometry of one sequence, shared by the host checks, the plan, the
 // split kernel and the reduce. A sequence of length L carries Q query tokens
@@ -195,6 +215,12 @@ __host__ __device__ inline int split_base(int L, int Q, int W) {
 // max(1, ceil((L - split_base) / T)).
 __host__ __device__ inline int splits_of(int L, int Q, int W, int T) {
   const int n = (L - split_base(L, Q, W) + T - 1) / T;
+  return n > 1 ? n : 1;
+}
+
+// splits_of with T as a FastDiv (L < 2^28, as the split-count bound ensures).
+__device__ __forceinline__ int splits_of(int L, int Q, int W, const FastDiv &T) {
+  const int n = T.div(L - split_base(L, Q, W) + (int)T.d - 1);
   return n > 1 ? n : 1;
 }
 
