@@ -849,7 +849,8 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
                                                float (&sm_m)[NW][G], float (&sm_l)[NW][G],
                                                float (&sm_acc)[NW][G][D], int sb0 = 0,
                                                int sb1 = 0, int ulo_wg = 0, int uhi_wg = -1,
-                                               int s_own = -1) {
+                                               int s_own = -1, int pre_staged = 0,
+                                               int pre_own = 0) {
   // Group entry (s_own >= 0, uniform): the workgroup stages sequence s's
   // blocks and this wave's rows belong to sequence s_own.
   const bool grouped = STAGED && s_own >= 0;
@@ -932,7 +933,10 @@ __device__ __forceinline__ void wave_pass_mfma(const DecodeParams &p, int s, int
         const int nl = c0 + lane;
         const bool lane_ok = nl < c1;
         int my_id = 0, own_id = 0;
-        if (lane_ok) {
+        if (kGroup && c0 == 0) {  // a group walk's first chunk: read with the lengths
+          my_id = lane_ok ? pre_staged : 0;
+          own_id = lane_ok ? pre_own : 0;
+        } else if (lane_ok) {
           my_id = p.block_tables[(int64_t)s * p.max_blocks_per_seq + b0 + nl];
           if (kGroup) own_id = p.block_tables[(int64_t)s_own * p.max_blocks_per_seq + b0 + nl];
         }
@@ -1219,6 +1223,18 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
     if (group > 0) return g < group ? min(G, Q * p.group) : 0;
     return min(G, R_end - (R0 + g * G));
   };
+  // A group entry (made only without a window) walks split j from block
+  // j * T / 16 whatever the lengths, so the first 64 table words of the
+  // staged sequence and of this wave's own are read before the lengths, in
+  // the same round trip (each read stays inside its table row).
+  int pre_staged = 0, pre_own = 0;
+  if (group > 0) {
+    const int col = j * (p.split_tokens / kBlock) + lane;
+    if (col < p.max_blocks_per_seq) {
+      pre_staged = p.block_tables[(int64_t)s * p.max_blocks_per_seq + col];
+      pre_own = p.block_tables[(int64_t)s_rg * p.max_blocks_per_seq + col];
+    }
+  }
   const int L = group > 0 ? max(0, min(p.context_lens[s_rg], lmax)) : len;
   const int base = split_base(L, Q, W);
   const bool has_split = Q > 0 && j < splits_of(L, Q, W, p.fd_split);
@@ -1270,7 +1286,7 @@ __device__ __forceinline__ void process_split(const DecodeParams &p, int s, int 
       }
       wave_pass_mfma<QT, CT, D, G, NW, 0, kStageable>(
           p, group > 0 ? s : s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave, sm_m, sm_l,
-          sm_acc, sb0, sb1, ulo, uhi, group > 0 ? s_rg : -1);
+          sm_acc, sb0, sb1, ulo, uhi, group > 0 ? s_rg : -1, pre_staged, pre_own);
     } else if (rw > 1)
       wave_pass_mfma<QT, CT, D, G, NW, 0>(p, s_rg, kvh, Rg, nrows, rr, b0, wb0, wb1, lane, wave,
                                           sm_m, sm_l, sm_acc);
