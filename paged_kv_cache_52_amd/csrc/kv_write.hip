@@ -20,14 +20,17 @@ __device__ __forceinline__ void kv_copy_thread(const WriteParams &p, int row_byt
   const int chunk = (int)(gid - row * cpr);
   const int64_t t = row / p.num_kv_heads;
   const int h = (int)(row - t * p.num_kv_heads);
+  // The source chunk is read with the slot, not after it (one round trip).
+  const int64_t src = row * row_bytes + chunk * 16;
+  const u32x4 kx = *(const u32x4 *)((const char *)p.k + src);
+  const u32x4 vx = *(const u32x4 *)((const char *)p.v + src);
   const int64_t slot = p.slot_mapping[t];
   if (slot < 0 || slot >= p.num_blocks * kBlock) return;
   const int64_t b = slot / kBlock;
   const int o = (int)(slot - b * kBlock);
   const int64_t dst = ((b * p.num_kv_heads + h) * kBlock + o) * row_bytes + chunk * 16;
-  const int64_t src = row * row_bytes + chunk * 16;
-  *(u32x4 *)((char *)p.k_cache + dst) = *(const u32x4 *)((const char *)p.k + src);
-  *(u32x4 *)((char *)p.v_cache + dst) = *(const u32x4 *)((const char *)p.v + src);
+  *(u32x4 *)((char *)p.k_cache + dst) = kx;
+  *(u32x4 *)((char *)p.v_cache + dst) = vx;
 }
 
 // OCP E4M3 code of x: the nearest value (ties to the even mantissa) among
@@ -48,15 +51,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | (uint32_t)(((e + 7) << 3) | (q - 8));
 }
 
-// INT8 / FP8 quantiser: a group of D/8 lanes owns one (token, head) row, 8
-// values per lane. absmax is combined across the group with DPP; the scale is
-// absmax / 127 (INT8) or absmax / 448 (FP8), the division by it is IEEE fp32
-// (correctly rounded), and both roundings are to nearest, ties to even.
-template <int CT, int IT, int D>
-__device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, int part,
-                                             uint8_t *dst, float *scale_dst, bool write_scale) {
-  constexpr int LPG = D / 8;
-  float x[8];
+// Lane `part`'s 8 values of source row src_row, widened to fp32.
+template <int IT, int D>
+__device__ __forceinline__ void load_row_part(const void *src, int64_t src_row, int part,
+                                              float (&x)[8]) {
   if constexpr (IT == PA_BF16) {
     const u32x4 w = *(const u32x4 *)((const uint16_t *)src + src_row * D + part * 8);
 #pragma unroll
@@ -74,6 +72,16 @@ __device__ __forceinline__ void quantise_row(const void *src, int64_t src_row, i
       x[4 + k] = __uint_as_float(w1[k]);
     }
   }
+}
+
+// INT8 / FP8 quantiser: a group of D/8 lanes owns one (token, head) row, 8
+// values per lane. absmax is combined across the group with DPP; the scale is
+// absmax / 127 (INT8) or absmax / 448 (FP8), the division by it is IEEE fp32
+// (correctly rounded), and both roundings are to nearest, ties to even.
+template <int CT, int D>
+__device__ __forceinline__ void quantise_row(const float (&x)[8], int part, uint8_t *dst,
+                                             float *scale_dst, bool write_scale) {
+  constexpr int LPG = D / 8;
   float a = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
@@ -109,15 +117,17 @@ __device__ __forceinline__ void kv_quant_thread(const WriteParams &p, int64_t gi
   const int part = (int)(gid % LPG);
   const int64_t t = row / p.num_kv_heads;
   const int h = (int)(row - t * p.num_kv_heads);
+  // The source values are read with the slot, not after it (one round trip).
+  float xk[8], xv[8];
+  load_row_part<IT, D>(p.k, row, part, xk);
+  load_row_part<IT, D>(p.v, row, part, xv);
   const int64_t slot = p.slot_mapping[t];
   if (slot < 0 || slot >= p.num_blocks * kBlock) return;  // same for the whole group
   const int64_t b = slot / kBlock;
   const int o = (int)(slot - b * kBlock);
   const int64_t srow = (b * p.num_kv_heads + h) * kBlock + o;  // scale index
-  quantise_row<CT, IT, D>(p.k, row, part, (uint8_t *)p.k_cache + srow * D, p.k_scale + srow,
-                          part == 0);
-  quantise_row<CT, IT, D>(p.v, row, part, (uint8_t *)p.v_cache + srow * D, p.v_scale + srow,
-                          part == 0);
+  quantise_row<CT, D>(xk, part, (uint8_t *)p.k_cache + srow * D, p.k_scale + srow, part == 0);
+  quantise_row<CT, D>(xv, part, (uint8_t *)p.v_cache + srow * D, p.v_scale + srow, part == 0);
 }
 
 // Write variants: 0 copies; 1..4 quantise to INT8 and 5..8 to FP8, each for
