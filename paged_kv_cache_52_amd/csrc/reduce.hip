@@ -11,6 +11,7 @@ constexpr int kReduceManySplits = 32;  // from this many splits, 4 waves share o
 constexpr int kReduceU = 4;            // splits whose acc rows are loaded together
 constexpr int kReduceRowsForFour = 16384;  // from this many rows (and at most kReduceU
                                            // splits), each wave reduces four
+constexpr int kReduceManyU = 16;  // many splits: acc rows loaded together per wave
 
 __device__ __forceinline__ float lane_value(float x, int j) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
@@ -128,13 +129,12 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_rows_kernel(const 
 // finds the maximum M of the split maxima (lane-parallel), then sums its
 // contiguous range of splits: lane j of a 64-split chunk turns split j's
 // (m_j, l_j) into w_j = exp(m_j - M) (0 for an empty split), and the chunk's
-// acc rows are added with those weights, four rows loaded at a time. The
+// acc rows are added with those weights, 16 rows loaded at a time. The
 // waves' sums meet in LDS. Rows as in reduce_rows_kernel; with packed queries
 // the row's sequence is found by a 64-ary search.
 template <int OT, int D>
 __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const ReduceParams p) {
   constexpr int DPL = D / kWave;  // dims per lane
-  constexpr int U = kReduceU;
   constexpr int WPH = kReduceWaves;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -173,25 +173,19 @@ __global__ __launch_bounds__(kReduceWaves *kWave) void reduce_kernel(const Reduc
     den += group_sum<kWave>(w * lj);
     const int cnt = min(kWave, j1 - base);
     const float *arow = p.part_acc + (row0 + base) * D + lane;
-    int i = 0;
-    for (; i + U <= cnt; i += U) {
-      float r[U][DPL];
+    // kReduceManyU acc rows requested at a time (the last group masked).
+    for (int i = 0; i < cnt; i += kReduceManyU) {
+      float r[kReduceManyU][DPL];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < kReduceManyU; ++u)
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) r[u][k] = arow[(i + u) * D + k * kWave];
+        for (int k = 0; k < DPL; ++k) r[u][k] = i + u < cnt ? arow[(i + u) * D + k * kWave] : 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wu = lane_value(w, i + u);
+      for (int u = 0; u < kReduceManyU; ++u) {
+        const float wu = i + u < cnt ? lane_value(w, (i + u) & (kWave - 1)) : 0.f;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wu, wu != 0.f ? r[u][k] : 0.f, acc[k]);
       }
-    }
-    for (; i < cnt; ++i) {
-      const float wi = lane_value(w, i);
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wi, wi != 0.f ? arow[i * D + k * kWave] : 0.f,
-                                                  acc[k]);
     }
   }
 
