@@ -36,6 +36,10 @@
 namespace pa {
 
 constexpr int kMaxTileBuckets = PA_MAX_SPLIT_TOKENS / kBlock;  // tile counts 1..256
+// Grouped plans of one chunk take a faster path when no sequence has more
+// full splits than this (one bit of a mask each).
+constexpr int kJoinSplits = 16;
+static_assert(kJoinSplits <= 32, "one 32-bit mask per sequence");
 
 __device__ __forceinline__ int clamp_len(const PlanParams &p, int s) {
   return max(0, min(p.context_lens[s], p.max_len));
@@ -146,13 +150,18 @@ static __device__ void plan_workgroup(const PlanParams &p) {
   __shared__ int chunk_len[kPlanThreads];
   __shared__ int chunk_per[kPlanThreads];    // entries per split of each sequence
   __shared__ int chunk_splits[kPlanThreads]; // splits of each sequence
+  __shared__ uint32_t join_mask[kPlanThreads];  // grouping, one chunk: see below
+  __shared__ int many_full;  // some sequence has more than kJoinSplits full splits
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const bool packed = p.query_start != nullptr;
 
   for (int i = tid; i <= kMaxTileBuckets; i += kPlanThreads) bucket[i] = 0;
-  if (tid == 0) carry = 0;
+  if (tid == 0) {
+    carry = 0;
+    many_full = 0;
+  }
   __syncthreads();
 
   // Pass 1: the full splits. Per chunk of kPlanThreads sequences, a
@@ -166,6 +175,7 @@ static __device__ void plan_workgroup(const PlanParams &p) {
     SeqPlan sp{0, 0, 1, 0};
     if (valid) sp = seq_plan(p, s);
     const int f = (sp.splits - 1) * sp.per_split;
+    if (f > kJoinSplits) many_full = 1;
     int incl = f;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -196,6 +206,69 @@ static __device__ void plan_workgroup(const PlanParams &p) {
       }
       __syncthreads();
       if (tid == 0) carry += total;
+      __syncthreads();
+    } else if (p.num_seqs <= kPlanThreads && !many_full) {
+      // Grouping with the whole batch in one chunk and at most kJoinSplits
+      // full splits per sequence: the entries and their order are those of
+      // the general loop below, found with one round of table reads. Thread s
+      // reads the first table word of each of its full splits and of its
+      // predecessor's same split (all at once), and keeps the splits on which
+      // the two share a block as a bit mask in LDS. Split j of s is listed
+      // unless s joins its predecessor inside the aligned run of M; a listed
+      // split counts the following sequences of the run that join one after
+      // another. One workgroup scan places every sequence's listed splits.
+      const int M = p.group_members;
+      const int step = p.split_tokens / kBlock;  // blocks per split (no window: base 0)
+      const int fp = tid > 0 ? chunk_splits[tid - 1] - 1 : 0;  // predecessor's full splits
+      int own[kJoinSplits], prev[kJoinSplits];
+#pragma unroll
+      for (int j = 0; j < kJoinSplits; ++j) {
+        own[j] = 0;
+        prev[j] = -1;
+        if (j < f) {
+          own[j] = p.block_tables[(int64_t)s * p.max_blocks_per_seq + j * step];
+          if (j < fp) prev[j] = p.block_tables[(int64_t)(s - 1) * p.max_blocks_per_seq + j * step];
+        }
+      }
+      uint32_t joined = 0u;
+#pragma unroll
+      for (int j = 0; j < kJoinSplits; ++j)
+        if (j < f && j < fp && own[j] == prev[j]) joined |= 1u << j;
+      join_mask[tid] = joined;
+      __syncthreads();
+      const int pos = s % M;
+      const uint32_t full = f > 0 ? (~0u >> (32 - f)) : 0u;
+      const uint32_t listed = pos > 0 ? full & ~joined : full;
+      uint32_t follow[PA_MAX_GROUP_MEMBERS];  // follow[c]: splits that s + c joins (c >= 1)
+#pragma unroll
+      for (int c = 1; c < PA_MAX_GROUP_MEMBERS; ++c)
+        follow[c] = pos + c < M && s + c < p.num_seqs ? join_mask[tid + c] : 0u;
+      const int nk = __builtin_popcount(listed);
+      int incl_k = nk;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl_k, o);
+        if (lane >= o) incl_k += y;
+      }
+      if (lane == kWave - 1) wave_sum[wave] = incl_k;
+      __syncthreads();
+      int before_k = 0, total_k = 0;
+#pragma unroll
+      for (int w = 0; w < kPlanThreads / kWave; ++w) {
+        if (w < wave) before_k += wave_sum[w];
+        total_k += wave_sum[w];
+      }
+      int idx = carry + before_k + incl_k - nk;
+      for (uint32_t m = listed; m != 0u; m &= m - 1u) {
+        const int j = __builtin_ctz(m);
+        int cnt = 1;
+#pragma unroll
+        for (int c = 1; c < PA_MAX_GROUP_MEMBERS; ++c)
+          if (cnt == c && ((follow[c] >> j) & 1u)) ++cnt;
+        put_entry(p, idx++, entry_word(s, j), cnt > 1 ? -cnt : sp.L);
+      }
+      __syncthreads();
+      if (tid == 0) carry += total_k;
       __syncthreads();
     } else {
       // Grouping (one entry per split, no packed queries): an entry (s, j)

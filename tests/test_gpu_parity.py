@@ -1090,7 +1090,10 @@ def _expected_group_entries(tables, lens, T, M):
     return out
 
 
-@pytest.mark.parametrize("T,M", [(64, 2), (64, 4), (512, 4), (16, 3)])
+# Lengths reach 2600 tokens: at T = 160 the longest sequence has 16 full
+# splits, at T = 144 it has 18 (the plan's one-round path takes at most 16).
+@pytest.mark.parametrize("T,M", [(64, 2), (64, 4), (512, 4), (16, 3), (144, 4), (160, 4),
+                                 (160, 3), (1024, 4)])
 def test_grouped_plan(T, M):
     """Group entries cover every full split exactly once, only join
     sequences whose split starts on the same block, and keep the list order."""
