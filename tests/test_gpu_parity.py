@@ -589,10 +589,14 @@ def test_sequence_indices_past_32767(dtype, D):
         _check_out(out32, ref, _tol(b), f"40000 sequences T={T}")
 
 
-@pytest.mark.parametrize("T", [16, 512])
+# At T = 16 and 48 the longest sequence has 63 and 21 full splits (all
+# threads list the entries together), at T = 64 and 512 15 and 1 (each
+# sequence's thread lists its own).
+@pytest.mark.parametrize("T", [16, 48, 64, 512])
 def test_plan_lists_every_split_once(T):
     """The plan kernel's work list holds each (sequence, split) exactly once:
-    full splits first, then last splits ordered by decreasing tile count."""
+    full splits first, sequence by sequence in split order, then last splits
+    ordered by decreasing tile count."""
     print(f"[case] plan T={T}", flush=True)
     lens = [0, 1, 15, 16, 17, 511, 512, 513, 1024, 31, 2, 700]
     b = workloads.make_batch("llama8b_bf16", 151, "cpu", num_seqs=len(lens),
@@ -612,6 +616,7 @@ def test_plan_lists_every_split_once(T):
     assert sorted(entries) == sorted((s, j) for s in range(len(lens)) for j in range(nsplit[s]))
     n_full = n - len(lens)
     assert all(j < nsplit[s] - 1 for s, j in entries[:n_full])
+    assert entries[:n_full] == sorted(entries[:n_full])
     tiles = [max(1, -(-(lens[s] - j * T) // 16)) if lens[s] else 1 for s, j in entries[n_full:]]
     assert tiles == sorted(tiles, reverse=True)
 
