@@ -1136,6 +1136,35 @@ def test_grouped_plan(T, M):
                                    for j in range(max(1, -(-L[s] // T))))
 
 
+@pytest.mark.parametrize("T,M", [(512, 4), (1024, 3), (64, 3)])
+def test_grouped_plan_across_chunks(T, M):
+    """A grouped plan of 320 sequences (40 prompts x 8 samples) spans two
+    256-sequence chunks of the plan workgroup. Sequence 256 is given the
+    prefix blocks of sequence 255 (another prompt's), so with runs of 3 a group
+    straddles the chunk boundary. The entries match the independent listing."""
+    print(f"[case] grouped plan across chunks T={T} M={M}", flush=True)
+    b = workloads.make_batch("shared_prefix_bf16", 252, "cpu", groups=40, suffix_max=600)
+    assert b.num_seqs == 320
+    t = b.block_tables.clone()
+    t[256, :125] = t[255, :125]  # the 2000-token prefix: 125 blocks
+    b.block_tables = t
+    g = _to(b, "cuda")
+    mb = g.block_tables.shape[1]
+    plan = pa().paged_attn_plan(g.context_lens, mb, max_context_len=g.max_context_len,
+                                split_tokens=T, block_tables=g.block_tables, group_members=M)
+    torch.cuda.synchronize()
+    sched = plan.sched.cpu().numpy()
+    lmax = min(g.max_context_len, 16 * mb)
+    L = [min(int(x), lmax) for x in b.context_lens]
+    full = _expected_group_entries(b.block_tables.numpy(), L, T, M)
+    n = len(full) + len(L)
+    assert list(sched[:8]) == [n, T, len(L), lmax, 1, 0, M, 0]
+    got = list(zip(sched[8:8 + 2 * len(full):2].tolist(), sched[9:9 + 2 * len(full):2].tolist()))
+    assert got == full
+    if M == 3:
+        assert any(w1 < 0 and (w0 >> 16) < 256 <= (w0 >> 16) - w1 - 1 for w0, w1 in got)
+
+
 SCALE_CASES = [0.0, -0.0884, 3.0]
 
 
